@@ -1,0 +1,261 @@
+"""Workload shapes and the seeded recipe of every input tensor.
+
+Every tensor has its own stream, keyed by (seed + owner rank, tag). A tensor
+owned by rank s (an activation shard, an incoming partial from peer s) uses
+seed + s; the local rank's weights use seed + rank. The default seed is 42.
+
+Arrays come back as raw storage bits: uint16 for bf16, uint8 for OCP E4M3FN.
+Nothing here computes any part of the method.
+"""
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+from .gen import stream_key, uniform_bf16, normal_bf16, normal_e4m3
+
+SEED = 42
+
+
+# --------------------------------------------------------------------------
+# staged all-gather GEMM: D = alpha * A * B^T + beta * C, A in P row slices
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class AgCase:
+    name: str
+    M: int
+    N: int
+    K: int
+    P: int
+    rank: int = 0
+    dtype: str = "bf16"          # operand type of A and B: "bf16" or "e4m3"
+    b_layout: str = "nk"         # "nk": B is (N, K) row-major; "kn": (K, N)
+    dist: str = "u11"            # "u11": U(-1,1); "n05": clip(0.5 N(0,1), +-448)
+    c_dist: str = "u11"          # "u11" or "n01"
+    alpha: float = 1.0
+    beta: float = 1.0
+    swiglu: bool = False         # epilogue silu(u) * v over paired column halves
+
+    @property
+    def m(self):
+        return self.M // self.P
+
+    @property
+    def flop(self):
+        return 2.0 * self.M * self.N * self.K
+
+
+def ag_inputs(case: AgCase, seed: int = SEED):
+    """Return dict(a_slices=[P x (m, K)], b=(N,K) or (K,N), c=(M, N out) or None)."""
+    m, K, N = case.m, case.K, case.N
+
+    def operand(key, shape):
+        if case.dist == "u11":
+            assert case.dtype == "bf16"
+            return uniform_bf16(key, shape, -1.0, 1.0)
+        if case.dist == "n05":
+            if case.dtype == "e4m3":
+                return normal_e4m3(key, shape, scale=0.5, clip=448.0)
+            return normal_bf16(key, shape, 0.0, 0.5)
+        if case.dist == "n002":
+            assert case.dtype == "bf16"
+            return normal_bf16(key, shape, 0.0, 0.02)
+        if case.dist == "n01":
+            return normal_bf16(key, shape, 0.0, 1.0)
+        raise ValueError(case.dist)
+
+    a_slices = [operand(stream_key(seed + s, "ag.a"), (m, K)) for s in range(case.P)]
+    bshape = (N, K) if case.b_layout == "nk" else (K, N)
+    b = operand(stream_key(seed + case.rank, "ag.b"), bshape)
+    n_out = N // 2 if case.swiglu else N
+    c = None
+    if case.beta != 0.0:
+        ckey = stream_key(seed + case.rank, "ag.c")
+        if case.c_dist == "u11":
+            c = uniform_bf16(ckey, (case.M, n_out), -1.0, 1.0)
+        else:
+            c = normal_bf16(ckey, (case.M, n_out), 0.0, 1.0)
+    return dict(a_slices=a_slices, b=b, c=c)
+
+
+# --------------------------------------------------------------------------
+# staged GEMM + reduce-scatter dual
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class RsCase:
+    name: str
+    M: int          # rows of the full partial product (P blocks of M/P)
+    N: int
+    K: int          # local K shard
+    P: int
+    rank: int = 0
+    b_layout: str = "nk"
+    std: float = 0.02
+    incoming: bool = True        # seeded N(0,1) partials from the P-1 peers
+    alpha: float = 1.0
+
+    @property
+    def m(self):
+        return self.M // self.P
+
+    @property
+    def flop(self):
+        return 2.0 * self.M * self.N * self.K
+
+
+def rs_inputs(case: RsCase, seed: int = SEED):
+    """Return dict(a=(M,K), b=(N,K)|(K,N), incoming=[P entries, None at rank])."""
+    a = normal_bf16(stream_key(seed + case.rank, "rs.a"), (case.M, case.K), 0.0, case.std)
+    bshape = (case.N, case.K) if case.b_layout == "nk" else (case.K, case.N)
+    b = normal_bf16(stream_key(seed + case.rank, "rs.b"), bshape, 0.0, case.std)
+    incoming = [None] * case.P
+    if case.incoming:
+        for j in range(case.P):
+            if j != case.rank:
+                incoming[j] = normal_bf16(stream_key(seed + j, "rs.in"), (case.m, case.N), 0.0, 1.0)
+    return dict(a=a, b=b, incoming=incoming)
+
+
+# --------------------------------------------------------------------------
+# per-token-slot FFN (dispatched input [P*B, L, D], L = T/P slots)
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class FfnCase:
+    name: str
+    B: int
+    T: int
+    D: int
+    k: int
+    P: int
+    rank: int = 0
+    affine: bool = False         # LN gamma ~ U(0.5,1.5), beta ~ U(-0.5,0.5); else 1, 0
+    big_bias: bool = False       # biases ~ U(-1,1) instead of the He bound
+    eps: float = 1e-5
+
+    @property
+    def L(self):
+        return self.T // self.P
+
+    @property
+    def H(self):
+        return self.D * self.k
+
+    @property
+    def PB(self):
+        return self.P * self.B
+
+    @property
+    def flop(self):
+        rows = self.PB * self.L
+        return 2.0 * rows * self.D * 2 * self.H + 2.0 * rows * self.H * self.D
+
+
+def he_bound(fan_in):
+    """He-uniform bound sqrt(6 / fan_in) (He et al., 2015, uniform variant)."""
+    return math.sqrt(6.0 / fan_in)
+
+
+def ffn_inputs(case: FfnCase, seed: int = SEED):
+    s = seed + case.rank
+    L, D, H, PB = case.L, case.D, case.H, case.PB
+    b1_ = he_bound(D)
+    bo_ = he_bound(H)
+    x = normal_bf16(stream_key(s, "ffn.x"), (PB, L, D), 0.0, 1.0)
+    w1 = uniform_bf16(stream_key(s, "ffn.w1"), (L, D, 2 * H), -b1_, b1_)
+    wout = uniform_bf16(stream_key(s, "ffn.wout"), (L, H, D), -bo_, bo_)
+    if case.big_bias:
+        b1 = uniform_bf16(stream_key(s, "ffn.b1"), (L, 2 * H), -1.0, 1.0)
+        bout = uniform_bf16(stream_key(s, "ffn.bout"), (L, D), -1.0, 1.0)
+    else:
+        b1 = uniform_bf16(stream_key(s, "ffn.b1"), (L, 2 * H), -b1_, b1_)
+        bout = uniform_bf16(stream_key(s, "ffn.bout"), (L, D), -bo_, bo_)
+    if case.affine:
+        gx = uniform_bf16(stream_key(s, "ffn.gx"), (H,), 0.5, 1.5)
+        bx = uniform_bf16(stream_key(s, "ffn.bx"), (H,), -0.5, 0.5)
+        gg = uniform_bf16(stream_key(s, "ffn.gg"), (H,), 0.5, 1.5)
+        bg = uniform_bf16(stream_key(s, "ffn.bg"), (H,), -0.5, 0.5)
+    else:
+        one = np.full((H,), 0x3F80, dtype=np.uint16)     # bf16 1.0
+        zero = np.zeros((H,), dtype=np.uint16)
+        gx, bx, gg, bg = one, zero, one.copy(), zero.copy()
+    return dict(x=x, w1=w1, b1=b1, wout=wout, bout=bout, gx=gx, bx=bx, gg=gg, bg=bg)
+
+
+def permute_sources(B, T, D, P, seed: int = SEED, dtype="bf16"):
+    """Per-rank layer inputs [B, T, D] for ranks 0..P-1 (rank s uses seed + s)."""
+    if dtype == "bf16":
+        return [normal_bf16(stream_key(seed + s, "perm.in"), (B, T, D)) for s in range(P)]
+    if dtype == "u8":
+        from .gen import _raw
+        out = []
+        for s in range(P):
+            n = B * T * D
+            out.append((_raw(stream_key(seed + s, "perm.in8"), 0, n) & np.uint64(0xFF))
+                       .astype(np.uint8).reshape(B, T, D))
+        return out
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# SwiGLU tensor-parallel block: AG GEMM with silu(u)*v epilogue, then RS GEMM
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class SwigluCase:
+    name: str
+    S: int          # tokens per sequence shard
+    D: int          # model dim
+    F: int          # local hidden (w1 and w3 column shards are F wide each)
+    P: int
+    rank: int = 0
+    std: float = 0.02
+
+    @property
+    def M(self):
+        return self.S * self.P
+
+    @property
+    def flop(self):
+        return 2.0 * self.M * self.D * 2 * self.F + 2.0 * self.M * self.F * self.D
+
+
+def swiglu_inputs(case: SwigluCase, seed: int = SEED):
+    """x shards [P x (S, D)] N(0,1); w13 (D, 2F) = [w1 | w3]; w2 (F, D)."""
+    xs = [normal_bf16(stream_key(seed + s, "sw.x"), (case.S, case.D)) for s in range(case.P)]
+    w13 = normal_bf16(stream_key(seed + case.rank, "sw.w13"), (case.D, 2 * case.F), 0.0, case.std)
+    w2 = normal_bf16(stream_key(seed + case.rank, "sw.w2"), (case.F, case.D), 0.0, case.std)
+    return dict(x_shards=xs, w13=w13, w2=w2)
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size, and small parity variants with ragged tails
+# --------------------------------------------------------------------------
+C1 = AgCase("ag_bf16_p2_256x256x512", M=256, N=256, K=512, P=2, dtype="bf16",
+            dist="u11", c_dist="u11", alpha=1.0, beta=1.0)
+C2 = AgCase("ag_e4m3_p8_8192x1024x8192", M=8192, N=1024, K=8192, P=8, dtype="e4m3",
+            dist="n05", c_dist="n01", alpha=1.0, beta=1.0)
+C2_BETA0 = AgCase("ag_e4m3_p8_8192x1024x8192_beta0", M=8192, N=1024, K=8192, P=8,
+                  dtype="e4m3", dist="n05", c_dist="n01", alpha=1.0, beta=0.0)
+C3 = RsCase("rs_bf16_p8_8192x8192x3584", M=8192, N=8192, K=3584, P=8)
+C4 = FfnCase("ffn_slot_b512_t64_d1280_k6_p8", B=512, T=64, D=1280, k=6, P=8)
+C5 = SwigluCase("swiglu_p8_s1024_d4096_f1792", S=1024, D=4096, F=1792, P=8)
+
+SMALL_AG = [
+    AgCase("ag_bf16_p2_small", M=2 * 200, N=328, K=520, P=2, dist="u11"),
+    AgCase("ag_bf16_p4_kn_small", M=4 * 136, N=264, K=200, P=4, b_layout="kn", dist="u11",
+           alpha=0.75, beta=-0.5),
+    AgCase("ag_e4m3_p4_small", M=4 * 96, N=200, K=544, P=4, dtype="e4m3", dist="n05",
+           c_dist="n01", rank=1),
+    AgCase("ag_e4m3_p2_beta0_small", M=2 * 130, N=136, K=256, P=2, dtype="e4m3", dist="n05",
+           beta=0.0),
+    AgCase("ag_bf16_p8_swiglu_small", M=8 * 40, N=2 * 136, K=264, P=8, b_layout="kn",
+           dist="n05", beta=0.0, swiglu=True, rank=3),
+]
+SMALL_RS = [
+    RsCase("rs_bf16_p4_small", M=4 * 136, N=264, K=328, P=4, rank=2, std=0.5),
+    RsCase("rs_bf16_p2_kn_small", M=2 * 100, N=200, K=136, P=2, rank=0, b_layout="kn", std=0.5),
+]
+SMALL_FFN = [
+    FfnCase("ffn_public_b4_t16_d128_k2_p2", B=4, T=16, D=128, k=2, P=2),
+    FfnCase("ffn_small_affine", B=6, T=16, D=136, k=3, P=4, affine=True, big_bias=True, rank=1),
+]
+SMALL_SWIGLU = [SwigluCase("swiglu_small", S=72, D=264, F=136, P=4, rank=1, std=0.1)]

@@ -1,0 +1,76 @@
+"""Pins of the oracle's format decoders and of the seeded generator (CPU)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import gen
+
+
+def test_e4m3_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+    (0x38, 1.0), (0x7E, 448.0), (0xFE, -448.0), (0xB8, -1.0), (0x3C, 1.5)])
+def test_e4m3_spec_values(code, value):
+    # OCP 8-bit floating point spec values for E4M3
+    assert oracle.decode_e4m3(np.array([code], np.uint8))[0] == value
+
+
+def test_e4m3_nan_and_monotone():
+    d = oracle.decode_e4m3(np.arange(256, dtype=np.uint8))
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.isfinite(d[:0x7F]).all()
+    assert np.all(np.diff(d[:0x7F]) > 0)
+
+
+def test_bf16_all_codes_match_torch():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode_bf16(codes)
+    ref = torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+def test_encoders_are_rne_like_torch():
+    rng = np.random.default_rng(0)
+    f = (rng.standard_normal(100000) * 3).astype(np.float32).astype(np.float64)
+    ties = (np.arange(1, 2000) * 2 + 1) * 2.0 ** -9 + 1.0   # bf16 midpoints in [1, 2)
+    f = np.concatenate([f, ties, -ties, [0.0]])
+    tb = torch.from_numpy(f.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gen.encode_bf16(f), tb)
+    small = f[np.abs(f) <= 448]
+    te = torch.from_numpy(small.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(gen.encode_e4m3(small), te)
+    assert gen.encode_e4m3(np.array([1000.0, -1e6]))[0] == 0x7E      # saturates to 448
+
+
+def test_encode_decode_round_trip():
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]
+    v = oracle.decode_e4m3(codes)
+    back = gen.encode_e4m3(v)
+    # +0 and -0 both decode to 0.0; everything else round-trips exactly
+    assert np.array_equal(back[codes != 0x80], codes[codes != 0x80])
+    b = np.arange(0x3000, 0x5000, dtype=np.uint16)
+    assert np.array_equal(gen.encode_bf16(oracle.decode_bf16(b)), b)
+
+
+def test_generator_is_counter_based_and_seeded():
+    k = gen.stream_key(42, "x")
+    big = gen.normal(k, (1 << 22) + 7)
+    assert np.array_equal(gen.normal(k, 1001), big[:1001])      # prefix stable across chunks
+    assert not np.array_equal(gen.normal(gen.stream_key(43, "x"), 100), big[:100])
+    assert not np.array_equal(gen.normal(gen.stream_key(42, "y"), 100), big[:100])
+    assert abs(big.mean()) < 3e-3 and abs(big.std() - 1) < 3e-3
+    u = gen.uniform(k, 1 << 20, -1.0, 1.0)
+    assert u.min() >= -1 and u.max() < 1 and abs(u.mean()) < 3e-3
+    # SplitMix64 reference value: first output for state 0 (published test vector)
+    assert int(gen._raw(np.uint64(0), 0, 1)[0]) == 0xE220A8397B1DCDAF

@@ -1,0 +1,184 @@
+"""Pins of the oracle's staged all-gather GEMM and reduce-scatter dual (CPU).
+
+Each pin checks the oracle against something other than itself: scalar
+brute force, closed forms, the unsharded product of the full matrices, or
+mathematical invariants of the staging.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gen
+
+
+def bf16_bits(x):
+    return gen.encode_bf16(np.asarray(x, dtype=np.float64))
+
+
+def rand_int_bf16(rng, shape, lo=-2, hi=2):
+    """Small integers: exactly representable, so every sum below is exact."""
+    return bf16_bits(rng.integers(lo, hi + 1, size=shape))
+
+
+def brute_ag(a_slices, b, c, alpha, beta, dec, b_layout):
+    A = [[dec(v) for v in row] for s in a_slices for row in s]
+    Bv = [[dec(v) for v in row] for row in b]
+    M, K = len(A), len(A[0])
+    N = len(Bv) if b_layout == "nk" else len(Bv[0])
+    out = [[0.0] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            acc = 0.0
+            for k in range(K):
+                bkj = Bv[j][k] if b_layout == "nk" else Bv[k][j]
+                acc += A[i][k] * bkj
+            cv = float(oracle.decode_bf16(c[i, j])) if beta != 0 else 0.0
+            out[i][j] = alpha * acc + beta * cv
+    return np.array(out)
+
+
+@pytest.mark.parametrize("dtype,b_layout", [("bf16", "nk"), ("bf16", "kn"), ("e4m3", "nk")])
+def test_ag_matches_brute_force(dtype, b_layout):
+    rng = np.random.default_rng(1)
+    P, m, N, K = 2, 3, 5, 8
+    if dtype == "bf16":
+        slices = [rand_int_bf16(rng, (m, K)) for _ in range(P)]
+        b = rand_int_bf16(rng, (N, K) if b_layout == "nk" else (K, N))
+        dec = lambda v: float(oracle.decode_bf16(v))
+    else:
+        slices = [gen.encode_e4m3(rng.integers(-4, 5, size=(m, K)) * 0.25) for _ in range(P)]
+        b = gen.encode_e4m3(rng.integers(-4, 5, size=(N, K)) * 0.5)
+        dec = lambda v: float(oracle.decode_e4m3(v))
+    c = rand_int_bf16(rng, (P * m, N))
+    for rank in range(P):
+        got = oracle.gemm_ag(slices, b, c, 0.5, -2.0, rank, dtype, b_layout)
+        ref = brute_ag(slices, b, c, 0.5, -2.0, dec, b_layout)
+        assert np.array_equal(got, ref)
+
+
+def test_ag_closed_form_ones():
+    # A = B = 1  =>  D = alpha * K + beta * C
+    P, m, N, K = 4, 8, 16, 512
+    one = np.full((m, K), 0x3F80, np.uint16)
+    b = np.full((N, K), 0x3F80, np.uint16)
+    c = bf16_bits(np.random.default_rng(2).uniform(-1, 1, (P * m, N)))
+    D = oracle.gemm_ag([one] * P, b, c, 1.0, 1.0, 0)
+    assert np.array_equal(D, 512.0 + oracle.decode_bf16(c))
+
+
+def test_ag_one_hot_selects_columns():
+    rng = np.random.default_rng(3)
+    P, m, K = 2, 5, 16
+    perm = rng.permutation(K)[:7]
+    b = np.zeros((7, K), np.uint16)
+    b[np.arange(7), perm] = 0x3F80
+    slices = [bf16_bits(rng.uniform(-1, 1, (m, K))) for _ in range(P)]
+    D = oracle.gemm_ag(slices, b, None, 1.0, 0.0, 1)
+    A = np.concatenate([oracle.decode_bf16(s) for s in slices])
+    assert np.array_equal(D, A[:, perm])
+
+
+def test_ag_beta_zero_never_reads_c_and_alpha_zero():
+    rng = np.random.default_rng(4)
+    slices = [bf16_bits(rng.uniform(-1, 1, (4, 8))) for _ in range(2)]
+    b = bf16_bits(rng.uniform(-1, 1, (6, 8)))
+    nan_c = np.full((8, 6), 0x7FC0, np.uint16)          # bf16 NaN
+    assert np.isfinite(oracle.gemm_ag(slices, b, nan_c, 1.0, 0.0, 0)).all()
+    c = bf16_bits(rng.uniform(-1, 1, (8, 6)))
+    assert np.array_equal(oracle.gemm_ag(slices, b, c, 0.0, 1.5, 1), 1.5 * oracle.decode_bf16(c))
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+def test_ag_staged_equals_unstaged_every_rank(P):
+    rng = np.random.default_rng(5 + P)
+    m, N, K = 3, 7, 24
+    slices = [rand_int_bf16(rng, (m, K)) for _ in range(P)]
+    b = rand_int_bf16(rng, (N, K))
+    c = rand_int_bf16(rng, (P * m, N))
+    ref = oracle.gemm_ag(slices, b, c, 1.0, 1.0, 0, staged=False)
+    for rank in range(P):
+        assert np.array_equal(oracle.gemm_ag(slices, b, c, 1.0, 1.0, rank), ref)
+
+
+def test_ag_stage_order_is_a_rotation_local_first():
+    for P in (1, 2, 4, 8):
+        for r in range(P):
+            order = oracle.ag_stage_order(P, r)
+            assert order[0] == r and sorted(order) == list(range(P))
+            assert all((order[t + 1] - order[t]) % P == 1 for t in range(P - 1))
+            rs = oracle.rs_block_order(P, r)
+            assert rs[-1] == r and sorted(rs) == list(range(P))
+
+
+def test_ag_linearity_and_layouts():
+    rng = np.random.default_rng(6)
+    slices = [rand_int_bf16(rng, (4, 16)) for _ in range(2)]
+    bnk = rand_int_bf16(rng, (6, 16))
+    bkn = np.ascontiguousarray(bnk.T)
+    c = rand_int_bf16(rng, (8, 6))
+    d10 = oracle.gemm_ag(slices, bnk, None, 1.0, 0.0, 0)
+    d = oracle.gemm_ag(slices, bkn, c, 0.5, 3.0, 1, b_layout="kn")
+    assert np.array_equal(d, 0.5 * d10 + 3.0 * oracle.decode_bf16(c))
+
+
+def test_ag_rows_sampling_matches_full():
+    rng = np.random.default_rng(7)
+    slices = [bf16_bits(rng.uniform(-1, 1, (5, 32))) for _ in range(4)]
+    b = bf16_bits(rng.uniform(-1, 1, (9, 32)))
+    c = bf16_bits(rng.uniform(-1, 1, (20, 9)))
+    full = oracle.gemm_ag(slices, b, c, 1.0, 1.0, 2)
+    rows = [0, 4, 5, 13, 19]
+    np.testing.assert_allclose(oracle.gemm_ag_rows(slices, b, c, 1.0, 1.0, "bf16", "nk", rows),
+                               full[rows], rtol=1e-13, atol=1e-13)
+
+
+def test_ag_swiglu_pairs_halves():
+    rng = np.random.default_rng(8)
+    P, m, K, n = 2, 3, 8, 4
+    slices = [rand_int_bf16(rng, (m, K), -1, 1) for _ in range(P)]
+    w = rand_int_bf16(rng, (K, 2 * n), -1, 1)
+    got = oracle.gemm_ag(slices, w, None, 1.0, 0.0, 0, b_layout="kn", swiglu=True)
+    A = np.concatenate([oracle.decode_bf16(s) for s in slices])
+    W = oracle.decode_bf16(w)
+    for i, j in itertools.product(range(P * m), range(n)):
+        u = sum(A[i, k] * W[k, j] for k in range(K))
+        v = sum(A[i, k] * W[k, n + j] for k in range(K))
+        assert abs(got[i, j] - u / (1 + np.exp(-u)) * v) < 1e-12
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_rs_distributed_identity(P):
+    """Simulate all P ranks: rank r holds K-shard r of A and B. Feeding every
+    rank the partials its peers emitted for its block must give the rows of
+    the unsharded product A_full @ B_full^T (integer data: exact)."""
+    rng = np.random.default_rng(10 + P)
+    m, N, Ks = 3, 5, 4
+    A = [rand_int_bf16(rng, (P * m, Ks), -1, 1) for _ in range(P)]
+    Bs = [rand_int_bf16(rng, (N, Ks), -1, 1) for _ in range(P)]
+    emitted = [oracle.gemm_rs(A[r], Bs[r], None, 1.0, r, P) for r in range(P)]
+    full = np.concatenate([oracle.decode_bf16(a) for a in A], axis=1) @ \
+        np.concatenate([oracle.decode_bf16(b) for b in Bs], axis=1).T
+    for r in range(P):
+        incoming = [None if j == r else bf16_bits(emitted[j][r * m:(r + 1) * m]) for j in range(P)]
+        out = oracle.gemm_rs(A[r], Bs[r], incoming, 1.0, r, P)
+        assert np.array_equal(out[r * m:(r + 1) * m], full[r * m:(r + 1) * m])
+        for blk in range(P):       # emitted blocks are this rank's own partials
+            if blk != r:
+                own = oracle.decode_bf16(A[r][blk * m:(blk + 1) * m]) @ oracle.decode_bf16(Bs[r]).T
+                assert np.array_equal(out[blk * m:(blk + 1) * m], own)
+
+
+def test_rs_rows_and_layout():
+    rng = np.random.default_rng(20)
+    P, m, N, K = 4, 3, 6, 8
+    a = bf16_bits(rng.uniform(-1, 1, (P * m, K)))
+    bnk = bf16_bits(rng.uniform(-1, 1, (N, K)))
+    inc = [None if j == 1 else bf16_bits(rng.uniform(-1, 1, (m, N))) for j in range(P)]
+    full = oracle.gemm_rs(a, bnk, inc, 0.5, 1, P)
+    full_kn = oracle.gemm_rs(a, np.ascontiguousarray(bnk.T), inc, 0.5, 1, P, b_layout="kn")
+    np.testing.assert_array_equal(full, full_kn)
+    rows = [0, 3, 4, 5, 11]
+    np.testing.assert_allclose(oracle.gemm_rs_rows(a, bnk, inc, 0.5, 1, P, "nk", rows), full[rows],
+                               rtol=1e-13, atol=1e-13)
