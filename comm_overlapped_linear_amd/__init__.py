@@ -1,0 +1,253 @@
+"""Python binding of libtpgemm, the MI355X staged tensor-parallel GEMM share.
+
+Argument marshalling only: every step of the path (deliveries, gates, GEMMs,
+epilogues, LayerNorm, permutes) runs in the HIP library. PyTorch supplies
+device memory and the current stream. Tensors are passed by data_ptr(); bf16
+tensors may be torch.bfloat16 or raw int16/uint16 bits, e4m3 tensors
+torch.float8_e4m3fn or raw uint8 bits.
+
+The names follow the C ABI in include/tpgemm.h:
+    stage_ag, stage_rs, ffn_slot_forward, dispatch_permute, combine_permute
+(plus the *_workspace_size queries, last_error, release_caches, profile_read).
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtpgemm.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+BF16, E4M3 = 0, 1
+B_NK, B_KN = 0, 1
+EPI_ALPHA_BETA, EPI_SWIGLU = 0, 1
+UNSTAGED, NO_COPY, NO_GRAPH, COPY_BLIT, SERIAL_STAGES, PROFILE = 1, 2, 4, 8, 16, 32
+
+_STATUS = {OK: "OK", ERR_INVALID: "INVALID", ERR_UNSUPPORTED: "UNSUPPORTED",
+           ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP"}
+
+
+class TpgError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"tpgemm {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class AgArgs(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("P", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("ab_dtype", ctypes.c_int32), ("b_layout", ctypes.c_int32), ("epilogue", ctypes.c_int32),
+                ("a_slices", ctypes.POINTER(ctypes.c_void_p)), ("b", ctypes.c_void_p),
+                ("c", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("flags", ctypes.c_uint32)]
+
+
+class RsArgs(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("P", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("ab_dtype", ctypes.c_int32), ("b_layout", ctypes.c_int32),
+                ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("incoming", ctypes.POINTER(ctypes.c_void_p)), ("d", ctypes.c_void_p),
+                ("alpha", ctypes.c_float),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("flags", ctypes.c_uint32)]
+
+
+class FfnArgs(ctypes.Structure):
+    _fields_ = [("PB", ctypes.c_int64), ("L", ctypes.c_int64), ("D", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("x", ctypes.c_void_p), ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("wout", ctypes.c_void_p), ("bout", ctypes.c_void_p),
+                ("gx", ctypes.c_void_p), ("bx", ctypes.c_void_p), ("gg", ctypes.c_void_p), ("bg", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("y", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        for name, argt, rest in [
+            ("tpgemm_stage_ag", [ctypes.POINTER(AgArgs), vp], i32),
+            ("tpgemm_stage_ag_workspace_size", [ctypes.POINTER(AgArgs)], ctypes.c_size_t),
+            ("tpgemm_stage_rs", [ctypes.POINTER(RsArgs), vp], i32),
+            ("tpgemm_stage_rs_workspace_size", [ctypes.POINTER(RsArgs)], ctypes.c_size_t),
+            ("ffn_slot_forward", [ctypes.POINTER(FfnArgs), vp], i32),
+            ("ffn_slot_forward_workspace_size", [ctypes.POINTER(FfnArgs)], ctypes.c_size_t),
+            ("dispatch_permute", [ctypes.POINTER(vp), vp, i32, i32, i64, i64, i64, i32, vp], i32),
+            ("combine_permute", [ctypes.POINTER(vp), vp, i32, i32, i64, i64, i64, i32, vp], i32),
+            ("tpg_last_error", [], ctypes.c_char_p),
+            ("tpg_release_caches", [], None),
+            ("tpg_profile_read", [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double), i32], i32),
+        ]:
+            fn = getattr(L, name)
+            fn.argtypes = argt
+            fn.restype = rest
+        _lib = L
+    return _lib
+
+
+def last_error():
+    return lib().tpg_last_error().decode()
+
+
+def _check(status):
+    if status != OK:
+        raise TpgError(status, last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t) if t is not None else None
+    return arr
+
+
+class Workspace:
+    """A grow-only device scratch buffer (the same pointer is reused, so
+    repeated calls replay their cached graph)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            dev = self.device if self.device is not None else torch.cuda.current_device()
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=dev)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, nbytes):
+    if ws is not None:
+        return ws
+    dev = torch.cuda.current_device()
+    if dev not in _default_ws:
+        _default_ws[dev] = Workspace(dev)
+    return _default_ws[dev].get(nbytes)
+
+
+def ag_args(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, epilogue=EPI_ALPHA_BETA,
+            alpha=1.0, beta=1.0, flags=0):
+    slices = _ptr_array(a_slices)
+    args = AgArgs(M=M, N=N, K=K, P=len(a_slices), rank=rank, ab_dtype=dtype, b_layout=b_layout,
+                  epilogue=epilogue, a_slices=ctypes.cast(slices, ctypes.POINTER(ctypes.c_void_p)),
+                  b=_ptr(b), c=_ptr(c), d=_ptr(d), alpha=alpha, beta=beta, flags=flags)
+    args._keep = slices
+    return args
+
+
+def stage_ag_workspace_size(args):
+    return lib().tpgemm_stage_ag_workspace_size(ctypes.byref(args))
+
+
+def stage_ag(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, epilogue=EPI_ALPHA_BETA,
+             alpha=1.0, beta=1.0, flags=0, workspace=None, stream=None):
+    """Staged all-gather GEMM: d = alpha * A b^T + beta * c (see tpgemm.h)."""
+    args = ag_args(a_slices, b, c, d, M=M, N=N, K=K, rank=rank, dtype=dtype, b_layout=b_layout,
+                   epilogue=epilogue, alpha=alpha, beta=beta, flags=flags)
+    need = stage_ag_workspace_size(args)
+    ws = _workspace(workspace, need)
+    args.workspace = _ptr(ws) if ws is not None else None
+    args.workspace_bytes = ws.numel() if ws is not None else 0
+    _check(lib().tpgemm_stage_ag(ctypes.byref(args), _stream(stream)))
+
+
+def rs_args(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0):
+    inc = _ptr_array(incoming) if incoming is not None else None
+    args = RsArgs(M=M, N=N, K=K, P=P, rank=rank, ab_dtype=dtype, b_layout=b_layout, a=_ptr(a), b=_ptr(b),
+                  incoming=ctypes.cast(inc, ctypes.POINTER(ctypes.c_void_p)) if inc is not None else None,
+                  d=_ptr(d), alpha=alpha, flags=flags)
+    args._keep = inc
+    return args
+
+
+def stage_rs_workspace_size(args):
+    return lib().tpgemm_stage_rs_workspace_size(ctypes.byref(args))
+
+
+def stage_rs(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0,
+             workspace=None, stream=None):
+    """Staged GEMM + reduce-scatter share (see tpgemm.h)."""
+    args = rs_args(a, b, incoming, d, M=M, N=N, K=K, P=P, rank=rank, dtype=dtype, b_layout=b_layout,
+                   alpha=alpha, flags=flags)
+    need = stage_rs_workspace_size(args)
+    ws = _workspace(workspace, need)
+    args.workspace = _ptr(ws) if ws is not None else None
+    args.workspace_bytes = ws.numel() if ws is not None else 0
+    _check(lib().tpgemm_stage_rs(ctypes.byref(args), _stream(stream)))
+
+
+def ffn_args(x, w1, b1, wout, bout, gx, bx, gg, bg, y, *, PB, L, D, H, eps=1e-5, flags=0):
+    return FfnArgs(PB=PB, L=L, D=D, H=H, x=_ptr(x), w1=_ptr(w1), b1=_ptr(b1), wout=_ptr(wout),
+                   bout=_ptr(bout), gx=_ptr(gx), bx=_ptr(bx), gg=_ptr(gg), bg=_ptr(bg), eps=eps,
+                   y=_ptr(y), flags=flags)
+
+
+def ffn_slot_forward_workspace_size(args):
+    return lib().ffn_slot_forward_workspace_size(ctypes.byref(args))
+
+
+def ffn_slot_forward(x, w1, b1, wout, bout, gx, bx, gg, bg, y, *, PB, L, D, H, eps=1e-5, flags=0,
+                     workspace=None, stream=None):
+    """Per-token-slot FFN (comp-only part of the layer), see tpgemm.h."""
+    args = ffn_args(x, w1, b1, wout, bout, gx, bx, gg, bg, y, PB=PB, L=L, D=D, H=H, eps=eps, flags=flags)
+    need = ffn_slot_forward_workspace_size(args)
+    ws = _workspace(workspace, need)
+    args.workspace = _ptr(ws) if ws is not None else None
+    args.workspace_bytes = ws.numel() if ws is not None else 0
+    _check(lib().ffn_slot_forward(ctypes.byref(args), _stream(stream)))
+
+
+def dispatch_permute(srcs, dst, *, rank, B, T, D, elem_bytes, stream=None):
+    arr = _ptr_array(srcs)
+    _check(lib().dispatch_permute(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), _ptr(dst), len(srcs),
+                                  rank, B, T, D, elem_bytes, _stream(stream)))
+
+
+def combine_permute(srcs, dst, *, rank, B, T, D, elem_bytes, stream=None):
+    arr = _ptr_array(srcs)
+    _check(lib().combine_permute(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), _ptr(dst), len(srcs),
+                                 rank, B, T, D, elem_bytes, _stream(stream)))
+
+
+def release_caches():
+    lib().tpg_release_caches()
+
+
+def profile_read(cap=4096):
+    ms = (ctypes.c_float * cap)()
+    fl = (ctypes.c_double * cap)()
+    n = lib().tpg_profile_read(ms, fl, cap)
+    return [(ms[i], fl[i]) for i in range(n)]

@@ -1,0 +1,811 @@
+// C ABI of libtpgemm: validation, the stage scheduler and the graph cache.
+//
+// The scheduler follows "Distributed GEMM" (Hassani et al., SHI Labs,
+// Dec 2024): the copy engine moves the peers' shards while the matrix cores
+// run the local stage, and the stage kernels need no communication code of
+// their own (Introduction; Approach, observations 2 and 4; Background,
+// Figure 4: local shard first, then rotate). On one MI355X the peers' shards
+// are buffers in the same HBM: each delivery is one hipMemcpyAsync on a
+// library-owned copy stream (the SDMA copy engines unless TPG_COPY_BLIT),
+// followed by an event that gates exactly the stage that reads it. Stage
+// kernels fan out over up to four compute streams so that several small
+// stages can share the 256 CUs; everything forks from and joins back into the
+// caller's stream. Unless TPG_NO_GRAPH, one call is recorded once into a
+// hipGraph (launch gaps between stages are overhead, Approach observation 4)
+// and replayed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "gemm.h"
+#include "tpgemm.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tpg_status fail(tpg_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail(TPG_ERR_HIP, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int kStreams = 4;       // compute streams per call (index 0 = root)
+constexpr int kMaxP = 64;
+constexpr size_t kMaxGraphs = 512;
+constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_BLIT |
+                                 TPG_SERIAL_STAGES | TPG_PROFILE;
+
+struct ProfRec {
+  hipEvent_t a, b;
+  double flop;
+};
+
+struct Ctx {
+  int device = -1;
+  hipStream_t copy = nullptr;
+  hipStream_t comp[kStreams] = {};   // comp[0] unused: the root stream takes its place
+  hipStream_t capture = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_copy_done = nullptr;
+  hipEvent_t ev_copy[kMaxP] = {};
+  hipEvent_t ev_join[kStreams] = {};
+  std::unordered_map<std::string, hipGraphExec_t> graphs;
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> prof_pool;
+};
+
+std::mutex g_mu;
+std::unordered_map<int, Ctx*> g_ctx;
+
+tpg_status make_ctx(int dev, Ctx** out) {
+  Ctx* c = new Ctx();
+  c->device = dev;
+  HIP_TRY(hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking));
+  for (int i = 1; i < kStreams; ++i) HIP_TRY(hipStreamCreateWithFlags(&c->comp[i], hipStreamNonBlocking));
+  HIP_TRY(hipStreamCreateWithFlags(&c->capture, hipStreamNonBlocking));
+  HIP_TRY(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&c->ev_copy_done, hipEventDisableTiming));
+  for (int i = 0; i < kMaxP; ++i) HIP_TRY(hipEventCreateWithFlags(&c->ev_copy[i], hipEventDisableTiming));
+  for (int i = 0; i < kStreams; ++i) HIP_TRY(hipEventCreateWithFlags(&c->ev_join[i], hipEventDisableTiming));
+  *out = c;
+  return TPG_OK;
+}
+
+tpg_status get_ctx(Ctx** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ctx.find(dev);
+  if (it != g_ctx.end()) {
+    *out = it->second;
+    return TPG_OK;
+  }
+  Ctx* c = nullptr;
+  tpg_status st = make_ctx(dev, &c);
+  if (st != TPG_OK) return st;
+  g_ctx[dev] = c;
+  *out = c;
+  return TPG_OK;
+}
+
+void destroy_ctx(Ctx* c) {
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& r : c->prof) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (auto e : c->prof_pool) (void)hipEventDestroy(e);
+  if (c->copy) (void)hipStreamDestroy(c->copy);
+  for (int i = 1; i < kStreams; ++i)
+    if (c->comp[i]) (void)hipStreamDestroy(c->comp[i]);
+  if (c->capture) (void)hipStreamDestroy(c->capture);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_copy_done) (void)hipEventDestroy(c->ev_copy_done);
+  for (int i = 0; i < kMaxP; ++i)
+    if (c->ev_copy[i]) (void)hipEventDestroy(c->ev_copy[i]);
+  for (int i = 0; i < kStreams; ++i)
+    if (c->ev_join[i]) (void)hipEventDestroy(c->ev_join[i]);
+  delete c;
+}
+
+// ---------------------------------------------------------------- helpers
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(const Range& x, const Range& y) {
+  if (!x.p || !y.p || x.bytes == 0 || y.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), a1 = a0 + x.bytes;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(y.p), b1 = b0 + y.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int elem_bytes(int32_t dt) { return dt == TPG_E4M3 ? 1 : 2; }
+
+bool fits_int(int64_t v) { return v >= 0 && v < (int64_t(1) << 31); }
+
+struct Launch {
+  hipStream_t root;
+  bool profile;
+};
+
+tpg_status gemm_on(Ctx& cx, const Launch& L, hipStream_t s, const tpg::GemmParams& p, int dtype,
+                   int layout, int epi) {
+  ProfRec rec{nullptr, nullptr, 2.0 * p.M * double(p.N) * p.K};
+  if (L.profile) {
+    for (hipEvent_t* e : {&rec.a, &rec.b}) {
+      if (!cx.prof_pool.empty()) {
+        *e = cx.prof_pool.back();
+        cx.prof_pool.pop_back();
+      } else {
+        HIP_TRY(hipEventCreate(e));
+      }
+    }
+    HIP_TRY(hipEventRecord(rec.a, s));
+  }
+  hipError_t e = tpg::launch_gemm(p, dtype, layout, epi, s);
+  if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("gemm launch failed: ") + hipGetErrorString(e));
+  if (L.profile) {
+    HIP_TRY(hipEventRecord(rec.b, s));
+    cx.prof.push_back(rec);
+  }
+  return TPG_OK;
+}
+
+// Fork n-1 internal compute streams from the root; comp[0] is the root.
+tpg_status fork_streams(Ctx& cx, hipStream_t root, int n, hipStream_t* streams) {
+  streams[0] = root;
+  if (n > 1) HIP_TRY(hipEventRecord(cx.ev_fork, root));
+  for (int i = 1; i < n; ++i) {
+    streams[i] = cx.comp[i];
+    HIP_TRY(hipStreamWaitEvent(streams[i], cx.ev_fork, 0));
+  }
+  return TPG_OK;
+}
+
+tpg_status join_streams(Ctx& cx, hipStream_t root, int n, const hipStream_t* streams, bool copies) {
+  for (int i = 1; i < n; ++i) {
+    HIP_TRY(hipEventRecord(cx.ev_join[i], streams[i]));
+    HIP_TRY(hipStreamWaitEvent(root, cx.ev_join[i], 0));
+  }
+  if (copies) {
+    HIP_TRY(hipEventRecord(cx.ev_copy_done, cx.copy));
+    HIP_TRY(hipStreamWaitEvent(root, cx.ev_copy_done, 0));
+  }
+  return TPG_OK;
+}
+
+hipMemcpyKind copy_kind(uint32_t flags) {
+  return (flags & TPG_COPY_BLIT) ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+}
+
+// Records `enqueue` into a graph once per key and replays it on `user`, or
+// runs it eagerly.
+tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t user,
+                    const std::function<tpg_status(const Launch&)>& enqueue) {
+  const bool eager = (flags & (TPG_NO_GRAPH | TPG_PROFILE)) != 0;
+  if (eager) return enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
+  auto it = cx.graphs.find(key);
+  if (it == cx.graphs.end()) {
+    if (cx.graphs.size() >= kMaxGraphs) {
+      HIP_TRY(hipDeviceSynchronize());
+      for (auto& kv : cx.graphs) (void)hipGraphExecDestroy(kv.second);
+      cx.graphs.clear();
+    }
+    HIP_TRY(hipStreamBeginCapture(cx.capture, hipStreamCaptureModeThreadLocal));
+    tpg_status st = enqueue(Launch{cx.capture, false});
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(cx.capture, &g);
+    if (st != TPG_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return st;
+    }
+    if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("graph instantiate failed: ") + hipGetErrorString(e));
+    it = cx.graphs.emplace(key, ex).first;
+  }
+  HIP_TRY(hipGraphLaunch(it->second, user));
+  return TPG_OK;
+}
+
+template <typename T>
+void put(std::ostringstream& os, const T& v) {
+  os << v << '|';
+}
+
+// ---------------------------------------------------------------- all-gather
+tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
+  if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
+  if (a->P < 1 || a->P > kMaxP) return fail(TPG_ERR_INVALID, "P must be in [1, 64]");
+  if (a->rank < 0 || a->rank >= a->P) return fail(TPG_ERR_INVALID, "rank must be in [0, P)");
+  if (a->M < 0 || a->N < 0 || a->K < 0) return fail(TPG_ERR_INVALID, "negative dimension");
+  if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
+  if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
+  if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
+  if (a->epilogue != TPG_EPI_ALPHA_BETA && a->epilogue != TPG_EPI_SWIGLU)
+    return fail(TPG_ERR_INVALID, "bad epilogue");
+  const bool sw = a->epilogue == TPG_EPI_SWIGLU;
+  if (sw && (a->N % 2)) return fail(TPG_ERR_INVALID, "SWIGLU needs an even N");
+  if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
+    return fail(TPG_ERR_UNSUPPORTED, "dimensions must be below 2^31");
+  if (a->ab_dtype == TPG_E4M3 && a->b_layout == TPG_B_KN)
+    return fail(TPG_ERR_UNSUPPORTED, "e4m3 operands need the NK layout of B");
+  if (a->K % (a->ab_dtype == TPG_E4M3 ? 16 : 8))
+    return fail(TPG_ERR_UNSUPPORTED, "K must be a multiple of 8 (bf16) or 16 (e4m3)");
+  const int64_t nout = sw ? a->N / 2 : a->N;
+  if (a->b_layout == TPG_B_KN && (nout % 8 || a->N % 8))
+    return fail(TPG_ERR_UNSUPPORTED, "KN layout needs N (and N/2 with SWIGLU) multiple of 8");
+  if (a->beta != 0.0f && !a->c) return fail(TPG_ERR_INVALID, "beta != 0 needs C");
+  const int eb = elem_bytes(a->ab_dtype);
+  const int64_t m = a->M / a->P;
+  const size_t slice_b = size_t(m) * a->K * eb;
+  if (!a->a_slices && a->M > 0) return fail(TPG_ERR_INVALID, "a_slices is NULL");
+  std::vector<Range> inputs;
+  for (int s = 0; a->M > 0 && s < a->P; ++s) {
+    if (!a->a_slices[s] && slice_b) return fail(TPG_ERR_INVALID, "NULL A slice");
+    if (!aligned16(a->a_slices[s])) return fail(TPG_ERR_UNSUPPORTED, "A slice not 16-byte aligned");
+    inputs.push_back({a->a_slices[s], slice_b});
+  }
+  const size_t b_b = size_t(a->N) * a->K * eb;
+  if (!a->b && b_b) return fail(TPG_ERR_INVALID, "B is NULL");
+  if (!aligned16(a->b)) return fail(TPG_ERR_UNSUPPORTED, "B not 16-byte aligned");
+  inputs.push_back({a->b, b_b});
+  const size_t d_b = size_t(a->M) * nout * 2;
+  if (a->beta != 0.0f) {
+    if (!aligned16(a->c)) return fail(TPG_ERR_UNSUPPORTED, "C not 16-byte aligned");
+    inputs.push_back({a->c, d_b});
+  }
+  if (!a->d && d_b) return fail(TPG_ERR_INVALID, "D is NULL");
+  if (!aligned16(a->d)) return fail(TPG_ERR_UNSUPPORTED, "D not 16-byte aligned");
+  const Range dr{a->d, d_b}, wr{a->workspace, need};
+  for (const auto& r : inputs) {
+    if (overlaps(dr, r)) return fail(TPG_ERR_INVALID, "D overlaps an input");
+    if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
+  }
+  if (overlaps(dr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps D");
+  if (need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_ag_workspace_size()");
+  if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  if ((a->flags & TPG_UNSTAGED) && (a->flags & TPG_NO_COPY) && a->M > 0) {
+    for (int s = 1; s < a->P; ++s)
+      if (static_cast<const char*>(a->a_slices[s]) != static_cast<const char*>(a->a_slices[0]) + s * slice_b)
+        return fail(TPG_ERR_UNSUPPORTED, "UNSTAGED|NO_COPY needs the slices to be contiguous");
+  }
+  return TPG_OK;
+}
+
+size_t ag_ws(const tpg_ag_args* a) {
+  if (!a || a->P < 1 || a->M < 0 || a->K < 0 || (a->flags & TPG_NO_COPY)) return 0;
+  const size_t m = size_t(a->M) / a->P;
+  const size_t slice = m * a->K * elem_bytes(a->ab_dtype);
+  if (a->flags & TPG_UNSTAGED) return slice * a->P;
+  return slice * (a->P - 1);
+}
+
+tpg::GemmParams base_params() {
+  tpg::GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.add_row0 = 0;
+  p.add_row1 = 0;
+  return p;
+}
+
+tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
+  const int P = a.P, r = a.rank;
+  const int eb = elem_bytes(a.ab_dtype);
+  const int64_t m = a.M / P;
+  const bool sw = a.epilogue == TPG_EPI_SWIGLU;
+  const int64_t nout = sw ? a.N / 2 : a.N;
+  const size_t slice_b = size_t(m) * a.K * eb;
+  const bool copies = !(a.flags & TPG_NO_COPY) && slice_b > 0 && (P > 1 || (a.flags & TPG_UNSTAGED));
+  const hipMemcpyKind kind = copy_kind(a.flags);
+  char* ws = static_cast<char*>(a.workspace);
+
+  tpg::GemmParams p = base_params();
+  p.b = a.b;
+  p.ldb = a.b_layout == TPG_B_NK ? a.K : a.N;
+  p.lda = a.K;
+  p.ldc = nout;
+  p.ldd = nout;
+  p.N = static_cast<int>(a.N);
+  p.K = static_cast<int>(a.K);
+  p.alpha = a.alpha;
+  p.beta = a.beta;
+  p.vec_ok = (nout % 4) == 0;
+  const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
+  const int layout = a.b_layout == TPG_B_KN ? tpg::kKN : tpg::kNK;
+  const int epi = sw ? tpg::kEpiSwiglu : tpg::kEpiAlphaBeta;
+
+  if (copies) {
+    HIP_TRY(hipEventRecord(cx.ev_fork, L.root));
+    HIP_TRY(hipStreamWaitEvent(cx.copy, cx.ev_fork, 0));
+  }
+
+  if (a.flags & TPG_UNSTAGED) {
+    // single stage: gather every slice (rank order), then one GEMM over all M rows
+    const void* A = a.M > 0 ? a.a_slices[0] : nullptr;
+    if (copies) {
+      for (int s = 0; s < P; ++s)
+        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, cx.copy));
+      HIP_TRY(hipEventRecord(cx.ev_copy_done, cx.copy));
+      HIP_TRY(hipStreamWaitEvent(L.root, cx.ev_copy_done, 0));
+      A = ws;
+    }
+    p.a = A;
+    p.c = static_cast<const uint16_t*>(a.c);
+    p.d = static_cast<uint16_t*>(a.d);
+    p.M = static_cast<int>(a.M);
+    return gemm_on(cx, L, L.root, p, dtype, layout, epi);
+  }
+
+  // staged: stage t multiplies slice s = (rank + t) mod P, local first
+  if (copies) {
+    for (int t = 1; t < P; ++t) {
+      const int s = (r + t) % P;
+      HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], slice_b, kind, cx.copy));
+      HIP_TRY(hipEventRecord(cx.ev_copy[t], cx.copy));
+    }
+  }
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(P, kStreams);
+  hipStream_t st[kStreams];
+  tpg_status stat = fork_streams(cx, L.root, ns, st);
+  if (stat != TPG_OK) return stat;
+  p.M = static_cast<int>(m);
+  for (int t = 0; t < P; ++t) {
+    const int s = (r + t) % P;
+    hipStream_t cs = st[t % ns];
+    const void* A = a.a_slices[s];
+    if (copies && t > 0) {
+      HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[t], 0));
+      A = ws + (t - 1) * slice_b;
+    }
+    p.a = A;
+    p.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
+    p.d = static_cast<uint16_t*>(a.d) + s * m * nout;
+    stat = gemm_on(cx, L, cs, p, dtype, layout, epi);
+    if (stat != TPG_OK) return stat;
+  }
+  return join_streams(cx, L.root, ns, st, copies);
+}
+
+std::string ag_key(const tpg_ag_args& a) {
+  std::ostringstream os;
+  os << "ag|";
+  put(os, a.M); put(os, a.N); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.ab_dtype);
+  put(os, a.b_layout); put(os, a.epilogue); put(os, a.b); put(os, a.c); put(os, a.d);
+  put(os, a.alpha); put(os, a.beta); put(os, a.workspace); put(os, a.flags);
+  for (int s = 0; s < a.P && a.a_slices; ++s) put(os, a.a_slices[s]);
+  return os.str();
+}
+
+// ---------------------------------------------------------------- reduce-scatter
+size_t rs_slot(const tpg_rs_args* a) { return round_up(size_t(a->M / a->P) * a->N * 2, 256); }
+
+size_t rs_ws(const tpg_rs_args* a) {
+  if (!a || a->P < 1 || a->M < 0 || a->N < 0 || !a->incoming || (a->flags & TPG_NO_COPY)) return 0;
+  return rs_slot(a) * (a->P - 1);
+}
+
+tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
+  if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
+  if (a->P < 1 || a->P > kMaxP) return fail(TPG_ERR_INVALID, "P must be in [1, 64]");
+  if (a->rank < 0 || a->rank >= a->P) return fail(TPG_ERR_INVALID, "rank must be in [0, P)");
+  if (a->M < 0 || a->N < 0 || a->K < 0) return fail(TPG_ERR_INVALID, "negative dimension");
+  if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
+  if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
+  if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
+  if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
+    return fail(TPG_ERR_UNSUPPORTED, "dimensions must be below 2^31");
+  if (a->ab_dtype == TPG_E4M3 && a->b_layout == TPG_B_KN)
+    return fail(TPG_ERR_UNSUPPORTED, "e4m3 operands need the NK layout of B");
+  if (a->K % (a->ab_dtype == TPG_E4M3 ? 16 : 8))
+    return fail(TPG_ERR_UNSUPPORTED, "K must be a multiple of 8 (bf16) or 16 (e4m3)");
+  if (a->b_layout == TPG_B_KN && a->N % 8) return fail(TPG_ERR_UNSUPPORTED, "KN layout needs N % 8 == 0");
+  const int eb = elem_bytes(a->ab_dtype);
+  const int64_t m = a->M / a->P;
+  std::vector<Range> inputs;
+  const size_t a_b = size_t(a->M) * a->K * eb, b_b = size_t(a->N) * a->K * eb;
+  if (!a->a && a_b) return fail(TPG_ERR_INVALID, "A is NULL");
+  if (!a->b && b_b) return fail(TPG_ERR_INVALID, "B is NULL");
+  if (!aligned16(a->a) || !aligned16(a->b)) return fail(TPG_ERR_UNSUPPORTED, "A/B not 16-byte aligned");
+  inputs.push_back({a->a, a_b});
+  inputs.push_back({a->b, b_b});
+  int n_in = 0;
+  const size_t part_b = size_t(m) * a->N * 2;
+  if (a->incoming) {
+    for (int j = 0; j < a->P; ++j) {
+      if (j == a->rank || !a->incoming[j]) continue;
+      if (!aligned16(a->incoming[j])) return fail(TPG_ERR_UNSUPPORTED, "incoming partial not 16-byte aligned");
+      inputs.push_back({a->incoming[j], part_b});
+      ++n_in;
+    }
+  }
+  if ((a->flags & TPG_NO_COPY) && n_in > tpg::kMaxAddList)
+    return fail(TPG_ERR_UNSUPPORTED, "NO_COPY reads at most 16 incoming partials in place");
+  const size_t d_b = size_t(a->M) * a->N * 2;
+  if (!a->d && d_b) return fail(TPG_ERR_INVALID, "D is NULL");
+  if (!aligned16(a->d)) return fail(TPG_ERR_UNSUPPORTED, "D not 16-byte aligned");
+  const Range dr{a->d, d_b}, wr{a->workspace, need};
+  for (const auto& r : inputs) {
+    if (overlaps(dr, r)) return fail(TPG_ERR_INVALID, "D overlaps an input");
+    if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
+  }
+  if (overlaps(dr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps D");
+  if (need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_rs_workspace_size()");
+  if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  return TPG_OK;
+}
+
+tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
+  const int P = a.P, r = a.rank;
+  const int eb = elem_bytes(a.ab_dtype);
+  const int64_t m = a.M / P;
+  const size_t part_b = size_t(m) * a.N * 2;
+  const size_t slot = rs_slot(&a);
+  char* ws = static_cast<char*>(a.workspace);
+  const hipMemcpyKind kind = copy_kind(a.flags);
+
+  // peers whose partial for block `rank` arrives, in ring order rank+1, rank+2, ...
+  std::vector<int> peers;
+  if (a.incoming)
+    for (int t = 1; t < P; ++t) {
+      const int j = (r + t) % P;
+      if (a.incoming[j]) peers.push_back(j);
+    }
+  const bool copies = !(a.flags & TPG_NO_COPY) && !peers.empty() && part_b > 0;
+
+  tpg::GemmParams p = base_params();
+  p.b = a.b;
+  p.ldb = a.b_layout == TPG_B_NK ? a.K : a.N;
+  p.lda = a.K;
+  p.ldd = a.N;
+  p.ld_add = a.N;
+  p.N = static_cast<int>(a.N);
+  p.K = static_cast<int>(a.K);
+  p.alpha = a.alpha;
+  p.beta = 0.0f;
+  p.vec_ok = (a.N % 4) == 0;
+  const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
+  const int layout = a.b_layout == TPG_B_KN ? tpg::kKN : tpg::kNK;
+
+  auto set_adds = [&](tpg::GemmParams& q) {
+    if (copies) {
+      q.add_base = reinterpret_cast<const uint16_t*>(ws);
+      q.add_stride = static_cast<int64_t>(slot / 2);
+      q.n_add_strided = static_cast<int>(peers.size());
+    } else {
+      for (size_t i = 0; i < peers.size(); ++i)
+        q.add_list[i] = static_cast<const uint16_t*>(a.incoming[peers[i]]);
+      q.n_add_list = static_cast<int>(peers.size());
+    }
+  };
+
+  if (copies) {
+    HIP_TRY(hipEventRecord(cx.ev_fork, L.root));
+    HIP_TRY(hipStreamWaitEvent(cx.copy, cx.ev_fork, 0));
+    for (size_t i = 0; i < peers.size(); ++i)
+      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], part_b, kind, cx.copy));
+    HIP_TRY(hipEventRecord(cx.ev_copy[0], cx.copy));
+  }
+
+  if (a.flags & TPG_UNSTAGED) {
+    // one GEMM over all blocks once every partial has arrived; the adds apply
+    // to the rows of the own block only
+    if (copies) HIP_TRY(hipStreamWaitEvent(L.root, cx.ev_copy[0], 0));
+    p.a = a.a;
+    p.d = static_cast<uint16_t*>(a.d);
+    p.M = static_cast<int>(a.M);
+    p.add_row0 = static_cast<int>(r * m);
+    p.add_row1 = static_cast<int>((r + 1) * m);
+    set_adds(p);
+    tpg_status st = gemm_on(cx, L, L.root, p, dtype, layout, tpg::kEpiAlphaBeta);
+    if (st != TPG_OK) return st;
+    if (copies) {
+      HIP_TRY(hipEventRecord(cx.ev_copy_done, cx.copy));
+      HIP_TRY(hipStreamWaitEvent(L.root, cx.ev_copy_done, 0));
+    }
+    return TPG_OK;
+  }
+
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(P, kStreams);
+  hipStream_t st[kStreams];
+  tpg_status stat = fork_streams(cx, L.root, ns, st);
+  if (stat != TPG_OK) return stat;
+  p.M = static_cast<int>(m);
+  for (int t = 0; t < P; ++t) {
+    const int blk = (r + 1 + t) % P;       // own block last
+    hipStream_t cs = st[t % ns];
+    tpg::GemmParams q = p;
+    q.a = static_cast<const char*>(a.a) + size_t(blk) * m * a.K * eb;
+    q.d = static_cast<uint16_t*>(a.d) + blk * m * a.N;
+    if (blk == r) {
+      if (copies) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[0], 0));
+      q.add_row0 = 0;
+      q.add_row1 = static_cast<int>(m);
+      set_adds(q);
+    }
+    stat = gemm_on(cx, L, cs, q, dtype, layout, tpg::kEpiAlphaBeta);
+    if (stat != TPG_OK) return stat;
+  }
+  return join_streams(cx, L.root, ns, st, copies);
+}
+
+std::string rs_key(const tpg_rs_args& a) {
+  std::ostringstream os;
+  os << "rs|";
+  put(os, a.M); put(os, a.N); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.ab_dtype);
+  put(os, a.b_layout); put(os, a.a); put(os, a.b); put(os, a.d); put(os, a.alpha);
+  put(os, a.workspace); put(os, a.flags);
+  for (int j = 0; a.incoming && j < a.P; ++j) put(os, a.incoming[j]);
+  return os.str();
+}
+
+// ---------------------------------------------------------------- FFN
+int ffn_bufs(uint32_t flags) { return (flags & TPG_SERIAL_STAGES) ? 1 : 2; }
+
+size_t ffn_ws(const tpg_ffn_args* a) {
+  if (!a || a->PB < 0 || a->H < 0) return 0;
+  return size_t(ffn_bufs(a->flags)) * round_up(size_t(a->PB) * 3 * a->H * 2, 256);
+}
+
+tpg_status validate_ffn(const tpg_ffn_args* a, size_t need) {
+  if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
+  if (a->PB < 0 || a->L < 0 || a->D < 0 || a->H < 0) return fail(TPG_ERR_INVALID, "negative dimension");
+  if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if (!fits_int(a->PB) || !fits_int(a->L * a->D) || !fits_int(2 * a->H))
+    return fail(TPG_ERR_UNSUPPORTED, "dimensions too large");
+  if (a->D % 8 || a->H % 8) return fail(TPG_ERR_UNSUPPORTED, "D and H must be multiples of 8");
+  if (a->H > 8 * 256 * 8) return fail(TPG_ERR_UNSUPPORTED, "H above 16384");
+  if (!(a->eps >= 0.0f)) return fail(TPG_ERR_INVALID, "eps must be >= 0");
+  const size_t PB = a->PB, L = a->L, D = a->D, H = a->H;
+  const Range in[] = {{a->x, PB * L * D * 2}, {a->w1, L * D * 2 * H * 2}, {a->b1, L * 2 * H * 2},
+                      {a->wout, L * H * D * 2}, {a->bout, L * D * 2}, {a->gx, H * 2},
+                      {a->bx, H * 2}, {a->gg, H * 2}, {a->bg, H * 2}};
+  const bool work = PB * L * D > 0;
+  for (const auto& r : in) {
+    if (work && r.bytes && !r.p) return fail(TPG_ERR_INVALID, "NULL FFN tensor");
+    if (!aligned16(r.p)) return fail(TPG_ERR_UNSUPPORTED, "FFN tensor not 16-byte aligned");
+  }
+  const Range yr{a->y, PB * L * D * 2}, wr{a->workspace, need};
+  if (work && !a->y) return fail(TPG_ERR_INVALID, "y is NULL");
+  if (!aligned16(a->y)) return fail(TPG_ERR_UNSUPPORTED, "y not 16-byte aligned");
+  for (const auto& r : in) {
+    if (overlaps(yr, r)) return fail(TPG_ERR_INVALID, "y overlaps an input");
+    if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
+  }
+  if (overlaps(yr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps y");
+  if (work && need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than ffn_slot_forward_workspace_size()");
+  if (!aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  return TPG_OK;
+}
+
+tpg_status enqueue_ffn(Ctx& cx, const tpg_ffn_args& a, const Launch& L) {
+  const int64_t PB = a.PB, Ls = a.L, D = a.D, H = a.H;
+  if (PB == 0 || Ls == 0 || D == 0) return TPG_OK;
+  const int nb = ffn_bufs(a.flags);
+  hipStream_t st[kStreams];
+  tpg_status stat = fork_streams(cx, L.root, nb, st);
+  if (stat != TPG_OK) return stat;
+  const size_t buf_b = round_up(size_t(PB) * 3 * H * 2, 256);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* w1 = static_cast<const uint16_t*>(a.w1);
+  const uint16_t* b1 = static_cast<const uint16_t*>(a.b1);
+  const uint16_t* wo = static_cast<const uint16_t*>(a.wout);
+  const uint16_t* bo = static_cast<const uint16_t*>(a.bout);
+  uint16_t* y = static_cast<uint16_t*>(a.y);
+  for (int64_t l = 0; l < Ls; ++l) {
+    hipStream_t cs = st[l % nb];
+    uint16_t* z = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + (l % nb) * buf_b);
+    uint16_t* h = z + PB * 2 * H;
+    if (H > 0) {
+      tpg::GemmParams g1 = base_params();
+      g1.a = x + l * D;  g1.lda = Ls * D;
+      g1.b = w1 + l * D * 2 * H;  g1.ldb = 2 * H;
+      g1.bias = b1 + l * 2 * H;
+      g1.d = z;  g1.ldd = 2 * H;
+      g1.M = static_cast<int>(PB);  g1.N = static_cast<int>(2 * H);  g1.K = static_cast<int>(D);
+      g1.alpha = 1.0f;  g1.vec_ok = 1;
+      stat = gemm_on(cx, L, cs, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
+      if (stat != TPG_OK) return stat;
+      hipError_t e = tpg::launch_ln_silu(z, 2 * H, h, H, static_cast<int>(PB), static_cast<int>(H),
+                                         static_cast<const uint16_t*>(a.gx), static_cast<const uint16_t*>(a.bx),
+                                         static_cast<const uint16_t*>(a.gg), static_cast<const uint16_t*>(a.bg),
+                                         a.eps, cs);
+      if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("ln_silu launch failed: ") + hipGetErrorString(e));
+    }
+    tpg::GemmParams g2 = base_params();
+    g2.a = h;  g2.lda = H;
+    g2.b = wo + l * H * D;  g2.ldb = D;
+    g2.bias = bo + l * D;
+    g2.d = y + l * D;  g2.ldd = Ls * D;
+    g2.M = static_cast<int>(PB);  g2.N = static_cast<int>(D);  g2.K = static_cast<int>(H);
+    g2.alpha = 1.0f;  g2.vec_ok = 1;
+    stat = gemm_on(cx, L, cs, g2, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
+    if (stat != TPG_OK) return stat;
+  }
+  return join_streams(cx, L.root, nb, st, false);
+}
+
+std::string ffn_key(const tpg_ffn_args& a) {
+  std::ostringstream os;
+  os << "ffn|";
+  put(os, a.PB); put(os, a.L); put(os, a.D); put(os, a.H); put(os, a.x); put(os, a.w1); put(os, a.b1);
+  put(os, a.wout); put(os, a.bout); put(os, a.gx); put(os, a.bx); put(os, a.gg); put(os, a.bg);
+  put(os, a.eps); put(os, a.y); put(os, a.workspace); put(os, a.flags);
+  return os.str();
+}
+
+// ---------------------------------------------------------------- permutes
+tpg_status permute_common(bool dispatch, const void* const* src, void* dst, int32_t P, int32_t rank,
+                          int64_t B, int64_t T, int64_t D, int32_t eb, void* stream) {
+  if (P < 1 || P > kMaxP) return fail(TPG_ERR_INVALID, "P must be in [1, 64]");
+  if (rank < 0 || rank >= P) return fail(TPG_ERR_INVALID, "rank must be in [0, P)");
+  if (B < 0 || T < 0 || D < 0) return fail(TPG_ERR_INVALID, "negative dimension");
+  if (T % P) return fail(TPG_ERR_INVALID, "T must be a multiple of P");
+  if (eb != 1 && eb != 2 && eb != 4 && eb != 8) return fail(TPG_ERR_INVALID, "elem_bytes must be 1, 2, 4 or 8");
+  const int64_t L = T / P;
+  const size_t total = size_t(B) * T * D * eb;     // bytes of one source (= of dst)
+  if (total == 0) return TPG_OK;
+  if (!src || !dst) return fail(TPG_ERR_INVALID, "NULL src or dst");
+  tpg::PermuteParams p;
+  std::memset(&p, 0, sizeof(p));
+  const Range dr{dst, total};
+  for (int s = 0; s < P; ++s) {
+    if (!src[s]) return fail(TPG_ERR_INVALID, "NULL source");
+    if (overlaps(dr, Range{src[s], total})) return fail(TPG_ERR_INVALID, "dst overlaps a source");
+    p.src[s] = static_cast<const uint8_t*>(src[s]);
+  }
+  p.dst = static_cast<uint8_t*>(dst);
+  p.B = B;
+  p.run_bytes = L * D * eb;
+  if (dispatch) {   // dst[s*B + b, l] = src_s[b, rank*L + l]
+    p.src_base = rank * L * D * eb;
+    p.src_bstride = T * D * eb;
+    p.dst_sstride = B * L * D * eb;
+    p.dst_bstride = L * D * eb;
+  } else {          // dst[b, s*L + l] = src_s[rank*B + b, l]
+    p.src_base = rank * B * L * D * eb;
+    p.src_bstride = L * D * eb;
+    p.dst_sstride = L * D * eb;
+    p.dst_bstride = T * D * eb;
+  }
+  hipError_t e = tpg::launch_permute(p, P, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("permute launch failed: ") + hipGetErrorString(e));
+  return TPG_OK;
+}
+
+template <typename F>
+tpg_status guarded(F&& f) {
+  try {
+    g_err.clear();
+    return f();
+  } catch (const std::exception& ex) {
+    return fail(TPG_ERR_HIP, std::string("host exception: ") + ex.what());
+  } catch (...) {
+    return fail(TPG_ERR_HIP, "unknown host exception");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tpgemm_stage_ag_workspace_size(const tpg_ag_args* args) { return ag_ws(args); }
+
+tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
+  return guarded([&]() -> tpg_status {
+    std::lock_guard<std::mutex> lk(g_mu);
+    tpg_status st = validate_ag(args, ag_ws(args));
+    if (st != TPG_OK) return st;
+    if (args->M == 0 || args->N == 0) return TPG_OK;       // empty output: nothing to enqueue
+    Ctx* cx = nullptr;
+    st = get_ctx(&cx);
+    if (st != TPG_OK) return st;
+    const tpg_ag_args a = *args;
+    return run_call(*cx, a.flags, ag_key(a), static_cast<hipStream_t>(stream),
+                    [&](const Launch& L) { return enqueue_ag(*cx, a, L); });
+  });
+}
+
+size_t tpgemm_stage_rs_workspace_size(const tpg_rs_args* args) { return rs_ws(args); }
+
+tpg_status tpgemm_stage_rs(const tpg_rs_args* args, void* stream) {
+  return guarded([&]() -> tpg_status {
+    std::lock_guard<std::mutex> lk(g_mu);
+    tpg_status st = validate_rs(args, rs_ws(args));
+    if (st != TPG_OK) return st;
+    if (args->M == 0 || args->N == 0) return TPG_OK;       // empty output: nothing to enqueue
+    Ctx* cx = nullptr;
+    st = get_ctx(&cx);
+    if (st != TPG_OK) return st;
+    const tpg_rs_args a = *args;
+    return run_call(*cx, a.flags, rs_key(a), static_cast<hipStream_t>(stream),
+                    [&](const Launch& L) { return enqueue_rs(*cx, a, L); });
+  });
+}
+
+size_t ffn_slot_forward_workspace_size(const tpg_ffn_args* args) { return ffn_ws(args); }
+
+tpg_status ffn_slot_forward(const tpg_ffn_args* args, void* stream) {
+  return guarded([&]() -> tpg_status {
+    std::lock_guard<std::mutex> lk(g_mu);
+    tpg_status st = validate_ffn(args, ffn_ws(args));
+    if (st != TPG_OK) return st;
+    if (args->PB == 0 || args->L == 0 || args->D == 0) return TPG_OK;
+    Ctx* cx = nullptr;
+    st = get_ctx(&cx);
+    if (st != TPG_OK) return st;
+    const tpg_ffn_args a = *args;
+    return run_call(*cx, a.flags, ffn_key(a), static_cast<hipStream_t>(stream),
+                    [&](const Launch& L) { return enqueue_ffn(*cx, a, L); });
+  });
+}
+
+tpg_status dispatch_permute(const void* const* src, void* dst, int32_t P, int32_t rank, int64_t B,
+                            int64_t T, int64_t D, int32_t elem_bytes, void* stream) {
+  return guarded([&]() { return permute_common(true, src, dst, P, rank, B, T, D, elem_bytes, stream); });
+}
+
+tpg_status combine_permute(const void* const* src, void* dst, int32_t P, int32_t rank, int64_t B,
+                           int64_t T, int64_t D, int32_t elem_bytes, void* stream) {
+  return guarded([&]() { return permute_common(false, src, dst, P, rank, B, T, D, elem_bytes, stream); });
+}
+
+const char* tpg_last_error(void) { return g_err.c_str(); }
+
+void tpg_release_caches(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_ctx.empty()) return;
+  (void)hipDeviceSynchronize();
+  for (auto& kv : g_ctx) destroy_ctx(kv.second);
+  g_ctx.clear();
+}
+
+int32_t tpg_profile_read(float* ms, double* flop, int32_t cap) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int32_t n = 0;
+  for (auto& kv : g_ctx) {
+    Ctx& c = *kv.second;
+    for (auto& r : c.prof) {
+      if (n < cap && hipEventSynchronize(r.b) == hipSuccess) {
+        float t = 0.0f;
+        if (hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+          if (ms) ms[n] = t;
+          if (flop) flop[n] = r.flop;
+          ++n;
+        }
+      }
+      c.prof_pool.push_back(r.a);
+      c.prof_pool.push_back(r.b);
+    }
+    c.prof.clear();
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal interface of the stage GEMM kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpg {
+
+constexpr int kMaxAddList = 16;
+
+// One GEMM launch: D = epilogue(alpha * A * B^T) over an (M, Ncols) block.
+// A (M, K) with row stride lda elements; B (N, K) (nk) or (K, N) (kn) with
+// row stride ldb. C / D / bias / addends are bf16 bit patterns.
+struct GemmParams {
+  const void* a;
+  const void* b;
+  const uint16_t* c;
+  uint16_t* d;
+  const uint16_t* bias;        // [N out] or nullptr
+  int64_t lda, ldb, ldc, ldd;  // in elements
+  int M, N, K;                 // N = accumulator columns (2n for swiglu)
+  float alpha, beta;
+  // extra bf16 addends summed into rows [add_row0, add_row1) of the output
+  // (the reduce-scatter incoming partials), fp32 accumulate:
+  //   add_list[0..n_add_list) and add_base + i * add_stride (i < n_add_strided)
+  const uint16_t* add_list[kMaxAddList];
+  int n_add_list;
+  const uint16_t* add_base;
+  int64_t add_stride;          // elements between strided addends
+  int n_add_strided;
+  int64_t ld_add;              // row stride of every addend (elements)
+  int add_row0, add_row1;
+  int vec_ok;                  // 1 if ldc, ldd, ld_add are multiples of 4 (8-byte rows groups)
+};
+
+enum GemmDtype { kBf16 = 0, kE4m3 = 1 };
+enum GemmLayout { kNK = 0, kKN = 1 };
+enum GemmEpi { kEpiAlphaBeta = 0, kEpiSwiglu = 1 };
+
+// Picks a tile shape for (M, N) and launches on `s`. Host-side checks of the
+// shapes and alignment are the caller's job (api.cpp validates every call).
+hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);
+
+// Workgroup count the launcher would use (for tests of the tile choice).
+int gemm_grid_size(int M, int N, int epi);
+
+// Row-wise LayerNorm(u) * silu(LayerNorm(g)) over z = [u | g] (each H wide).
+hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t ldh, int rows, int H,
+                          const uint16_t* gx, const uint16_t* bx, const uint16_t* gg,
+                          const uint16_t* bg, float eps, hipStream_t s);
+
+// Bit-exact run permute used by dispatch / combine.
+struct PermuteParams {
+  const uint8_t* src[64];
+  uint8_t* dst;
+  int64_t B;              // runs per source
+  int64_t run_bytes;
+  int64_t src_base, src_bstride;
+  int64_t dst_sstride, dst_bstride;
+};
+hipError_t launch_permute(const PermuteParams& p, int P, hipStream_t s);
+
+}  // namespace tpg

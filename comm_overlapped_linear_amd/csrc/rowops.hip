@@ -1,0 +1,198 @@
+// Row kernels: the FFN's LayerNorm / SiLU gate and the All-to-All permutes.
+//
+// ln_silu: for each row of z = [u | g] (p04 statement, "Computation and
+// communication example"), h = LN(u; gx, bx) * silu(LN(g; gg, bg)) with
+// LN(v) = (v - mean) / sqrt(mean((v - mean)^2) + eps) * gamma + beta.
+// One 256-thread workgroup per row; the row is read once from HBM into
+// registers (16-byte loads), the mean and then the centred second moment are
+// formed with wave64 butterfly reductions plus a 4-entry LDS exchange, and
+// the gated product is written as bf16. HBM-bound: 6H bytes per row.
+//
+// permute: the dispatch / combine layout maps of the same statement ("Interface,
+// layout, and parameters") are unions of contiguous runs (one per source rank
+// and batch row, L*D elements long); each workgroup copies 16-byte chunks of
+// one run, bit-exactly.
+#include "common.h"
+#include "gemm.h"
+
+namespace tpg {
+
+namespace {
+
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum over the workgroup of two values at once.
+__device__ __forceinline__ float2 block_sum2(float a, float b, float2* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = make_float2(a, b);
+  __syncthreads();
+  float2 s = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) { s.x += red[w].x; s.y += red[w].y; }
+  return s;
+}
+
+__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(w[i] & 0xffff);
+    f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+
+// CH = 8-element chunks per thread per half (H <= 8 * 256 * CH).
+template <int CH>
+__global__ __launch_bounds__(kRowThreads) void ln_silu_kernel(
+    const uint16_t* __restrict__ z, int64_t ldz, uint16_t* __restrict__ h, int64_t ldh, int H,
+    const uint16_t* __restrict__ gx, const uint16_t* __restrict__ bx,
+    const uint16_t* __restrict__ gg, const uint16_t* __restrict__ bg, float eps) {
+  __shared__ float2 red[kRowThreads / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t* zu = z + row * ldz;
+  const uint16_t* zg = zu + H;
+  const int nchunk = H >> 3;
+  float u[CH][8], g[CH][8];
+  float su = 0.f, sg = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = c * kRowThreads + threadIdx.x;
+    if (ch < nchunk) {
+      unpack8(*reinterpret_cast<const uint4*>(zu + ch * 8), u[c]);
+      unpack8(*reinterpret_cast<const uint4*>(zg + ch * 8), g[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { su += u[c][e]; sg += g[c][e]; }
+    }
+  }
+  const float inv_h = 1.0f / static_cast<float>(H);
+  float2 s = block_sum2(su, sg, red);
+  const float mu = s.x * inv_h, mg = s.y * inv_h;
+  float qu = 0.f, qg = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = c * kRowThreads + threadIdx.x;
+    if (ch < nchunk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float du = u[c][e] - mu, dg = g[c][e] - mg;
+        qu += du * du;
+        qg += dg * dg;
+      }
+    }
+  }
+  s = block_sum2(qu, qg, red);
+  const float ru = rsqrtf(s.x * inv_h + eps), rg = rsqrtf(s.y * inv_h + eps);
+  uint16_t* hr = h + row * ldh;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = c * kRowThreads + threadIdx.x;
+    if (ch < nchunk) {
+      float a[8], b[8], cc[8], d[8];
+      unpack8(*reinterpret_cast<const uint4*>(gx + ch * 8), a);
+      unpack8(*reinterpret_cast<const uint4*>(bx + ch * 8), b);
+      unpack8(*reinterpret_cast<const uint4*>(gg + ch * 8), cc);
+      unpack8(*reinterpret_cast<const uint4*>(bg + ch * 8), d);
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float x0 = (u[c][e] - mu) * ru * a[e] + b[e];
+        const float x1 = (u[c][e + 1] - mu) * ru * a[e + 1] + b[e + 1];
+        const float y0 = (g[c][e] - mg) * rg * cc[e] + d[e];
+        const float y1 = (g[c][e + 1] - mg) * rg * cc[e + 1] + d[e + 1];
+        o[e / 2] = f32_to_bf16(x0 * silu_f32(y0)) |
+                   (static_cast<uint32_t>(f32_to_bf16(x1 * silu_f32(y1))) << 16);
+      }
+      *reinterpret_cast<uint4*>(hr + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+constexpr int kPermThreads = 256;
+constexpr int kPermUnroll = 4;
+
+__global__ __launch_bounds__(kPermThreads) void permute16_kernel(const PermuteParams p) {
+  const int64_t run = blockIdx.x;          // run = s * B + b
+  const int s = static_cast<int>(run / p.B);
+  const int64_t b = run - s * p.B;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* src = reinterpret_cast<const u32x4*>(p.src[s] + p.src_base + b * p.src_bstride);
+  u32x4* dst = reinterpret_cast<u32x4*>(p.dst + s * p.dst_sstride + b * p.dst_bstride);
+  const int64_t nvec = p.run_bytes >> 4;
+  const int64_t base = static_cast<int64_t>(blockIdx.y) * kPermThreads * kPermUnroll + threadIdx.x;
+  u32x4 v[kPermUnroll];
+#pragma unroll
+  for (int u = 0; u < kPermUnroll; ++u) {
+    const int64_t i = base + u * kPermThreads;
+    if (i < nvec) v[u] = __builtin_nontemporal_load(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < kPermUnroll; ++u) {
+    const int64_t i = base + u * kPermThreads;
+    if (i < nvec) __builtin_nontemporal_store(v[u], dst + i);
+  }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute1_kernel(const PermuteParams p) {
+  const int64_t run = blockIdx.x;
+  const int s = static_cast<int>(run / p.B);
+  const int64_t b = run - s * p.B;
+  const uint8_t* src = p.src[s] + p.src_base + b * p.src_bstride;
+  uint8_t* dst = p.dst + s * p.dst_sstride + b * p.dst_bstride;
+  for (int64_t i = static_cast<int64_t>(blockIdx.y) * kPermThreads + threadIdx.x; i < p.run_bytes;
+       i += static_cast<int64_t>(gridDim.y) * kPermThreads)
+    dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t ldh, int rows, int H,
+                          const uint16_t* gx, const uint16_t* bx, const uint16_t* gg,
+                          const uint16_t* bg, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int nchunk = H / 8;
+  const int per = (nchunk + kRowThreads - 1) / kRowThreads;
+  dim3 grid(rows), block(kRowThreads);
+  if (per <= 1)
+    hipLaunchKernelGGL(ln_silu_kernel<1>, grid, block, 0, s, z, ldz, h, ldh, H, gx, bx, gg, bg, eps);
+  else if (per <= 2)
+    hipLaunchKernelGGL(ln_silu_kernel<2>, grid, block, 0, s, z, ldz, h, ldh, H, gx, bx, gg, bg, eps);
+  else if (per <= 4)
+    hipLaunchKernelGGL(ln_silu_kernel<4>, grid, block, 0, s, z, ldz, h, ldh, H, gx, bx, gg, bg, eps);
+  else if (per <= 8)
+    hipLaunchKernelGGL(ln_silu_kernel<8>, grid, block, 0, s, z, ldz, h, ldh, H, gx, bx, gg, bg, eps);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const PermuteParams& p, int P, hipStream_t s) {
+  const int64_t runs = static_cast<int64_t>(P) * p.B;
+  if (runs == 0 || p.run_bytes == 0) return hipSuccess;
+  bool aligned = (p.run_bytes % 16 == 0) && (p.src_base % 16 == 0) && (p.src_bstride % 16 == 0) &&
+                 (p.dst_sstride % 16 == 0) && (p.dst_bstride % 16 == 0) &&
+                 (reinterpret_cast<uintptr_t>(p.dst) % 16 == 0);
+  for (int i = 0; i < P; ++i) aligned = aligned && (reinterpret_cast<uintptr_t>(p.src[i]) % 16 == 0);
+  if (aligned) {
+    const int64_t nvec = p.run_bytes / 16;
+    const int64_t gx = (nvec + kPermThreads * kPermUnroll - 1) / (kPermThreads * kPermUnroll);
+    hipLaunchKernelGGL(permute16_kernel, dim3(static_cast<unsigned>(runs), static_cast<unsigned>(gx)),
+                       dim3(kPermThreads), 0, s, p);
+  } else {
+    int64_t gx = (p.run_bytes + kPermThreads - 1) / kPermThreads;
+    if (gx > 64) gx = 64;
+    hipLaunchKernelGGL(permute1_kernel, dim3(static_cast<unsigned>(runs), static_cast<unsigned>(gx)),
+                       dim3(kPermThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpg

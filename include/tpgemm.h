@@ -1,0 +1,229 @@
+/*
+ * tpgemm.h -- C ABI of the MI355X (gfx950) staged tensor-parallel GEMM share.
+ *
+ * One GPU runs the rank-local share of a tensor-parallel GEMM as P ordered
+ * stages. The peers' shards are ordinary device buffers in the same HBM;
+ * each stage's input is delivered by an asynchronous device-to-device copy on
+ * a library-owned copy stream and gated by a HIP event, so the matrix cores
+ * start on the local shard while the copy engine delivers the rest
+ * ("Distributed GEMM", Hassani et al., SHI Labs, Dec 2024: Introduction and
+ * Background, Figures 3 and 4).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers to tensor data are DEVICE pointers owned by the caller;
+ *     pointer arrays (a_slices, incoming, src) are HOST arrays of device
+ *     pointers, read during the call only. The library never frees or
+ *     retains caller memory beyond the cached graphs described below.
+ *   - Matrices are dense row-major with the leading dimension equal to the
+ *     row length stated for each argument. bf16 is IEEE binary32's top half;
+ *     e4m3 is OCP 8-bit E4M3FN (bias 7, max 448, no infinities).
+ *   - Every call is asynchronous on `stream` (a hipStream_t, NULL = the
+ *     legacy default stream): the call forks its internal streams from
+ *     `stream` and joins them back before returning, so work enqueued later
+ *     on `stream` sees the results. No call blocks the host on the GPU.
+ *   - Inputs are never written (p04 statement, "Interface, layout, and
+ *     parameters": inputs must not be mutated).
+ *   - Arguments are validated before anything is enqueued; a failing call
+ *     enqueues nothing and returns a non-zero status, with a message from
+ *     tpg_last_error(). There is no fallback path.
+ *   - Graph cache: unless TPG_NO_GRAPH is set, the first call with a given
+ *     (entry point, shapes, pointers, scalars, flags, stream-independent
+ *     plan) records the call into a hipGraph that later identical calls
+ *     replay. A changed pointer makes a new graph, never a stale replay.
+ *     Freeing a buffer a cached graph refers to is safe as long as that
+ *     exact argument set is not called again; tpg_release_caches() drops
+ *     all graphs.
+ *   - Calls on one device serialise on an internal lock; two calls whose
+ *     workspaces overlap must not be in flight at once on different streams.
+ */
+#ifndef TPGEMM_H
+#define TPGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TPG_OK = 0,
+  TPG_ERR_INVALID = 1,      /* bad shape, rank, NULL pointer, aliasing, beta != 0 without C */
+  TPG_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (dtype/layout/alignment) */
+  TPG_ERR_WORKSPACE = 3,    /* workspace missing or smaller than *_workspace_size() */
+  TPG_ERR_HIP = 4           /* a HIP runtime call failed; see tpg_last_error() */
+} tpg_status;
+
+typedef enum { TPG_BF16 = 0, TPG_E4M3 = 1 } tpg_dtype;
+
+/* Layout of the B operand. NK: B is (N, K) row-major, as the distributed GEMM
+ * op takes it ("Pytorch Op for blackwell distributed gemm", Note on Tensor
+ * Layouts). KN: B is (K, N) row-major, the weight layout of the p04 FFN
+ * (w1 [L, D, 2H], wout [L, H, D]) and of the torchtitan SwiGLU shards. */
+typedef enum { TPG_B_NK = 0, TPG_B_KN = 1 } tpg_blayout;
+
+typedef enum {
+  TPG_EPI_ALPHA_BETA = 0,   /* D = alpha * acc + beta * C */
+  TPG_EPI_SWIGLU = 1        /* acc has N = 2n columns [u | v]; D = silu(alpha u) * (alpha v) + beta * C, D is (M, n) */
+} tpg_epilogue;
+
+/* flags (bitwise or) */
+enum {
+  TPG_UNSTAGED = 1u,        /* single stage: deliver everything, then one GEMM (the non-overlapped baseline) */
+  TPG_NO_COPY = 2u,         /* read peer buffers in place; no deliveries (compute-only timing) */
+  TPG_NO_GRAPH = 4u,        /* enqueue eagerly instead of capturing / replaying a hipGraph */
+  TPG_COPY_BLIT = 8u,       /* deliver with the shader copy (uses CUs) instead of the copy engines */
+  TPG_SERIAL_STAGES = 16u,  /* run all stage GEMMs on one compute stream (no inter-stage concurrency) */
+  TPG_PROFILE = 32u         /* eager only: time every GEMM launch with HIP events (tpg_profile_read) */
+};
+
+/* ------------------------------------------------------------------------
+ * All-gather staged GEMM.
+ * D = alpha * A * B^T + beta * C with A (M, K) split into P row slices of
+ * m = M/P rows; slice s is rank s's shard ("Pytorch Op for blackwell
+ * distributed gemm", Usage: alpha * (A @ B_T) + beta * C; "Distributed GEMM",
+ * Approach: schedule AllGather1D_TilingCD_RotatingA, C and D tiled by the same
+ * rows). Stage t computes rows [s*m, (s+1)*m) of D from slice
+ * s = (rank + t) mod P, the local slice first (Background, Figure 4).
+ *
+ *   M, N, K      M % P == 0. N = rows of B (NK) or columns of B (KN);
+ *                with TPG_EPI_SWIGLU N is even and D has N/2 columns.
+ *   P, rank      1 <= P <= 64, 0 <= rank < P.
+ *   ab_dtype     TPG_BF16 (K % 8 == 0) or TPG_E4M3 (K % 16 == 0, NK only).
+ *   b_layout     TPG_B_NK or TPG_B_KN (KN needs N % 8 == 0).
+ *   a_slices     host array of P device pointers, each (m, K) row-major.
+ *   b            (N, K) or (K, N) row-major.
+ *   c            bf16 (M, Nout); never read when beta == 0 (may be NULL then).
+ *   d            bf16 (M, Nout) output; must not overlap any input.
+ *   workspace    device buffer of at least tpgemm_stage_ag_workspace_size()
+ *                bytes (receive slots for the P-1 delivered slices; with
+ *                TPG_UNSTAGED the whole gathered A). May be NULL if that size
+ *                is 0. Contents are scratch.
+ * All device pointers must be 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t M, N, K;
+  int32_t P, rank;
+  int32_t ab_dtype;
+  int32_t b_layout;
+  int32_t epilogue;
+  const void* const* a_slices;
+  const void* b;
+  const void* c;
+  void* d;
+  float alpha, beta;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+} tpg_ag_args;
+
+size_t tpgemm_stage_ag_workspace_size(const tpg_ag_args* args);
+tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Reduce-scatter staged GEMM (the dual).
+ * A (M, K) is this rank's K shard, so E = alpha * A * B^T is a partial sum
+ * whose P row blocks of m = M/P belong to the P ranks ("Distributed GEMM",
+ * Background, Figure 3: GEMM + Reduce Scatter; Approach: schedule
+ * ReduceScatter1D_TilingA_RotatingC). Stage t computes block
+ * (rank + 1 + t) mod P, own block last. Block b != rank of D receives the
+ * emitted partial alpha * E_b; block rank receives
+ * alpha * E_rank + sum_{j != rank} incoming[j], accumulated in fp32 and
+ * rounded once to bf16. The incoming partials are delivered into the
+ * workspace by the copy stream and gate the last stage only.
+ *
+ *   M, N, K      M % P == 0; K % 8 == 0 (bf16) or 16 (e4m3, NK only).
+ *   a            (M, K) row-major.   b  (N, K) or (K, N) row-major.
+ *   incoming     NULL, or a host array of P device pointers to bf16 (m, N)
+ *                partials; entry [rank] and NULL entries are ignored.
+ *   d            bf16 (M, N) output; must not overlap any input.
+ *   workspace    >= tpgemm_stage_rs_workspace_size() bytes (receive slots).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t M, N, K;
+  int32_t P, rank;
+  int32_t ab_dtype;
+  int32_t b_layout;
+  const void* a;
+  const void* b;
+  const void* const* incoming;
+  void* d;
+  float alpha;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+} tpg_rs_args;
+
+size_t tpgemm_stage_rs_workspace_size(const tpg_rs_args* args);
+tpg_status tpgemm_stage_rs(const tpg_rs_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-token-slot FFN, compute-only part of the p04 layer ("Computation and
+ * communication example"; comp_only in "Interface, layout, and parameters").
+ * For n < PB = P*B rows and slot l < L = T/P, with H the hidden width:
+ *   z = x[n, l, :] @ w1[l] + b1[l];  u = z[:H], g = z[H:]
+ *   h = LN(u; gx, bx) * silu(LN(g; gg, bg)),  LN with population variance
+ *       and eps inside the square root
+ *   y[n, l, :] = h @ wout[l] + bout[l]
+ * All tensors bf16, row-major: x, y [PB, L, D]; w1 [L, D, 2H]; b1 [L, 2H];
+ * wout [L, H, D]; bout [L, D]; gx, bx, gg, bg [H]. D % 8 == 0, H % 8 == 0.
+ * Intermediates z (bf16) and h (bf16) live in the workspace
+ * (>= ffn_slot_forward_workspace_size() bytes); accumulation and the
+ * LayerNorm statistics are fp32.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t PB, L, D, H;
+  const void* x;
+  const void* w1;
+  const void* b1;
+  const void* wout;
+  const void* bout;
+  const void* gx;
+  const void* bx;
+  const void* gg;
+  const void* bg;
+  float eps;
+  void* y;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+} tpg_ffn_args;
+
+size_t ffn_slot_forward_workspace_size(const tpg_ffn_args* args);
+tpg_status ffn_slot_forward(const tpg_ffn_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * All-to-All dispatch / combine as single-GPU layout permutes (p04 statement,
+ * "Interface, layout, and parameters" and "Computation and communication
+ * example"). With L = T/P (T % P == 0):
+ *   dispatch_permute: dst[s*B + b, l, :] = src[s][b, rank*L + l, :]
+ *     src: host array of P device pointers, each [B, T, D]; dst [P*B, L, D].
+ *   combine_permute:  dst[b, s*L + l, :] = src[s][rank*B + b, l, :]
+ *     src: host array of P device pointers, each [P*B, L, D]; dst [B, T, D].
+ * elem_bytes is the element size (1, 2, 4 or 8); the copy is bit-exact.
+ * dst must not overlap any source. 1 <= P <= 64.
+ * ---------------------------------------------------------------------- */
+tpg_status dispatch_permute(const void* const* src, void* dst, int32_t P, int32_t rank,
+                            int64_t B, int64_t T, int64_t D, int32_t elem_bytes, void* stream);
+tpg_status combine_permute(const void* const* src, void* dst, int32_t P, int32_t rank,
+                           int64_t B, int64_t T, int64_t D, int32_t elem_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ * tpg_last_error: message of the last failing call on this host thread
+ *   (empty string if none); valid until the next call on the thread.
+ * tpg_release_caches: synchronises the device, then destroys cached graphs,
+ *   internal streams and events. Later calls recreate them.
+ * tpg_profile_read: after calls made with TPG_PROFILE (and a host sync),
+ *   writes up to `cap` per-GEMM-launch durations in milliseconds and their
+ *   algorithmic flop counts, oldest first, clears the record and returns how
+ *   many were written.
+ * ---------------------------------------------------------------------- */
+const char* tpg_last_error(void);
+void tpg_release_caches(void);
+int32_t tpg_profile_read(float* ms, double* flop, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPGEMM_H */

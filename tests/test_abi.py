@@ -1,0 +1,97 @@
+"""C ABI checks that need no GPU: every symbol the header declares is
+exported, argument validation rejects bad calls before enqueuing anything,
+and the workspace-size queries are pure functions of the arguments."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import comm_overlapped_linear_amd as tp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tpgemm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tp.LIB_PATH), reason="libtpgemm.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"tpgemm_stage_ag", "tpgemm_stage_rs", "ffn_slot_forward", "dispatch_permute",
+            "combine_permute"} <= set(names)
+    L = ctypes.CDLL(tp.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+FAKE = 0x10000000   # a 16-byte aligned non-NULL address; validation never dereferences it
+
+
+def ag(**kw):
+    P = kw.pop("P", 2)
+    slices = (ctypes.c_void_p * P)(*[FAKE + i * 0x1000000 for i in range(P)])
+    base = dict(M=256, N=256, K=512, P=P, rank=0, ab_dtype=tp.BF16, b_layout=tp.B_NK, epilogue=0,
+                a_slices=ctypes.cast(slices, ctypes.POINTER(ctypes.c_void_p)), b=FAKE + 0x10000000,
+                c=FAKE + 0x20000000, d=FAKE + 0x30000000, alpha=1.0, beta=1.0, workspace=FAKE + 0x40000000,
+                workspace_bytes=1 << 30, flags=0)
+    base.update(kw)
+    a = tp.AgArgs(**base)
+    a._keep = slices
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=255), tp.ERR_INVALID),                      # M % P
+    (dict(rank=2), tp.ERR_INVALID),
+    (dict(P=65), tp.ERR_INVALID),
+    (dict(c=None), tp.ERR_INVALID),                     # beta != 0 without C
+    (dict(K=500), tp.ERR_UNSUPPORTED),                  # K % 8
+    (dict(ab_dtype=tp.E4M3, K=520), tp.ERR_UNSUPPORTED),  # K % 16 for e4m3
+    (dict(ab_dtype=tp.E4M3, b_layout=tp.B_KN), tp.ERR_UNSUPPORTED),
+    (dict(b=FAKE + 0x10000008), tp.ERR_UNSUPPORTED),    # misaligned
+    (dict(d=FAKE), tp.ERR_INVALID),                     # D aliases slice 0
+    (dict(workspace_bytes=10), tp.ERR_WORKSPACE),
+    (dict(flags=1 << 20), tp.ERR_INVALID),
+    (dict(epilogue=tp.EPI_SWIGLU, N=255), tp.ERR_INVALID),
+])
+def test_ag_validation_rejects_before_enqueue(kw, status):
+    a = ag(**kw)
+    assert tp.lib().tpgemm_stage_ag(ctypes.byref(a), None) == status
+    assert tp.last_error()
+
+
+def test_workspace_sizes_are_pure():
+    a = ag(P=8, M=8192, K=8192, ab_dtype=tp.E4M3)
+    assert tp.stage_ag_workspace_size(a) == 7 * 1024 * 8192
+    a.flags = tp.UNSTAGED
+    assert tp.stage_ag_workspace_size(a) == 8 * 1024 * 8192
+    a.flags = tp.NO_COPY
+    assert tp.stage_ag_workspace_size(a) == 0
+    inc = (ctypes.c_void_p * 8)(*[FAKE] * 8)
+    r = tp.RsArgs(M=8192, N=8192, K=3584, P=8, rank=0, ab_dtype=0, b_layout=0, a=FAKE, b=FAKE,
+                  incoming=ctypes.cast(inc, ctypes.POINTER(ctypes.c_void_p)), d=FAKE, alpha=1.0,
+                  workspace=None, workspace_bytes=0, flags=0)
+    assert tp.stage_rs_workspace_size(r) == 7 * 1024 * 8192 * 2
+    f = tp.FfnArgs(PB=4096, L=8, D=1280, H=7680, flags=0)
+    assert tp.ffn_slot_forward_workspace_size(f) == 2 * 4096 * 3 * 7680 * 2
+
+
+def test_rs_and_ffn_and_permute_validation():
+    r = tp.RsArgs(M=100, N=64, K=64, P=8, rank=0, ab_dtype=0, b_layout=0, a=FAKE, b=FAKE + 0x1000000,
+                  incoming=None, d=FAKE + 0x2000000, alpha=1.0, workspace=None, workspace_bytes=0, flags=0)
+    assert tp.lib().tpgemm_stage_rs(ctypes.byref(r), None) == tp.ERR_INVALID      # M % P
+    f = tp.FfnArgs(PB=8, L=2, D=12, H=16, x=FAKE, w1=FAKE, b1=FAKE, wout=FAKE, bout=FAKE, gx=FAKE,
+                   bx=FAKE, gg=FAKE, bg=FAKE, eps=1e-5, y=FAKE + 0x1000000, flags=0)
+    assert tp.lib().ffn_slot_forward(ctypes.byref(f), None) == tp.ERR_UNSUPPORTED   # D % 8
+    srcs = (ctypes.c_void_p * 2)(FAKE, FAKE + 0x100000)
+    sp = ctypes.cast(srcs, ctypes.POINTER(ctypes.c_void_p))
+    assert tp.lib().dispatch_permute(sp, FAKE + 0x200000, 2, 0, 1, 3, 4, 2, None) == tp.ERR_INVALID  # T % P
+    assert tp.lib().combine_permute(sp, FAKE + 0x200000, 2, 2, 1, 2, 4, 2, None) == tp.ERR_INVALID   # rank
+    assert tp.lib().dispatch_permute(sp, FAKE, 2, 0, 1, 2, 4, 2, None) == tp.ERR_INVALID             # aliasing
+    assert tp.lib().dispatch_permute(sp, FAKE + 0x200000, 2, 0, 1, 2, 4, 3, None) == tp.ERR_INVALID  # elem size

@@ -1,0 +1,117 @@
+"""GPU parity of the staged all-gather GEMM against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import comm_overlapped_linear_amd as tp
+import oracle
+from synth import gen, workloads as W
+from tests.devutil import say, dev, bf16_empty, host_f64, bf16_bits_of
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"graph": 0, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED, "no_copy": tp.NO_COPY,
+         "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "blit": tp.COPY_BLIT}
+
+
+def run_ag(case, inp, flags, rank=None):
+    slices = [dev(s) for s in inp["a_slices"]]
+    if flags & tp.UNSTAGED and flags & tp.NO_COPY:
+        raise ValueError("not used")
+    b, c = dev(inp["b"]), dev(inp["c"])
+    nout = case.N // 2 if case.swiglu else case.N
+    d = bf16_empty(case.M, nout)
+    tp.stage_ag(slices, b, c, d, M=case.M, N=case.N, K=case.K, rank=case.rank if rank is None else rank,
+                dtype=tp.E4M3 if case.dtype == "e4m3" else tp.BF16,
+                b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK,
+                epilogue=tp.EPI_SWIGLU if case.swiglu else tp.EPI_ALPHA_BETA,
+                alpha=case.alpha, beta=case.beta, flags=flags)
+    torch.cuda.synchronize()
+    return d
+
+
+def oracle_ag(case, inp):
+    return oracle.gemm_ag(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, case.rank,
+                          case.dtype, case.b_layout, swiglu=case.swiglu)
+
+
+@pytest.mark.parametrize("case", W.SMALL_AG + [W.C1], ids=lambda c: c.name)
+def test_ag_parity_all_modes(case):
+    inp = W.ag_inputs(case)
+    ref = oracle_ag(case, inp)
+    outs = {}
+    for name, flags in MODES.items():
+        say(f"ag: {case.name} mode={name}")
+        d = run_ag(case, inp, flags)
+        assert_parity(host_f64(d), ref, f"{case.name}/{name}")
+        outs[name] = d.cpu()
+    # staging only partitions rows: every mode is bitwise identical
+    for name in MODES:
+        assert torch.equal(outs[name], outs["graph"]), name
+
+
+def test_ag_integer_inputs_are_bit_exact():
+    """Inputs in {-1, 0, 1}: fp32 sums are exact, so D must equal the
+    round-to-nearest-even of the exact result, bit for bit."""
+    rng = np.random.default_rng(3)
+    P, m, N, K = 4, 72, 136, 320
+    slices = [gen.encode_bf16(rng.integers(-1, 2, (m, K))) for _ in range(P)]
+    b = gen.encode_bf16(rng.integers(-1, 2, (N, K)))
+    c = gen.encode_bf16(rng.integers(-3, 4, (P * m, N)) * 0.5)
+    case = W.AgCase("int", M=P * m, N=N, K=K, P=P, rank=2, alpha=1.0, beta=1.0)
+    say("ag: integer exactness")
+    d = run_ag(case, dict(a_slices=slices, b=b, c=c), 0)
+    ref = oracle.gemm_ag(slices, b, c, 1.0, 1.0, 2)
+    assert np.array_equal(d.cpu().numpy(), bf16_bits_of(ref))
+    # e4m3 with quarter-integers: still exact in fp32
+    s8 = [gen.encode_e4m3(rng.integers(-4, 5, (m, K)) * 0.25) for _ in range(P)]
+    b8 = gen.encode_e4m3(rng.integers(-4, 5, (N, K)) * 0.5)
+    case8 = W.AgCase("int8", M=P * m, N=N, K=K, P=P, rank=1, dtype="e4m3", alpha=1.0, beta=0.0)
+    d8 = run_ag(case8, dict(a_slices=s8, b=b8, c=None), 0)
+    ref8 = oracle.gemm_ag(s8, b8, None, 1.0, 0.0, 1, "e4m3")
+    assert np.array_equal(d8.cpu().numpy(), bf16_bits_of(ref8))
+
+
+def test_ag_beta_zero_never_reads_c():
+    case = W.SMALL_AG[3]
+    inp = W.ag_inputs(case)
+    say("ag: beta=0 with NaN C")
+    slices = [dev(s) for s in inp["a_slices"]]
+    nan_c = bf16_empty(case.M, case.N)          # NaN everywhere
+    d = bf16_empty(case.M, case.N)
+    tp.stage_ag(slices, dev(inp["b"]), nan_c, d, M=case.M, N=case.N, K=case.K, dtype=tp.E4M3,
+                alpha=1.0, beta=0.0)
+    torch.cuda.synchronize()
+    assert_parity(host_f64(d), oracle_ag(case, inp), "beta0")
+
+
+def test_ag_graph_replay_sees_new_data():
+    case = W.SMALL_AG[0]
+    inp = W.ag_inputs(case)
+    slices = [dev(s) for s in inp["a_slices"]]
+    b, c = dev(inp["b"]), dev(inp["c"])
+    d = bf16_empty(case.M, case.N)
+    kw = dict(M=case.M, N=case.N, K=case.K, rank=0, alpha=1.0, beta=1.0)
+    say("ag: graph replay with changed inputs")
+    for it in range(3):
+        tp.stage_ag(slices, b, c, d, **kw)      # same pointers: replays one graph
+        torch.cuda.synchronize()
+        ref = oracle.gemm_ag([s.cpu().numpy().view(np.uint16) for s in slices], inp["b"],
+                             c.cpu().numpy().view(np.uint16), 1.0, 1.0, 0)
+        assert_parity(host_f64(d), ref, f"replay {it}")
+        for s in slices:                          # new slice contents in place
+            s.copy_(torch.roll(s, 1, dims=0))
+        c.copy_(torch.flip(c, dims=[0]))
+
+
+def test_ag_empty_and_single_stage():
+    say("ag: M=0 and P=1")
+    b = torch.zeros((64, 64), dtype=torch.int16, device="cuda")
+    d = torch.zeros((0, 64), dtype=torch.int16, device="cuda")
+    s0 = torch.zeros((0, 64), dtype=torch.int16, device="cuda")
+    tp.stage_ag([s0, s0.clone()], b, None, d, M=0, N=64, K=64, alpha=1.0, beta=0.0)
+    case = W.AgCase("p1", M=136, N=72, K=264, P=1, dist="u11")
+    inp = W.ag_inputs(case)
+    d = run_ag(case, inp, 0)
+    assert_parity(host_f64(d), oracle_ag(case, inp), "P=1")
