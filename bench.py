@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the staged tensor-parallel GEMM share on one MI355X.
+
+Default workload: the fp8 all-gather GEMM rank share, P = 8: A e4m3
+8192 x 8192 in eight ring-ordered 1024-row slices, B e4m3 1024 x 8192 (N x K),
+C bf16 8192 x 1024, alpha = beta = 1, bf16 out. One step is one full call of
+tpgemm_stage_ag: seven slice deliveries on the copy stream, eight gated stage
+GEMMs, the fused alpha/beta epilogue, replayed from its hipGraph. Inputs are
+resident in HBM before the timed region starts.
+
+Prints ONE JSON line. Diagnostics (compute-only time, delivery-only time,
+hidden fraction, unstaged time, L2-flushed time, other workloads) go into its
+"detail" object and to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import comm_overlapped_linear_amd as tp  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+METRIC = "staged TP-GEMM TFLOP/s + % MFMA peak (bf16/fp8) on 1 GPU; FFN-layer µs"
+PEAK_TFLOPS = {"fp8_e4m3": 5000.0, "bf16": 2500.0}     # MI355X dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(bits):
+    view = np.int16 if bits.dtype == np.uint16 else np.uint8
+    return torch.from_numpy(np.ascontiguousarray(bits).view(view)).cuda()
+
+
+class Hip:
+    """Direct HIP runtime calls used only for measurement (raw deliveries)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_int, ctypes.c_void_p]
+        self.lib.hipMemcpyAsync.restype = ctypes.c_int
+
+    def copy(self, dst, src, nbytes, kind, stream):
+        rc = self.lib.hipMemcpyAsync(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, kind,
+                                     ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed: {rc}")
+
+
+def time_steps(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def time_flushed(fn, steps, warmup, scratch):
+    """Per-call times with the caches flushed (a 512 MiB write) before each call."""
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(steps):
+        scratch.add_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    times = times[1:] if len(times) > 1 else times
+    return dict(mean=float(np.mean(times)), min=float(np.min(times)), max=float(np.max(times)),
+                median=float(np.median(times)))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max(i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas")
+    except Exception:
+        return os.cpu_count()
+
+
+# --------------------------------------------------------------------------- workloads
+def setup_ag(case):
+    inp = W.ag_inputs(case)
+    slices = [dev(s) for s in inp["a_slices"]]
+    b, c = dev(inp["b"]), dev(inp["c"]) if inp["c"] is not None else None
+    nout = case.N // 2 if case.swiglu else case.N
+    d = torch.empty((case.M, nout), dtype=torch.int16, device="cuda")
+    kw = dict(M=case.M, N=case.N, K=case.K, rank=case.rank,
+              dtype=tp.E4M3 if case.dtype == "e4m3" else tp.BF16,
+              b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK,
+              epilogue=tp.EPI_SWIGLU if case.swiglu else tp.EPI_ALPHA_BETA,
+              alpha=case.alpha, beta=case.beta)
+    eb = 1 if case.dtype == "e4m3" else 2
+    slice_bytes = case.m * case.K * eb
+    ws = torch.empty(slice_bytes * case.P, dtype=torch.uint8, device="cuda")   # fits every mode
+    prepared = tp.prepare_stage_ag(slices, b, c, d, workspace=ws, flags=tp.UNSTAGED, **kw)
+
+    def call(flags=0):
+        prepared(flags=flags)
+
+    side = [torch.cuda.Stream() for _ in range(4)]
+
+    def deliveries(hip, kind):
+        """The P-1 deliveries alone, spread over four streams like the library's copy streams."""
+        cur = torch.cuda.current_stream()
+        for st in side:
+            st.wait_stream(cur)
+        for t in range(1, case.P):
+            s = (case.rank + t) % case.P
+            hip.copy(ws.data_ptr() + (t - 1) * slice_bytes, slices[s].data_ptr(), slice_bytes, kind,
+                     side[(t - 1) % 4].cuda_stream)
+        for st in side:
+            cur.wait_stream(st)
+    return inp, call, deliveries, dict(d=d)
+
+
+def cpu_baseline_ag(case, inp):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.gemm_ag(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, case.rank,
+                   case.dtype, case.b_layout, swiglu=case.swiglu)
+    dt = time.perf_counter() - t0
+    return dict(value=case.flop / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                sample=f"the whole workload once ({case.flop / 1e9:.1f} GFLOP, float64 numpy), {dt:.2f} s")
+
+
+def bench_ag(case, args, detail):
+    inp, call, deliveries, bufs = setup_ag(case)
+    dtype = "fp8_e4m3" if case.dtype == "e4m3" else "bf16"
+    flop = case.flop
+    hip = Hip()
+
+    ms = time_steps(lambda: call(0), args.steps, args.warmup)
+    value = flop / (ms * 1e-3) / 1e12
+    log(f"[{case.name}] staged (graph, copy engines): {ms * 1e3:.1f} us/step  {value:.1f} TFLOP/s")
+
+    # dominant kernel: the stage GEMM, timed per launch with HIP events on its own stream
+    call(tp.PROFILE)
+    torch.cuda.synchronize()
+    tp.profile_read()
+    for _ in range(args.steps):
+        call(tp.PROFILE)
+    torch.cuda.synchronize()
+    recs = tp.profile_read()
+    kms = float(np.mean([r[0] for r in recs]))
+    kflop = float(np.mean([r[1] for r in recs]))
+    achieved = kflop / (kms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=None,
+                    kernel="gemm_kernel (one stage)", launches=len(recs),
+                    avg_launch_us=round(kms * 1e3, 2), flop_per_launch=kflop)
+    log(f"[{case.name}] stage GEMM: {kms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s per launch "
+        f"({len(recs)} launches, eager with events)")
+
+    if not args.quick:
+        t_compute = time_steps(lambda: call(tp.NO_COPY), args.steps, args.warmup)
+        t_serial_compute = time_steps(lambda: call(tp.NO_COPY | tp.SERIAL_STAGES), args.steps, args.warmup)
+        t_copy = time_steps(lambda: deliveries(hip, 1024), args.steps, args.warmup)
+        t_copy_blit = time_steps(lambda: deliveries(hip, 3), args.steps, args.warmup)
+        t_unstaged = time_steps(lambda: call(tp.UNSTAGED), args.steps, args.warmup)
+        t_blit = time_steps(lambda: call(tp.COPY_BLIT), args.steps, args.warmup)
+        t_eager = time_steps(lambda: call(tp.NO_GRAPH), args.steps, args.warmup)
+        hidden = 1.0 - (ms - t_compute) / t_copy if t_copy > 0 else None
+        hidden_blit = 1.0 - (t_blit - t_compute) / t_copy_blit if t_copy_blit > 0 else None
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flushed = time_flushed(lambda: call(0), max(args.steps, 10), 2, scratch)
+        del scratch
+        detail.update({
+            "us_staged": round(ms * 1e3, 2),
+            "us_compute_only": round(t_compute * 1e3, 2),
+            "us_compute_only_serial_stages": round(t_serial_compute * 1e3, 2),
+            "us_deliveries_copy_engine": round(t_copy * 1e3, 2),
+            "us_deliveries_blit": round(t_copy_blit * 1e3, 2),
+            "hidden_fraction": None if hidden is None else round(hidden, 3),
+            "us_staged_blit": round(t_blit * 1e3, 2),
+            "hidden_fraction_blit": None if hidden_blit is None else round(hidden_blit, 3),
+            "us_unstaged": round(t_unstaged * 1e3, 2),
+            "us_staged_eager": round(t_eager * 1e3, 2),
+            "us_staged_l2_flushed": {k: round(v * 1e3, 2) for k, v in flushed.items()},
+            "tflops_compute_only": round(flop / (t_compute * 1e-3) / 1e12, 1),
+        })
+        log(f"[{case.name}] detail: {json.dumps(detail)}")
+    return dict(value=value, ms=ms, dtype=dtype, roofline=roofline, inp=inp)
+
+
+def bench_ffn(case, args):
+    inp = W.ffn_inputs(case)
+    t = {k: dev(v) for k, v in inp.items()}
+    y = torch.empty((case.PB, case.L, case.D), dtype=torch.int16, device="cuda")
+    call = tp.prepare_ffn_slot_forward(t["x"], t["w1"], t["b1"], t["wout"], t["bout"], t["gx"], t["bx"],
+                                       t["gg"], t["bg"], y, PB=case.PB, L=case.L, D=case.D, H=case.H,
+                                       eps=case.eps)
+    ms = time_steps(call, max(3, args.steps // 2), 2)
+    return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1))
+
+
+WORKLOADS = {"ag_e4m3_p8": W.C2, "ag_e4m3_p8_beta0": W.C2_BETA0, "ag_bf16_p2": W.C1}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ag_e4m3_p8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline and roofline only")
+    ap.add_argument("--ffn", action="store_true", help="also time the per-slot FFN layer")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the rank-local share on ONE GPU; peers are buffers in the same HBM. "
+              "Multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    tp.lib()
+
+    case = WORKLOADS[args.workload]
+    detail = {}
+    r = bench_ag(case, args, detail)
+    if args.ffn:
+        detail["ffn_layer"] = bench_ffn(W.C4, args)
+        log(f"[ffn] {detail['ffn_layer']}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_ag(case, r["inp"])
+        log(f"[cpu] {cpu}")
+
+    peak = PEAK_TFLOPS[r["dtype"]]
+    out = {
+        "metric": METRIC,
+        "value": round(r["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["dtype"],
+        "data": "synthetic",
+        "config": {"workload": case.name, "M": case.M, "N": case.N, "K": case.K, "P": case.P,
+                   "rank": case.rank, "alpha": case.alpha, "beta": case.beta, "b_layout": case.b_layout,
+                   "pct_mfma_peak": round(100.0 * r["value"] / peak, 2), "parallelism": "tp8 rank share"},
+        "roofline": r["roofline"],
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

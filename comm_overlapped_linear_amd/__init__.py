@@ -242,6 +242,47 @@ def combine_permute(srcs, dst, *, rank, B, T, D, elem_bytes, stream=None):
                                  rank, B, T, D, elem_bytes, _stream(stream)))
 
 
+class Prepared:
+    """A call whose C argument struct is built once; calling it only enters
+    the C library (the tensors must stay alive and in place)."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self, stream=None, flags=None):
+        if flags is not None:
+            self._args.flags = flags
+        _check(self._fn(ctypes.byref(self._args), _stream(stream)))
+
+
+def _attach_workspace(args, size_fn, workspace):
+    need = size_fn(args)
+    ws = _workspace(workspace, need) if workspace is None or need else workspace
+    if ws is not None and ws.numel() < need:
+        raise ValueError(f"workspace of {ws.numel()} bytes, {need} needed")
+    args.workspace = _ptr(ws) if ws is not None else None
+    args.workspace_bytes = ws.numel() if ws is not None else 0
+    return ws
+
+
+def prepare_stage_ag(a_slices, b, c, d, *, workspace=None, **kw):
+    args = ag_args(a_slices, b, c, d, **kw)
+    ws = _attach_workspace(args, stage_ag_workspace_size, workspace)
+    return Prepared(lib().tpgemm_stage_ag, args, (a_slices, b, c, d, ws))
+
+
+def prepare_stage_rs(a, b, incoming, d, *, workspace=None, **kw):
+    args = rs_args(a, b, incoming, d, **kw)
+    ws = _attach_workspace(args, stage_rs_workspace_size, workspace)
+    return Prepared(lib().tpgemm_stage_rs, args, (a, b, incoming, d, ws))
+
+
+def prepare_ffn_slot_forward(x, w1, b1, wout, bout, gx, bx, gg, bg, y, *, workspace=None, **kw):
+    args = ffn_args(x, w1, b1, wout, bout, gx, bx, gg, bg, y, **kw)
+    ws = _attach_workspace(args, ffn_slot_forward_workspace_size, workspace)
+    return Prepared(lib().ffn_slot_forward, args, (x, w1, b1, wout, bout, gx, bx, gg, bg, y, ws))
+
+
 def release_caches():
     lib().tpg_release_caches()
 

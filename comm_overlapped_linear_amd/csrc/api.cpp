@@ -45,6 +45,7 @@ tpg_status fail(tpg_status st, const std::string& msg) {
   } while (0)
 
 constexpr int kStreams = 4;       // compute streams per call (index 0 = root)
+constexpr int kCopyStreams = 4;   // copy streams: deliveries spread over several copy engines
 constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_BLIT |
@@ -57,12 +58,13 @@ struct ProfRec {
 
 struct Ctx {
   int device = -1;
-  hipStream_t copy = nullptr;
+  hipStream_t copy[kCopyStreams] = {};
   hipStream_t comp[kStreams] = {};   // comp[0] unused: the root stream takes its place
   hipStream_t capture = nullptr;
   hipEvent_t ev_fork = nullptr, ev_copy_done = nullptr;
   hipEvent_t ev_copy[kMaxP] = {};
   hipEvent_t ev_join[kStreams] = {};
+  hipEvent_t ev_copy_join[kCopyStreams] = {};
   std::unordered_map<std::string, hipGraphExec_t> graphs;
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> prof_pool;
@@ -74,7 +76,9 @@ std::unordered_map<int, Ctx*> g_ctx;
 tpg_status make_ctx(int dev, Ctx** out) {
   Ctx* c = new Ctx();
   c->device = dev;
-  HIP_TRY(hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking));
+  for (int i = 0; i < kCopyStreams; ++i) HIP_TRY(hipStreamCreateWithFlags(&c->copy[i], hipStreamNonBlocking));
+  for (int i = 0; i < kCopyStreams; ++i)
+    HIP_TRY(hipEventCreateWithFlags(&c->ev_copy_join[i], hipEventDisableTiming));
   for (int i = 1; i < kStreams; ++i) HIP_TRY(hipStreamCreateWithFlags(&c->comp[i], hipStreamNonBlocking));
   HIP_TRY(hipStreamCreateWithFlags(&c->capture, hipStreamNonBlocking));
   HIP_TRY(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming));
@@ -108,7 +112,10 @@ void destroy_ctx(Ctx* c) {
     (void)hipEventDestroy(r.b);
   }
   for (auto e : c->prof_pool) (void)hipEventDestroy(e);
-  if (c->copy) (void)hipStreamDestroy(c->copy);
+  for (int i = 0; i < kCopyStreams; ++i) {
+    if (c->copy[i]) (void)hipStreamDestroy(c->copy[i]);
+    if (c->ev_copy_join[i]) (void)hipEventDestroy(c->ev_copy_join[i]);
+  }
   for (int i = 1; i < kStreams; ++i)
     if (c->comp[i]) (void)hipStreamDestroy(c->comp[i]);
   if (c->capture) (void)hipStreamDestroy(c->capture);
@@ -181,15 +188,28 @@ tpg_status fork_streams(Ctx& cx, hipStream_t root, int n, hipStream_t* streams) 
   return TPG_OK;
 }
 
+// The root waits for everything issued so far on the copy streams.
+tpg_status wait_copies(Ctx& cx, hipStream_t root) {
+  for (int i = 0; i < kCopyStreams; ++i) {
+    HIP_TRY(hipEventRecord(cx.ev_copy_join[i], cx.copy[i]));
+    HIP_TRY(hipStreamWaitEvent(root, cx.ev_copy_join[i], 0));
+  }
+  return TPG_OK;
+}
+
 tpg_status join_streams(Ctx& cx, hipStream_t root, int n, const hipStream_t* streams, bool copies) {
   for (int i = 1; i < n; ++i) {
     HIP_TRY(hipEventRecord(cx.ev_join[i], streams[i]));
     HIP_TRY(hipStreamWaitEvent(root, cx.ev_join[i], 0));
   }
-  if (copies) {
-    HIP_TRY(hipEventRecord(cx.ev_copy_done, cx.copy));
-    HIP_TRY(hipStreamWaitEvent(root, cx.ev_copy_done, 0));
-  }
+  if (copies) return wait_copies(cx, root);
+  return TPG_OK;
+}
+
+// Forks the copy streams from the root.
+tpg_status fork_copies(Ctx& cx, hipStream_t root) {
+  HIP_TRY(hipEventRecord(cx.ev_fork, root));
+  for (int i = 0; i < kCopyStreams; ++i) HIP_TRY(hipStreamWaitEvent(cx.copy[i], cx.ev_fork, 0));
   return TPG_OK;
 }
 
@@ -333,14 +353,14 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   p.K = static_cast<int>(a.K);
   p.alpha = a.alpha;
   p.beta = a.beta;
-  p.vec_ok = (nout % 4) == 0;
+  p.vec_ok = (nout % 8) == 0;
   const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
   const int layout = a.b_layout == TPG_B_KN ? tpg::kKN : tpg::kNK;
   const int epi = sw ? tpg::kEpiSwiglu : tpg::kEpiAlphaBeta;
 
   if (copies) {
-    HIP_TRY(hipEventRecord(cx.ev_fork, L.root));
-    HIP_TRY(hipStreamWaitEvent(cx.copy, cx.ev_fork, 0));
+    tpg_status fs = fork_copies(cx, L.root);
+    if (fs != TPG_OK) return fs;
   }
 
   if (a.flags & TPG_UNSTAGED) {
@@ -348,9 +368,9 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     const void* A = a.M > 0 ? a.a_slices[0] : nullptr;
     if (copies) {
       for (int s = 0; s < P; ++s)
-        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, cx.copy));
-      HIP_TRY(hipEventRecord(cx.ev_copy_done, cx.copy));
-      HIP_TRY(hipStreamWaitEvent(L.root, cx.ev_copy_done, 0));
+        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, cx.copy[s % kCopyStreams]));
+      tpg_status ws_ = wait_copies(cx, L.root);
+      if (ws_ != TPG_OK) return ws_;
       A = ws;
     }
     p.a = A;
@@ -364,8 +384,9 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   if (copies) {
     for (int t = 1; t < P; ++t) {
       const int s = (r + t) % P;
-      HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], slice_b, kind, cx.copy));
-      HIP_TRY(hipEventRecord(cx.ev_copy[t], cx.copy));
+      hipStream_t cp = cx.copy[(t - 1) % kCopyStreams];
+      HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], slice_b, kind, cp));
+      HIP_TRY(hipEventRecord(cx.ev_copy[t], cp));
     }
   }
   const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(P, kStreams);
@@ -488,7 +509,7 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   p.K = static_cast<int>(a.K);
   p.alpha = a.alpha;
   p.beta = 0.0f;
-  p.vec_ok = (a.N % 4) == 0;
+  p.vec_ok = (a.N % 8) == 0;
   const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
   const int layout = a.b_layout == TPG_B_KN ? tpg::kKN : tpg::kNK;
 
@@ -504,18 +525,25 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     }
   };
 
+  const int ncs = std::min<int>(kCopyStreams, static_cast<int>(peers.size()));
   if (copies) {
-    HIP_TRY(hipEventRecord(cx.ev_fork, L.root));
-    HIP_TRY(hipStreamWaitEvent(cx.copy, cx.ev_fork, 0));
+    tpg_status fs = fork_copies(cx, L.root);
+    if (fs != TPG_OK) return fs;
     for (size_t i = 0; i < peers.size(); ++i)
-      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], part_b, kind, cx.copy));
-    HIP_TRY(hipEventRecord(cx.ev_copy[0], cx.copy));
+      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], part_b, kind, cx.copy[i % kCopyStreams]));
+    for (int i = 0; i < ncs; ++i) HIP_TRY(hipEventRecord(cx.ev_copy[i], cx.copy[i]));
   }
+  // the stage that sums the incoming partials waits for every delivery
+  auto wait_all = [&](hipStream_t cs) -> tpg_status {
+    for (int i = 0; copies && i < ncs; ++i) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[i], 0));
+    return TPG_OK;
+  };
 
   if (a.flags & TPG_UNSTAGED) {
     // one GEMM over all blocks once every partial has arrived; the adds apply
     // to the rows of the own block only
-    if (copies) HIP_TRY(hipStreamWaitEvent(L.root, cx.ev_copy[0], 0));
+    tpg_status ws_ = wait_all(L.root);
+    if (ws_ != TPG_OK) return ws_;
     p.a = a.a;
     p.d = static_cast<uint16_t*>(a.d);
     p.M = static_cast<int>(a.M);
@@ -524,11 +552,7 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     set_adds(p);
     tpg_status st = gemm_on(cx, L, L.root, p, dtype, layout, tpg::kEpiAlphaBeta);
     if (st != TPG_OK) return st;
-    if (copies) {
-      HIP_TRY(hipEventRecord(cx.ev_copy_done, cx.copy));
-      HIP_TRY(hipStreamWaitEvent(L.root, cx.ev_copy_done, 0));
-    }
-    return TPG_OK;
+    return copies ? wait_copies(cx, L.root) : TPG_OK;
   }
 
   const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(P, kStreams);
@@ -543,7 +567,8 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     q.a = static_cast<const char*>(a.a) + size_t(blk) * m * a.K * eb;
     q.d = static_cast<uint16_t*>(a.d) + blk * m * a.N;
     if (blk == r) {
-      if (copies) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[0], 0));
+      tpg_status ws_ = wait_all(cs);
+      if (ws_ != TPG_OK) return ws_;
       q.add_row0 = 0;
       q.add_row1 = static_cast<int>(m);
       set_adds(q);

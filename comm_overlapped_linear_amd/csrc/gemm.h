@@ -29,7 +29,7 @@ struct GemmParams {
   int n_add_strided;
   int64_t ld_add;              // row stride of every addend (elements)
   int add_row0, add_row1;
-  int vec_ok;                  // 1 if ldc, ldd, ld_add are multiples of 4 (8-byte rows groups)
+  int vec_ok;                  // 1 if ldc, ldd and ld_add are multiples of 8 (16-byte row vectors)
 };
 
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };

@@ -84,6 +84,113 @@ __device__ __forceinline__ int b_col(int tn, int i, int N) {
   return u < nh ? u + half * nh : -1;
 }
 
+// Adds beta * C, the bias and the addends to x[0..8) for output (row, col ..
+// col + 7) and stores bf16. Full 16-byte vectors when the row stride allows.
+__device__ __forceinline__ void add_row8(const uint16_t* src, int64_t off, bool vec, int n, float scale,
+                                         float* x) {
+  if (vec) {
+    const uint4 c = *reinterpret_cast<const uint4*>(src + off);
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] += scale * bf16_to_f32(w[e] & 0xffff);
+      x[2 * e + 1] += scale * bf16_to_f32(w[e] >> 16);
+    }
+  } else {
+    for (int e = 0; e < n; ++e) x[e] += scale * bf16_to_f32(src[off + e]);
+  }
+}
+
+__device__ __forceinline__ void epilogue_vec8(const GemmParams& p, int row, int col, int nout, float* x) {
+  const int n = min(8, nout - col);
+  const bool vec = p.vec_ok && n == 8;
+  if (p.beta != 0.0f) add_row8(p.c, static_cast<int64_t>(row) * p.ldc + col, vec, n, p.beta, x);
+  if (p.bias) add_row8(p.bias, col, n == 8, n, 1.0f, x);
+  if (row >= p.add_row0 && row < p.add_row1) {
+    const int64_t off = static_cast<int64_t>(row - p.add_row0) * p.ld_add + col;
+    for (int t = 0; t < p.n_add_list; ++t) add_row8(p.add_list[t], off, vec, n, 1.0f, x);
+    for (int t = 0; t < p.n_add_strided; ++t) add_row8(p.add_base + t * p.add_stride, off, vec, n, 1.0f, x);
+  }
+  uint16_t* dst = p.d + static_cast<int64_t>(row) * p.ldd + col;
+  if (vec) {
+    uint4 o;
+    o.x = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    o.y = f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+    o.z = f32_to_bf16(x[4]) | (static_cast<uint32_t>(f32_to_bf16(x[5])) << 16);
+    o.w = f32_to_bf16(x[6]) | (static_cast<uint32_t>(f32_to_bf16(x[7])) << 16);
+    *reinterpret_cast<uint4*>(dst) = o;
+  } else {
+    for (int e = 0; e < n; ++e) dst[e] = f32_to_bf16(x[e]);
+  }
+}
+
+// Epilogue shared by both kernels, staged through LDS in FM passes of 2 x 32
+// rows: (1) every wave writes alpha * acc (or silu(u) * v) of its rows
+// wm*WTM + i*32 + [0, 32) as fp32 into a [64][BNO + 4] LDS block; (2) all 256
+// threads sweep that block in 8-column vectors: + beta * C, + bias, + addends,
+// one bf16 rounding, 16-byte coalesced stores. The caller has synchronised
+// the workgroup, so the LDS is free.
+template <int BM, int BN, bool SWIGLU>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16_t (&acc)[BM / 64][BN / 64],
+                                           uint8_t* smem, int tm, int tn) {
+  constexpr int WN = 2;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int m0 = tm * BM;
+  constexpr int JN = SWIGLU ? FN / 2 : FN;     // output column blocks per wave
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;    // output columns per tile
+  constexpr int WNO = BNO / WN;                // output columns per wave
+  constexpr int SLD = BNO + 4;                 // padded LDS row (floats)
+  static_assert(2 * 32 * SLD * 4 <= 2 * (BM + BN) * kRowBytes, "epilogue stage fits in LDS");
+  float* stage = reinterpret_cast<float*>(smem);
+  const int nout = SWIGLU ? (p.N >> 1) : p.N;
+  const int tcol0 = tn * BNO;
+  constexpr int VEC_PER_ROW = BNO / 8;
+  constexpr int VEC_PASS = 64 * VEC_PER_ROW;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    float* wst = stage + (wm * 32 + l32) * SLD + wn * WNO + half * 4;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 o;
+        float* ov = reinterpret_cast<float*>(&o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x = p.alpha * acc[i][j][g * 4 + q];
+          if constexpr (SWIGLU) {
+            ov[q] = silu_f32(x) * (p.alpha * acc[i][j + FN / 2][g * 4 + q]);
+          } else {
+            ov[q] = x;
+          }
+        }
+        *reinterpret_cast<float4*>(wst + j * 32 + g * 8) = o;
+      }
+    }
+    __syncthreads();
+    for (int v = tid; v < VEC_PASS; v += kThreads) {
+      const int sr = v / VEC_PER_ROW, sc = (v % VEC_PER_ROW) * 8;
+      const int row = m0 + (sr >> 5) * WTM + i * 32 + (sr & 31);
+      const int col = tcol0 + sc;
+      if (row >= p.M || col >= nout) continue;
+      float x[8];
+      const float4 lo = *reinterpret_cast<const float4*>(stage + sr * SLD + sc);
+      const float4 hi = *reinterpret_cast<const float4*>(stage + sr * SLD + sc + 4);
+      x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+      x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+      epilogue_vec8(p, row, col, nout, x);
+    }
+    __syncthreads();
+  }
+}
+
 template <typename Op, int BM, int BN, bool KN, bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
   constexpr int WM = 2, WN = 2;
@@ -240,72 +347,174 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows m0 + wm*WTM + i*32 + l32, 4 consecutive columns per reg group
-  const int nout = SWIGLU ? (p.N >> 1) : p.N;
-  constexpr int JN = SWIGLU ? FN / 2 : FN;
-  const int ncol0 = SWIGLU ? tn * (BN / 2) + wn * (WTN / 2) : tn * BN + wn * WTN;
+  store_tile<BM, BN, SWIGLU>(p, acc, smem, tm, tn);
+}
+
+// ---------------------------------------------------------------------------
+// v2 mainloop: direct-to-LDS loads (gfx950 global_load_lds_dwordx4).
+// Each 16-byte chunk goes from HBM straight into its LDS slot, with no
+// staging registers, into a ring of STAGES tile buffers, so several K-steps
+// of loads are in flight while the MFMAs consume the oldest one. A DMA
+// instruction of one wave fills 1 KB of LDS, lane q at byte 16 q, i.e. eight
+// 128-byte rows; the XOR swizzle is realised by which global chunk lane q
+// fetches. The loads are issued from inline assembly so that the compiler
+// does not order every LDS read after every outstanding DMA; the waits are
+// explicit (vmcnt for this wave's DMA, then a barrier for everyone's).
+// Requires K * element size to be a multiple of 128 bytes and B in (N, K).
+// m0 carries the LDS destination; nothing else in these kernels uses m0 on
+// gfx950 (LDS instructions do not read it), so clobbering it is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// all LDS reads of this wave done, then workgroup barrier (no fence: the
+// DMA loads still in flight must not be waited for here)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until this wave's DMA of the oldest pending stage has landed, with
+// `ahead` younger stages (INSTR instructions each) allowed to stay in flight.
+template <int INSTR, int STAGES>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (STAGES >= 4) {
+    if (ahead >= 2) { wait_vmcnt<2 * INSTR>(); return; }
+  }
+  if constexpr (STAGES >= 3) {
+    if (ahead >= 1) { wait_vmcnt<INSTR>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+template <typename Op, int BM, int BN, int STAGES, bool SWIGLU>
+__global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams p) {
+  constexpr int WN = 2;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INSTR = BM / 32, B_INSTR = BN / 32, INSTR = A_INSTR + B_INSTR;
+  static_assert(STAGES >= 2 && (STAGES - 2) * INSTR <= 63, "vmcnt range");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  // consecutive workgroups land on different XCDs: give each XCD a
+  // contiguous run of tiles (M fastest) so its L2 sees shared B columns
+  int bid = blockIdx.x;
+  const int nt = gridDim.x;
+  if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);
+  const int ntm = (p.M + BM - 1) / BM;
+  const int tm = bid % ntm;
+  const int tn = bid / ntm;
+  const int m0 = tm * BM;
+
+  const uint8_t* A = static_cast<const uint8_t*>(p.a);
+  const uint8_t* Bp = static_cast<const uint8_t*>(p.b);
+  const int64_t lda_b = p.lda * Op::kElemBytes;
+  const int64_t ldb_b = p.ldb * Op::kElemBytes;
+  const int nk = (p.K * Op::kElemBytes) / kRowBytes;
+  const uint32_t lds0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem));
+
+  // this lane's source chunk in each DMA instruction; rows past the edge read
+  // a valid row instead (their products only reach outputs never stored)
+  const int rsub = lane >> 3, pc = lane & 7;
+  const uint8_t* asrc[A_INSTR];
+  const uint8_t* bsrc[B_INSTR];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row = m0 + wm * WTM + i * 32 + l32;
-    if (row >= p.M) continue;
-    const bool do_add = row >= p.add_row0 && row < p.add_row1;
+  for (int j = 0; j < A_INSTR; ++j) {
+    const int r = (j * 4 + wave) * 8 + rsub;
+    const int grow = min(m0 + r, p.M - 1);
+    asrc[j] = A + grow * lda_b + (pc ^ ((r >> 1) & 7)) * 16;
+  }
 #pragma unroll
-    for (int j = 0; j < JN; ++j) {
+  for (int j = 0; j < B_INSTR; ++j) {
+    const int r = (j * 4 + wave) * 8 + rsub;
+    int n = b_col<SWIGLU, BN>(tn, r, p.N);
+    if (n < 0) n = 0;
+    bsrc[j] = Bp + n * ldb_b + (pc ^ ((r >> 1) & 7)) * 16;
+  }
+
+  auto issue = [&](int kt, int buf) {
+    const uint32_t sb = lds0 + buf * STAGE;
+    const int kb = kt * kRowBytes;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = ncol0 + j * 32 + g * 8 + half * 4;
-        if (col >= nout) continue;
-        float v[4];
+    for (int j = 0; j < A_INSTR; ++j)
+      dma16(asrc[j] + kb, __builtin_amdgcn_readfirstlane(sb + (j * 4 + wave) * 1024));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float x = p.alpha * acc[i][j][g * 4 + q];
-          if (SWIGLU) {
-            const float y = p.alpha * acc[i][j + JN][g * 4 + q];
-            v[q] = silu_f32(x) * y;
-          } else {
-            v[q] = x;
-          }
-        }
-        const bool full = p.vec_ok && (col + 3 < nout);
-        auto add_src = [&](const uint16_t* src, int64_t ld, float scale) {
-          if (full) {
-            const uint2 cv = *reinterpret_cast<const uint2*>(src + row * ld + col);
-            v[0] += scale * bf16_to_f32(cv.x & 0xffff);
-            v[1] += scale * bf16_to_f32(cv.x >> 16);
-            v[2] += scale * bf16_to_f32(cv.y & 0xffff);
-            v[3] += scale * bf16_to_f32(cv.y >> 16);
-          } else {
+    for (int j = 0; j < B_INSTR; ++j)
+      dma16(bsrc[j] + kb, __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * 4 + wave) * 1024));
+  };
+
+  f32x16_t acc[FM][FN];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (col + q < nout) v[q] += scale * bf16_to_f32(src[row * ld + col + q]);
-          }
-        };
-        if (p.beta != 0.0f) add_src(p.c, p.ldc, p.beta);
-        if (p.bias) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (col + q < nout) v[q] += bf16_to_f32(p.bias[col + q]);
-        }
-        if (do_add) {   // addends are (add_row1 - add_row0) x nout blocks
-          const int64_t shift = static_cast<int64_t>(p.add_row0) * p.ld_add;
-          for (int t = 0; t < p.n_add_list; ++t) add_src(p.add_list[t] - shift, p.ld_add, 1.0f);
-          for (int t = 0; t < p.n_add_strided; ++t)
-            add_src(p.add_base + t * p.add_stride - shift, p.ld_add, 1.0f);
-        }
-        uint16_t* dst = p.d + row * p.ldd + col;
-        if (full) {
-          uint2 o;
-          o.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-          o.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-          *reinterpret_cast<uint2*>(dst) = o;
-        } else {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (col + q < nout) dst[q] = f32_to_bf16(v[q]);
-        }
-      }
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto b_row = [&](int j) {
+    if (!SWIGLU) return wn * WTN + j * 32 + l32;
+    const int hj = j % (FN / 2), part = j / (FN / 2);
+    return part * (BN / 2) + wn * (WTN / 2) + hj * 32 + l32;
+  };
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, st);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_stage<INSTR, STAGES>(min(nk - 1, kt + STAGES - 2) - kt);
+    lds_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const uint8_t* la = smem + (kt % STAGES) * STAGE;
+    const uint8_t* lb = la + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < Op::kSubSteps; ++kk) {
+      typename Op::frag_t fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = Op::load(la, wm * WTM + i * 32 + l32, kk, half);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = Op::load(lb, b_row(j), kk, half);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = Op::mma(fb[j], fa[i], acc[i][j]);
     }
   }
+  __syncthreads();
+  store_tile<BM, BN, SWIGLU>(p, acc, smem, tm, tn);
+}
+
+template <typename Op, int BM, int BN, int STAGES, bool SWIGLU>
+hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
+  constexpr int smem = STAGES * (BM + BN) * kRowBytes;
+  auto kern = gemm_dma_kernel<Op, BM, BN, STAGES, SWIGLU>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  const int grid = ((p.M + BM - 1) / BM) * nout_tiles;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, s, p);
+  return hipGetLastError();
 }
 
 template <typename Op, int BM, int BN, bool KN, bool SWIGLU>
@@ -340,6 +549,14 @@ int pick_tile(int M, int N, int epi) {
 
 template <typename Op, bool KN, bool SW>
 hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
+  const bool dma = !KN && p.M > 0 && p.N > 0 && (p.K * Op::kElemBytes) % kRowBytes == 0;
+  if (dma) {
+    switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta)) {
+      case 0: return launch_dma_tile<Op, 256, 256, 2, SW>(p, s);
+      case 1: return launch_dma_tile<Op, 256, 128, 3, SW>(p, s);
+      default: return launch_dma_tile<Op, 128, 128, 4, SW>(p, s);
+    }
+  }
   switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta)) {
     case 0: return launch_tile<Op, 256, 256, KN, SW>(p, s);
     case 1: return launch_tile<Op, 256, 128, KN, SW>(p, s);

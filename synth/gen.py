@@ -13,6 +13,9 @@ Encoders: round-to-nearest, ties-to-even, to bf16 (8 significant bits) and to
 OCP 8-bit E4M3FN (bias 7, 3 mantissa bits, subnormal quantum 2^-9, largest
 finite value 448, no infinities), saturating at +-448.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -54,20 +57,35 @@ def _u01(key, start, count):
     return (_raw(key, start, count) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
 
 
+def _chunked(n, fill):
+    """Runs fill(start, count) over _CHUNK-sized pieces on a thread pool.
+    Every element depends only on its own counter, so the pieces are
+    independent and the result does not depend on the thread count."""
+    starts = list(range(0, n, _CHUNK))
+    if len(starts) <= 1:
+        for s in starts:
+            fill(s, min(_CHUNK, n - s))
+        return
+    workers = min(len(starts), int(os.environ.get("SYNTH_THREADS", os.cpu_count() or 1)), 16)
+    with ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        list(ex.map(lambda s: fill(s, min(_CHUNK, n - s)), starts))
+
+
 def uniform(key, n, lo, hi):
     """n doubles, U[lo, hi)."""
     out = np.empty(n, dtype=np.float64)
-    for s in range(0, n, _CHUNK):
-        c = min(_CHUNK, n - s)
+
+    def fill(s, c):
         out[s:s + c] = lo + (hi - lo) * _u01(key, s, c)
+    _chunked(n, fill)
     return out
 
 
 def normal(key, n, mean=0.0, std=1.0):
     """n doubles, N(mean, std^2), by Box-Muller over counter pairs."""
     out = np.empty(n, dtype=np.float64)
-    for s in range(0, n, _CHUNK):      # _CHUNK is even, so pairs never straddle
-        c = min(_CHUNK, n - s)
+
+    def fill(s, c):                    # _CHUNK is even, so pairs never straddle
         first, last = s // 2, (s + c - 1) // 2
         npair = last - first + 1
         u = _u01(key, 2 * first, 2 * npair).reshape(npair, 2)
@@ -76,6 +94,7 @@ def normal(key, n, mean=0.0, std=1.0):
         pair = np.stack([r * np.cos(th), r * np.sin(th)], axis=1).reshape(-1)
         off = s - 2 * first
         out[s:s + c] = mean + std * pair[off:off + c]
+    _chunked(n, fill)
     return out
 
 
@@ -109,17 +128,26 @@ def encode_e4m3(x):
     return (sign | (E.astype(np.uint8) << np.uint8(3)) | M.astype(np.uint8)).astype(np.uint8)
 
 
+def _encode_chunked(v, enc, dtype):
+    out = np.empty(v.shape[0], dtype=dtype)
+
+    def fill(s, c):
+        out[s:s + c] = enc(v[s:s + c])
+    _chunked(v.shape[0], fill)
+    return out
+
+
 def uniform_bf16(key, shape, lo, hi):
     n = int(np.prod(shape))
-    return encode_bf16(uniform(key, n, lo, hi)).reshape(shape)
+    return _encode_chunked(uniform(key, n, lo, hi), encode_bf16, np.uint16).reshape(shape)
 
 
 def normal_bf16(key, shape, mean=0.0, std=1.0):
     n = int(np.prod(shape))
-    return encode_bf16(normal(key, n, mean, std)).reshape(shape)
+    return _encode_chunked(normal(key, n, mean, std), encode_bf16, np.uint16).reshape(shape)
 
 
 def normal_e4m3(key, shape, scale=1.0, clip=448.0):
     n = int(np.prod(shape))
     v = np.clip(scale * normal(key, n), -clip, clip)
-    return encode_e4m3(v).reshape(shape)
+    return _encode_chunked(v, encode_e4m3, np.uint8).reshape(shape)

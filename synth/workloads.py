@@ -249,10 +249,22 @@ SMALL_AG = [
            beta=0.0),
     AgCase("ag_bf16_p8_swiglu_small", M=8 * 40, N=2 * 136, K=264, P=8, b_layout="kn",
            dist="n05", beta=0.0, swiglu=True, rank=3),
+    # K * element size a multiple of 128 bytes: the direct-to-LDS mainloop
+    AgCase("ag_bf16_p2_dma_small", M=2 * 200, N=328, K=384, P=2, dist="u11", rank=1),
+    AgCase("ag_e4m3_p4_dma_small", M=4 * 96, N=200, K=640, P=4, dtype="e4m3", dist="n05",
+           c_dist="n01", rank=2),
+    AgCase("ag_bf16_p4_dma_swiglu_small", M=4 * 72, N=2 * 200, K=256, P=4, dist="n05", beta=0.0,
+           swiglu=True),
+    # medium: the single-stage launch takes the 256x256 / 256x128 tiles
+    AgCase("ag_bf16_p2_dma_medium", M=2 * 2000, N=4040, K=192, P=2, dist="u11", alpha=0.5, beta=2.0),
+    AgCase("ag_e4m3_p2_dma_medium", M=2 * 1500, N=2600, K=256, P=2, dtype="e4m3", dist="n05",
+           c_dist="n01"),
 ]
 SMALL_RS = [
     RsCase("rs_bf16_p4_small", M=4 * 136, N=264, K=328, P=4, rank=2, std=0.5),
     RsCase("rs_bf16_p2_kn_small", M=2 * 100, N=200, K=136, P=2, rank=0, b_layout="kn", std=0.5),
+    RsCase("rs_bf16_p4_dma_small", M=4 * 136, N=264, K=448, P=4, rank=3, std=0.5),
+    RsCase("rs_bf16_p4_dma_medium", M=4 * 1000, N=4040, K=128, P=4, rank=1, std=0.5),
 ]
 SMALL_FFN = [
     FfnCase("ffn_public_b4_t16_d128_k2_p2", B=4, T=16, D=128, k=2, P=2),

@@ -1,0 +1,122 @@
+"""Full-size GPU parity: the five workloads at their real shapes, in the launch
+configuration the benchmark times (graph replay, copy-engine deliveries).
+
+The oracle computes sampled output rows one by one (every stage's first and
+last row plus seeded random rows); properties that hold at any size (staged
+equals unstaged bit for bit, the own reduce-scatter block minus the incoming
+partials equals the plain partial) cover the rest of each output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import comm_overlapped_linear_amd as tp
+import oracle
+from synth import workloads as W
+from tests.devutil import say, dev, bf16_empty, host_f64
+from tests.parity import assert_parity
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def sample_rows(M, m, n_random=24, seed=0):
+    rows = set()
+    for s in range(M // m):
+        rows.update({s * m, s * m + m - 1})
+    rows.update(np.random.default_rng(seed).integers(0, M, n_random).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("case", [W.C2, W.C2_BETA0], ids=lambda c: c.name)
+def test_full_ag_fp8(case):
+    say(f"full: {case.name} generate")
+    inp = W.ag_inputs(case)
+    slices = [dev(s) for s in inp["a_slices"]]
+    b, c = dev(inp["b"]), dev(inp["c"])
+    kw = dict(M=case.M, N=case.N, K=case.K, rank=case.rank, dtype=tp.E4M3, alpha=case.alpha, beta=case.beta)
+    d = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} staged")
+    tp.stage_ag(slices, b, c, d, **kw)
+    torch.cuda.synchronize()
+    rows = sample_rows(case.M, case.m)
+    ref = oracle.gemm_ag_rows(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, "e4m3", "nk", rows)
+    assert_parity(host_f64(d)[rows], ref, case.name)
+    d2 = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} unstaged")
+    tp.stage_ag(slices, b, c, d2, flags=tp.UNSTAGED, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(d, d2)
+
+
+def test_full_rs_bf16():
+    case = W.C3
+    say(f"full: {case.name} generate")
+    inp = W.rs_inputs(case)
+    a, b = dev(inp["a"]), dev(inp["b"])
+    inc = [dev(x) if x is not None else None for x in inp["incoming"]]
+    kw = dict(M=case.M, N=case.N, K=case.K, P=case.P, rank=case.rank)
+    d = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} staged")
+    tp.stage_rs(a, b, inc, d, **kw)
+    torch.cuda.synchronize()
+    got = host_f64(d)
+    rows = sample_rows(case.M, case.m)
+    ref = oracle.gemm_rs_rows(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P, "nk", rows)
+    r_rows = [i for i, r in enumerate(rows) if r // case.m == case.rank]
+    e_rows = [i for i, r in enumerate(rows) if r // case.m != case.rank]
+    assert_parity(got[rows][e_rows], ref[e_rows], "emitted blocks")
+    assert_parity(got[rows][r_rows], ref[r_rows], "own block")
+    # own partial inside the reduced block, at a tolerance scaled to the partial itself
+    own_rows = [r for r in rows if r // case.m == case.rank]
+    inc_sum = sum(oracle.decode_bf16(x[[r % case.m for r in own_rows]]) for x in inp["incoming"] if x is not None)
+    e_r = oracle.gemm_rs_rows(inp["a"], inp["b"], None, 1.0, case.rank, case.P, "nk", own_rows)
+    ulp_out = np.exp2(np.floor(np.log2(np.maximum(np.abs(got[own_rows]), 1e-30))) - 7)
+    assert np.all(np.abs(got[own_rows] - inc_sum - e_r) <= 0.02 * np.sqrt(np.mean(e_r ** 2)) + ulp_out)
+    d2 = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} unstaged")
+    tp.stage_rs(a, b, inc, d2, flags=tp.UNSTAGED, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(d, d2)
+
+
+def test_full_ffn():
+    case = W.C4
+    say(f"full: {case.name} generate")
+    inp = W.ffn_inputs(case)
+    t = {k: dev(v) for k, v in inp.items()}
+    y = bf16_empty(case.PB, case.L, case.D)
+    say(f"full: {case.name} run")
+    tp.ffn_slot_forward(t["x"], t["w1"], t["b1"], t["wout"], t["bout"], t["gx"], t["bx"], t["gg"], t["bg"], y,
+                        PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps)
+    torch.cuda.synchronize()
+    got = host_f64(y)
+    rng = np.random.default_rng(1)
+    pairs = [(0, 0), (case.PB - 1, case.L - 1)] + [(int(n), int(l)) for n, l in
+                                                   zip(rng.integers(0, case.PB, 30), rng.integers(0, case.L, 30))]
+    ref = oracle.ffn_slot_rows(inp, pairs, case.eps)
+    assert_parity(np.stack([got[n, l] for n, l in pairs]), ref, case.name)
+    y2 = bf16_empty(case.PB, case.L, case.D)
+    tp.ffn_slot_forward(t["x"], t["w1"], t["b1"], t["wout"], t["bout"], t["gx"], t["bx"], t["gg"], t["bg"], y2,
+                        PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps, flags=tp.SERIAL_STAGES)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+def test_full_swiglu_block():
+    case = W.C5
+    say(f"full: {case.name} generate")
+    inp = W.swiglu_inputs(case)
+    xs = [dev(x) for x in inp["x_shards"]]
+    w13, w2 = dev(inp["w13"]), dev(inp["w2"])
+    h = bf16_empty(case.M, case.F)
+    out = bf16_empty(case.M, case.D)
+    say(f"full: {case.name} run")
+    tp.stage_ag(xs, w13, None, h, M=case.M, N=2 * case.F, K=case.D, rank=case.rank, b_layout=tp.B_KN,
+                epilogue=tp.EPI_SWIGLU, alpha=1.0, beta=0.0)
+    tp.stage_rs(h, w2, None, out, M=case.M, N=case.D, K=case.F, P=case.P, rank=case.rank, b_layout=tp.B_KN)
+    torch.cuda.synchronize()
+    rows = sample_rows(case.M, case.S)
+    h_ref = oracle.swiglu_hidden_rows(inp["x_shards"], inp["w13"], rows)
+    assert_parity(host_f64(h)[rows], h_ref, "h")
+    out_ref = h_ref @ oracle.decode_bf16(inp["w2"])
+    assert_parity(host_f64(out)[rows], out_ref, "partial blocks")
