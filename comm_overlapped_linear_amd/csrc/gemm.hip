@@ -34,16 +34,25 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;   // K bytes per tile row per K-step
 
-// 16-byte chunk swizzle inside a 128-byte LDS row.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// 16-byte chunk swizzle inside an LDS row of ROWB bytes (128: 8 chunks,
+// 64: 4 chunks). Any 16 consecutive rows read at one logical chunk hit 16
+// distinct 16-byte bank groups of a 256-byte bank window.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (ROWB == 128) return chunk ^ ((row >> 1) & 7);
+  else return chunk ^ ((row >> 2) & 3);
+}
 
 struct OpBf16 {
   static constexpr int kElemBytes = 2;
-  static constexpr int kSubSteps = 4;   // 32-byte k slices per K-step
+  static constexpr int kSliceBytes = 32;   // k bytes per lane-half pair of one MFMA
+  static constexpr int kSubSteps = 4;      // 32-byte k slices per 128-byte K-step
+  static constexpr int kReadsPerFrag = 1;
   typedef bf16x8_t frag_t;
+  template <int ROWB = kRowBytes>
   __device__ static frag_t load(const uint8_t* lds, int row, int kk, int half) {
     const int c = kk * 2 + half;
-    uint4 v = *reinterpret_cast<const uint4*>(lds + row * kRowBytes + swz(row, c) * 16);
+    uint4 v = *reinterpret_cast<const uint4*>(lds + row * ROWB + swz<ROWB>(row, c) * 16);
     return __builtin_bit_cast(frag_t, v);
   }
   __device__ static f32x16_t mma(frag_t x, frag_t y, f32x16_t acc) {
@@ -53,12 +62,15 @@ struct OpBf16 {
 
 struct OpE4m3 {
   static constexpr int kElemBytes = 1;
-  static constexpr int kSubSteps = 2;   // 64-byte k slices per K-step
+  static constexpr int kSliceBytes = 64;
+  static constexpr int kSubSteps = 2;      // 64-byte k slices per 128-byte K-step
+  static constexpr int kReadsPerFrag = 2;
   typedef i32x8_t frag_t;
+  template <int ROWB = kRowBytes>
   __device__ static frag_t load(const uint8_t* lds, int row, int kk, int half) {
     const int c = kk * 4 + half * 2;
-    uint4 lo = *reinterpret_cast<const uint4*>(lds + row * kRowBytes + swz(row, c) * 16);
-    uint4 hi = *reinterpret_cast<const uint4*>(lds + row * kRowBytes + swz(row, c + 1) * 16);
+    uint4 lo = *reinterpret_cast<const uint4*>(lds + row * ROWB + swz<ROWB>(row, c) * 16);
+    uint4 hi = *reinterpret_cast<const uint4*>(lds + row * ROWB + swz<ROWB>(row, c + 1) * 16);
     i32x8_t f;
     f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
     f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
@@ -272,14 +284,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
     for (int i = 0; i < A_LD; ++i) {
       const int id = i * kThreads + tid;
       const int r = id >> 3, c = id & 7;
-      *reinterpret_cast<uint4*>(la + r * kRowBytes + swz(r, c) * 16) = ra[i];
+      *reinterpret_cast<uint4*>(la + r * kRowBytes + swz<kRowBytes>(r, c) * 16) = ra[i];
     }
     if (!KN) {
 #pragma unroll
       for (int i = 0; i < B_LD_NK; ++i) {
         const int id = i * kThreads + tid;
         const int r = id >> 3, c = id & 7;
-        *reinterpret_cast<uint4*>(lb + r * kRowBytes + swz(r, c) * 16) = rb[i];
+        *reinterpret_cast<uint4*>(lb + r * kRowBytes + swz<kRowBytes>(r, c) * 16) = rb[i];
       }
     } else {
 #pragma unroll
@@ -298,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
               o[j] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
             }
             const int r = nb * 8 + c;
-            *reinterpret_cast<uint4*>(lb + r * kRowBytes + swz(r, kb8) * 16) =
+            *reinterpret_cast<uint4*>(lb + r * kRowBytes + swz<kRowBytes>(r, kb8) * 16) =
                 make_uint4(o[0], o[1], o[2], o[3]);
           }
         }
@@ -379,27 +391,59 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Wait until this wave's DMA of the oldest pending stage has landed, with
-// `ahead` younger stages (INSTR instructions each) allowed to stay in flight.
-template <int INSTR, int STAGES>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if constexpr (STAGES >= 4) {
-    if (ahead >= 2) { wait_vmcnt<2 * INSTR>(); return; }
-  }
-  if constexpr (STAGES >= 3) {
-    if (ahead >= 1) { wait_vmcnt<INSTR>(); return; }
-  }
-  wait_vmcnt<0>();
+// (K, N)-layout B tiles: chunk swizzle of a k-row and the transposing
+// fragment read (ds_read_b64_tr_b16, two per 8-k fragment).
+__device__ __forceinline__ int kn_swz(int kr) { return (kr & 7) << 1; }
+
+template <int BN>
+__device__ __forceinline__ bf16x8_t load_kn_frag(const uint8_t* lb, int kr, int n) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  constexpr int PITCH = BN * 2;
+  auto addr = [&](int k) {
+    const int c = (n >> 3) ^ kn_swz(k);
+    return (__attribute__((address_space(3))) v4i16*)(lb + k * PITCH + c * 16 + (n & 7) * 2);
+  };
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(addr(kr));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(addr(kr + 4));
+  bf16x8_t f;
+  const v4i16 both[2] = {lo, hi};
+  f = __builtin_bit_cast(bf16x8_t, both);
+  return f;
 }
 
-template <typename Op, int BM, int BN, int STAGES, bool SWIGLU>
+// Scheduling pattern for one sub-step: NM MFMAs with NR LDS reads spread
+// evenly between them (one sched_group_barrier per group, constant counts).
+template <int I, int NM, int NR>
+struct Interleave {
+  __device__ __forceinline__ static void run() {
+    if constexpr (I < NM) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int reads = ((I + 1) * NR) / NM - (I * NR) / NM;
+      if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);
+      Interleave<I + 1, NM, NR>::run();
+    }
+  }
+};
+
+template <typename Op, int BM, int BN, int ROWB, int STAGES, bool KN, bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams p) {
   constexpr int WN = 2;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_INSTR = BM / 32, B_INSTR = BN / 32, INSTR = A_INSTR + B_INSTR;
-  static_assert(STAGES >= 2 && (STAGES - 2) * INSTR <= 63, "vmcnt range");
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
+  constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                // rows per DMA instruction (1 KB)
+  constexpr int A_INSTR = BM / (4 * RPI), B_INSTR = BN / (4 * RPI), INSTR = A_INSTR + B_INSTR;
+  constexpr int KSUB = ROWB / Op::kSliceBytes; // MFMA k slices per K-step
+  constexpr int UNR = (KSUB % 2 == 0) ? 1 : 2; // K-steps per loop trip: fragment set stays static
+  static_assert(KSUB >= 1 && STAGES >= 2 && (STAGES - 1) * INSTR <= 63, "pipeline shape");
+  static_assert(!KN || (Op::kElemBytes == 2 && ROWB == 128), "(K, N) B tiles: bf16, 64 k-rows per K-step");
+  // (K, N) layout: the B tile sits in LDS as [64 k-rows][BN n] exactly as in
+  // memory; 16-byte chunks of a k-row are XOR-swizzled by (k-row mod 8) so the
+  // transposing fragment reads of four consecutive k-rows hit distinct banks
+  constexpr int CPRB = BN * 2 / 16;            // chunks per k-row
+  constexpr int RPIB = 64 / CPRB;              // k-rows per DMA instruction
+  static_assert(2 * 32 * ((SWIGLU ? BN / 2 : BN) + 4) * 4 <= STAGES * STAGE, "epilogue stage fits in LDS");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -424,38 +468,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
   const uint8_t* Bp = static_cast<const uint8_t*>(p.b);
   const int64_t lda_b = p.lda * Op::kElemBytes;
   const int64_t ldb_b = p.ldb * Op::kElemBytes;
-  const int nk = (p.K * Op::kElemBytes) / kRowBytes;
+  const int nk = (p.K * Op::kElemBytes) / ROWB;
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem));
 
   // this lane's source chunk in each DMA instruction; rows past the edge read
   // a valid row instead (their products only reach outputs never stored)
-  const int rsub = lane >> 3, pc = lane & 7;
+  const int rsub = lane / CPR, pc = lane % CPR;
   const uint8_t* asrc[A_INSTR];
   const uint8_t* bsrc[B_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
-    const int r = (j * 4 + wave) * 8 + rsub;
+    const int r = (j * 4 + wave) * RPI + rsub;
     const int grow = min(m0 + r, p.M - 1);
-    asrc[j] = A + grow * lda_b + (pc ^ ((r >> 1) & 7)) * 16;
+    asrc[j] = A + grow * lda_b + swz<ROWB>(r, pc) * 16;
   }
 #pragma unroll
   for (int j = 0; j < B_INSTR; ++j) {
-    const int r = (j * 4 + wave) * 8 + rsub;
-    int n = b_col<SWIGLU, BN>(tn, r, p.N);
-    if (n < 0) n = 0;
-    bsrc[j] = Bp + n * ldb_b + (pc ^ ((r >> 1) & 7)) * 16;
+    if constexpr (!KN) {
+      const int r = (j * 4 + wave) * RPI + rsub;
+      int n = b_col<SWIGLU, BN>(tn, r, p.N);
+      if (n < 0) n = 0;
+      bsrc[j] = Bp + n * ldb_b + swz<ROWB>(r, pc) * 16;
+    } else {
+      const int kr = (j * 4 + wave) * RPIB + lane / CPRB;
+      const int c = (lane % CPRB) ^ kn_swz(kr);
+      int n = b_col<SWIGLU, BN>(tn, c * 8, p.N);
+      if (n < 0) n = 0;
+      bsrc[j] = Bp + kr * ldb_b + n * 2;
+    }
   }
+  const int64_t b_step = KN ? 64 * ldb_b : ROWB;   // B bytes per K-step
 
   auto issue = [&](int kt, int buf) {
     const uint32_t sb = lds0 + buf * STAGE;
-    const int kb = kt * kRowBytes;
+    const int kb = kt * ROWB;
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
       dma16(asrc[j] + kb, __builtin_amdgcn_readfirstlane(sb + (j * 4 + wave) * 1024));
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j)
-      dma16(bsrc[j] + kb, __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * 4 + wave) * 1024));
+      dma16(bsrc[j] + kt * b_step, __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * 4 + wave) * 1024));
   };
 
   f32x16_t acc[FM][FN];
@@ -472,37 +525,82 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
     return part * (BN / 2) + wn * (WTN / 2) + hj * 32 + l32;
   };
 
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nk) issue(st, st);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stage<INSTR, STAGES>(min(nk - 1, kt + STAGES - 2) - kt);
-    lds_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    const uint8_t* la = smem + (kt % STAGES) * STAGE;
+  // Software pipeline. Fragments are double-buffered: the LDS reads of
+  // sub-step g+1 are issued before the MFMAs of sub-step g. Before the last
+  // sub-step of K-step kt the wave waits for its DMA of K-step kt+1, joins the
+  // barrier (after which every wave has finished reading K-step kt's buffer)
+  // and refills that buffer with K-step kt+STAGES.
+  typename Op::frag_t fa[2][FM], fb[2][FN];
+  auto load_frags = [&](int set, const uint8_t* la, int kk) {
     const uint8_t* lb = la + A_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < Op::kSubSteps; ++kk) {
-      typename Op::frag_t fa[FM], fb[FN];
+    for (int i = 0; i < FM; ++i) fa[set][i] = Op::template load<ROWB>(la, wm * WTM + i * 32 + l32, kk, half);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = Op::load(la, wm * WTM + i * 32 + l32, kk, half);
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (!KN) {
+        fb[set][j] = Op::template load<ROWB>(lb, b_row(j), kk, half);
+      } else {
+        // lane l of 16-lane group g: k-rows kk*16 + 8*(g>>1) + (l'>>2) (+4),
+        // columns col0(j) + 16*(g&1) + 4*(l'&3); the hardware transposes each
+        // 16-lane group so lane l ends with 8 consecutive k of column col0 + l%32
+        const int g = lane >> 4, lq = lane & 15;
+        const int kr = kk * 16 + 8 * (g >> 1) + (lq >> 2);
+        const int n = b_row(j) - l32 + 16 * (g & 1) + 4 * (lq & 3);
+        fb[set][j] = load_kn_frag<BN>(lb, kr, n);
+      }
+    }
+  };
+  auto mma_all = [&](int set) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = Op::load(lb, b_row(j), kk, half);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j) acc[i][j] = Op::mma(fb[set][j], fa[set][i], acc[i][j]);
+  };
+  // interleave the MFMAs of one sub-step with the LDS reads of the next in
+  // proportion, so no MFMA waits behind a long queue of younger reads
+  constexpr int NMFMA = FM * FN;
+  constexpr int NREAD = (FM + FN) * Op::kReadsPerFrag;
+
+  // The loop body has no branches, so the scheduler sees each sub-step as one
+  // region: every K-step issues exactly one DMA group (past the end of K it
+  // re-reads the last K-step, an L2 hit, into a buffer nobody reads again),
+  // which also makes every vmcnt wait a constant. nk >= 1 and nk % UNR == 0
+  // (host-checked).
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = Op::mma(fb[j], fa[i], acc[i][j]);
+  for (int st = 0; st < STAGES; ++st) issue(min(st, nk - 1), st);
+  wait_vmcnt<(STAGES - 1) * INSTR>();
+  lds_barrier();
+  load_frags(0, smem, 0);
+  for (int kt = 0; kt < nk; kt += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int ks = kt + u;
+      const uint8_t* la = smem + (ks % STAGES) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk) {
+        const int cur = (u * KSUB + kk) & 1;
+        if (kk + 1 < KSUB) {
+          load_frags(cur ^ 1, la, kk + 1);
+        } else {
+          wait_vmcnt<(STAGES - 2) * INSTR>();
+          lds_barrier();
+          issue(min(ks + STAGES, nk - 1), ks % STAGES);
+          load_frags(cur ^ 1, smem + ((ks + 1) % STAGES) * STAGE, 0);
+        }
+        mma_all(cur);
+        Interleave<0, NMFMA, NREAD>::run();
+      }
     }
   }
+  wait_vmcnt<0>();
   __syncthreads();
   store_tile<BM, BN, SWIGLU>(p, acc, smem, tm, tn);
 }
 
-template <typename Op, int BM, int BN, int STAGES, bool SWIGLU>
+template <typename Op, int BM, int BN, int ROWB, int STAGES, bool KN, bool SWIGLU>
 hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
-  constexpr int smem = STAGES * (BM + BN) * kRowBytes;
-  auto kern = gemm_dma_kernel<Op, BM, BN, STAGES, SWIGLU>;
+  constexpr int smem = STAGES * (BM + BN) * ROWB;
+  auto kern = gemm_dma_kernel<Op, BM, BN, ROWB, STAGES, KN, SWIGLU>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -549,12 +647,14 @@ int pick_tile(int M, int N, int epi) {
 
 template <typename Op, bool KN, bool SW>
 hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
-  const bool dma = !KN && p.M > 0 && p.N > 0 && (p.K * Op::kElemBytes) % kRowBytes == 0;
+  // direct-to-LDS mainloop: 128-byte K-steps (measured faster on gfx950 than
+  // 64-byte K-steps with twice the ring depth: half the barriers per byte)
+  const bool dma = p.M > 0 && p.N > 0 && p.K > 0 && (p.K * Op::kElemBytes) % 128 == 0;
   if (dma) {
     switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta)) {
-      case 0: return launch_dma_tile<Op, 256, 256, 2, SW>(p, s);
-      case 1: return launch_dma_tile<Op, 256, 128, 3, SW>(p, s);
-      default: return launch_dma_tile<Op, 128, 128, 4, SW>(p, s);
+      case 0: return launch_dma_tile<Op, 256, 256, 128, 2, KN, SW>(p, s);
+      case 1: return launch_dma_tile<Op, 256, 128, 128, 3, KN, SW>(p, s);
+      default: return launch_dma_tile<Op, 128, 128, 128, 4, KN, SW>(p, s);
     }
   }
   switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta)) {

@@ -259,15 +259,23 @@ SMALL_AG = [
     AgCase("ag_bf16_p2_dma_medium", M=2 * 2000, N=4040, K=192, P=2, dist="u11", alpha=0.5, beta=2.0),
     AgCase("ag_e4m3_p2_dma_medium", M=2 * 1500, N=2600, K=256, P=2, dtype="e4m3", dist="n05",
            c_dist="n01"),
+    # (K, N) weights, K a multiple of 64: transposing LDS reads of DMA'd B tiles
+    AgCase("ag_bf16_p4_kn_dma_small", M=4 * 72, N=200, K=192, P=4, b_layout="kn", dist="u11",
+           alpha=1.5, beta=0.5, rank=1),
+    AgCase("ag_bf16_p4_kn_dma_swiglu_small", M=4 * 72, N=2 * 136, K=256, P=4, b_layout="kn",
+           dist="n05", beta=0.0, swiglu=True, rank=2),
+    AgCase("ag_bf16_p2_kn_dma_medium", M=2 * 2000, N=4040, K=128, P=2, b_layout="kn", dist="u11"),
 ]
 SMALL_RS = [
     RsCase("rs_bf16_p4_small", M=4 * 136, N=264, K=328, P=4, rank=2, std=0.5),
     RsCase("rs_bf16_p2_kn_small", M=2 * 100, N=200, K=136, P=2, rank=0, b_layout="kn", std=0.5),
     RsCase("rs_bf16_p4_dma_small", M=4 * 136, N=264, K=448, P=4, rank=3, std=0.5),
     RsCase("rs_bf16_p4_dma_medium", M=4 * 1000, N=4040, K=128, P=4, rank=1, std=0.5),
+    RsCase("rs_bf16_p4_kn_dma_small", M=4 * 100, N=264, K=192, P=4, rank=0, b_layout="kn", std=0.5),
 ]
 SMALL_FFN = [
     FfnCase("ffn_public_b4_t16_d128_k2_p2", B=4, T=16, D=128, k=2, P=2),
     FfnCase("ffn_small_affine", B=6, T=16, D=136, k=3, P=4, affine=True, big_bias=True, rank=1),
 ]
-SMALL_SWIGLU = [SwigluCase("swiglu_small", S=72, D=264, F=136, P=4, rank=1, std=0.1)]
+SMALL_SWIGLU = [SwigluCase("swiglu_small", S=72, D=264, F=136, P=4, rank=1, std=0.1),
+                SwigluCase("swiglu_dma_small", S=40, D=256, F=192, P=4, rank=3, std=0.1)]

@@ -21,7 +21,8 @@ def run_ffn(case, inp, flags):
     return host_f64(y)
 
 
-FFN_CASES = W.SMALL_FFN + [W.FfnCase("ffn_mid_ragged", B=9, T=32, D=264, k=3, P=4, rank=2, big_bias=True)]
+FFN_CASES = W.SMALL_FFN + [W.FfnCase("ffn_mid_ragged", B=9, T=32, D=264, k=3, P=4, rank=2, big_bias=True),
+                           W.FfnCase("ffn_dma_ragged", B=5, T=16, D=192, k=2, P=4, rank=1, affine=True)]
 
 
 @pytest.mark.parametrize("case", FFN_CASES, ids=lambda c: c.name)
