@@ -91,6 +91,27 @@ def time_flushed(fn, steps, warmup, scratch):
                 median=float(np.median(times)))
 
 
+def stored_traffic(case_name):
+    """HBM bytes per stage-GEMM launch from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_dma_kernel_{case_name}.md")
+    src = os.path.join(ROOT, "comm_overlapped_linear_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("gemm.hip sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return float(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -100,7 +121,7 @@ def blas_threads():
 
 
 # --------------------------------------------------------------------------- workloads
-def setup_ag(case):
+def setup_ag(case, extra_flags=0):
     inp = W.ag_inputs(case)
     slices = [dev(s) for s in inp["a_slices"]]
     b, c = dev(inp["b"]), dev(inp["c"]) if inp["c"] is not None else None
@@ -116,20 +137,26 @@ def setup_ag(case):
     ws = torch.empty(slice_bytes * case.P, dtype=torch.uint8, device="cuda")   # fits every mode
     prepared = tp.prepare_stage_ag(slices, b, c, d, workspace=ws, flags=tp.UNSTAGED, **kw)
 
-    def call(flags=0):
-        prepared(flags=flags)
+    def call(flags=0, groups=0):
+        prepared._args.groups = groups
+        prepared(flags=flags | extra_flags)
 
     side = [torch.cuda.Stream() for _ in range(4)]
+    remote = case.P - 1
+    tiles = remote * case.m * case.N / (256.0 * 128.0)
+    groups = max(1, min(remote, int(tiles / 256.0 + 1.5)))     # the library's default grouping
 
     def deliveries(hip, kind):
-        """The P-1 deliveries alone, spread over four streams like the library's copy streams."""
+        """The P-1 deliveries alone, issued as the library issues them: stage
+        runs in ring order, run g on copy stream g mod 4."""
         cur = torch.cuda.current_stream()
         for st in side:
             st.wait_stream(cur)
-        for t in range(1, case.P):
-            s = (case.rank + t) % case.P
-            hip.copy(ws.data_ptr() + (t - 1) * slice_bytes, slices[s].data_ptr(), slice_bytes, kind,
-                     side[(t - 1) % 4].cuda_stream)
+        for g in range(groups):
+            for t in range(1 + (g * remote) // groups, 1 + ((g + 1) * remote) // groups):
+                s = (case.rank + t) % case.P
+                hip.copy(ws.data_ptr() + (t - 1) * slice_bytes, slices[s].data_ptr(), slice_bytes, kind,
+                         side[g % 4].cuda_stream)
         for st in side:
             cur.wait_stream(st)
     return inp, call, deliveries, dict(d=d)
@@ -146,14 +173,15 @@ def cpu_baseline_ag(case, inp):
 
 
 def bench_ag(case, args, detail):
-    inp, call, deliveries, bufs = setup_ag(case)
+    inp, call, deliveries, bufs = setup_ag(
+        case, (tp.NO_COPY | tp.SERIAL_STAGES) if args.isolate_kernels else 0)
     dtype = "fp8_e4m3" if case.dtype == "e4m3" else "bf16"
     flop = case.flop
     hip = Hip()
 
     ms = time_steps(lambda: call(0), args.steps, args.warmup)
     value = flop / (ms * 1e-3) / 1e12
-    log(f"[{case.name}] staged (graph, copy engines): {ms * 1e3:.1f} us/step  {value:.1f} TFLOP/s")
+    log(f"[{case.name}] staged (graph replay): {ms * 1e3:.1f} us/step  {value:.1f} TFLOP/s")
 
     # dominant kernel: the stage GEMM, timed per launch with HIP events on its own stream
     call(tp.PROFILE)
@@ -165,39 +193,40 @@ def bench_ag(case, args, detail):
     recs = tp.profile_read()
     kms = float(np.mean([r[0] for r in recs]))
     kflop = float(np.mean([r[1] for r in recs]))
-    achieved = kflop / (kms * 1e-3) / 1e12
+    achieved = kflop / (kms * 1e-3) / 1e12            # = sum(flop) / sum(duration)
     peak = PEAK_TFLOPS[dtype]
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=None,
-                    kernel="gemm_kernel (one stage)", launches=len(recs),
+                    frac=round(achieved / peak, 4), traffic=stored_traffic(case.name),
+                    kernel="gemm_dma_kernel (stage runs of one call)", launches=len(recs),
+                    launches_per_step=len(recs) // args.steps,
                     avg_launch_us=round(kms * 1e3, 2), flop_per_launch=kflop)
-    log(f"[{case.name}] stage GEMM: {kms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s per launch "
-        f"({len(recs)} launches, eager with events)")
+    log(f"[{case.name}] stage GEMM launches: {kms * 1e3:.1f} us avg, {achieved:.1f} TFLOP/s "
+        f"({len(recs)} launches, eager, HIP events on each launch's stream)")
 
     if not args.quick:
         t_compute = time_steps(lambda: call(tp.NO_COPY), args.steps, args.warmup)
-        t_serial_compute = time_steps(lambda: call(tp.NO_COPY | tp.SERIAL_STAGES), args.steps, args.warmup)
-        t_copy = time_steps(lambda: deliveries(hip, 1024), args.steps, args.warmup)
-        t_copy_blit = time_steps(lambda: deliveries(hip, 3), args.steps, args.warmup)
+        t_copy = time_steps(lambda: deliveries(hip, 3), args.steps, args.warmup)          # shader copy
+        t_copy_sdma = time_steps(lambda: deliveries(hip, 1024), args.steps, args.warmup)  # copy engines
         t_unstaged = time_steps(lambda: call(tp.UNSTAGED), args.steps, args.warmup)
-        t_blit = time_steps(lambda: call(tp.COPY_BLIT), args.steps, args.warmup)
+        t_per_stage = time_steps(lambda: call(0, case.P - 1), args.steps, args.warmup)
+        t_sdma = time_steps(lambda: call(tp.COPY_SDMA), args.steps, args.warmup)
         t_eager = time_steps(lambda: call(tp.NO_GRAPH), args.steps, args.warmup)
         hidden = 1.0 - (ms - t_compute) / t_copy if t_copy > 0 else None
-        hidden_blit = 1.0 - (t_blit - t_compute) / t_copy_blit if t_copy_blit > 0 else None
+        hidden_sdma = 1.0 - (t_sdma - t_compute) / t_copy_sdma if t_copy_sdma > 0 else None
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         flushed = time_flushed(lambda: call(0), max(args.steps, 10), 2, scratch)
         del scratch
         detail.update({
             "us_staged": round(ms * 1e3, 2),
             "us_compute_only": round(t_compute * 1e3, 2),
-            "us_compute_only_serial_stages": round(t_serial_compute * 1e3, 2),
-            "us_deliveries_copy_engine": round(t_copy * 1e3, 2),
-            "us_deliveries_blit": round(t_copy_blit * 1e3, 2),
+            "us_deliveries_alone": round(t_copy * 1e3, 2),
             "hidden_fraction": None if hidden is None else round(hidden, 3),
-            "us_staged_blit": round(t_blit * 1e3, 2),
-            "hidden_fraction_blit": None if hidden_blit is None else round(hidden_blit, 3),
             "us_unstaged": round(t_unstaged * 1e3, 2),
+            "us_one_gate_per_stage": round(t_per_stage * 1e3, 2),
             "us_staged_eager": round(t_eager * 1e3, 2),
+            "us_staged_copy_engines": round(t_sdma * 1e3, 2),
+            "us_deliveries_alone_copy_engines": round(t_copy_sdma * 1e3, 2),
+            "hidden_fraction_copy_engines": None if hidden_sdma is None else round(hidden_sdma, 3),
             "us_staged_l2_flushed": {k: round(v * 1e3, 2) for k, v in flushed.items()},
             "tflops_compute_only": round(flop / (t_compute * 1e-3) / 1e12, 1),
         })
@@ -216,6 +245,48 @@ def bench_ffn(case, args):
     return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1))
 
 
+def bench_rs(case, args):
+    inp = W.rs_inputs(case)
+    a, b = dev(inp["a"]), dev(inp["b"])
+    inc = [dev(x) if x is not None else None for x in inp["incoming"]]
+    d = torch.empty((case.M, case.N), dtype=torch.int16, device="cuda")
+    ws = torch.empty(max(1, case.m * case.N * 2 * case.P), dtype=torch.uint8, device="cuda")
+    call = tp.prepare_stage_rs(a, b, inc, d, workspace=ws, M=case.M, N=case.N, K=case.K, P=case.P,
+                               rank=case.rank, b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK)
+    steps = max(5, args.steps // 2)
+    ms = time_steps(call, steps, 3)
+    mc = time_steps(lambda: call(flags=tp.NO_COPY), steps, 3)
+    return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1),
+                us_compute_only=round(mc * 1e3, 1))
+
+
+def bench_swiglu(case, args):
+    inp = W.swiglu_inputs(case)
+    xs = [dev(x) for x in inp["x_shards"]]
+    w13, w2 = dev(inp["w13"]), dev(inp["w2"])
+    h = torch.empty((case.M, case.F), dtype=torch.int16, device="cuda")
+    out = torch.empty((case.M, case.D), dtype=torch.int16, device="cuda")
+    ws = torch.empty(case.S * case.D * 2 * case.P, dtype=torch.uint8, device="cuda")
+    ag = tp.prepare_stage_ag(xs, w13, None, h, workspace=ws, M=case.M, N=2 * case.F, K=case.D,
+                             rank=case.rank, b_layout=tp.B_KN, epilogue=tp.EPI_SWIGLU, alpha=1.0, beta=0.0)
+    rs = tp.prepare_stage_rs(h, w2, None, out, M=case.M, N=case.D, K=case.F, P=case.P, rank=case.rank,
+                             b_layout=tp.B_KN)
+
+    def block():
+        ag()
+        rs()
+    ms = time_steps(block, max(5, args.steps // 2), 3)
+    return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1))
+
+
+def bench_small_ag(case, args):
+    inp, call, _, _ = setup_ag(case)
+    ms = time_steps(lambda: call(0), args.steps, args.warmup)
+    mu = time_steps(lambda: call(tp.UNSTAGED), args.steps, args.warmup)
+    return dict(us=round(ms * 1e3, 2), us_unstaged=round(mu * 1e3, 2),
+                tflops=round(case.flop / (ms * 1e-3) / 1e12, 2))
+
+
 WORKLOADS = {"ag_e4m3_p8": W.C2, "ag_e4m3_p8_beta0": W.C2_BETA0, "ag_bf16_p2": W.C1}
 
 
@@ -227,7 +298,14 @@ def main():
     ap.add_argument("--workload", default="ag_e4m3_p8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline and roofline only")
-    ap.add_argument("--ffn", action="store_true", help="also time the per-slot FFN layer")
+    ap.add_argument("--no-ffn", action="store_true", help="skip timing the per-slot FFN layer")
+    ap.add_argument("--all", action="store_true", help="also time the other four workloads")
+    ap.add_argument("--isolate-kernels", action="store_true",
+                    help="run every call with no deliveries and one compute stream, so that each GEMM "
+                         "dispatch runs alone (for per-dispatch hardware counters)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run one plain 256 MiB copy (identity permute) whose HBM bytes are known, "
+                         "to scale FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures the rank-local share on ONE GPU; peers are buffers in the same HBM. "
@@ -241,10 +319,24 @@ def main():
 
     case = WORKLOADS[args.workload]
     detail = {}
+    if args.calibration_copy:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        evict = torch.empty(4 * n, dtype=torch.uint8, device="cuda").fill_(2)   # push src out of L2 / MALL
+        torch.cuda.synchronize()
+        tp.dispatch_permute([src], dst, rank=0, B=1, T=1, D=n, elem_bytes=1)
+        torch.cuda.synchronize()
+        del src, dst, evict
     r = bench_ag(case, args, detail)
-    if args.ffn:
+    if not args.no_ffn and not args.quick:
         detail["ffn_layer"] = bench_ffn(W.C4, args)
         log(f"[ffn] {detail['ffn_layer']}")
+    if args.all:
+        detail["ag_bf16_p2_256x256x512"] = bench_small_ag(W.C1, args)
+        detail["rs_bf16_p8_8192x8192x3584"] = bench_rs(W.C3, args)
+        detail["swiglu_p8_s1024_d4096_f1792"] = bench_swiglu(W.C5, args)
+        log(f"[other] {json.dumps({k: detail[k] for k in ('ag_bf16_p2_256x256x512', 'rs_bf16_p8_8192x8192x3584', 'swiglu_p8_s1024_d4096_f1792')})}")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -22,7 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, E4M3 = 0, 1
 B_NK, B_KN = 0, 1
 EPI_ALPHA_BETA, EPI_SWIGLU = 0, 1
-UNSTAGED, NO_COPY, NO_GRAPH, COPY_BLIT, SERIAL_STAGES, PROFILE = 1, 2, 4, 8, 16, 32
+UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE = 1, 2, 4, 8, 16, 32
 
 _STATUS = {OK: "OK", ERR_INVALID: "INVALID", ERR_UNSUPPORTED: "UNSUPPORTED",
            ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP"}
@@ -42,7 +42,7 @@ class AgArgs(ctypes.Structure):
                 ("c", ctypes.c_void_p), ("d", ctypes.c_void_p),
                 ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32)]
 
 
 class RsArgs(ctypes.Structure):
@@ -53,7 +53,7 @@ class RsArgs(ctypes.Structure):
                 ("incoming", ctypes.POINTER(ctypes.c_void_p)), ("d", ctypes.c_void_p),
                 ("alpha", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32)]
 
 
 class FfnArgs(ctypes.Structure):
@@ -159,11 +159,11 @@ def _workspace(ws, nbytes):
 
 
 def ag_args(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, epilogue=EPI_ALPHA_BETA,
-            alpha=1.0, beta=1.0, flags=0):
+            alpha=1.0, beta=1.0, flags=0, groups=0):
     slices = _ptr_array(a_slices)
     args = AgArgs(M=M, N=N, K=K, P=len(a_slices), rank=rank, ab_dtype=dtype, b_layout=b_layout,
                   epilogue=epilogue, a_slices=ctypes.cast(slices, ctypes.POINTER(ctypes.c_void_p)),
-                  b=_ptr(b), c=_ptr(c), d=_ptr(d), alpha=alpha, beta=beta, flags=flags)
+                  b=_ptr(b), c=_ptr(c), d=_ptr(d), alpha=alpha, beta=beta, flags=flags, groups=groups)
     args._keep = slices
     return args
 
@@ -173,10 +173,10 @@ def stage_ag_workspace_size(args):
 
 
 def stage_ag(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, epilogue=EPI_ALPHA_BETA,
-             alpha=1.0, beta=1.0, flags=0, workspace=None, stream=None):
+             alpha=1.0, beta=1.0, flags=0, groups=0, workspace=None, stream=None):
     """Staged all-gather GEMM: d = alpha * A b^T + beta * c (see tpgemm.h)."""
     args = ag_args(a_slices, b, c, d, M=M, N=N, K=K, rank=rank, dtype=dtype, b_layout=b_layout,
-                   epilogue=epilogue, alpha=alpha, beta=beta, flags=flags)
+                   epilogue=epilogue, alpha=alpha, beta=beta, flags=flags, groups=groups)
     need = stage_ag_workspace_size(args)
     ws = _workspace(workspace, need)
     args.workspace = _ptr(ws) if ws is not None else None
@@ -184,11 +184,12 @@ def stage_ag(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, e
     _check(lib().tpgemm_stage_ag(ctypes.byref(args), _stream(stream)))
 
 
-def rs_args(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0):
+def rs_args(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0,
+            groups=0):
     inc = _ptr_array(incoming) if incoming is not None else None
     args = RsArgs(M=M, N=N, K=K, P=P, rank=rank, ab_dtype=dtype, b_layout=b_layout, a=_ptr(a), b=_ptr(b),
                   incoming=ctypes.cast(inc, ctypes.POINTER(ctypes.c_void_p)) if inc is not None else None,
-                  d=_ptr(d), alpha=alpha, flags=flags)
+                  d=_ptr(d), alpha=alpha, flags=flags, groups=groups)
     args._keep = inc
     return args
 
@@ -198,10 +199,10 @@ def stage_rs_workspace_size(args):
 
 
 def stage_rs(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0,
-             workspace=None, stream=None):
+             groups=0, workspace=None, stream=None):
     """Staged GEMM + reduce-scatter share (see tpgemm.h)."""
     args = rs_args(a, b, incoming, d, M=M, N=N, K=K, P=P, rank=rank, dtype=dtype, b_layout=b_layout,
-                   alpha=alpha, flags=flags)
+                   alpha=alpha, flags=flags, groups=groups)
     need = stage_rs_workspace_size(args)
     ws = _workspace(workspace, need)
     args.workspace = _ptr(ws) if ws is not None else None

@@ -1,13 +1,14 @@
 // C ABI of libtpgemm: validation, the stage scheduler and the graph cache.
 //
 // The scheduler follows "Distributed GEMM" (Hassani et al., SHI Labs,
-// Dec 2024): the copy engine moves the peers' shards while the matrix cores
-// run the local stage, and the stage kernels need no communication code of
-// their own (Introduction; Approach, observations 2 and 4; Background,
-// Figure 4: local shard first, then rotate). On one MI355X the peers' shards
-// are buffers in the same HBM: each delivery is one hipMemcpyAsync on a
-// library-owned copy stream (the SDMA copy engines unless TPG_COPY_BLIT),
-// followed by an event that gates exactly the stage that reads it. Stage
+// Dec 2024): the peers' shards are moved by asynchronous copies while the
+// matrix cores run the local stage, and the stage kernels need no
+// communication code of their own (Introduction; Approach, observations 2 and
+// 4; Background, Figure 4: local shard first, then rotate). On one MI355X the
+// peers' shards are buffers in the same HBM: each delivery is one
+// hipMemcpyAsync on a library-owned copy stream (the shader copy, or the SDMA
+// copy engines with TPG_COPY_SDMA), followed by an event that gates exactly
+// the stage run that reads it. Stage
 // kernels fan out over up to four compute streams so that several small
 // stages can share the 256 CUs; everything forks from and joins back into the
 // caller's stream. Unless TPG_NO_GRAPH, one call is recorded once into a
@@ -48,7 +49,7 @@ constexpr int kStreams = 4;       // compute streams per call (index 0 = root)
 constexpr int kCopyStreams = 4;   // copy streams: deliveries spread over several copy engines
 constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
-constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_BLIT |
+constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
                                  TPG_SERIAL_STAGES | TPG_PROFILE;
 
 struct ProfRec {
@@ -156,7 +157,7 @@ struct Launch {
 
 tpg_status gemm_on(Ctx& cx, const Launch& L, hipStream_t s, const tpg::GemmParams& p, int dtype,
                    int layout, int epi) {
-  ProfRec rec{nullptr, nullptr, 2.0 * p.M * double(p.N) * p.K};
+  ProfRec rec{nullptr, nullptr, 2.0 * p.M * double(p.N) * p.K * p.batch};
   if (L.profile) {
     for (hipEvent_t* e : {&rec.a, &rec.b}) {
       if (!cx.prof_pool.empty()) {
@@ -214,7 +215,7 @@ tpg_status fork_copies(Ctx& cx, hipStream_t root) {
 }
 
 hipMemcpyKind copy_kind(uint32_t flags) {
-  return (flags & TPG_COPY_BLIT) ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+  return (flags & TPG_COPY_SDMA) ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
 }
 
 // Records `enqueue` into a graph once per key and replays it on `user`, or
@@ -255,6 +256,17 @@ void put(std::ostringstream& os, const T& v) {
 }
 
 // ---------------------------------------------------------------- all-gather
+// Default number of gated stage runs: one more than the number of full
+// waves of 256x128 tiles the remote stages make on 256 CUs (small stages are
+// merged, stages that fill the chip on their own keep one gate each). On
+// MI355X the fixed cost of a delivery (~5-10 us per copy) and of a launch
+// outweighs the finer pipeline when a stage is well under one wave.
+int auto_groups(int64_t rows_per_stage, int64_t n, int remote) {
+  const double tiles = double(remote) * double(rows_per_stage) * double(n) / (256.0 * 128.0);
+  const int g = static_cast<int>(tiles / 256.0 + 1.5);
+  return std::max(1, std::min(remote, g));
+}
+
 tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
   if (a->P < 1 || a->P > kMaxP) return fail(TPG_ERR_INVALID, "P must be in [1, 64]");
@@ -329,6 +341,7 @@ tpg::GemmParams base_params() {
   std::memset(&p, 0, sizeof(p));
   p.add_row0 = 0;
   p.add_row1 = 0;
+  p.batch = 1;
   return p;
 }
 
@@ -380,33 +393,58 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     return gemm_on(cx, L, L.root, p, dtype, layout, epi);
   }
 
-  // staged: stage t multiplies slice s = (rank + t) mod P, local first
+  // staged: stage t multiplies slice s = (rank + t) mod P, local first. The
+  // P-1 remote stages are cut into G runs; run g waits for one event and is
+  // one GEMM launch per stretch of D rows that does not wrap past slice P-1.
+  const int remote = P - 1;
+  const int G = remote == 0 ? 0 : (a.groups > 0 ? std::min(a.groups, remote) : auto_groups(m, a.N, remote));
+  auto t0 = [&](int g) { return 1 + (g * remote) / G; };
+  auto adjacent = [&](int s, int run) {   // a_slices[s .. s+run) back to back in memory
+    for (int i = 1; i < run; ++i)
+      if (static_cast<const char*>(a.a_slices[s + i]) != static_cast<const char*>(a.a_slices[s]) + i * slice_b)
+        return false;
+    return true;
+  };
   if (copies) {
-    for (int t = 1; t < P; ++t) {
-      const int s = (r + t) % P;
-      hipStream_t cp = cx.copy[(t - 1) % kCopyStreams];
-      HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], slice_b, kind, cp));
-      HIP_TRY(hipEventRecord(cx.ev_copy[t], cp));
+    for (int g = 0; g < G; ++g) {
+      hipStream_t cp = cx.copy[g % kCopyStreams];
+      for (int t = t0(g); t < t0(g + 1);) {
+        const int s = (r + t) % P;
+        int run = 1;
+        while (t + run < t0(g + 1) && s + run < P && adjacent(s, run + 1)) ++run;
+        HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], run * slice_b, kind, cp));
+        t += run;
+      }
+      HIP_TRY(hipEventRecord(cx.ev_copy[g], cp));
     }
   }
-  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(P, kStreams);
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(G + 1, kStreams);
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, ns, st);
   if (stat != TPG_OK) return stat;
-  p.M = static_cast<int>(m);
-  for (int t = 0; t < P; ++t) {
-    const int s = (r + t) % P;
-    hipStream_t cs = st[t % ns];
-    const void* A = a.a_slices[s];
-    if (copies && t > 0) {
-      HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[t], 0));
-      A = ws + (t - 1) * slice_b;
+  auto launch_rows = [&](hipStream_t cs, const void* A, int s, int run) {
+    tpg::GemmParams q = p;
+    q.a = A;
+    q.M = static_cast<int>(run * m);
+    q.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
+    q.d = static_cast<uint16_t*>(a.d) + s * m * nout;
+    return gemm_on(cx, L, cs, q, dtype, layout, epi);
+  };
+  stat = launch_rows(st[0], a.a_slices[r], r, 1);        // stage 0: the local slice
+  if (stat != TPG_OK) return stat;
+  for (int g = 0; g < G; ++g) {
+    hipStream_t cs = st[(g + 1) % ns];
+    if (copies) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
+    for (int t = t0(g); t < t0(g + 1);) {
+      const int s = (r + t) % P;
+      int run = std::min(t0(g + 1) - t, P - s);
+      if (!copies)
+        while (run > 1 && !adjacent(s, run)) --run;      // in place: one launch per adjacent stretch
+      const void* A = copies ? static_cast<const void*>(ws + (t - 1) * slice_b) : a.a_slices[s];
+      stat = launch_rows(cs, A, s, run);
+      if (stat != TPG_OK) return stat;
+      t += run;
     }
-    p.a = A;
-    p.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
-    p.d = static_cast<uint16_t*>(a.d) + s * m * nout;
-    stat = gemm_on(cx, L, cs, p, dtype, layout, epi);
-    if (stat != TPG_OK) return stat;
   }
   return join_streams(cx, L.root, ns, st, copies);
 }
@@ -416,7 +454,7 @@ std::string ag_key(const tpg_ag_args& a) {
   os << "ag|";
   put(os, a.M); put(os, a.N); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.ab_dtype);
   put(os, a.b_layout); put(os, a.epilogue); put(os, a.b); put(os, a.c); put(os, a.d);
-  put(os, a.alpha); put(os, a.beta); put(os, a.workspace); put(os, a.flags);
+  put(os, a.alpha); put(os, a.beta); put(os, a.workspace); put(os, a.flags); put(os, a.groups);
   for (int s = 0; s < a.P && a.a_slices; ++s) put(os, a.a_slices[s]);
   return os.str();
 }
@@ -529,8 +567,16 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   if (copies) {
     tpg_status fs = fork_copies(cx, L.root);
     if (fs != TPG_OK) return fs;
-    for (size_t i = 0; i < peers.size(); ++i)
-      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], part_b, kind, cx.copy[i % kCopyStreams]));
+    // partials that sit back to back in memory (and in the slots) move as one copy
+    for (size_t i = 0; i < peers.size();) {
+      size_t run = 1;
+      while (slot == part_b && i + run < peers.size() &&
+             static_cast<const char*>(a.incoming[peers[i + run]]) ==
+                 static_cast<const char*>(a.incoming[peers[i]]) + run * part_b)
+        ++run;
+      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], run * part_b, kind, cx.copy[i % kCopyStreams]));
+      i += run;
+    }
     for (int i = 0; i < ncs; ++i) HIP_TRY(hipEventRecord(cx.ev_copy[i], cx.copy[i]));
   }
   // the stage that sums the incoming partials waits for every delivery
@@ -555,27 +601,44 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     return copies ? wait_copies(cx, L.root) : TPG_OK;
   }
 
-  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(P, kStreams);
+  // stages 0..P-2 emit the blocks (rank+1+t) mod P, cut into G runs (one
+  // launch per run and non-wrapping stretch); the own block is the last stage
+  const int emit = P - 1;
+  // emitted blocks wait for nothing: by default one launch per non-wrapping
+  // stretch, so each launch fills the chip with the largest tiles
+  const int G = emit == 0 ? 0 : (a.groups > 0 ? std::min(a.groups, emit) : 1);
+  auto t0 = [&](int g) { return (g * emit) / G; };
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(G + 1, kStreams);
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, ns, st);
   if (stat != TPG_OK) return stat;
-  p.M = static_cast<int>(m);
-  for (int t = 0; t < P; ++t) {
-    const int blk = (r + 1 + t) % P;       // own block last
-    hipStream_t cs = st[t % ns];
+  auto launch_blocks = [&](hipStream_t cs, int blk, int run, bool own) {
     tpg::GemmParams q = p;
+    q.M = static_cast<int>(run * m);
     q.a = static_cast<const char*>(a.a) + size_t(blk) * m * a.K * eb;
     q.d = static_cast<uint16_t*>(a.d) + blk * m * a.N;
-    if (blk == r) {
-      tpg_status ws_ = wait_all(cs);
-      if (ws_ != TPG_OK) return ws_;
+    if (own) {
       q.add_row0 = 0;
       q.add_row1 = static_cast<int>(m);
       set_adds(q);
     }
-    stat = gemm_on(cx, L, cs, q, dtype, layout, tpg::kEpiAlphaBeta);
-    if (stat != TPG_OK) return stat;
+    return gemm_on(cx, L, cs, q, dtype, layout, tpg::kEpiAlphaBeta);
+  };
+  for (int g = 0; g < G; ++g) {
+    hipStream_t cs = st[g % ns];
+    for (int t = t0(g); t < t0(g + 1);) {
+      const int blk = (r + 1 + t) % P;
+      const int run = std::min(t0(g + 1) - t, P - blk);
+      stat = launch_blocks(cs, blk, run, false);
+      if (stat != TPG_OK) return stat;
+      t += run;
+    }
   }
+  hipStream_t cs_own = st[G % ns];
+  stat = wait_all(cs_own);
+  if (stat != TPG_OK) return stat;
+  stat = launch_blocks(cs_own, r, 1, true);
+  if (stat != TPG_OK) return stat;
   return join_streams(cx, L.root, ns, st, copies);
 }
 
@@ -584,12 +647,18 @@ std::string rs_key(const tpg_rs_args& a) {
   os << "rs|";
   put(os, a.M); put(os, a.N); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.ab_dtype);
   put(os, a.b_layout); put(os, a.a); put(os, a.b); put(os, a.d); put(os, a.alpha);
-  put(os, a.workspace); put(os, a.flags);
+  put(os, a.workspace); put(os, a.flags); put(os, a.groups);
   for (int j = 0; a.incoming && j < a.P; ++j) put(os, a.incoming[j]);
   return os.str();
 }
 
 // ---------------------------------------------------------------- FFN
+// Slots are pipelined over two compute streams, each with its own z / h
+// buffers: the LayerNorm pass of one slot (HBM-bound) overlaps the GEMMs of
+// the next (MFMA-bound), and the two slots' z (126 MB each at the workload
+// size) stay in the 256 MB Infinity Cache between GEMM1 and the LayerNorm
+// pass. (One batched launch over all slots was measured slower: its 1 GB z
+// round-trips through HBM.) TPG_SERIAL_STAGES uses one stream and one buffer.
 int ffn_bufs(uint32_t flags) { return (flags & TPG_SERIAL_STAGES) ? 1 : 2; }
 
 size_t ffn_ws(const tpg_ffn_args* a) {

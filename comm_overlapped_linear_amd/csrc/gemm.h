@@ -30,6 +30,10 @@ struct GemmParams {
   int64_t ld_add;              // row stride of every addend (elements)
   int add_row0, add_row1;
   int vec_ok;                  // 1 if ldc, ldd and ld_add are multiples of 8 (16-byte row vectors)
+  // batched launch (blockIdx.y = batch index): element strides between the
+  // operands of consecutive batches (0 = shared); C and addends unbatched
+  int batch;                   // >= 1
+  int64_t a_bstride, b_bstride, d_bstride, bias_bstride;
 };
 
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };

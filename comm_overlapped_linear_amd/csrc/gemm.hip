@@ -96,6 +96,27 @@ __device__ __forceinline__ int b_col(int tn, int i, int N) {
   return u < nh ? u + half * nh : -1;
 }
 
+// Operand pointers of batch blockIdx.y of a batched launch. (The parameter
+// block itself stays in the kernel-argument segment: a private copy would be
+// spilled to scratch because the epilogue indexes add_list dynamically.)
+struct BatchPtrs {
+  const uint8_t* a;
+  const uint8_t* b;
+  uint16_t* d;
+  const uint16_t* bias;
+};
+
+template <int EB>
+__device__ __forceinline__ BatchPtrs batch_ptrs(const GemmParams& p) {
+  const int64_t z = blockIdx.y;
+  BatchPtrs q;
+  q.a = static_cast<const uint8_t*>(p.a) + z * p.a_bstride * EB;
+  q.b = static_cast<const uint8_t*>(p.b) + z * p.b_bstride * EB;
+  q.d = p.d + z * p.d_bstride;
+  q.bias = p.bias ? p.bias + z * p.bias_bstride : nullptr;
+  return q;
+}
+
 // Adds beta * C, the bias and the addends to x[0..8) for output (row, col ..
 // col + 7) and stores bf16. Full 16-byte vectors when the row stride allows.
 __device__ __forceinline__ void add_row8(const uint16_t* src, int64_t off, bool vec, int n, float scale,
@@ -113,17 +134,18 @@ __device__ __forceinline__ void add_row8(const uint16_t* src, int64_t off, bool 
   }
 }
 
-__device__ __forceinline__ void epilogue_vec8(const GemmParams& p, int row, int col, int nout, float* x) {
+__device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPtrs& bp, int row, int col, int nout,
+                                              float* x) {
   const int n = min(8, nout - col);
   const bool vec = p.vec_ok && n == 8;
   if (p.beta != 0.0f) add_row8(p.c, static_cast<int64_t>(row) * p.ldc + col, vec, n, p.beta, x);
-  if (p.bias) add_row8(p.bias, col, n == 8, n, 1.0f, x);
+  if (bp.bias) add_row8(bp.bias, col, n == 8, n, 1.0f, x);
   if (row >= p.add_row0 && row < p.add_row1) {
     const int64_t off = static_cast<int64_t>(row - p.add_row0) * p.ld_add + col;
     for (int t = 0; t < p.n_add_list; ++t) add_row8(p.add_list[t], off, vec, n, 1.0f, x);
     for (int t = 0; t < p.n_add_strided; ++t) add_row8(p.add_base + t * p.add_stride, off, vec, n, 1.0f, x);
   }
-  uint16_t* dst = p.d + static_cast<int64_t>(row) * p.ldd + col;
+  uint16_t* dst = bp.d + static_cast<int64_t>(row) * p.ldd + col;
   if (vec) {
     uint4 o;
     o.x = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
@@ -143,8 +165,9 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, int row, int 
 // one bf16 rounding, 16-byte coalesced stores. The caller has synchronised
 // the workgroup, so the LDS is free.
 template <int BM, int BN, bool SWIGLU>
-__device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16_t (&acc)[BM / 64][BN / 64],
-                                           uint8_t* smem, int tm, int tn) {
+__device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs& bp,
+                                           const f32x16_t (&acc)[BM / 64][BN / 64], uint8_t* smem, int tm,
+                                           int tn) {
   constexpr int WN = 2;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -197,14 +220,16 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16_t (
       const float4 hi = *reinterpret_cast<const float4*>(stage + sr * SLD + sc + 4);
       x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
       x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
-      epilogue_vec8(p, row, col, nout, x);
+      epilogue_vec8(p, bp, row, col, nout, x);
     }
     __syncthreads();
   }
 }
 
+
 template <typename Op, int BM, int BN, bool KN, bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
+  const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
   constexpr int WM = 2, WN = 2;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -229,8 +254,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
   const int tn = blockIdx.x / ntm;
   const int m0 = tm * BM;
 
-  const uint8_t* A = static_cast<const uint8_t*>(p.a);
-  const uint8_t* Bp = static_cast<const uint8_t*>(p.b);
+  const uint8_t* A = bp.a;
+  const uint8_t* Bp = bp.b;
   const int64_t lda_b = p.lda * Op::kElemBytes;
   const int64_t ldb_b = p.ldb * Op::kElemBytes;
   const int kbytes = p.K * Op::kElemBytes;
@@ -359,7 +384,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  store_tile<BM, BN, SWIGLU>(p, acc, smem, tm, tn);
+  store_tile<BM, BN, SWIGLU>(p, bp, acc, smem, tm, tn);
+}
+
+// Workgroup -> output tile. Consecutive workgroup ids are dealt round-robin
+// to the 8 XCDs, each with its own L2, so id b is first re-numbered to
+// (b mod 8) * (nt / 8) + b / 8: each XCD then owns one contiguous run of the
+// tile order. The tile order walks groups of GM tile-rows column by column,
+// with GM chosen so that one XCD's run is a compact rectangle of tiles
+// (about sqrt(run) rows): its A rows and B columns are shared in its L2.
+template <int BM, int BN, bool SWIGLU>
+__device__ __forceinline__ void tile_of_block(const GemmParams& p, int ntm, int& tm, int& tn) {
+  const int nt = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);
+  const int run = (nt & 7) == 0 ? (nt >> 3) : nt;
+  int gm = 1;
+  while ((gm * 2) * (gm * 2) <= run && gm * 2 <= ntm) gm *= 2;
+  const int ntn = nt / ntm;
+  const int group = bid / (gm * ntn);
+  const int first = group * gm;
+  const int rows = min(gm, ntm - first);
+  const int in_group = bid - group * gm * ntn;
+  tm = first + in_group % rows;
+  tn = in_group / rows;
 }
 
 // ---------------------------------------------------------------------------
@@ -411,14 +459,17 @@ __device__ __forceinline__ bf16x8_t load_kn_frag(const uint8_t* lb, int kr, int 
   return f;
 }
 
-// Scheduling pattern for one sub-step: NM MFMAs with NR LDS reads spread
-// evenly between them (one sched_group_barrier per group, constant counts).
+// Scheduling pattern for one sub-step: NM MFMAs with the NR LDS reads of the
+// next sub-step spread over the first half of them, so the reads have at
+// least NM/2 MFMAs of time to land before they are needed (one
+// sched_group_barrier per group, constant counts).
 template <int I, int NM, int NR>
 struct Interleave {
   __device__ __forceinline__ static void run() {
     if constexpr (I < NM) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      constexpr int reads = ((I + 1) * NR) / NM - (I * NR) / NM;
+      constexpr int H = NM / 2 > 0 ? NM / 2 : 1;
+      constexpr int reads = I < H ? ((I + 1) * NR) / H - (I * NR) / H : 0;
       if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);
       Interleave<I + 1, NM, NR>::run();
     }
@@ -427,6 +478,7 @@ struct Interleave {
 
 template <typename Op, int BM, int BN, int ROWB, int STAGES, bool KN, bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams p) {
+  const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
   constexpr int WN = 2;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -454,18 +506,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // consecutive workgroups land on different XCDs: give each XCD a
-  // contiguous run of tiles (M fastest) so its L2 sees shared B columns
-  int bid = blockIdx.x;
-  const int nt = gridDim.x;
-  if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);
   const int ntm = (p.M + BM - 1) / BM;
-  const int tm = bid % ntm;
-  const int tn = bid / ntm;
+  int tm, tn;
+  tile_of_block<BM, BN, SWIGLU>(p, ntm, tm, tn);
   const int m0 = tm * BM;
 
-  const uint8_t* A = static_cast<const uint8_t*>(p.a);
-  const uint8_t* Bp = static_cast<const uint8_t*>(p.b);
+  const uint8_t* A = bp.a;
+  const uint8_t* Bp = bp.b;
   const int64_t lda_b = p.lda * Op::kElemBytes;
   const int64_t ldb_b = p.ldb * Op::kElemBytes;
   const int nk = (p.K * Op::kElemBytes) / ROWB;
@@ -594,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
   }
   wait_vmcnt<0>();
   __syncthreads();
-  store_tile<BM, BN, SWIGLU>(p, acc, smem, tm, tn);
+  store_tile<BM, BN, SWIGLU>(p, bp, acc, smem, tm, tn);
 }
 
 template <typename Op, int BM, int BN, int ROWB, int STAGES, bool KN, bool SWIGLU>
@@ -610,8 +657,8 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   }
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int grid = ((p.M + BM - 1) / BM) * nout_tiles;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, s, p);
+  if (grid == 0 || p.batch < 1) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(kThreads), smem, s, p);
   return hipGetLastError();
 }
 
@@ -628,21 +675,46 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
   }
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int grid = ((p.M + BM - 1) / BM) * nout_tiles;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, s, p);
+  if (grid == 0 || p.batch < 1) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(kThreads), smem, s, p);
   return hipGetLastError();
 }
 
-// Tile choice: the largest tile that still gives about one workgroup per CU.
-int pick_tile(int M, int N, int epi) {
+// Number of compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Tile choice by a small cost model: waves of workgroups over the CUs times
+// the tile's work divided by its relative MFMA efficiency (measured on
+// MI355X: a 256x128 tile runs at ~0.82 and a 128x128 tile at ~0.73 of the
+// 256x256 tile's per-CU rate, for both bf16 and fp8).
+int pick_tile(int M, int N, int epi, int batch) {
   const int n = epi == kEpiSwiglu ? N / 2 : N;
   const int bn_div = epi == kEpiSwiglu ? 2 : 1;
-  auto tiles = [&](int bm, int bn) {
-    return ((M + bm - 1) / bm) * ((n + bn / bn_div - 1) / (bn / bn_div));
-  };
-  if (tiles(256, 256) >= 240) return 0;
-  if (tiles(256, 128) >= 240) return 1;
-  return 2;
+  const int cus = cu_count();
+  const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
+  const double eff[3] = {1.0, 0.82, 0.73};
+  int best = 0;
+  double best_cost = 0.0;
+  for (int t = 0; t < 3; ++t) {
+    const long tiles = long(batch) * ((M + bm[t] - 1) / bm[t]) * ((n + bn[t] / bn_div - 1) / (bn[t] / bn_div));
+    const long waves = (tiles + cus - 1) / cus;
+    const double cost = double(waves) * bm[t] * bn[t] / eff[t];
+    if (t == 0 || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 template <typename Op, bool KN, bool SW>
@@ -651,13 +723,13 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   // 64-byte K-steps with twice the ring depth: half the barriers per byte)
   const bool dma = p.M > 0 && p.N > 0 && p.K > 0 && (p.K * Op::kElemBytes) % 128 == 0;
   if (dma) {
-    switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta)) {
+    switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta, p.batch)) {
       case 0: return launch_dma_tile<Op, 256, 256, 128, 2, KN, SW>(p, s);
       case 1: return launch_dma_tile<Op, 256, 128, 128, 3, KN, SW>(p, s);
       default: return launch_dma_tile<Op, 128, 128, 128, 4, KN, SW>(p, s);
     }
   }
-  switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta)) {
+  switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta, p.batch)) {
     case 0: return launch_tile<Op, 256, 256, KN, SW>(p, s);
     case 1: return launch_tile<Op, 256, 128, KN, SW>(p, s);
     default: return launch_tile<Op, 128, 128, KN, SW>(p, s);
@@ -667,7 +739,7 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 int gemm_grid_size(int M, int N, int epi) {
-  const int t = pick_tile(M, N, epi);
+  const int t = pick_tile(M, N, epi, 1);
   const int bm = t == 2 ? 128 : 256, bn = t == 0 ? 256 : 128;
   const int n = epi == kEpiSwiglu ? N / 2 : N;
   const int bno = epi == kEpiSwiglu ? bn / 2 : bn;

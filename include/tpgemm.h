@@ -5,9 +5,11 @@
  * stages. The peers' shards are ordinary device buffers in the same HBM;
  * each stage's input is delivered by an asynchronous device-to-device copy on
  * a library-owned copy stream and gated by a HIP event, so the matrix cores
- * start on the local shard while the copy engine delivers the rest
- * ("Distributed GEMM", Hassani et al., SHI Labs, Dec 2024: Introduction and
- * Background, Figures 3 and 4).
+ * start on the local shard while the rest is delivered ("Distributed GEMM",
+ * Hassani et al., SHI Labs, Dec 2024: Introduction and Background, Figures 3
+ * and 4). The copy is hipMemcpyAsync's shader copy by default: on MI355X an
+ * 8 MiB device-to-device copy takes ~4 us that way and ~140 us on one SDMA
+ * copy engine, so the engines (TPG_COPY_SDMA) are opt-in.
  *
  * Conventions shared by every entry point
  *   - All pointers to tensor data are DEVICE pointers owned by the caller;
@@ -72,7 +74,7 @@ enum {
   TPG_UNSTAGED = 1u,        /* single stage: deliver everything, then one GEMM (the non-overlapped baseline) */
   TPG_NO_COPY = 2u,         /* read peer buffers in place; no deliveries (compute-only timing) */
   TPG_NO_GRAPH = 4u,        /* enqueue eagerly instead of capturing / replaying a hipGraph */
-  TPG_COPY_BLIT = 8u,       /* deliver with the shader copy (uses CUs) instead of the copy engines */
+  TPG_COPY_SDMA = 8u,       /* deliver with the SDMA copy engines (no CUs) instead of the shader copy */
   TPG_SERIAL_STAGES = 16u,  /* run all stage GEMMs on one compute stream (no inter-stage concurrency) */
   TPG_PROFILE = 32u         /* eager only: time every GEMM launch with HIP events (tpg_profile_read) */
 };
@@ -99,6 +101,15 @@ enum {
  *                bytes (receive slots for the P-1 delivered slices; with
  *                TPG_UNSTAGED the whole gathered A). May be NULL if that size
  *                is 0. Contents are scratch.
+ *   groups       how the P-1 remote stages are gated: they are cut, in ring
+ *                order, into `groups` runs of consecutive stages; each run
+ *                gets one completion event and one GEMM launch over its
+ *                (contiguous) receive slots, and deliveries of slices that are
+ *                adjacent in memory are merged into one copy. groups = P-1 is
+ *                one gate per stage; 1 runs the local stage while everything
+ *                else is delivered; 0 lets the library choose from the tile
+ *                count. Values above P-1 are clamped. The result does not
+ *                depend on it.
  * All device pointers must be 16-byte aligned.
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -115,6 +126,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   uint32_t flags;
+  int32_t groups;
 } tpg_ag_args;
 
 size_t tpgemm_stage_ag_workspace_size(const tpg_ag_args* args);
@@ -138,6 +150,10 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream);
  *                partials; entry [rank] and NULL entries are ignored.
  *   d            bf16 (M, N) output; must not overlap any input.
  *   workspace    >= tpgemm_stage_rs_workspace_size() bytes (receive slots).
+ *   groups       the P-1 emitted blocks (stages 0..P-2) are computed by
+ *                `groups` launches of consecutive blocks (0: library choice;
+ *                clamped to [1, P-1]); the own block is always its own launch,
+ *                gated on every delivery. The result does not depend on it.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t M, N, K;
@@ -152,6 +168,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   uint32_t flags;
+  int32_t groups;
 } tpg_rs_args;
 
 size_t tpgemm_stage_rs_workspace_size(const tpg_rs_args* args);

@@ -12,7 +12,7 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 MODES = {"graph": 0, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED, "no_copy": tp.NO_COPY,
-         "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "blit": tp.COPY_BLIT}
+         "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "blit": tp.COPY_SDMA}
 
 
 def run_ag(case, inp, flags, rank=None):
@@ -115,3 +115,29 @@ def test_ag_empty_and_single_stage():
     inp = W.ag_inputs(case)
     d = run_ag(case, inp, 0)
     assert_parity(host_f64(d), oracle_ag(case, inp), "P=1")
+
+
+@pytest.mark.parametrize("contiguous", [False, True])
+def test_ag_stage_groups_are_bitwise_identical(contiguous):
+    """Every grouping of the remote stages (one gate per stage, one gate for
+    all, auto) and merged deliveries of adjacent slices give the same bits."""
+    case = W.AgCase("groups", M=8 * 96, N=264, K=256, P=8, rank=5, dist="u11")
+    inp = W.ag_inputs(case)
+    if contiguous:      # all peer slices back to back in one allocation
+        whole = dev(np.concatenate(inp["a_slices"], axis=0))
+        slices = [whole[s * case.m:(s + 1) * case.m] for s in range(case.P)]
+    else:
+        slices = [dev(s) for s in inp["a_slices"]]
+    b, c = dev(inp["b"]), dev(inp["c"])
+    ref = oracle_ag(case, inp)
+    outs = []
+    for groups in (0, 1, 2, 3, 7, 9):
+        for flags in (0, tp.NO_GRAPH, tp.NO_COPY, tp.COPY_SDMA):
+            say(f"ag groups: contiguous={contiguous} groups={groups} flags={flags}")
+            d = bf16_empty(case.M, case.N)
+            tp.stage_ag(slices, b, c, d, M=case.M, N=case.N, K=case.K, rank=case.rank, alpha=1.0, beta=1.0,
+                        flags=flags, groups=groups)
+            torch.cuda.synchronize()
+            outs.append(d.cpu())
+    assert_parity(host_f64(d), ref, "groups")
+    assert all(torch.equal(o, outs[0]) for o in outs)

@@ -12,7 +12,7 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 MODES = {"graph": 0, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED, "no_copy": tp.NO_COPY,
-         "serial": tp.SERIAL_STAGES, "blit": tp.COPY_BLIT | tp.NO_GRAPH}
+         "serial": tp.SERIAL_STAGES, "blit": tp.COPY_SDMA | tp.NO_GRAPH}
 
 
 def run_rs(case, inp, flags, incoming=True):
@@ -54,3 +54,33 @@ def test_rs_parity_all_modes(case):
     rms_e = np.sqrt(np.mean(e_r ** 2))
     ulp_out = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref[rows]), 1e-30))) - 7)
     assert np.all(np.abs(own - e_r) <= 0.02 * rms_e + ulp_out), "own partial mis-scaled or missing"
+
+
+@pytest.mark.parametrize("contiguous", [False, True])
+def test_rs_groups_are_bitwise_identical(contiguous):
+    case = W.RsCase("rs_groups", M=8 * 64, N=264, K=192, P=8, rank=6, std=0.5)
+    inp = W.rs_inputs(case)
+    a, b = dev(inp["a"]), dev(inp["b"])
+    if contiguous:
+        peers = [j for j in range(case.P) if j != case.rank]
+        whole = dev(np.concatenate([inp["incoming"][j] for j in peers], axis=0))
+        inc = [None] * case.P
+        for i, j in enumerate(peers):
+            inc[j] = whole[i * case.m:(i + 1) * case.m]
+    else:
+        inc = [dev(x) if x is not None else None for x in inp["incoming"]]
+    ref = oracle.gemm_rs(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P)
+    outs = []
+    for groups in (0, 1, 3, 7):
+        for flags in (0, tp.NO_GRAPH, tp.NO_COPY):
+            say(f"rs groups: contiguous={contiguous} groups={groups} flags={flags}")
+            d = bf16_empty(case.M, case.N)
+            tp.stage_rs(a, b, inc, d, M=case.M, N=case.N, K=case.K, P=case.P, rank=case.rank, flags=flags,
+                        groups=groups)
+            torch.cuda.synchronize()
+            outs.append(d.cpu())
+    got = host_f64(d)
+    for blk in range(case.P):
+        rows = slice(blk * case.m, (blk + 1) * case.m)
+        assert_parity(got[rows], ref[rows], f"block {blk}")
+    assert all(torch.equal(o, outs[0]) for o in outs)
