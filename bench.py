@@ -134,31 +134,34 @@ def setup_ag(case, extra_flags=0):
               alpha=case.alpha, beta=case.beta)
     eb = 1 if case.dtype == "e4m3" else 2
     slice_bytes = case.m * case.K * eb
-    ws = torch.empty(slice_bytes * case.P, dtype=torch.uint8, device="cuda")   # fits every mode
+    # the unstaged call needs the most workspace (all P slices, then the K-split buffers)
+    need = tp.stage_ag_workspace_size(tp.ag_args(slices, b, c, d, flags=tp.UNSTAGED, **kw))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     prepared = tp.prepare_stage_ag(slices, b, c, d, workspace=ws, flags=tp.UNSTAGED, **kw)
 
     def call(flags=0, groups=0):
         prepared._args.groups = groups
         prepared(flags=flags | extra_flags)
 
-    side = [torch.cuda.Stream() for _ in range(4)]
-    remote = case.P - 1
-    tiles = remote * case.m * case.N / (256.0 * 128.0)
-    groups = max(1, min(remote, int(tiles / 256.0 + 1.5)))     # the library's default grouping
+    side = torch.cuda.Stream()
 
     def deliveries(hip, kind):
-        """The P-1 deliveries alone, issued as the library issues them: stage
-        runs in ring order, run g on copy stream g mod 4."""
-        cur = torch.cuda.current_stream()
-        for st in side:
-            st.wait_stream(cur)
-        for g in range(groups):
-            for t in range(1 + (g * remote) // groups, 1 + ((g + 1) * remote) // groups):
+        """The P-1 deliveries alone, as the library issues them: ring order,
+        back to back on one copy stream, recorded once into a graph so that
+        replays time the copies rather than the host calls."""
+        def issue():
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            for t in range(1, case.P):
                 s = (case.rank + t) % case.P
                 hip.copy(ws.data_ptr() + (t - 1) * slice_bytes, slices[s].data_ptr(), slice_bytes, kind,
-                         side[g % 4].cuda_stream)
-        for st in side:
-            cur.wait_stream(st)
+                         side.cuda_stream)
+            cur.wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            issue()
+        return g.replay
     return inp, call, deliveries, dict(d=d)
 
 
@@ -205,8 +208,8 @@ def bench_ag(case, args, detail):
 
     if not args.quick:
         t_compute = time_steps(lambda: call(tp.NO_COPY), args.steps, args.warmup)
-        t_copy = time_steps(lambda: deliveries(hip, 3), args.steps, args.warmup)          # shader copy
-        t_copy_sdma = time_steps(lambda: deliveries(hip, 1024), args.steps, args.warmup)  # copy engines
+        t_copy = time_steps(deliveries(hip, 3), args.steps, args.warmup)          # shader copy
+        t_copy_sdma = time_steps(deliveries(hip, 1024), args.steps, args.warmup)  # copy engines
         t_unstaged = time_steps(lambda: call(tp.UNSTAGED), args.steps, args.warmup)
         t_per_stage = time_steps(lambda: call(0, case.P - 1), args.steps, args.warmup)
         t_sdma = time_steps(lambda: call(tp.COPY_SDMA), args.steps, args.warmup)
@@ -250,9 +253,11 @@ def bench_rs(case, args):
     a, b = dev(inp["a"]), dev(inp["b"])
     inc = [dev(x) if x is not None else None for x in inp["incoming"]]
     d = torch.empty((case.M, case.N), dtype=torch.int16, device="cuda")
-    ws = torch.empty(max(1, case.m * case.N * 2 * case.P), dtype=torch.uint8, device="cuda")
-    call = tp.prepare_stage_rs(a, b, inc, d, workspace=ws, M=case.M, N=case.N, K=case.K, P=case.P,
-                               rank=case.rank, b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK)
+    kw = dict(M=case.M, N=case.N, K=case.K, P=case.P, rank=case.rank,
+              b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK)
+    need = tp.stage_rs_workspace_size(tp.rs_args(a, b, inc, d, flags=tp.UNSTAGED, **kw))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    call = tp.prepare_stage_rs(a, b, inc, d, workspace=ws, **kw)
     steps = max(5, args.steps // 2)
     ms = time_steps(call, steps, 3)
     mc = time_steps(lambda: call(flags=tp.NO_COPY), steps, 3)
@@ -266,8 +271,7 @@ def bench_swiglu(case, args):
     w13, w2 = dev(inp["w13"]), dev(inp["w2"])
     h = torch.empty((case.M, case.F), dtype=torch.int16, device="cuda")
     out = torch.empty((case.M, case.D), dtype=torch.int16, device="cuda")
-    ws = torch.empty(case.S * case.D * 2 * case.P, dtype=torch.uint8, device="cuda")
-    ag = tp.prepare_stage_ag(xs, w13, None, h, workspace=ws, M=case.M, N=2 * case.F, K=case.D,
+    ag = tp.prepare_stage_ag(xs, w13, None, h, M=case.M, N=2 * case.F, K=case.D,
                              rank=case.rank, b_layout=tp.B_KN, epilogue=tp.EPI_SWIGLU, alpha=1.0, beta=0.0)
     rs = tp.prepare_stage_rs(h, w2, None, out, M=case.M, N=case.D, K=case.F, P=case.P, rank=case.rank,
                              b_layout=tp.B_KN)

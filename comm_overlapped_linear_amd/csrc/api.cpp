@@ -46,7 +46,11 @@ tpg_status fail(tpg_status st, const std::string& msg) {
   } while (0)
 
 constexpr int kStreams = 4;       // compute streams per call (index 0 = root)
-constexpr int kCopyStreams = 4;   // copy streams: deliveries spread over several copy engines
+// One copy stream: every delivery of a call goes back to back in ring
+// order. Shader copies issued on several streams at once were measured to
+// slow each other down (seven 8 MiB copies: 33 us on one stream, 85 us over
+// four), and each run's gate is then a single event on that stream.
+constexpr int kCopyStreams = 1;
 constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
@@ -405,6 +409,33 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
         return false;
     return true;
   };
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(G + 1, kStreams);
+  hipStream_t st[kStreams];
+  tpg_status stat = fork_streams(cx, L.root, ns, st);
+  if (stat != TPG_OK) return stat;
+  // Stage runs on parallel streams share the chip: each launch sizes its
+  // tiles for the CUs its run's rows would get (runs that must share a
+  // stream get proportionally more), so the launches in flight together form
+  // about one wave of tiles rather than each sizing its tiles for the chip.
+  const int stack = (G + 1 + ns - 1) / ns;                // runs per stream
+  auto budget = [&](int stages) {
+    if (ns == 1) return 0;
+    return static_cast<int>(std::min<int64_t>(tpg::device_cus(),
+                                              std::max<int64_t>(8, int64_t(tpg::device_cus()) * stages * stack / P)));
+  };
+  auto launch_rows = [&](hipStream_t cs, const void* A, int s, int run, int cus) {
+    tpg::GemmParams q = p;
+    q.a = A;
+    q.M = static_cast<int>(run * m);
+    q.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
+    q.d = static_cast<uint16_t*>(a.d) + s * m * nout;
+    q.cu_budget = cus;
+    return gemm_on(cx, L, cs, q, dtype, layout, epi);
+  };
+  // the local stage is issued before the deliveries so that nothing queues
+  // ahead of the one launch that needs no data from elsewhere
+  stat = launch_rows(st[0], a.a_slices[r], r, 1, budget(1));   // stage 0: the local slice
+  if (stat != TPG_OK) return stat;
   if (copies) {
     for (int g = 0; g < G; ++g) {
       hipStream_t cp = cx.copy[g % kCopyStreams];
@@ -418,20 +449,6 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
       HIP_TRY(hipEventRecord(cx.ev_copy[g], cp));
     }
   }
-  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(G + 1, kStreams);
-  hipStream_t st[kStreams];
-  tpg_status stat = fork_streams(cx, L.root, ns, st);
-  if (stat != TPG_OK) return stat;
-  auto launch_rows = [&](hipStream_t cs, const void* A, int s, int run) {
-    tpg::GemmParams q = p;
-    q.a = A;
-    q.M = static_cast<int>(run * m);
-    q.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
-    q.d = static_cast<uint16_t*>(a.d) + s * m * nout;
-    return gemm_on(cx, L, cs, q, dtype, layout, epi);
-  };
-  stat = launch_rows(st[0], a.a_slices[r], r, 1);        // stage 0: the local slice
-  if (stat != TPG_OK) return stat;
   for (int g = 0; g < G; ++g) {
     hipStream_t cs = st[(g + 1) % ns];
     if (copies) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
@@ -441,7 +458,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
       if (!copies)
         while (run > 1 && !adjacent(s, run)) --run;      // in place: one launch per adjacent stretch
       const void* A = copies ? static_cast<const void*>(ws + (t - 1) * slice_b) : a.a_slices[s];
-      stat = launch_rows(cs, A, s, run);
+      stat = launch_rows(cs, A, s, run, budget(t0(g + 1) - t0(g)));
       if (stat != TPG_OK) return stat;
       t += run;
     }

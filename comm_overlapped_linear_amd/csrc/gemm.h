@@ -34,18 +34,22 @@ struct GemmParams {
   // operands of consecutive batches (0 = shared); C and addends unbatched
   int batch;                   // >= 1
   int64_t a_bstride, b_bstride, d_bstride, bias_bstride;
+  // CUs the tile choice may count on (0: the whole device). Stage launches
+  // that run side by side each get their share, so that together they make
+  // one wave of tiles instead of each sizing its tiles for the whole chip.
+  int cu_budget;
 };
 
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };
 enum GemmLayout { kNK = 0, kKN = 1 };
 enum GemmEpi { kEpiAlphaBeta = 0, kEpiSwiglu = 1 };
 
+// Compute units of the current device.
+int device_cus();
+
 // Picks a tile shape for (M, N) and launches on `s`. Host-side checks of the
 // shapes and alignment are the caller's job (api.cpp validates every call).
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);
-
-// Workgroup count the launcher would use (for tests of the tile choice).
-int gemm_grid_size(int M, int N, int epi);
 
 // Row-wise LayerNorm(u) * silu(LayerNorm(g)) over z = [u | g] (each H wide).
 hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t ldh, int rows, int H,

@@ -25,6 +25,8 @@
 //    v_mfma_f32_32x32x64_f8f6f4 with both formats E4M3 (32 bytes per lane).
 //    Accumulation is fp32; D is rounded once to bf16 (nearest even).
 #include "common.h"
+#include <algorithm>
+
 #include "gemm.h"
 
 namespace tpg {
@@ -158,18 +160,18 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPt
   }
 }
 
-// Epilogue shared by both kernels, staged through LDS in FM passes of 2 x 32
+// Epilogue shared by both kernels, staged through LDS in FM passes of WM x 32
 // rows: (1) every wave writes alpha * acc (or silu(u) * v) of its rows
-// wm*WTM + i*32 + [0, 32) as fp32 into a [64][BNO + 4] LDS block; (2) all 256
+// wm*WTM + i*32 + [0, 32) as fp32 into a [WM*32][BNO + 4] LDS block; (2) all
 // threads sweep that block in 8-column vectors: + beta * C, + bias, + addends,
 // one bf16 rounding, 16-byte coalesced stores. The caller has synchronised
 // the workgroup, so the LDS is free.
-template <int BM, int BN, bool SWIGLU>
+template <int BM, int BN, int WM, int WN, bool SWIGLU>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs& bp,
-                                           const f32x16_t (&acc)[BM / 64][BN / 64], uint8_t* smem, int tm,
-                                           int tn) {
-  constexpr int WN = 2;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+                                           const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32], uint8_t* smem,
+                                           int tm, int tn) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,12 +184,11 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs&
   constexpr int BNO = SWIGLU ? BN / 2 : BN;    // output columns per tile
   constexpr int WNO = BNO / WN;                // output columns per wave
   constexpr int SLD = BNO + 4;                 // padded LDS row (floats)
-  static_assert(2 * 32 * SLD * 4 <= 2 * (BM + BN) * kRowBytes, "epilogue stage fits in LDS");
   float* stage = reinterpret_cast<float*>(smem);
   const int nout = SWIGLU ? (p.N >> 1) : p.N;
   const int tcol0 = tn * BNO;
   constexpr int VEC_PER_ROW = BNO / 8;
-  constexpr int VEC_PASS = 64 * VEC_PER_ROW;
+  constexpr int VEC_PASS = WM * 32 * VEC_PER_ROW;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     float* wst = stage + (wm * 32 + l32) * SLD + wn * WNO + half * 4;
@@ -210,7 +211,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs&
       }
     }
     __syncthreads();
-    for (int v = tid; v < VEC_PASS; v += kThreads) {
+    for (int v = tid; v < VEC_PASS; v += NT) {
       const int sr = v / VEC_PER_ROW, sc = (v % VEC_PER_ROW) * 8;
       const int row = m0 + (sr >> 5) * WTM + i * 32 + (sr & 31);
       const int col = tcol0 + sc;
@@ -239,6 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
   constexpr int B_BLK_KN = (BN / 8) * 8;             // 8x8 blocks per K-step (kn, bf16)
   constexpr int B_LD_KN = (B_BLK_KN + kThreads - 1) / kThreads;
   static_assert(!SWIGLU || (FN % 2 == 0), "swiglu pairs wave column blocks");
+  static_assert(2 * 32 * ((SWIGLU ? BN / 2 : BN) + 4) * 4 <= 2 * (BM + BN) * kRowBytes, "epilogue stage fits in LDS");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  store_tile<BM, BN, SWIGLU>(p, bp, acc, smem, tm, tn);
+  store_tile<BM, BN, 2, 2, SWIGLU>(p, bp, acc, smem, tm, tn);
 }
 
 // Workgroup -> output tile. Consecutive workgroup ids are dealt round-robin
@@ -393,8 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
 // tile order. The tile order walks groups of GM tile-rows column by column,
 // with GM chosen so that one XCD's run is a compact rectangle of tiles
 // (about sqrt(run) rows): its A rows and B columns are shared in its L2.
-template <int BM, int BN, bool SWIGLU>
-__device__ __forceinline__ void tile_of_block(const GemmParams& p, int ntm, int& tm, int& tn) {
+__device__ __forceinline__ void tile_of_block(int ntm, int& tm, int& tn) {
   const int nt = gridDim.x;
   int bid = blockIdx.x;
   if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);
@@ -476,16 +477,18 @@ struct Interleave {
   }
 };
 
-template <typename Op, int BM, int BN, int ROWB, int STAGES, bool KN, bool SWIGLU>
-__global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams p) {
+template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU>
+__global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(const GemmParams p) {
   const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
-  constexpr int WN = 2;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int NW = WM * WN;                  // waves: 4 (one per SIMD) or 8 (two per SIMD)
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
   constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;                // rows per DMA instruction (1 KB)
-  constexpr int A_INSTR = BM / (4 * RPI), B_INSTR = BN / (4 * RPI), INSTR = A_INSTR + B_INSTR;
+  constexpr int A_INSTR = BM / (NW * RPI), B_INSTR = BN / (NW * RPI), INSTR = A_INSTR + B_INSTR;
+  static_assert(A_INSTR * NW * RPI == BM && B_INSTR * NW * RPI == BN, "DMA instructions cover the tile");
+  static_assert(!SWIGLU || (FN % 2 == 0), "swiglu pairs wave column blocks");
   constexpr int KSUB = ROWB / Op::kSliceBytes; // MFMA k slices per K-step
   constexpr int UNR = (KSUB % 2 == 0) ? 1 : 2; // K-steps per loop trip: fragment set stays static
   static_assert(KSUB >= 1 && STAGES >= 2 && (STAGES - 1) * INSTR <= 63, "pipeline shape");
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
   // transposing fragment reads of four consecutive k-rows hit distinct banks
   constexpr int CPRB = BN * 2 / 16;            // chunks per k-row
   constexpr int RPIB = 64 / CPRB;              // k-rows per DMA instruction
-  static_assert(2 * 32 * ((SWIGLU ? BN / 2 : BN) + 4) * 4 <= STAGES * STAGE, "epilogue stage fits in LDS");
+  static_assert(WM * 32 * ((SWIGLU ? BN / 2 : BN) + 4) * 4 <= STAGES * STAGE, "epilogue stage fits in LDS");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -508,13 +511,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
 
   const int ntm = (p.M + BM - 1) / BM;
   int tm, tn;
-  tile_of_block<BM, BN, SWIGLU>(p, ntm, tm, tn);
+  tile_of_block(ntm, tm, tn);
   const int m0 = tm * BM;
 
   const uint8_t* A = bp.a;
   const uint8_t* Bp = bp.b;
   const int64_t lda_b = p.lda * Op::kElemBytes;
   const int64_t ldb_b = p.ldb * Op::kElemBytes;
+  const int64_t b_step = KN ? 64 * ldb_b : ROWB;   // B bytes per K-step
   const int nk = (p.K * Op::kElemBytes) / ROWB;
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem));
@@ -526,36 +530,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
   const uint8_t* bsrc[B_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
-    const int r = (j * 4 + wave) * RPI + rsub;
+    const int r = (j * NW + wave) * RPI + rsub;
     const int grow = min(m0 + r, p.M - 1);
     asrc[j] = A + grow * lda_b + swz<ROWB>(r, pc) * 16;
   }
 #pragma unroll
   for (int j = 0; j < B_INSTR; ++j) {
     if constexpr (!KN) {
-      const int r = (j * 4 + wave) * RPI + rsub;
+      const int r = (j * NW + wave) * RPI + rsub;
       int n = b_col<SWIGLU, BN>(tn, r, p.N);
       if (n < 0) n = 0;
       bsrc[j] = Bp + n * ldb_b + swz<ROWB>(r, pc) * 16;
     } else {
-      const int kr = (j * 4 + wave) * RPIB + lane / CPRB;
+      const int kr = (j * NW + wave) * RPIB + lane / CPRB;
       const int c = (lane % CPRB) ^ kn_swz(kr);
       int n = b_col<SWIGLU, BN>(tn, c * 8, p.N);
       if (n < 0) n = 0;
       bsrc[j] = Bp + kr * ldb_b + n * 2;
     }
   }
-  const int64_t b_step = KN ? 64 * ldb_b : ROWB;   // B bytes per K-step
 
   auto issue = [&](int kt, int buf) {
     const uint32_t sb = lds0 + buf * STAGE;
     const int kb = kt * ROWB;
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
-      dma16(asrc[j] + kb, __builtin_amdgcn_readfirstlane(sb + (j * 4 + wave) * 1024));
+      dma16(asrc[j] + kb, __builtin_amdgcn_readfirstlane(sb + (j * NW + wave) * 1024));
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j)
-      dma16(bsrc[j] + kt * b_step, __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * 4 + wave) * 1024));
+      dma16(bsrc[j] + kt * b_step, __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * NW + wave) * 1024));
   };
 
   f32x16_t acc[FM][FN];
@@ -641,13 +644,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmParams 
   }
   wait_vmcnt<0>();
   __syncthreads();
-  store_tile<BM, BN, SWIGLU>(p, bp, acc, smem, tm, tn);
+  store_tile<BM, BN, WM, WN, SWIGLU>(p, bp, acc, smem, tm, tn);
 }
 
-template <typename Op, int BM, int BN, int ROWB, int STAGES, bool KN, bool SWIGLU>
+template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU>
 hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   constexpr int smem = STAGES * (BM + BN) * ROWB;
-  auto kern = gemm_dma_kernel<Op, BM, BN, ROWB, STAGES, KN, SWIGLU>;
+  constexpr int nt = 64 * WM * WN;
+  auto kern = gemm_dma_kernel<Op, BM, BN, WM, WN, ROWB, STAGES, KN, SWIGLU>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -658,7 +662,7 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int grid = ((p.M + BM - 1) / BM) * nout_tiles;
   if (grid == 0 || p.batch < 1) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(kThreads), smem, s, p);
+  hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }
 
@@ -695,14 +699,15 @@ int cu_count() {
 
 // Tile choice by a small cost model: waves of workgroups over the CUs times
 // the tile's work divided by its relative MFMA efficiency (measured on
-// MI355X: a 256x128 tile runs at ~0.82 and a 128x128 tile at ~0.73 of the
-// 256x256 tile's per-CU rate, for both bf16 and fp8).
-int pick_tile(int M, int N, int epi, int batch) {
+// MI355X with 8-wave workgroups: a 128x256 tile runs at ~0.86 and a 128x128
+// tile at ~0.73 of the 256x256 tile's per-CU rate). The v1 fallback uses the
+// same index for 256x256, 256x128 and 128x128.
+int pick_tile(int M, int N, int epi, int batch, int budget) {
   const int n = epi == kEpiSwiglu ? N / 2 : N;
   const int bn_div = epi == kEpiSwiglu ? 2 : 1;
-  const int cus = cu_count();
-  const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
-  const double eff[3] = {1.0, 0.82, 0.73};
+  const int cus = budget > 0 ? std::min(budget, cu_count()) : cu_count();
+  const int bm[3] = {256, 128, 128}, bn[3] = {256, 256, 128};
+  const double eff[3] = {1.0, 0.86, 0.73};
   int best = 0;
   double best_cost = 0.0;
   for (int t = 0; t < 3; ++t) {
@@ -722,14 +727,17 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   // direct-to-LDS mainloop: 128-byte K-steps (measured faster on gfx950 than
   // 64-byte K-steps with twice the ring depth: half the barriers per byte)
   const bool dma = p.M > 0 && p.N > 0 && p.K > 0 && (p.K * Op::kElemBytes) % 128 == 0;
+  const int epi = SW ? kEpiSwiglu : kEpiAlphaBeta;
   if (dma) {
-    switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta, p.batch)) {
-      case 0: return launch_dma_tile<Op, 256, 256, 128, 2, KN, SW>(p, s);
-      case 1: return launch_dma_tile<Op, 256, 128, 128, 3, KN, SW>(p, s);
-      default: return launch_dma_tile<Op, 128, 128, 128, 4, KN, SW>(p, s);
+    switch (pick_tile(p.M, p.N, epi, p.batch, p.cu_budget)) {
+      case 0: return launch_dma_tile<Op, 256, 256, 2, 4, 128, 2, KN, SW>(p, s);
+      case 1: return launch_dma_tile<Op, 128, 256, 2, 4, 128, 3, KN, SW>(p, s);
+      default:   // the SwiGLU epilogue pairs two column blocks per wave
+        if constexpr (SW) return launch_dma_tile<Op, 128, 128, 4, 2, 128, 4, KN, SW>(p, s);
+        else return launch_dma_tile<Op, 128, 128, 2, 4, 128, 4, KN, SW>(p, s);
     }
   }
-  switch (pick_tile(p.M, p.N, SW ? kEpiSwiglu : kEpiAlphaBeta, p.batch)) {
+  switch (pick_tile(p.M, p.N, epi, p.batch, p.cu_budget)) {
     case 0: return launch_tile<Op, 256, 256, KN, SW>(p, s);
     case 1: return launch_tile<Op, 256, 128, KN, SW>(p, s);
     default: return launch_tile<Op, 128, 128, KN, SW>(p, s);
@@ -738,13 +746,7 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
-int gemm_grid_size(int M, int N, int epi) {
-  const int t = pick_tile(M, N, epi, 1);
-  const int bm = t == 2 ? 128 : 256, bn = t == 0 ? 256 : 128;
-  const int n = epi == kEpiSwiglu ? N / 2 : N;
-  const int bno = epi == kEpiSwiglu ? bn / 2 : bn;
-  return ((M + bm - 1) / bm) * ((n + bno - 1) / bno);
-}
+int device_cus() { return cu_count(); }
 
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s) {
   const bool kn = layout == kKN, sw = epi == kEpiSwiglu;

@@ -265,6 +265,12 @@ SMALL_AG = [
     AgCase("ag_bf16_p4_kn_dma_swiglu_small", M=4 * 72, N=2 * 136, K=256, P=4, b_layout="kn",
            dist="n05", beta=0.0, swiglu=True, rank=2),
     AgCase("ag_bf16_p2_kn_dma_medium", M=2 * 2000, N=4040, K=128, P=2, b_layout="kn", dist="u11"),
+    # long K over a narrow output (the shape class of the fp8 rank share)
+    AgCase("ag_e4m3_p4_longk_medium", M=4 * 250, N=520, K=4096, P=4, dtype="e4m3", dist="n05",
+           c_dist="n01", rank=1),
+    AgCase("ag_bf16_p4_longk_medium", M=4 * 512, N=1000, K=2048, P=4, dist="u11", alpha=0.5, rank=3),
+    AgCase("ag_bf16_p2_kn_longk_swiglu", M=2 * 300, N=2 * 512, K=2048, P=2, b_layout="kn", dist="n05",
+           beta=0.0, swiglu=True, rank=1),
 ]
 SMALL_RS = [
     RsCase("rs_bf16_p4_small", M=4 * 136, N=264, K=328, P=4, rank=2, std=0.5),
@@ -272,6 +278,7 @@ SMALL_RS = [
     RsCase("rs_bf16_p4_dma_small", M=4 * 136, N=264, K=448, P=4, rank=3, std=0.5),
     RsCase("rs_bf16_p4_dma_medium", M=4 * 1000, N=4040, K=128, P=4, rank=1, std=0.5),
     RsCase("rs_bf16_p4_kn_dma_small", M=4 * 100, N=264, K=192, P=4, rank=0, b_layout="kn", std=0.5),
+    RsCase("rs_bf16_p4_longk_medium", M=4 * 256, N=768, K=2048, P=4, rank=2, std=0.5),
 ]
 SMALL_FFN = [
     FfnCase("ffn_public_b4_t16_d128_k2_p2", B=4, T=16, D=128, k=2, P=2),

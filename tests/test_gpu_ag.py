@@ -71,6 +71,17 @@ def test_ag_integer_inputs_are_bit_exact():
     d8 = run_ag(case8, dict(a_slices=s8, b=b8, c=None), 0)
     ref8 = oracle.gemm_ag(s8, b8, None, 1.0, 0.0, 1, "e4m3")
     assert np.array_equal(d8.cpu().numpy(), bf16_bits_of(ref8))
+    # 64 K-steps of e4m3 (K = 4096) over every staging: still exact
+    Ks, ms, Ns = 4096, 130, 264
+    s8 = [gen.encode_e4m3(rng.integers(-4, 5, (ms, Ks)) * 0.25) for _ in range(2)]
+    b8 = gen.encode_e4m3(rng.integers(-2, 3, (Ns, Ks)) * 0.5)
+    c8 = gen.encode_bf16(rng.integers(-3, 4, (2 * ms, Ns)) * 0.5)
+    case8 = W.AgCase("int8longk", M=2 * ms, N=Ns, K=Ks, P=2, rank=1, dtype="e4m3", alpha=1.0, beta=1.0)
+    say("ag: integer exactness, K = 4096")
+    ref8 = bf16_bits_of(oracle.gemm_ag(s8, b8, c8, 1.0, 1.0, 1, "e4m3"))
+    for flags in (0, tp.UNSTAGED):
+        d8 = run_ag(case8, dict(a_slices=s8, b=b8, c=c8), flags)
+        assert np.array_equal(d8.cpu().numpy(), ref8), flags
 
 
 def test_ag_beta_zero_never_reads_c():
