@@ -160,6 +160,82 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPt
   }
 }
 
+__device__ __forceinline__ void add_vec8(const uint4 c, float scale, float* x) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] += scale * bf16_to_f32(w[e] & 0xffff);
+    x[2 * e + 1] += scale * bf16_to_f32(w[e] >> 16);
+  }
+}
+
+// The LDS sweep of one epilogue pass for a tile with no edge: every output
+// vector exists and rows are 16-byte aligned, so for each input (C, bias,
+// then each addend in order) the loads of all NV vectors of a thread are
+// issued together before any is used. The arithmetic, and so the result, is
+// that of epilogue_vec8; only the memory latency is overlapped.
+template <int NV>
+__device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchPtrs& bp, const float* stage,
+                                               int sld, int tid, int nt, int vec_per_row, int row0, int wtm,
+                                               int tcol0) {
+  float x[NV][8];
+  int row[NV], col[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int v = tid + u * nt;
+    const int sr = v / vec_per_row, sc = (v % vec_per_row) * 8;
+    row[u] = row0 + (sr >> 5) * wtm + (sr & 31);
+    col[u] = tcol0 + sc;
+    const float4 lo = *reinterpret_cast<const float4*>(stage + sr * sld + sc);
+    const float4 hi = *reinterpret_cast<const float4*>(stage + sr * sld + sc + 4);
+    x[u][0] = lo.x; x[u][1] = lo.y; x[u][2] = lo.z; x[u][3] = lo.w;
+    x[u][4] = hi.x; x[u][5] = hi.y; x[u][6] = hi.z; x[u][7] = hi.w;
+  }
+  uint4 c[NV];
+  if (p.beta != 0.0f) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) c[u] = *reinterpret_cast<const uint4*>(p.c + int64_t(row[u]) * p.ldc + col[u]);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) add_vec8(c[u], p.beta, x[u]);
+  }
+  if (bp.bias) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) c[u] = *reinterpret_cast<const uint4*>(bp.bias + col[u]);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) add_vec8(c[u], 1.0f, x[u]);
+  }
+  const int nadd = p.n_add_list + p.n_add_strided;
+  if (nadd > 0 && p.add_row1 > p.add_row0) {
+    // rows outside [add_row0, add_row1) take no addends; their (clamped,
+    // valid) loads are discarded
+    bool in[NV];
+    int64_t off[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      in[u] = row[u] >= p.add_row0 && row[u] < p.add_row1;
+      const int ra = min(max(row[u] - p.add_row0, 0), max(p.add_row1 - p.add_row0 - 1, 0));
+      off[u] = int64_t(ra) * p.ld_add + col[u];
+    }
+    for (int t = 0; t < nadd; ++t) {
+      const uint16_t* src = t < p.n_add_list ? p.add_list[t] : p.add_base + (t - p.n_add_list) * p.add_stride;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) c[u] = *reinterpret_cast<const uint4*>(src + off[u]);
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (in[u]) add_vec8(c[u], 1.0f, x[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    uint4 o;
+    o.x = f32_to_bf16(x[u][0]) | (static_cast<uint32_t>(f32_to_bf16(x[u][1])) << 16);
+    o.y = f32_to_bf16(x[u][2]) | (static_cast<uint32_t>(f32_to_bf16(x[u][3])) << 16);
+    o.z = f32_to_bf16(x[u][4]) | (static_cast<uint32_t>(f32_to_bf16(x[u][5])) << 16);
+    o.w = f32_to_bf16(x[u][6]) | (static_cast<uint32_t>(f32_to_bf16(x[u][7])) << 16);
+    *reinterpret_cast<uint4*>(bp.d + int64_t(row[u]) * p.ldd + col[u]) = o;
+  }
+}
+
 // Epilogue shared by both kernels, staged through LDS in FM passes of WM x 32
 // rows: (1) every wave writes alpha * acc (or silu(u) * v) of its rows
 // wm*WTM + i*32 + [0, 32) as fp32 into a [WM*32][BNO + 4] LDS block; (2) all
@@ -189,6 +265,9 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs&
   const int tcol0 = tn * BNO;
   constexpr int VEC_PER_ROW = BNO / 8;
   constexpr int VEC_PASS = WM * 32 * VEC_PER_ROW;
+  constexpr int NV = VEC_PASS / NT;            // 8-column vectors per thread and pass
+  static_assert(NV * NT == VEC_PASS, "each thread sweeps the same number of vectors");
+  const bool interior = p.vec_ok && m0 + BM <= p.M && tcol0 + BNO <= nout;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     float* wst = stage + (wm * 32 + l32) * SLD + wn * WNO + half * 4;
@@ -211,17 +290,26 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs&
       }
     }
     __syncthreads();
-    for (int v = tid; v < VEC_PASS; v += NT) {
-      const int sr = v / VEC_PER_ROW, sc = (v % VEC_PER_ROW) * 8;
-      const int row = m0 + (sr >> 5) * WTM + i * 32 + (sr & 31);
-      const int col = tcol0 + sc;
-      if (row >= p.M || col >= nout) continue;
-      float x[8];
-      const float4 lo = *reinterpret_cast<const float4*>(stage + sr * SLD + sc);
-      const float4 hi = *reinterpret_cast<const float4*>(stage + sr * SLD + sc + 4);
-      x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
-      x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
-      epilogue_vec8(p, bp, row, col, nout, x);
+    if (interior) {
+      // at most four vectors in flight per thread (register budget)
+      constexpr int G = NV < 4 ? NV : 4;
+      static_assert(NV % G == 0, "vector groups");
+#pragma unroll
+      for (int g0 = 0; g0 < NV; g0 += G)
+        sweep_interior<G>(p, bp, stage, SLD, tid + g0 * NT, NT, VEC_PER_ROW, m0 + i * 32, WTM, tcol0);
+    } else {
+      for (int v = tid; v < VEC_PASS; v += NT) {
+        const int sr = v / VEC_PER_ROW, sc = (v % VEC_PER_ROW) * 8;
+        const int row = m0 + (sr >> 5) * WTM + i * 32 + (sr & 31);
+        const int col = tcol0 + sc;
+        if (row >= p.M || col >= nout) continue;
+        float x[8];
+        const float4 lo = *reinterpret_cast<const float4*>(stage + sr * SLD + sc);
+        const float4 hi = *reinterpret_cast<const float4*>(stage + sr * SLD + sc + 4);
+        x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+        x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+        epilogue_vec8(p, bp, row, col, nout, x);
+      }
     }
     __syncthreads();
   }
@@ -355,9 +443,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
 
   // LDS row (within the B tile) read by this lane for wave column block j
   auto b_row = [&](int j) {
-    if (!SWIGLU) return wn * WTN + j * 32 + l32;
-    const int hj = j % (FN / 2), part = j / (FN / 2);
-    return part * (BN / 2) + wn * (WTN / 2) + hj * 32 + l32;
+    if constexpr (!SWIGLU) {
+      return wn * WTN + j * 32 + l32;
+    } else {
+      const int hj = j % (FN / 2), part = j / (FN / 2);
+      return part * (BN / 2) + wn * (WTN / 2) + hj * 32 + l32;
+    }
   };
 
   if (nk > 0) {
@@ -395,9 +486,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
 // tile order. The tile order walks groups of GM tile-rows column by column,
 // with GM chosen so that one XCD's run is a compact rectangle of tiles
 // (about sqrt(run) rows): its A rows and B columns are shared in its L2.
-__device__ __forceinline__ void tile_of_block(int ntm, int& tm, int& tn) {
-  const int nt = gridDim.x;
-  int bid = blockIdx.x;
+__device__ __forceinline__ void tile_of_block(int vt, int nt, int ntm, int& tm, int& tn) {
+  int bid = vt;
   if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);
   const int run = (nt & 7) == 0 ? (nt >> 3) : nt;
   int gm = 1;
@@ -426,8 +516,19 @@ __device__ __forceinline__ void tile_of_block(int ntm, int& tm, int& tn) {
 // gfx950 (LDS instructions do not read it), so clobbering it is safe here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+// Whether a DMA tile shape runs as persistent workgroups. The fp8 256 x 256
+// tile does not: its 256 registers per lane leave no room for the tile loop
+// (the loop would spill), so it keeps one workgroup per tile.
+template <typename Op, int BM, int BN>
+constexpr bool persistent_tiles() {
+  return !(Op::kElemBytes == 1 && BM == 256 && BN == 256);
+}
+
+// 16 bytes per lane from base + voff (a uniform 64-bit base in SGPRs and a
+// 32-bit per-lane offset) into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -510,9 +611,8 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   const int l32 = lane & 31;
 
   const int ntm = (p.M + BM - 1) / BM;
-  int tm, tn;
-  tile_of_block(ntm, tm, tn);
-  const int m0 = tm * BM;
+  const int ntn = SWIGLU ? ((p.N >> 1) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  const int ntiles = ntm * ntn;
 
   const uint8_t* A = bp.a;
   const uint8_t* Bp = bp.b;
@@ -523,16 +623,29 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem));
 
-  // this lane's source chunk in each DMA instruction; rows past the edge read
-  // a valid row instead (their products only reach outputs never stored)
+  // Persistent workgroups: each walks tiles vt = blockIdx.x + i * gridDim.x
+  // (a grid of at most one workgroup per CU), so the next tile's loads are
+  // issued right behind this tile's output stores instead of waiting for a
+  // new workgroup to be dispatched once every wave of this one has retired.
+  // With a grid that is a multiple of 8, all tiles of a workgroup come from
+  // its own XCD's run of the tile order.
   const int rsub = lane / CPR, pc = lane % CPR;
-  const uint8_t* asrc[A_INSTR];
-  const uint8_t* bsrc[B_INSTR];
+  auto run_tile = [&](int vt) {
+  int tm, tn;
+  tile_of_block(vt, ntiles, ntm, tm, tn);
+  const int m0 = tm * BM;
+  // This lane's source chunk in each DMA instruction, as a 32-bit offset
+  // from a uniform base (the tile's first A row; B itself), which the host
+  // keeps below 2^31. Rows past the edge read a valid row instead (their
+  // products only reach outputs never stored).
+  const uint8_t* a_tile = A + int64_t(m0) * lda_b;
+  uint32_t aoff[A_INSTR];
+  uint32_t boff[B_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
     const int r = (j * NW + wave) * RPI + rsub;
     const int grow = min(m0 + r, p.M - 1);
-    asrc[j] = A + grow * lda_b + swz<ROWB>(r, pc) * 16;
+    aoff[j] = static_cast<uint32_t>(int64_t(grow - m0) * lda_b + swz<ROWB>(r, pc) * 16);
   }
 #pragma unroll
   for (int j = 0; j < B_INSTR; ++j) {
@@ -540,25 +653,26 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
       const int r = (j * NW + wave) * RPI + rsub;
       int n = b_col<SWIGLU, BN>(tn, r, p.N);
       if (n < 0) n = 0;
-      bsrc[j] = Bp + n * ldb_b + swz<ROWB>(r, pc) * 16;
+      boff[j] = static_cast<uint32_t>(int64_t(n) * ldb_b + swz<ROWB>(r, pc) * 16);
     } else {
       const int kr = (j * NW + wave) * RPIB + lane / CPRB;
       const int c = (lane % CPRB) ^ kn_swz(kr);
       int n = b_col<SWIGLU, BN>(tn, c * 8, p.N);
       if (n < 0) n = 0;
-      bsrc[j] = Bp + kr * ldb_b + n * 2;
+      boff[j] = static_cast<uint32_t>(int64_t(kr) * ldb_b + n * 2);
     }
   }
 
   auto issue = [&](int kt, int buf) {
     const uint32_t sb = lds0 + buf * STAGE;
-    const int kb = kt * ROWB;
+    const uint8_t* ab = a_tile + int64_t(kt) * ROWB;
+    const uint8_t* bb = Bp + int64_t(kt) * b_step;
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
-      dma16(asrc[j] + kb, __builtin_amdgcn_readfirstlane(sb + (j * NW + wave) * 1024));
+      dma16(ab, aoff[j], __builtin_amdgcn_readfirstlane(sb + (j * NW + wave) * 1024));
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j)
-      dma16(bsrc[j] + kt * b_step, __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * NW + wave) * 1024));
+      dma16(bb, boff[j], __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * NW + wave) * 1024));
   };
 
   f32x16_t acc[FM][FN];
@@ -570,9 +684,12 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   auto b_row = [&](int j) {
-    if (!SWIGLU) return wn * WTN + j * 32 + l32;
-    const int hj = j % (FN / 2), part = j / (FN / 2);
-    return part * (BN / 2) + wn * (WTN / 2) + hj * 32 + l32;
+    if constexpr (!SWIGLU) {
+      return wn * WTN + j * 32 + l32;
+    } else {
+      const int hj = j % (FN / 2), part = j / (FN / 2);
+      return part * (BN / 2) + wn * (WTN / 2) + hj * 32 + l32;
+    }
   };
 
   // Software pipeline. Fragments are double-buffered: the LDS reads of
@@ -644,8 +761,16 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   }
   wait_vmcnt<0>();
   __syncthreads();
-  store_tile<BM, BN, WM, WN, SWIGLU>(p, bp, acc, smem, tm, tn);
+  store_tile<BM, BN, WM, WN, SWIGLU>(p, bp, acc, smem, tm, tn);   // ends with a barrier: LDS free
+  };
+  if constexpr (persistent_tiles<Op, BM, BN>()) {
+    for (int vt = blockIdx.x; vt < ntiles; vt += gridDim.x) run_tile(vt);
+  } else {
+    run_tile(blockIdx.x);
+  }
 }
+
+int cu_count();
 
 template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU>
 hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
@@ -660,8 +785,11 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
     attr_set = true;
   }
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-  const int grid = ((p.M + BM - 1) / BM) * nout_tiles;
-  if (grid == 0 || p.batch < 1) return hipSuccess;
+  const int tiles = ((p.M + BM - 1) / BM) * nout_tiles;
+  if (tiles == 0 || p.batch < 1) return hipSuccess;
+  // one persistent workgroup per CU of the budget (all tiles when batched)
+  const int cap = p.cu_budget > 0 ? std::min(p.cu_budget, cu_count()) : cu_count();
+  const int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN>()) ? std::min(tiles, cap) : tiles;
   hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }
@@ -726,7 +854,12 @@ template <typename Op, bool KN, bool SW>
 hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   // direct-to-LDS mainloop: 128-byte K-steps (measured faster on gfx950 than
   // 64-byte K-steps with twice the ring depth: half the barriers per byte)
-  const bool dma = p.M > 0 && p.N > 0 && p.K > 0 && (p.K * Op::kElemBytes) % 128 == 0;
+  // the DMA path addresses a tile's A rows and all of B with 31-bit offsets
+  const int64_t eb = Op::kElemBytes;
+  const bool offsets_fit = int64_t(256) * p.lda * eb < (int64_t(1) << 31) &&
+                           (KN ? int64_t(64) * p.ldb * eb + int64_t(p.N) * 2
+                               : int64_t(p.N) * p.ldb * eb) < (int64_t(1) << 31);
+  const bool dma = p.M > 0 && p.N > 0 && p.K > 0 && (p.K * Op::kElemBytes) % 128 == 0 && offsets_fit;
   const int epi = SW ? kEpiSwiglu : kEpiAlphaBeta;
   if (dma) {
     switch (pick_tile(p.M, p.N, epi, p.batch, p.cu_budget)) {
