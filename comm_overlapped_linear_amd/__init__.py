@@ -22,7 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, E4M3 = 0, 1
 B_NK, B_KN = 0, 1
 EPI_ALPHA_BETA, EPI_SWIGLU = 0, 1
-UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE = 1, 2, 4, 8, 16, 32
+UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE, FORCE_GRAPH = 1, 2, 4, 8, 16, 32, 64
 
 _STATUS = {OK: "OK", ERR_INVALID: "INVALID", ERR_UNSUPPORTED: "UNSUPPORTED",
            ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP"}

@@ -54,7 +54,10 @@ constexpr int kCopyStreams = 1;
 constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
-                                 TPG_SERIAL_STAGES | TPG_PROFILE;
+                                 TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH;
+// Staged calls below this many flops run on one stream: their GEMMs take
+// well under the few microseconds each cross-stream event and launch costs.
+constexpr double kLatencyBoundFlop = 1e9;
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -224,9 +227,11 @@ hipMemcpyKind copy_kind(uint32_t flags) {
 
 // Records `enqueue` into a graph once per key and replays it on `user`, or
 // runs it eagerly.
-tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t user,
+// `fans_out`: the call's launches use more than one stream (issue policy in
+// the header: such calls are issued eagerly unless TPG_FORCE_GRAPH is set).
+tpg_status run_call(Ctx& cx, uint32_t flags, bool fans_out, const std::string& key, hipStream_t user,
                     const std::function<tpg_status(const Launch&)>& enqueue) {
-  const bool eager = (flags & (TPG_NO_GRAPH | TPG_PROFILE)) != 0;
+  const bool eager = (flags & (TPG_NO_GRAPH | TPG_PROFILE)) != 0 || (fans_out && !(flags & TPG_FORCE_GRAPH));
   if (eager) return enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
   auto it = cx.graphs.find(key);
   if (it == cx.graphs.end()) {
@@ -260,16 +265,13 @@ void put(std::ostringstream& os, const T& v) {
 }
 
 // ---------------------------------------------------------------- all-gather
-// Default number of gated stage runs: one more than the number of full
-// waves of 256x128 tiles the remote stages make on 256 CUs (small stages are
-// merged, stages that fill the chip on their own keep one gate each). On
-// MI355X the fixed cost of a delivery (~5-10 us per copy) and of a launch
-// outweighs the finer pipeline when a stage is well under one wave.
-int auto_groups(int64_t rows_per_stage, int64_t n, int remote) {
-  const double tiles = double(remote) * double(rows_per_stage) * double(n) / (256.0 * 128.0);
-  const int g = static_cast<int>(tiles / 256.0 + 1.5);
-  return std::max(1, std::min(remote, g));
-}
+// Default stage runs of the all-gather: one gate for all P-1 remote stages.
+// On one GPU the deliveries (shader copies, ~33 us for 7 x 8 MiB) are short
+// next to the remote GEMM work, the local stage covers them, and one
+// full-chip launch over the delivered slices makes the fewest partial tile
+// waves; more runs were measured slower for every workload here (each run's
+// launch is smaller and runs sharing a stream serialise).
+int auto_groups(int remote) { return remote > 0 ? 1 : 0; }
 
 tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
@@ -375,15 +377,12 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   const int layout = a.b_layout == TPG_B_KN ? tpg::kKN : tpg::kNK;
   const int epi = sw ? tpg::kEpiSwiglu : tpg::kEpiAlphaBeta;
 
-  if (copies) {
-    tpg_status fs = fork_copies(cx, L.root);
-    if (fs != TPG_OK) return fs;
-  }
-
   if (a.flags & TPG_UNSTAGED) {
     // single stage: gather every slice (rank order), then one GEMM over all M rows
     const void* A = a.M > 0 ? a.a_slices[0] : nullptr;
     if (copies) {
+      tpg_status fs = fork_copies(cx, L.root);
+      if (fs != TPG_OK) return fs;
       for (int s = 0; s < P; ++s)
         HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, cx.copy[s % kCopyStreams]));
       tpg_status ws_ = wait_copies(cx, L.root);
@@ -401,7 +400,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   // P-1 remote stages are cut into G runs; run g waits for one event and is
   // one GEMM launch per stretch of D rows that does not wrap past slice P-1.
   const int remote = P - 1;
-  const int G = remote == 0 ? 0 : (a.groups > 0 ? std::min(a.groups, remote) : auto_groups(m, a.N, remote));
+  const int G = remote == 0 ? 0 : (a.groups > 0 ? std::min(a.groups, remote) : auto_groups(remote));
   auto t0 = [&](int g) { return 1 + (g * remote) / G; };
   auto adjacent = [&](int s, int run) {   // a_slices[s .. s+run) back to back in memory
     for (int i = 1; i < run; ++i)
@@ -432,26 +431,32 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     q.cu_budget = cus;
     return gemm_on(cx, L, cs, q, dtype, layout, epi);
   };
-  // the local stage is issued before the deliveries so that nothing queues
-  // ahead of the one launch that needs no data from elsewhere
-  stat = launch_rows(st[0], a.a_slices[r], r, 1, budget(1));   // stage 0: the local slice
+  // Stream roles. The deliveries run back to back on the root and the last
+  // run follows them there in stream order, so the call's critical path (last
+  // delivery, then the last run) waits on no other queue. The local stage,
+  // which needs no delivery, and the earlier runs go to the other streams,
+  // each earlier run gated by one event recorded on the root after its
+  // slices. (With the local stage on the root and the deliveries on a side
+  // stream, the first delivery started ~17 us late and the call took ~127 us.)
+  auto side = [&](int i) { return ns > 1 ? st[1 + i % (ns - 1)] : L.root; };
+  stat = launch_rows(side(0), a.a_slices[r], r, 1, budget(1));   // stage 0: the local slice
   if (stat != TPG_OK) return stat;
-  if (copies) {
-    for (int g = 0; g < G; ++g) {
-      hipStream_t cp = cx.copy[g % kCopyStreams];
+  for (int g = 0; g < G; ++g) {
+    if (copies) {
       for (int t = t0(g); t < t0(g + 1);) {
         const int s = (r + t) % P;
         int run = 1;
         while (t + run < t0(g + 1) && s + run < P && adjacent(s, run + 1)) ++run;
-        HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], run * slice_b, kind, cp));
+        HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], run * slice_b, kind, L.root));
         t += run;
       }
-      HIP_TRY(hipEventRecord(cx.ev_copy[g], cp));
     }
-  }
-  for (int g = 0; g < G; ++g) {
-    hipStream_t cs = st[(g + 1) % ns];
-    if (copies) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
+    const bool last = g == G - 1;
+    hipStream_t cs = last ? L.root : side(g + 1);
+    if (!last && copies && ns > 1) {
+      HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
+      HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
+    }
     for (int t = t0(g); t < t0(g + 1);) {
       const int s = (r + t) % P;
       int run = std::min(t0(g + 1) - t, P - s);
@@ -463,7 +468,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
       t += run;
     }
   }
-  return join_streams(cx, L.root, ns, st, copies);
+  return join_streams(cx, L.root, ns, st, false);
 }
 
 std::string ag_key(const tpg_ag_args& a) {
@@ -629,6 +634,10 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, ns, st);
   if (stat != TPG_OK) return stat;
+  // The own block waits for every delivery while the emitted blocks run;
+  // it sizes its tiles for the CUs the emitted launches leave idle in their
+  // last round of tiles, so that it fills that round instead of adding one.
+  int64_t emitted_tiles = 0;
   auto launch_blocks = [&](hipStream_t cs, int blk, int run, bool own) {
     tpg::GemmParams q = p;
     q.M = static_cast<int>(run * m);
@@ -638,6 +647,11 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
       q.add_row0 = 0;
       q.add_row1 = static_cast<int>(m);
       set_adds(q);
+      const int cus = tpg::device_cus();
+      const int rem = static_cast<int>(emitted_tiles % cus);
+      if (ns > 1 && rem > 0) q.cu_budget = cus - rem;
+    } else {
+      emitted_tiles += tpg::gemm_tiles(q.M, q.N, dtype, tpg::kEpiAlphaBeta, 1, 0);
     }
     return gemm_on(cx, L, cs, q, dtype, layout, tpg::kEpiAlphaBeta);
   };
@@ -837,8 +851,11 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
     Ctx* cx = nullptr;
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
-    const tpg_ag_args a = *args;
-    return run_call(*cx, a.flags, ag_key(a), static_cast<hipStream_t>(stream),
+    tpg_ag_args a = *args;
+    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+      a.flags |= TPG_SERIAL_STAGES;
+    const bool fans_out = !(a.flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES)) && a.P > 1;
+    return run_call(*cx, a.flags, fans_out, ag_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ag(*cx, a, L); });
   });
 }
@@ -854,8 +871,11 @@ tpg_status tpgemm_stage_rs(const tpg_rs_args* args, void* stream) {
     Ctx* cx = nullptr;
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
-    const tpg_rs_args a = *args;
-    return run_call(*cx, a.flags, rs_key(a), static_cast<hipStream_t>(stream),
+    tpg_rs_args a = *args;
+    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+      a.flags |= TPG_SERIAL_STAGES;
+    const bool fans_out = !(a.flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES)) && a.P > 1;
+    return run_call(*cx, a.flags, fans_out, rs_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_rs(*cx, a, L); });
   });
 }
@@ -872,7 +892,8 @@ tpg_status ffn_slot_forward(const tpg_ffn_args* args, void* stream) {
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
     const tpg_ffn_args a = *args;
-    return run_call(*cx, a.flags, ffn_key(a), static_cast<hipStream_t>(stream),
+    const bool fans_out = !(a.flags & TPG_SERIAL_STAGES) && a.L > 1;
+    return run_call(*cx, a.flags, fans_out, ffn_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ffn(*cx, a, L); });
   });
 }

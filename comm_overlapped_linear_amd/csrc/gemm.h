@@ -47,6 +47,9 @@ enum GemmEpi { kEpiAlphaBeta = 0, kEpiSwiglu = 1 };
 // Compute units of the current device.
 int device_cus();
 
+// Output tiles the DMA launcher would make for this shape and CU budget.
+int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget);
+
 // Picks a tile shape for (M, N) and launches on `s`. Host-side checks of the
 // shapes and alignment are the caller's job (api.cpp validates every call).
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);

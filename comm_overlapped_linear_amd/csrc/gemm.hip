@@ -787,9 +787,10 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int tiles = ((p.M + BM - 1) / BM) * nout_tiles;
   if (tiles == 0 || p.batch < 1) return hipSuccess;
-  // one persistent workgroup per CU of the budget (all tiles when batched)
-  const int cap = p.cu_budget > 0 ? std::min(p.cu_budget, cu_count()) : cu_count();
-  const int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN>()) ? std::min(tiles, cap) : tiles;
+  // at most one persistent workgroup per CU (all tiles when batched). The
+  // CU budget shaped the tiles only: once launches beside this one finish,
+  // their CUs are this launch's to use.
+  const int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN>()) ? std::min(tiles, cu_count()) : tiles;
   hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }
@@ -880,6 +881,14 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 int device_cus() { return cu_count(); }
+
+int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget) {
+  const int t = pick_tile(M, N, epi, batch, cu_budget);
+  const int bm = t == 0 ? 256 : 128, bn = t == 2 ? 128 : 256;
+  const int n = epi == kEpiSwiglu ? N / 2 : N, bno = epi == kEpiSwiglu ? bn / 2 : bn;
+  (void)dtype;
+  return batch * ((M + bm - 1) / bm) * ((n + bno - 1) / bno);
+}
 
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s) {
   const bool kn = layout == kKN, sw = epi == kEpiSwiglu;

@@ -28,13 +28,23 @@
  *   - Arguments are validated before anything is enqueued; a failing call
  *     enqueues nothing and returns a non-zero status, with a message from
  *     tpg_last_error(). There is no fallback path.
- *   - Graph cache: unless TPG_NO_GRAPH is set, the first call with a given
- *     (entry point, shapes, pointers, scalars, flags, stream-independent
- *     plan) records the call into a hipGraph that later identical calls
- *     replay. A changed pointer makes a new graph, never a stale replay.
- *     Freeing a buffer a cached graph refers to is safe as long as that
- *     exact argument set is not called again; tpg_release_caches() drops
- *     all graphs.
+ *   - Issue policy. A call whose launches form one chain on one stream
+ *     (TPG_UNSTAGED, TPG_SERIAL_STAGES, P = 1) is recorded into a hipGraph
+ *     on first use and replayed. A call that fans out over several streams
+ *     (the staged AG, RS and FFN pipelines) is issued eagerly: on MI355X
+ *     (ROCm 7) replaying such a graph was measured slower than issuing it
+ *     (e.g. the e4m3 AG share 128 vs 103 us, the bf16 RS share 528 vs
+ *     475 us); TPG_FORCE_GRAPH replays a graph anyway. A staged AG or RS
+ *     call of under 1 GFLOP that leaves the grouping to the library
+ *     (groups = 0) is latency-bound and runs as if TPG_SERIAL_STAGES were
+ *     set (one stream, graph replay): the same stages in the same order,
+ *     without the cross-stream events.
+ *     TPG_NO_GRAPH and TPG_PROFILE always issue eagerly.
+ *   - Graph cache: a recorded graph is keyed by (entry point, shapes,
+ *     pointers, scalars, flags). A changed pointer makes a new graph, never
+ *     a stale replay. Freeing a buffer a cached graph refers to is safe as
+ *     long as that exact argument set is not called again;
+ *     tpg_release_caches() drops all graphs.
  *   - Calls on one device serialise on an internal lock; two calls whose
  *     workspaces overlap must not be in flight at once on different streams.
  */
@@ -76,7 +86,8 @@ enum {
   TPG_NO_GRAPH = 4u,        /* enqueue eagerly instead of capturing / replaying a hipGraph */
   TPG_COPY_SDMA = 8u,       /* deliver with the SDMA copy engines (no CUs) instead of the shader copy */
   TPG_SERIAL_STAGES = 16u,  /* run all stage GEMMs on one compute stream (no inter-stage concurrency) */
-  TPG_PROFILE = 32u         /* eager only: time every GEMM launch with HIP events (tpg_profile_read) */
+  TPG_PROFILE = 32u,        /* eager only: time every GEMM launch with HIP events (tpg_profile_read) */
+  TPG_FORCE_GRAPH = 64u     /* replay a hipGraph even for a call that fans out over several streams */
 };
 
 /* ------------------------------------------------------------------------

@@ -11,8 +11,8 @@ from tests.parity import assert_parity
 
 pytestmark = pytest.mark.gpu
 
-MODES = {"graph": 0, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED, "no_copy": tp.NO_COPY,
-         "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "blit": tp.COPY_SDMA}
+MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
+         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "blit": tp.COPY_SDMA}
 
 
 def run_ag(case, inp, flags, rank=None):
@@ -48,7 +48,7 @@ def test_ag_parity_all_modes(case):
         outs[name] = d.cpu()
     # staging only partitions rows: every mode is bitwise identical
     for name in MODES:
-        assert torch.equal(outs[name], outs["graph"]), name
+        assert torch.equal(outs[name], outs["default"]), name
 
 
 def test_ag_integer_inputs_are_bit_exact():
@@ -143,7 +143,7 @@ def test_ag_stage_groups_are_bitwise_identical(contiguous):
     ref = oracle_ag(case, inp)
     outs = []
     for groups in (0, 1, 2, 3, 7, 9):
-        for flags in (0, tp.NO_GRAPH, tp.NO_COPY, tp.COPY_SDMA):
+        for flags in (0, tp.FORCE_GRAPH, tp.NO_GRAPH, tp.NO_COPY, tp.COPY_SDMA):
             say(f"ag groups: contiguous={contiguous} groups={groups} flags={flags}")
             d = bf16_empty(case.M, case.N)
             tp.stage_ag(slices, b, c, d, M=case.M, N=case.N, K=case.K, rank=case.rank, alpha=1.0, beta=1.0,

@@ -30,7 +30,7 @@ def test_ffn_parity(case):
     inp = W.ffn_inputs(case)
     ref = oracle.ffn_slot_forward(inp, case.eps)
     outs = []
-    for name, flags in {"graph": 0, "eager": tp.NO_GRAPH, "serial": tp.SERIAL_STAGES}.items():
+    for name, flags in {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "serial": tp.SERIAL_STAGES}.items():
         say(f"ffn: {case.name} mode={name}")
         got = run_ffn(case, inp, flags)
         assert_parity(got, ref, f"{case.name}/{name}")

@@ -11,8 +11,8 @@ from tests.parity import assert_parity
 
 pytestmark = pytest.mark.gpu
 
-MODES = {"graph": 0, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED, "no_copy": tp.NO_COPY,
-         "serial": tp.SERIAL_STAGES, "blit": tp.COPY_SDMA | tp.NO_GRAPH}
+MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
+         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "blit": tp.COPY_SDMA | tp.NO_GRAPH}
 
 
 def run_rs(case, inp, flags, incoming=True):
@@ -39,7 +39,7 @@ def test_rs_parity_all_modes(case):
             assert_parity(got[rows], ref[rows], f"{case.name}/{name}/block{blk}")
         outs[name] = got
     for name in MODES:
-        assert np.array_equal(outs[name], outs["graph"]), name
+        assert np.array_equal(outs[name], outs["default"]), name
     # the own block without incoming partials is the plain partial product
     say(f"rs: {case.name} own block without incoming")
     got0 = run_rs(case, inp, 0, incoming=False)
@@ -49,7 +49,7 @@ def test_rs_parity_all_modes(case):
     # at a tolerance scaled to E_r itself (the incoming sum dominates out_r)
     rows = slice(r * m, (r + 1) * m)
     inc_sum = sum(oracle.decode_bf16(x) for x in inp["incoming"] if x is not None)
-    own = outs["graph"][rows] - inc_sum
+    own = outs["default"][rows] - inc_sum
     e_r = ref0[rows]
     rms_e = np.sqrt(np.mean(e_r ** 2))
     ulp_out = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref[rows]), 1e-30))) - 7)
@@ -72,7 +72,7 @@ def test_rs_groups_are_bitwise_identical(contiguous):
     ref = oracle.gemm_rs(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P)
     outs = []
     for groups in (0, 1, 3, 7):
-        for flags in (0, tp.NO_GRAPH, tp.NO_COPY):
+        for flags in (0, tp.FORCE_GRAPH, tp.NO_GRAPH, tp.NO_COPY):
             say(f"rs groups: contiguous={contiguous} groups={groups} flags={flags}")
             d = bf16_empty(case.M, case.N)
             tp.stage_rs(a, b, inc, d, M=case.M, N=case.N, K=case.K, P=case.P, rank=case.rank, flags=flags,

@@ -32,7 +32,7 @@ def test_swiglu_block_parity(case):
     h_ref = oracle.swiglu_hidden(inp["x_shards"], inp["w13"])
     out_ref = oracle.swiglu_block(inp["x_shards"], inp["w13"], inp["w2"])
     res = []
-    for name, flags in {"graph": 0, "unstaged": tp.UNSTAGED, "eager": tp.NO_GRAPH}.items():
+    for name, flags in {"default": 0, "graph": tp.FORCE_GRAPH, "unstaged": tp.UNSTAGED, "eager": tp.NO_GRAPH}.items():
         say(f"swiglu: {case.name} mode={name}")
         h, out = run_block(case, inp, flags)
         assert_parity(h, h_ref, f"h/{name}")
