@@ -6,17 +6,18 @@
 // communication code of their own (Introduction; Approach, observations 2 and
 // 4; Background, Figure 4: local shard first, then rotate). On one MI355X the
 // peers' shards are buffers in the same HBM: each delivery is one
-// hipMemcpyAsync on a library-owned copy stream (the shader copy, or the SDMA
-// copy engines with TPG_COPY_SDMA), followed by an event that gates exactly
-// the stage run that reads it. Stage
-// kernels fan out over up to four compute streams so that several small
-// stages can share the 256 CUs; everything forks from and joins back into the
-// caller's stream. Unless TPG_NO_GRAPH, one call is recorded once into a
-// hipGraph (launch gaps between stages are overhead, Approach observation 4)
-// and replayed.
+// hipMemcpyAsync (the shader copy, or the SDMA copy engines with
+// TPG_COPY_SDMA), and one event after a run's deliveries gates exactly the
+// stage run that reads them. Stage launches fan out over up to four streams
+// forked from and joined back into the caller's stream; calls that fan out
+// are issued eagerly, one-stream calls are recorded once into a hipGraph and
+// replayed (launch gaps between stages are overhead, Approach observation 4;
+// the issue policy is measured and stated in tpgemm.h).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
+#include <thread>
 #include <cstdio>
 #include <cstring>
 #include <functional>
@@ -54,7 +55,8 @@ constexpr int kCopyStreams = 1;
 constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
-                                 TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH;
+                                 TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH |
+                                 TPG_DEBUG_HOLD_DELIVERIES;
 // Staged calls below this many flops run on one stream: their GEMMs take
 // well under the few microseconds each cross-stream event and launch costs.
 constexpr double kLatencyBoundFlop = 1e9;
@@ -221,6 +223,17 @@ tpg_status fork_copies(Ctx& cx, hipStream_t root) {
   return TPG_OK;
 }
 
+// TPG_DEBUG_HOLD_DELIVERIES: the deliveries queue behind a host callback
+// that sleeps, so every gated stage run is issued long before its slices
+// exist (an ordering test forced from the host; the results must not change).
+constexpr int kHoldMs = 20;
+void hold_cb(void*) { std::this_thread::sleep_for(std::chrono::milliseconds(kHoldMs)); }
+
+tpg_status hold_deliveries(uint32_t flags, hipStream_t s) {
+  if (flags & TPG_DEBUG_HOLD_DELIVERIES) HIP_TRY(hipLaunchHostFunc(s, hold_cb, nullptr));
+  return TPG_OK;
+}
+
 hipMemcpyKind copy_kind(uint32_t flags) {
   return (flags & TPG_COPY_SDMA) ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
 }
@@ -231,7 +244,8 @@ hipMemcpyKind copy_kind(uint32_t flags) {
 // the header: such calls are issued eagerly unless TPG_FORCE_GRAPH is set).
 tpg_status run_call(Ctx& cx, uint32_t flags, bool fans_out, const std::string& key, hipStream_t user,
                     const std::function<tpg_status(const Launch&)>& enqueue) {
-  const bool eager = (flags & (TPG_NO_GRAPH | TPG_PROFILE)) != 0 || (fans_out && !(flags & TPG_FORCE_GRAPH));
+  const bool eager = (flags & (TPG_NO_GRAPH | TPG_PROFILE | TPG_DEBUG_HOLD_DELIVERIES)) != 0 ||
+                     (fans_out && !(flags & TPG_FORCE_GRAPH));
   if (eager) return enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
   auto it = cx.graphs.find(key);
   if (it == cx.graphs.end()) {
@@ -383,6 +397,8 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     if (copies) {
       tpg_status fs = fork_copies(cx, L.root);
       if (fs != TPG_OK) return fs;
+      fs = hold_deliveries(a.flags, cx.copy[0]);
+      if (fs != TPG_OK) return fs;
       for (int s = 0; s < P; ++s)
         HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, cx.copy[s % kCopyStreams]));
       tpg_status ws_ = wait_copies(cx, L.root);
@@ -441,6 +457,10 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   auto side = [&](int i) { return ns > 1 ? st[1 + i % (ns - 1)] : L.root; };
   stat = launch_rows(side(0), a.a_slices[r], r, 1, budget(1));   // stage 0: the local slice
   if (stat != TPG_OK) return stat;
+  if (copies) {
+    stat = hold_deliveries(a.flags, L.root);
+    if (stat != TPG_OK) return stat;
+  }
   for (int g = 0; g < G; ++g) {
     if (copies) {
       for (int t = t0(g); t < t0(g + 1);) {
@@ -588,6 +608,8 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   const int ncs = std::min<int>(kCopyStreams, static_cast<int>(peers.size()));
   if (copies) {
     tpg_status fs = fork_copies(cx, L.root);
+    if (fs != TPG_OK) return fs;
+    fs = hold_deliveries(a.flags, cx.copy[0]);
     if (fs != TPG_OK) return fs;
     // partials that sit back to back in memory (and in the slots) move as one copy
     for (size_t i = 0; i < peers.size();) {

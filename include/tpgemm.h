@@ -39,7 +39,8 @@
  *     (groups = 0) is latency-bound and runs as if TPG_SERIAL_STAGES were
  *     set (one stream, graph replay): the same stages in the same order,
  *     without the cross-stream events.
- *     TPG_NO_GRAPH and TPG_PROFILE always issue eagerly.
+ *     TPG_NO_GRAPH, TPG_PROFILE and TPG_DEBUG_HOLD_DELIVERIES always issue
+ *     eagerly.
  *   - Graph cache: a recorded graph is keyed by (entry point, shapes,
  *     pointers, scalars, flags). A changed pointer makes a new graph, never
  *     a stale replay. Freeing a buffer a cached graph refers to is safe as
@@ -87,7 +88,9 @@ enum {
   TPG_COPY_SDMA = 8u,       /* deliver with the SDMA copy engines (no CUs) instead of the shader copy */
   TPG_SERIAL_STAGES = 16u,  /* run all stage GEMMs on one compute stream (no inter-stage concurrency) */
   TPG_PROFILE = 32u,        /* eager only: time every GEMM launch with HIP events (tpg_profile_read) */
-  TPG_FORCE_GRAPH = 64u     /* replay a hipGraph even for a call that fans out over several streams */
+  TPG_FORCE_GRAPH = 64u,    /* replay a hipGraph even for a call that fans out over several streams */
+  TPG_DEBUG_HOLD_DELIVERIES = 128u /* testing: issue eagerly, with the deliveries queued behind a 20 ms
+                                      host callback; every gated stage must still see its data */
 };
 
 /* ------------------------------------------------------------------------
