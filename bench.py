@@ -64,9 +64,15 @@ class Hip:
 
 
 def time_steps(fn, steps, warmup):
+    """ms per call over `steps` calls, after `warmup` calls and at least
+    WARM_MS of calls (the clocks settle over the first few ms of load)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        fn()
+        torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(steps):
@@ -74,6 +80,9 @@ def time_steps(fn, steps, warmup):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / steps
+
+
+WARM_MS = 30.0
 
 
 def time_flushed(fn, steps, warmup, scratch):
@@ -275,7 +284,9 @@ def bench_rs(case, args):
     steps = max(5, args.steps // 2)
     ms = time_steps(call, steps, 3)
     mc = time_steps(lambda: call(flags=tp.NO_COPY), steps, 3)
+    msh = time_steps(lambda: call(flags=tp.COPY_SHADER), steps, 3)
     return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1),
+                us_shader_copy=round(msh * 1e3, 1),
                 us_compute_only=round(mc * 1e3, 1))
 
 

@@ -23,7 +23,7 @@ BF16, E4M3 = 0, 1
 B_NK, B_KN = 0, 1
 EPI_ALPHA_BETA, EPI_SWIGLU = 0, 1
 UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE, FORCE_GRAPH = 1, 2, 4, 8, 16, 32, 64
-DEBUG_HOLD_DELIVERIES = 128
+DEBUG_HOLD_DELIVERIES, COPY_SHADER = 128, 256
 
 _STATUS = {OK: "OK", ERR_INVALID: "INVALID", ERR_UNSUPPORTED: "UNSUPPORTED",
            ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP"}

@@ -9,10 +9,10 @@
 // hipMemcpyAsync (the shader copy, or the SDMA copy engines with
 // TPG_COPY_SDMA), and one event after a run's deliveries gates exactly the
 // stage run that reads them. Stage launches fan out over up to four streams
-// forked from and joined back into the caller's stream; calls that fan out
-// are issued eagerly, one-stream calls are recorded once into a hipGraph and
-// replayed (launch gaps between stages are overhead, Approach observation 4;
-// the issue policy is measured and stated in tpgemm.h).
+// forked from and joined back into the caller's stream. Calls are issued
+// eagerly; with TPG_FORCE_GRAPH one call is recorded once into a hipGraph and
+// replayed on request (launch gaps between stages are overhead, Approach
+// observation 4; on MI355X eager issue measured faster, see tpgemm.h).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -47,18 +47,14 @@ tpg_status fail(tpg_status st, const std::string& msg) {
   } while (0)
 
 constexpr int kStreams = 4;       // compute streams per call (index 0 = root)
-// One copy stream: every delivery of a call goes back to back in ring
-// order. Shader copies issued on several streams at once were measured to
-// slow each other down (seven 8 MiB copies: 33 us on one stream, 85 us over
-// four), and each run's gate is then a single event on that stream.
-constexpr int kCopyStreams = 1;
 constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
                                  TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH |
-                                 TPG_DEBUG_HOLD_DELIVERIES;
+                                 TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER;
 // Staged calls below this many flops run on one stream: their GEMMs take
-// well under the few microseconds each cross-stream event and launch costs.
+// well under the few microseconds each cross-stream event costs (the P = 2
+// bf16 workload: 20 us on one stream, 40-45 us on two).
 constexpr double kLatencyBoundFlop = 1e9;
 
 struct ProfRec {
@@ -68,13 +64,11 @@ struct ProfRec {
 
 struct Ctx {
   int device = -1;
-  hipStream_t copy[kCopyStreams] = {};
   hipStream_t comp[kStreams] = {};   // comp[0] unused: the root stream takes its place
   hipStream_t capture = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_copy_done = nullptr;
+  hipEvent_t ev_fork = nullptr;
   hipEvent_t ev_copy[kMaxP] = {};
   hipEvent_t ev_join[kStreams] = {};
-  hipEvent_t ev_copy_join[kCopyStreams] = {};
   std::unordered_map<std::string, hipGraphExec_t> graphs;
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> prof_pool;
@@ -86,13 +80,9 @@ std::unordered_map<int, Ctx*> g_ctx;
 tpg_status make_ctx(int dev, Ctx** out) {
   Ctx* c = new Ctx();
   c->device = dev;
-  for (int i = 0; i < kCopyStreams; ++i) HIP_TRY(hipStreamCreateWithFlags(&c->copy[i], hipStreamNonBlocking));
-  for (int i = 0; i < kCopyStreams; ++i)
-    HIP_TRY(hipEventCreateWithFlags(&c->ev_copy_join[i], hipEventDisableTiming));
   for (int i = 1; i < kStreams; ++i) HIP_TRY(hipStreamCreateWithFlags(&c->comp[i], hipStreamNonBlocking));
   HIP_TRY(hipStreamCreateWithFlags(&c->capture, hipStreamNonBlocking));
   HIP_TRY(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming));
-  HIP_TRY(hipEventCreateWithFlags(&c->ev_copy_done, hipEventDisableTiming));
   for (int i = 0; i < kMaxP; ++i) HIP_TRY(hipEventCreateWithFlags(&c->ev_copy[i], hipEventDisableTiming));
   for (int i = 0; i < kStreams; ++i) HIP_TRY(hipEventCreateWithFlags(&c->ev_join[i], hipEventDisableTiming));
   *out = c;
@@ -122,15 +112,10 @@ void destroy_ctx(Ctx* c) {
     (void)hipEventDestroy(r.b);
   }
   for (auto e : c->prof_pool) (void)hipEventDestroy(e);
-  for (int i = 0; i < kCopyStreams; ++i) {
-    if (c->copy[i]) (void)hipStreamDestroy(c->copy[i]);
-    if (c->ev_copy_join[i]) (void)hipEventDestroy(c->ev_copy_join[i]);
-  }
   for (int i = 1; i < kStreams; ++i)
     if (c->comp[i]) (void)hipStreamDestroy(c->comp[i]);
   if (c->capture) (void)hipStreamDestroy(c->capture);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
-  if (c->ev_copy_done) (void)hipEventDestroy(c->ev_copy_done);
   for (int i = 0; i < kMaxP; ++i)
     if (c->ev_copy[i]) (void)hipEventDestroy(c->ev_copy[i]);
   for (int i = 0; i < kStreams; ++i)
@@ -198,28 +183,11 @@ tpg_status fork_streams(Ctx& cx, hipStream_t root, int n, hipStream_t* streams) 
   return TPG_OK;
 }
 
-// The root waits for everything issued so far on the copy streams.
-tpg_status wait_copies(Ctx& cx, hipStream_t root) {
-  for (int i = 0; i < kCopyStreams; ++i) {
-    HIP_TRY(hipEventRecord(cx.ev_copy_join[i], cx.copy[i]));
-    HIP_TRY(hipStreamWaitEvent(root, cx.ev_copy_join[i], 0));
-  }
-  return TPG_OK;
-}
-
-tpg_status join_streams(Ctx& cx, hipStream_t root, int n, const hipStream_t* streams, bool copies) {
+tpg_status join_streams(Ctx& cx, hipStream_t root, int n, const hipStream_t* streams) {
   for (int i = 1; i < n; ++i) {
     HIP_TRY(hipEventRecord(cx.ev_join[i], streams[i]));
     HIP_TRY(hipStreamWaitEvent(root, cx.ev_join[i], 0));
   }
-  if (copies) return wait_copies(cx, root);
-  return TPG_OK;
-}
-
-// Forks the copy streams from the root.
-tpg_status fork_copies(Ctx& cx, hipStream_t root) {
-  HIP_TRY(hipEventRecord(cx.ev_fork, root));
-  for (int i = 0; i < kCopyStreams; ++i) HIP_TRY(hipStreamWaitEvent(cx.copy[i], cx.ev_fork, 0));
   return TPG_OK;
 }
 
@@ -234,18 +202,21 @@ tpg_status hold_deliveries(uint32_t flags, hipStream_t s) {
   return TPG_OK;
 }
 
-hipMemcpyKind copy_kind(uint32_t flags) {
-  return (flags & TPG_COPY_SDMA) ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+// Delivery copy: the entry point's default unless a flag overrides it
+// (the defaults and their measurements are stated in tpgemm.h).
+hipMemcpyKind copy_kind(uint32_t flags, bool sdma_default) {
+  const bool sdma = (flags & TPG_COPY_SDMA) || (sdma_default && !(flags & TPG_COPY_SHADER));
+  return sdma ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
 }
 
 // Records `enqueue` into a graph once per key and replays it on `user`, or
 // runs it eagerly.
-// `fans_out`: the call's launches use more than one stream (issue policy in
-// the header: such calls are issued eagerly unless TPG_FORCE_GRAPH is set).
-tpg_status run_call(Ctx& cx, uint32_t flags, bool fans_out, const std::string& key, hipStream_t user,
+// Issue policy (stated and measured in tpgemm.h): eager unless
+// TPG_FORCE_GRAPH asks for a recorded graph.
+tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t user,
                     const std::function<tpg_status(const Launch&)>& enqueue) {
-  const bool eager = (flags & (TPG_NO_GRAPH | TPG_PROFILE | TPG_DEBUG_HOLD_DELIVERIES)) != 0 ||
-                     (fans_out && !(flags & TPG_FORCE_GRAPH));
+  const bool eager = !(flags & TPG_FORCE_GRAPH) ||
+                     (flags & (TPG_NO_GRAPH | TPG_PROFILE | TPG_DEBUG_HOLD_DELIVERIES)) != 0;
   if (eager) return enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
   auto it = cx.graphs.find(key);
   if (it == cx.graphs.end()) {
@@ -294,6 +265,8 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   if (a->M < 0 || a->N < 0 || a->K < 0) return fail(TPG_ERR_INVALID, "negative dimension");
   if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
+    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
   if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
   if (a->epilogue != TPG_EPI_ALPHA_BETA && a->epilogue != TPG_EPI_SWIGLU)
@@ -331,14 +304,14 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   }
   if (!a->d && d_b) return fail(TPG_ERR_INVALID, "D is NULL");
   if (!aligned16(a->d)) return fail(TPG_ERR_UNSUPPORTED, "D not 16-byte aligned");
+  if (need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_ag_workspace_size()");
   const Range dr{a->d, d_b}, wr{a->workspace, need};
   for (const auto& r : inputs) {
     if (overlaps(dr, r)) return fail(TPG_ERR_INVALID, "D overlaps an input");
     if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
   }
   if (overlaps(dr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps D");
-  if (need && (!a->workspace || a->workspace_bytes < need))
-    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_ag_workspace_size()");
   if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
   if ((a->flags & TPG_UNSTAGED) && (a->flags & TPG_NO_COPY) && a->M > 0) {
     for (int s = 1; s < a->P; ++s)
@@ -373,7 +346,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   const int64_t nout = sw ? a.N / 2 : a.N;
   const size_t slice_b = size_t(m) * a.K * eb;
   const bool copies = !(a.flags & TPG_NO_COPY) && slice_b > 0 && (P > 1 || (a.flags & TPG_UNSTAGED));
-  const hipMemcpyKind kind = copy_kind(a.flags);
+  const hipMemcpyKind kind = copy_kind(a.flags, false);
   char* ws = static_cast<char*>(a.workspace);
 
   tpg::GemmParams p = base_params();
@@ -395,14 +368,10 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     // single stage: gather every slice (rank order), then one GEMM over all M rows
     const void* A = a.M > 0 ? a.a_slices[0] : nullptr;
     if (copies) {
-      tpg_status fs = fork_copies(cx, L.root);
-      if (fs != TPG_OK) return fs;
-      fs = hold_deliveries(a.flags, cx.copy[0]);
-      if (fs != TPG_OK) return fs;
+      tpg_status hs = hold_deliveries(a.flags, L.root);
+      if (hs != TPG_OK) return hs;
       for (int s = 0; s < P; ++s)
-        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, cx.copy[s % kCopyStreams]));
-      tpg_status ws_ = wait_copies(cx, L.root);
-      if (ws_ != TPG_OK) return ws_;
+        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, L.root));
       A = ws;
     }
     p.a = A;
@@ -488,7 +457,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
       t += run;
     }
   }
-  return join_streams(cx, L.root, ns, st, false);
+  return join_streams(cx, L.root, ns, st);
 }
 
 std::string ag_key(const tpg_ag_args& a) {
@@ -516,6 +485,8 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
   if (a->M < 0 || a->N < 0 || a->K < 0) return fail(TPG_ERR_INVALID, "negative dimension");
   if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
+    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
   if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
   if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
@@ -549,14 +520,14 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
   const size_t d_b = size_t(a->M) * a->N * 2;
   if (!a->d && d_b) return fail(TPG_ERR_INVALID, "D is NULL");
   if (!aligned16(a->d)) return fail(TPG_ERR_UNSUPPORTED, "D not 16-byte aligned");
+  if (need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_rs_workspace_size()");
   const Range dr{a->d, d_b}, wr{a->workspace, need};
   for (const auto& r : inputs) {
     if (overlaps(dr, r)) return fail(TPG_ERR_INVALID, "D overlaps an input");
     if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
   }
   if (overlaps(dr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps D");
-  if (need && (!a->workspace || a->workspace_bytes < need))
-    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_rs_workspace_size()");
   if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
   return TPG_OK;
 }
@@ -568,7 +539,7 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   const size_t part_b = size_t(m) * a.N * 2;
   const size_t slot = rs_slot(&a);
   char* ws = static_cast<char*>(a.workspace);
-  const hipMemcpyKind kind = copy_kind(a.flags);
+  const hipMemcpyKind kind = copy_kind(a.flags, true);
 
   // peers whose partial for block `rank` arrives, in ring order rank+1, rank+2, ...
   std::vector<int> peers;
@@ -605,12 +576,12 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     }
   };
 
-  const int ncs = std::min<int>(kCopyStreams, static_cast<int>(peers.size()));
-  if (copies) {
-    tpg_status fs = fork_copies(cx, L.root);
-    if (fs != TPG_OK) return fs;
-    fs = hold_deliveries(a.flags, cx.copy[0]);
-    if (fs != TPG_OK) return fs;
+  // Deliveries go back to back on the root (the caller's stream or the
+  // capture stream); whatever reads them follows there in stream order.
+  auto deliver = [&]() -> tpg_status {
+    if (!copies) return TPG_OK;
+    tpg_status hs = hold_deliveries(a.flags, L.root);
+    if (hs != TPG_OK) return hs;
     // partials that sit back to back in memory (and in the slots) move as one copy
     for (size_t i = 0; i < peers.size();) {
       size_t run = 1;
@@ -618,31 +589,24 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
              static_cast<const char*>(a.incoming[peers[i + run]]) ==
                  static_cast<const char*>(a.incoming[peers[i]]) + run * part_b)
         ++run;
-      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], run * part_b, kind, cx.copy[i % kCopyStreams]));
+      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], run * part_b, kind, L.root));
       i += run;
     }
-    for (int i = 0; i < ncs; ++i) HIP_TRY(hipEventRecord(cx.ev_copy[i], cx.copy[i]));
-  }
-  // the stage that sums the incoming partials waits for every delivery
-  auto wait_all = [&](hipStream_t cs) -> tpg_status {
-    for (int i = 0; copies && i < ncs; ++i) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[i], 0));
     return TPG_OK;
   };
 
   if (a.flags & TPG_UNSTAGED) {
     // one GEMM over all blocks once every partial has arrived; the adds apply
     // to the rows of the own block only
-    tpg_status ws_ = wait_all(L.root);
-    if (ws_ != TPG_OK) return ws_;
+    tpg_status ds = deliver();
+    if (ds != TPG_OK) return ds;
     p.a = a.a;
     p.d = static_cast<uint16_t*>(a.d);
     p.M = static_cast<int>(a.M);
     p.add_row0 = static_cast<int>(r * m);
     p.add_row1 = static_cast<int>((r + 1) * m);
     set_adds(p);
-    tpg_status st = gemm_on(cx, L, L.root, p, dtype, layout, tpg::kEpiAlphaBeta);
-    if (st != TPG_OK) return st;
-    return copies ? wait_copies(cx, L.root) : TPG_OK;
+    return gemm_on(cx, L, L.root, p, dtype, layout, tpg::kEpiAlphaBeta);
   }
 
   // stages 0..P-2 emit the blocks (rank+1+t) mod P, cut into G runs (one
@@ -656,6 +620,7 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, ns, st);
   if (stat != TPG_OK) return stat;
+  auto side = [&](int i) { return ns > 1 ? st[1 + i % (ns - 1)] : L.root; };
   // The own block waits for every delivery while the emitted blocks run;
   // it sizes its tiles for the CUs the emitted launches leave idle in their
   // last round of tiles, so that it fills that round instead of adding one.
@@ -677,8 +642,11 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     }
     return gemm_on(cx, L, cs, q, dtype, layout, tpg::kEpiAlphaBeta);
   };
+  // Stream roles as in the all-gather: the emitted runs on the other streams
+  // start at once; the root takes the deliveries and then the own block,
+  // which reads them, in stream order.
   for (int g = 0; g < G; ++g) {
-    hipStream_t cs = st[g % ns];
+    hipStream_t cs = side(g);
     for (int t = t0(g); t < t0(g + 1);) {
       const int blk = (r + 1 + t) % P;
       const int run = std::min(t0(g + 1) - t, P - blk);
@@ -687,12 +655,11 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
       t += run;
     }
   }
-  hipStream_t cs_own = st[G % ns];
-  stat = wait_all(cs_own);
+  stat = deliver();
   if (stat != TPG_OK) return stat;
-  stat = launch_blocks(cs_own, r, 1, true);
+  stat = launch_blocks(L.root, r, 1, true);
   if (stat != TPG_OK) return stat;
-  return join_streams(cx, L.root, ns, st, copies);
+  return join_streams(cx, L.root, ns, st);
 }
 
 std::string rs_key(const tpg_rs_args& a) {
@@ -740,6 +707,8 @@ tpg_status validate_ffn(const tpg_ffn_args* a, size_t need) {
   const Range yr{a->y, PB * L * D * 2}, wr{a->workspace, need};
   if (work && !a->y) return fail(TPG_ERR_INVALID, "y is NULL");
   if (!aligned16(a->y)) return fail(TPG_ERR_UNSUPPORTED, "y not 16-byte aligned");
+  if (work && need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than ffn_slot_forward_workspace_size()");
   for (const auto& r : in) {
     if (overlaps(yr, r)) return fail(TPG_ERR_INVALID, "y overlaps an input");
     if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
@@ -795,7 +764,7 @@ tpg_status enqueue_ffn(Ctx& cx, const tpg_ffn_args& a, const Launch& L) {
     stat = gemm_on(cx, L, cs, g2, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
     if (stat != TPG_OK) return stat;
   }
-  return join_streams(cx, L.root, nb, st, false);
+  return join_streams(cx, L.root, nb, st);
 }
 
 std::string ffn_key(const tpg_ffn_args& a) {
@@ -876,8 +845,7 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
     tpg_ag_args a = *args;
     if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
-    const bool fans_out = !(a.flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES)) && a.P > 1;
-    return run_call(*cx, a.flags, fans_out, ag_key(a), static_cast<hipStream_t>(stream),
+    return run_call(*cx, a.flags, ag_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ag(*cx, a, L); });
   });
 }
@@ -896,8 +864,7 @@ tpg_status tpgemm_stage_rs(const tpg_rs_args* args, void* stream) {
     tpg_rs_args a = *args;
     if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
-    const bool fans_out = !(a.flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES)) && a.P > 1;
-    return run_call(*cx, a.flags, fans_out, rs_key(a), static_cast<hipStream_t>(stream),
+    return run_call(*cx, a.flags, rs_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_rs(*cx, a, L); });
   });
 }
@@ -914,8 +881,7 @@ tpg_status ffn_slot_forward(const tpg_ffn_args* args, void* stream) {
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
     const tpg_ffn_args a = *args;
-    const bool fans_out = !(a.flags & TPG_SERIAL_STAGES) && a.L > 1;
-    return run_call(*cx, a.flags, fans_out, ffn_key(a), static_cast<hipStream_t>(stream),
+    return run_call(*cx, a.flags, ffn_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ffn(*cx, a, L); });
   });
 }

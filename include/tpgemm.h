@@ -3,13 +3,17 @@
  *
  * One GPU runs the rank-local share of a tensor-parallel GEMM as P ordered
  * stages. The peers' shards are ordinary device buffers in the same HBM;
- * each stage's input is delivered by an asynchronous device-to-device copy on
- * a library-owned copy stream and gated by a HIP event, so the matrix cores
- * start on the local shard while the rest is delivered ("Distributed GEMM",
- * Hassani et al., SHI Labs, Dec 2024: Introduction and Background, Figures 3
- * and 4). The copy is hipMemcpyAsync's shader copy by default: on MI355X an
- * 8 MiB device-to-device copy takes ~4 us that way and ~140 us on one SDMA
- * copy engine, so the engines (TPG_COPY_SDMA) are opt-in.
+ * each stage's input is delivered by an asynchronous device-to-device copy
+ * (hipMemcpyAsync) and gated by a HIP event, so the matrix cores start on
+ * the local shard while the rest is delivered ("Distributed GEMM", Hassani
+ * et al., SHI Labs, Dec 2024: Introduction and Background, Figures 3 and 4).
+ * Which copy: the all-gather's deliveries are on its critical path, so it
+ * uses the faster shader copy (seven 8 MiB slices: ~34 us, against ~64 us
+ * on the SDMA copy engines; the SwiGLU AG share: 251 vs 329 us). The
+ * reduce-scatter's deliveries hide behind the emitted blocks, so it uses the
+ * copy engines, which take no CUs from those GEMMs, as the pages'
+ * copy-engine design intends (the bf16 RS share: equal within noise, 460 vs
+ * 459 us). TPG_COPY_SDMA / TPG_COPY_SHADER override either default.
  *
  * Conventions shared by every entry point
  *   - All pointers to tensor data are DEVICE pointers owned by the caller;
@@ -28,19 +32,17 @@
  *   - Arguments are validated before anything is enqueued; a failing call
  *     enqueues nothing and returns a non-zero status, with a message from
  *     tpg_last_error(). There is no fallback path.
- *   - Issue policy. A call whose launches form one chain on one stream
- *     (TPG_UNSTAGED, TPG_SERIAL_STAGES, P = 1) is recorded into a hipGraph
- *     on first use and replayed. A call that fans out over several streams
- *     (the staged AG, RS and FFN pipelines) is issued eagerly: on MI355X
- *     (ROCm 7) replaying such a graph was measured slower than issuing it
- *     (e.g. the e4m3 AG share 128 vs 103 us, the bf16 RS share 528 vs
- *     475 us); TPG_FORCE_GRAPH replays a graph anyway. A staged AG or RS
- *     call of under 1 GFLOP that leaves the grouping to the library
+ *   - Issue policy. Calls are issued eagerly by default. TPG_FORCE_GRAPH
+ *     records the call into a hipGraph on first use and replays it after.
+ *     On MI355X (ROCm 7) replay was measured no faster than eager issue for
+ *     every workload here, and slower for calls that fan out over streams
+ *     (us, eager vs graph: e4m3 AG share 104 vs 125, P = 2 bf16 AG 20 vs
+ *     35, SwiGLU AG 250 vs 273; bf16 RS 477 vs 472). A staged AG or RS call
+ *     of under 1 GFLOP that leaves the grouping to the library
  *     (groups = 0) is latency-bound and runs as if TPG_SERIAL_STAGES were
- *     set (one stream, graph replay): the same stages in the same order,
- *     without the cross-stream events.
- *     TPG_NO_GRAPH, TPG_PROFILE and TPG_DEBUG_HOLD_DELIVERIES always issue
- *     eagerly.
+ *     set: the same stages in the same order on one stream, without the
+ *     cross-stream events. TPG_NO_GRAPH, TPG_PROFILE and
+ *     TPG_DEBUG_HOLD_DELIVERIES never replay a graph.
  *   - Graph cache: a recorded graph is keyed by (entry point, shapes,
  *     pointers, scalars, flags). A changed pointer makes a new graph, never
  *     a stale replay. Freeing a buffer a cached graph refers to is safe as
@@ -84,13 +86,14 @@ typedef enum {
 enum {
   TPG_UNSTAGED = 1u,        /* single stage: deliver everything, then one GEMM (the non-overlapped baseline) */
   TPG_NO_COPY = 2u,         /* read peer buffers in place; no deliveries (compute-only timing) */
-  TPG_NO_GRAPH = 4u,        /* enqueue eagerly instead of capturing / replaying a hipGraph */
-  TPG_COPY_SDMA = 8u,       /* deliver with the SDMA copy engines (no CUs) instead of the shader copy */
+  TPG_NO_GRAPH = 4u,        /* enqueue eagerly even with TPG_FORCE_GRAPH */
+  TPG_COPY_SDMA = 8u,       /* deliver with the SDMA copy engines (no CUs); the RS default */
   TPG_SERIAL_STAGES = 16u,  /* run all stage GEMMs on one compute stream (no inter-stage concurrency) */
   TPG_PROFILE = 32u,        /* eager only: time every GEMM launch with HIP events (tpg_profile_read) */
-  TPG_FORCE_GRAPH = 64u,    /* replay a hipGraph even for a call that fans out over several streams */
-  TPG_DEBUG_HOLD_DELIVERIES = 128u /* testing: issue eagerly, with the deliveries queued behind a 20 ms
-                                      host callback; every gated stage must still see its data */
+  TPG_FORCE_GRAPH = 64u,    /* record the call into a hipGraph once, replay it after */
+  TPG_DEBUG_HOLD_DELIVERIES = 128u, /* testing: issue eagerly, with the deliveries queued behind a 20 ms
+                                       host callback; every gated stage must still see its data */
+  TPG_COPY_SHADER = 256u    /* deliver with the shader copy (uses CUs); the AG default */
 };
 
 /* ------------------------------------------------------------------------

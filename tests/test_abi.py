@@ -58,6 +58,7 @@ def ag(**kw):
     (dict(d=FAKE), tp.ERR_INVALID),                     # D aliases slice 0
     (dict(workspace_bytes=10), tp.ERR_WORKSPACE),
     (dict(flags=1 << 20), tp.ERR_INVALID),
+    (dict(flags=tp.COPY_SDMA | tp.COPY_SHADER), tp.ERR_INVALID),
     (dict(epilogue=tp.EPI_SWIGLU, N=255), tp.ERR_INVALID),
 ])
 def test_ag_validation_rejects_before_enqueue(kw, status):

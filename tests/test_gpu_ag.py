@@ -12,7 +12,7 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
-         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "blit": tp.COPY_SDMA}
+         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "sdma": tp.COPY_SDMA}
 
 
 def run_ag(case, inp, flags, rank=None):
@@ -103,7 +103,7 @@ def test_ag_graph_replay_sees_new_data():
     slices = [dev(s) for s in inp["a_slices"]]
     b, c = dev(inp["b"]), dev(inp["c"])
     d = bf16_empty(case.M, case.N)
-    kw = dict(M=case.M, N=case.N, K=case.K, rank=0, alpha=1.0, beta=1.0)
+    kw = dict(M=case.M, N=case.N, K=case.K, rank=0, alpha=1.0, beta=1.0, flags=tp.FORCE_GRAPH)
     say("ag: graph replay with changed inputs")
     for it in range(3):
         tp.stage_ag(slices, b, c, d, **kw)      # same pointers: replays one graph

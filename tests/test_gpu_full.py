@@ -1,5 +1,5 @@
 """Full-size GPU parity: the five workloads at their real shapes, in the launch
-configuration the benchmark times (graph replay, copy-engine deliveries).
+configuration the benchmark times (default issue, shader-copy deliveries).
 
 The oracle computes sampled output rows one by one (every stage's first and
 last row plus seeded random rows); properties that hold at any size (staged

@@ -59,7 +59,7 @@ def test_rs_own_block_waits_for_delayed_partials():
     kw = dict(M=case.M, N=case.N, K=case.K, P=case.P, rank=case.rank)
     probe = bf16_empty(case.M, case.N)
     need = tp.stage_rs_workspace_size(tp.rs_args(a, b, inc, probe, flags=tp.UNSTAGED, **kw))
-    for flags, groups in [(HOLD, 1), (HOLD, 3), (HOLD | tp.UNSTAGED, 0)]:
+    for flags, groups in [(HOLD, 1), (HOLD, 3), (HOLD | tp.COPY_SHADER, 3), (HOLD | tp.UNSTAGED, 0)]:
         say(f"gates: rs flags={flags} groups={groups}")
         ws = poisoned(need, 2)
         d = bf16_empty(case.M, case.N)
