@@ -12,7 +12,8 @@ Sources (pages of the reference set, cited by title and section):
   * "Distributed GEMM" (Hassani et al., SHI Labs, Dec 2024), Background
     (Figures 3 and 4: pipelined stages, local shard first, buffers rotate)
     and Approach (schedules AllGather1D_TilingCD_RotatingA,
-    ReduceScatter1D_TilingA_RotatingC).
+    ReduceScatter1D_TilingA_RotatingC, and their column duals
+    AllGather1D_TilingCD_RotatingB, ReduceScatter1D_TilingB_RotatingC).
   * The p04 problem statement ("Project objective"): "Interface, layout,
     and parameters" and "Computation and communication example" (the
     per-token-slot FFN, LayerNorm with eps 1e-5, SiLU gate, All-to-All
@@ -26,7 +27,8 @@ Every function is pinned by a CPU test against something other than itself
 example); see tests/test_oracle_*.py.
 """
 from .formats import decode_bf16, decode_e4m3, decode
-from .gemm import ag_stage_order, rs_block_order, gemm_ag, gemm_ag_rows, gemm_rs, gemm_rs_rows
+from .gemm import (ag_stage_order, rs_block_order, gemm_ag, gemm_ag_rows, gemm_rs, gemm_rs_rows,
+                   gemm_ag_rotb, gemm_ag_rotb_rows, gemm_rs_tileb, gemm_rs_tileb_rows)
 from .ffn import layer_norm, silu, ffn_slot_forward, ffn_slot_rows
 from .swiglu import swiglu_hidden, swiglu_hidden_rows, swiglu_block
 from .permute import dispatch, combine

@@ -21,6 +21,17 @@ own block last. Blocks b != rank are emitted as is; the own block receives
 the sum of the partials the other ranks computed for it (the rotating C),
 added once, in full precision, before the single rounding of the output.
 
+Column duals ("Distributed GEMM", Approach: the list of implemented
+schedules names AllGather1D_TilingCD_RotatingB and
+ReduceScatter1D_TilingB_RotatingC without spelling out their layout). The
+reading adopted is the column dual of the two above. RotatingB: A (M, K) is
+local and B's row slices (n = N/P rows each; in the (K, N) layout, column
+blocks) rotate, so stage t multiplies slice (rank + t) mod P and writes
+columns [s*n, (s+1)*n) of D. TilingB: the partial E = alpha * A @ B^T is
+split into P column blocks owed to the P ranks; stage t computes block
+(rank + 1 + t) mod P, the own block last, which adds the (M, n) partials
+the other ranks computed for it.
+
 Everything is float64; beta == 0 means C is not read (BLAS convention).
 """
 import numpy as np
@@ -127,4 +138,77 @@ def gemm_rs_rows(a, b, incoming, alpha, rank, P, b_layout, rows):
             for j in range(P):
                 if j != rank and incoming[j] is not None:
                     out[i] = out[i] + decode_bf16(incoming[j][r % m])
+    return out
+
+
+def _slice_as_nk(x, dtype, b_layout):
+    X = decode(x, dtype)
+    return X if b_layout == "nk" else X.T
+
+
+def gemm_ag_rotb(a, b_slices, c, alpha, beta, rank, dtype="bf16", b_layout="nk", staged=True):
+    """Full D (float64, M x N) of the all-gather with rotating B.
+
+    b_slices[s] is slice s of B: (n, K) rows of B, or in the (K, N) layout the
+    (K, n) column block of B^T. staged=False concatenates the slices in rank
+    order and multiplies once.
+    """
+    P = len(b_slices)
+    A = decode(a, dtype)
+    Bs = [_slice_as_nk(x, dtype, b_layout) for x in b_slices]
+    n = Bs[0].shape[0]
+    Cm = decode_bf16(c) if beta != 0.0 else None
+    if not staged:
+        out = alpha * (A @ np.concatenate(Bs, axis=0).T)
+        return out + beta * Cm if beta != 0.0 else out
+    D = np.empty((A.shape[0], P * n), dtype=np.float64)
+    for s in ag_stage_order(P, rank):
+        cols = slice(s * n, (s + 1) * n)
+        part = alpha * (A @ Bs[s].T)
+        D[:, cols] = part + beta * Cm[:, cols] if beta != 0.0 else part
+    return D
+
+
+def gemm_ag_rotb_rows(a, b_slices, c, alpha, beta, dtype, b_layout, rows):
+    """Rows `rows` of the rotating-B all-gather output."""
+    A = decode(a[np.asarray(rows)], dtype)
+    B = np.concatenate([_slice_as_nk(x, dtype, b_layout) for x in b_slices], axis=0)
+    out = alpha * (A @ B.T)
+    if beta != 0.0:
+        out = out + beta * decode_bf16(c[np.asarray(rows)])
+    return out
+
+
+def gemm_rs_tileb(a, b, incoming, alpha, rank, P, b_layout="nk"):
+    """Full output (float64, M x N) of the reduce-scatter with tiled B.
+
+    incoming[j] (j != rank) is the bf16 (M, n) partial of column block `rank`
+    that rank j computed; None entries (or incoming=None) contribute nothing.
+    """
+    Bm = _b_as_nk(b, "bf16", b_layout)
+    A = decode_bf16(a)
+    n = Bm.shape[0] // P
+    out = np.empty((A.shape[0], Bm.shape[0]), dtype=np.float64)
+    for blk in rs_block_order(P, rank):
+        cols = slice(blk * n, (blk + 1) * n)
+        part = alpha * (A @ Bm[cols].T)
+        if blk == rank and incoming is not None:
+            for j in range(P):
+                if j != rank and incoming[j] is not None:
+                    part = part + decode_bf16(incoming[j])
+        out[:, cols] = part
+    return out
+
+
+def gemm_rs_tileb_rows(a, b, incoming, alpha, rank, P, b_layout, rows):
+    """Rows `rows` of the tiled-B reduce-scatter output."""
+    Bm = _b_as_nk(b, "bf16", b_layout)
+    A = decode_bf16(a[np.asarray(rows)])
+    n = Bm.shape[0] // P
+    out = alpha * (A @ Bm.T)
+    if incoming is not None:
+        cols = slice(rank * n, (rank + 1) * n)
+        for j in range(P):
+            if j != rank and incoming[j] is not None:
+                out[:, cols] = out[:, cols] + decode_bf16(incoming[j][np.asarray(rows)])
     return out

@@ -182,3 +182,92 @@ def test_rs_rows_and_layout():
     rows = [0, 3, 4, 5, 11]
     np.testing.assert_allclose(oracle.gemm_rs_rows(a, bnk, inc, 0.5, 1, P, "nk", rows), full[rows],
                                rtol=1e-13, atol=1e-13)
+
+
+# ---- column duals: rotating B (all-gather) and tiled B (reduce-scatter)
+
+def col_blocks(b_nk, P, b_layout):
+    """B (N, K) split into P row slices, in the layout the call takes."""
+    n = b_nk.shape[0] // P
+    sl = [b_nk[s * n:(s + 1) * n] for s in range(P)]
+    return sl if b_layout == "nk" else [np.ascontiguousarray(x.T) for x in sl]
+
+
+@pytest.mark.parametrize("dtype,b_layout", [("bf16", "nk"), ("bf16", "kn"), ("e4m3", "nk")])
+def test_ag_rotb_matches_brute_force(dtype, b_layout):
+    """Integer data: the staged column blocks equal a plain triple loop."""
+    rng = np.random.default_rng(31)
+    P, M, n, K = 3, 4, 2, 8
+    if dtype == "bf16":
+        a = rand_int_bf16(rng, (M, K))
+        b = rand_int_bf16(rng, (P * n, K))
+        dec = lambda v: float(oracle.decode_bf16(v))
+    else:
+        a = gen.encode_e4m3(rng.integers(-4, 5, size=(M, K)) * 0.25)
+        b = gen.encode_e4m3(rng.integers(-4, 5, size=(P * n, K)) * 0.5)
+        dec = lambda v: float(oracle.decode_e4m3(v))
+    c = rand_int_bf16(rng, (M, P * n))
+    ref = brute_ag([a], b, c, 0.5, -2.0, dec, "nk")
+    for rank in range(P):
+        got = oracle.gemm_ag_rotb(a, col_blocks(b, P, b_layout), c, 0.5, -2.0, rank, dtype, b_layout)
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_ag_rotb_is_the_transposed_rota(P):
+    """(A B^T)^T = B A^T: rotating B over B's row slices is the rotating-A
+    all-gather with the roles of A and B exchanged, transposed."""
+    rng = np.random.default_rng(40 + P)
+    M, n, K = 5, 3, 16
+    a = bf16_bits(rng.uniform(-1, 1, (M, K)))
+    b = bf16_bits(rng.uniform(-1, 1, (P * n, K)))
+    c = bf16_bits(rng.uniform(-1, 1, (M, P * n)))
+    for rank in (0, P - 1):
+        got = oracle.gemm_ag_rotb(a, col_blocks(b, P, "nk"), c, 0.75, 0.5, rank)
+        dual = oracle.gemm_ag(col_blocks(b, P, "nk"), a, np.ascontiguousarray(c.T), 0.75, 0.5, rank)
+        np.testing.assert_allclose(got, dual.T, rtol=1e-13, atol=1e-13)
+        unst = oracle.gemm_ag_rotb(a, col_blocks(b, P, "kn"), c, 0.75, 0.5, rank, b_layout="kn", staged=False)
+        np.testing.assert_allclose(got, unst, rtol=1e-13, atol=1e-13)
+    rows = [0, 2, 4]
+    np.testing.assert_allclose(oracle.gemm_ag_rotb_rows(a, col_blocks(b, P, "nk"), c, 0.75, 0.5, "bf16", "nk",
+                                                        rows), got[rows], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_rs_tileb_is_the_transposed_rs(P):
+    """(A B^T)^T = B A^T: the tiled-B reduce-scatter over B's row blocks is
+    the tiled-A reduce-scatter with A and B exchanged, transposed, and the
+    incoming (M, n) partials transposed to (n, M)."""
+    rng = np.random.default_rng(60 + P)
+    M, n, K = 4, 3, 8
+    a = bf16_bits(rng.uniform(-1, 1, (M, K)))
+    b = bf16_bits(rng.uniform(-1, 1, (P * n, K)))
+    for rank in (0, P // 2):
+        inc = [None if j == rank else bf16_bits(rng.uniform(-1, 1, (M, n))) for j in range(P)]
+        got = oracle.gemm_rs_tileb(a, b, inc, 0.5, rank, P)
+        inc_t = [None if x is None else np.ascontiguousarray(x.T) for x in inc]
+        dual = oracle.gemm_rs(b, a, inc_t, 0.5, rank, P)
+        np.testing.assert_allclose(got, dual.T, rtol=1e-13, atol=1e-13)
+        got_kn = oracle.gemm_rs_tileb(a, np.ascontiguousarray(b.T), inc, 0.5, rank, P, b_layout="kn")
+        np.testing.assert_array_equal(got, got_kn)
+        rows = [0, 1, 3]
+        np.testing.assert_allclose(oracle.gemm_rs_tileb_rows(a, b, inc, 0.5, rank, P, "nk", rows), got[rows],
+                                   rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_rs_tileb_distributed_identity(P):
+    """Simulate all P ranks: rank r holds K-shard r of A and B. Feeding every
+    rank the column partials its peers emitted for its block gives the
+    columns of the unsharded product (integer data: exact)."""
+    rng = np.random.default_rng(80 + P)
+    M, n, Ks = 3, 2, 4
+    A = [rand_int_bf16(rng, (M, Ks), -1, 1) for _ in range(P)]
+    Bs = [rand_int_bf16(rng, (P * n, Ks), -1, 1) for _ in range(P)]
+    emitted = [oracle.gemm_rs_tileb(A[r], Bs[r], None, 1.0, r, P) for r in range(P)]
+    full = np.concatenate([oracle.decode_bf16(a) for a in A], axis=1) @ \
+        np.concatenate([oracle.decode_bf16(b) for b in Bs], axis=1).T
+    for r in range(P):
+        incoming = [None if j == r else bf16_bits(emitted[j][:, r * n:(r + 1) * n]) for j in range(P)]
+        out = oracle.gemm_rs_tileb(A[r], Bs[r], incoming, 1.0, r, P)
+        assert np.array_equal(out[:, r * n:(r + 1) * n], full[:, r * n:(r + 1) * n])
