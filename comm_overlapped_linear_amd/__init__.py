@@ -22,6 +22,8 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, E4M3 = 0, 1
 B_NK, B_KN = 0, 1
 EPI_ALPHA_BETA, EPI_SWIGLU = 0, 1
+ROTATE_A, ROTATE_B = 0, 1       # all-gather schedules
+TILE_A, TILE_B = 0, 1           # reduce-scatter schedules
 UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE, FORCE_GRAPH = 1, 2, 4, 8, 16, 32, 64
 DEBUG_HOLD_DELIVERIES, COPY_SHADER = 128, 256
 
@@ -43,7 +45,8 @@ class AgArgs(ctypes.Structure):
                 ("c", ctypes.c_void_p), ("d", ctypes.c_void_p),
                 ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32),
+                ("schedule", ctypes.c_int32), ("b_slices", ctypes.POINTER(ctypes.c_void_p))]
 
 
 class RsArgs(ctypes.Structure):
@@ -54,7 +57,7 @@ class RsArgs(ctypes.Structure):
                 ("incoming", ctypes.POINTER(ctypes.c_void_p)), ("d", ctypes.c_void_p),
                 ("alpha", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class FfnArgs(ctypes.Structure):
@@ -160,11 +163,28 @@ def _workspace(ws, nbytes):
 
 
 def ag_args(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, epilogue=EPI_ALPHA_BETA,
-            alpha=1.0, beta=1.0, flags=0, groups=0):
+            alpha=1.0, beta=1.0, flags=0, groups=0, schedule=None):
+    """Argument struct of tpgemm_stage_ag. With schedule=ROTATE_B, `a_slices`
+    is the local A (a tensor, or a one-element list) and `b` the list of the
+    P slices of B; otherwise `a_slices` is the list of P slices of A and `b`
+    one tensor."""
+    if schedule is None:
+        schedule = ROTATE_A
+    if schedule == ROTATE_B:
+        a_list = a_slices if isinstance(a_slices, (list, tuple)) else [a_slices]
+        slices = _ptr_array(a_list[:1])
+        bsl = _ptr_array(b)
+        args = AgArgs(M=M, N=N, K=K, P=len(b), rank=rank, ab_dtype=dtype, b_layout=b_layout,
+                      epilogue=epilogue, a_slices=ctypes.cast(slices, ctypes.POINTER(ctypes.c_void_p)),
+                      b=None, c=_ptr(c), d=_ptr(d), alpha=alpha, beta=beta, flags=flags, groups=groups,
+                      schedule=schedule, b_slices=ctypes.cast(bsl, ctypes.POINTER(ctypes.c_void_p)))
+        args._keep = (slices, bsl)
+        return args
     slices = _ptr_array(a_slices)
     args = AgArgs(M=M, N=N, K=K, P=len(a_slices), rank=rank, ab_dtype=dtype, b_layout=b_layout,
                   epilogue=epilogue, a_slices=ctypes.cast(slices, ctypes.POINTER(ctypes.c_void_p)),
-                  b=_ptr(b), c=_ptr(c), d=_ptr(d), alpha=alpha, beta=beta, flags=flags, groups=groups)
+                  b=_ptr(b), c=_ptr(c), d=_ptr(d), alpha=alpha, beta=beta, flags=flags, groups=groups,
+                  schedule=schedule, b_slices=None)
     args._keep = slices
     return args
 
@@ -174,10 +194,10 @@ def stage_ag_workspace_size(args):
 
 
 def stage_ag(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, epilogue=EPI_ALPHA_BETA,
-             alpha=1.0, beta=1.0, flags=0, groups=0, workspace=None, stream=None):
-    """Staged all-gather GEMM: d = alpha * A b^T + beta * c (see tpgemm.h)."""
+             alpha=1.0, beta=1.0, flags=0, groups=0, schedule=None, workspace=None, stream=None):
+    """Staged all-gather GEMM: d = alpha * A b^T + beta * c (see tpgemm.h and ag_args)."""
     args = ag_args(a_slices, b, c, d, M=M, N=N, K=K, rank=rank, dtype=dtype, b_layout=b_layout,
-                   epilogue=epilogue, alpha=alpha, beta=beta, flags=flags, groups=groups)
+                   epilogue=epilogue, alpha=alpha, beta=beta, flags=flags, groups=groups, schedule=schedule)
     need = stage_ag_workspace_size(args)
     ws = _workspace(workspace, need)
     args.workspace = _ptr(ws) if ws is not None else None
@@ -186,11 +206,12 @@ def stage_ag(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, e
 
 
 def rs_args(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0,
-            groups=0):
+            groups=0, schedule=None):
     inc = _ptr_array(incoming) if incoming is not None else None
     args = RsArgs(M=M, N=N, K=K, P=P, rank=rank, ab_dtype=dtype, b_layout=b_layout, a=_ptr(a), b=_ptr(b),
                   incoming=ctypes.cast(inc, ctypes.POINTER(ctypes.c_void_p)) if inc is not None else None,
-                  d=_ptr(d), alpha=alpha, flags=flags, groups=groups)
+                  d=_ptr(d), alpha=alpha, flags=flags, groups=groups,
+                  schedule=TILE_A if schedule is None else schedule)
     args._keep = inc
     return args
 
@@ -200,10 +221,10 @@ def stage_rs_workspace_size(args):
 
 
 def stage_rs(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0,
-             groups=0, workspace=None, stream=None):
+             groups=0, schedule=None, workspace=None, stream=None):
     """Staged GEMM + reduce-scatter share (see tpgemm.h)."""
     args = rs_args(a, b, incoming, d, M=M, N=N, K=K, P=P, rank=rank, dtype=dtype, b_layout=b_layout,
-                   alpha=alpha, flags=flags, groups=groups)
+                   alpha=alpha, flags=flags, groups=groups, schedule=schedule)
     need = stage_rs_workspace_size(args)
     ws = _workspace(workspace, need)
     args.workspace = _ptr(ws) if ws is not None else None

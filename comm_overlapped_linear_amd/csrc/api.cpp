@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <limits>
 #include <chrono>
 #include <thread>
 #include <cstdio>
@@ -263,7 +264,13 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   if (a->P < 1 || a->P > kMaxP) return fail(TPG_ERR_INVALID, "P must be in [1, 64]");
   if (a->rank < 0 || a->rank >= a->P) return fail(TPG_ERR_INVALID, "rank must be in [0, P)");
   if (a->M < 0 || a->N < 0 || a->K < 0) return fail(TPG_ERR_INVALID, "negative dimension");
-  if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
+  if (a->schedule != TPG_ROTATE_A && a->schedule != TPG_ROTATE_B) return fail(TPG_ERR_INVALID, "bad schedule");
+  const bool rotb = a->schedule == TPG_ROTATE_B;
+  if (!rotb && a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
+  if (rotb && a->N % a->P) return fail(TPG_ERR_INVALID, "TPG_ROTATE_B: N must be a multiple of P");
+  if (rotb && (a->N / a->P) % 8) return fail(TPG_ERR_UNSUPPORTED, "TPG_ROTATE_B: N/P must be a multiple of 8");
+  if (rotb && a->epilogue != TPG_EPI_ALPHA_BETA)
+    return fail(TPG_ERR_UNSUPPORTED, "TPG_ROTATE_B needs the alpha/beta epilogue");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
   if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
@@ -284,19 +291,33 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
     return fail(TPG_ERR_UNSUPPORTED, "KN layout needs N (and N/2 with SWIGLU) multiple of 8");
   if (a->beta != 0.0f && !a->c) return fail(TPG_ERR_INVALID, "beta != 0 needs C");
   const int eb = elem_bytes(a->ab_dtype);
-  const int64_t m = a->M / a->P;
-  const size_t slice_b = size_t(m) * a->K * eb;
-  if (!a->a_slices && a->M > 0) return fail(TPG_ERR_INVALID, "a_slices is NULL");
   std::vector<Range> inputs;
-  for (int s = 0; a->M > 0 && s < a->P; ++s) {
-    if (!a->a_slices[s] && slice_b) return fail(TPG_ERR_INVALID, "NULL A slice");
-    if (!aligned16(a->a_slices[s])) return fail(TPG_ERR_UNSUPPORTED, "A slice not 16-byte aligned");
-    inputs.push_back({a->a_slices[s], slice_b});
+  if (!rotb) {
+    const int64_t m = a->M / a->P;
+    const size_t slice_b = size_t(m) * a->K * eb;
+    if (!a->a_slices && a->M > 0) return fail(TPG_ERR_INVALID, "a_slices is NULL");
+    for (int s = 0; a->M > 0 && s < a->P; ++s) {
+      if (!a->a_slices[s] && slice_b) return fail(TPG_ERR_INVALID, "NULL A slice");
+      if (!aligned16(a->a_slices[s])) return fail(TPG_ERR_UNSUPPORTED, "A slice not 16-byte aligned");
+      inputs.push_back({a->a_slices[s], slice_b});
+    }
+    const size_t b_b = size_t(a->N) * a->K * eb;
+    if (!a->b && b_b) return fail(TPG_ERR_INVALID, "B is NULL");
+    if (!aligned16(a->b)) return fail(TPG_ERR_UNSUPPORTED, "B not 16-byte aligned");
+    inputs.push_back({a->b, b_b});
+  } else {
+    const size_t a_b = size_t(a->M) * a->K * eb;
+    const size_t bslice_b = size_t(a->N / a->P) * a->K * eb;
+    if (!a->a_slices || (!a->a_slices[0] && a_b)) return fail(TPG_ERR_INVALID, "A (a_slices[0]) is NULL");
+    if (!aligned16(a->a_slices[0])) return fail(TPG_ERR_UNSUPPORTED, "A not 16-byte aligned");
+    inputs.push_back({a->a_slices[0], a_b});
+    if (!a->b_slices && a->N > 0) return fail(TPG_ERR_INVALID, "b_slices is NULL");
+    for (int s = 0; a->N > 0 && s < a->P; ++s) {
+      if (!a->b_slices[s] && bslice_b) return fail(TPG_ERR_INVALID, "NULL B slice");
+      if (!aligned16(a->b_slices[s])) return fail(TPG_ERR_UNSUPPORTED, "B slice not 16-byte aligned");
+      inputs.push_back({a->b_slices[s], bslice_b});
+    }
   }
-  const size_t b_b = size_t(a->N) * a->K * eb;
-  if (!a->b && b_b) return fail(TPG_ERR_INVALID, "B is NULL");
-  if (!aligned16(a->b)) return fail(TPG_ERR_UNSUPPORTED, "B not 16-byte aligned");
-  inputs.push_back({a->b, b_b});
   const size_t d_b = size_t(a->M) * nout * 2;
   if (a->beta != 0.0f) {
     if (!aligned16(a->c)) return fail(TPG_ERR_UNSUPPORTED, "C not 16-byte aligned");
@@ -313,18 +334,27 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   }
   if (overlaps(dr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps D");
   if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
-  if ((a->flags & TPG_UNSTAGED) && (a->flags & TPG_NO_COPY) && a->M > 0) {
+  if ((a->flags & TPG_UNSTAGED) && (a->flags & TPG_NO_COPY) && a->M > 0 && a->N > 0) {
+    if (rotb && a->b_layout == TPG_B_KN)
+      return fail(TPG_ERR_UNSUPPORTED, "UNSTAGED|NO_COPY with TPG_ROTATE_B needs the NK layout");
+    const void* const* sl = rotb ? a->b_slices : a->a_slices;
+    const size_t slice_b = rotb ? size_t(a->N / a->P) * a->K * eb : size_t(a->M / a->P) * a->K * eb;
     for (int s = 1; s < a->P; ++s)
-      if (static_cast<const char*>(a->a_slices[s]) != static_cast<const char*>(a->a_slices[0]) + s * slice_b)
+      if (static_cast<const char*>(sl[s]) != static_cast<const char*>(sl[0]) + s * slice_b)
         return fail(TPG_ERR_UNSUPPORTED, "UNSTAGED|NO_COPY needs the slices to be contiguous");
   }
   return TPG_OK;
 }
 
+// Bytes of one delivered slice: an A row slice, or with TPG_ROTATE_B a B slice.
+size_t ag_slice_bytes(const tpg_ag_args* a) {
+  const size_t rows = a->schedule == TPG_ROTATE_B ? size_t(a->N) / a->P : size_t(a->M) / a->P;
+  return rows * a->K * elem_bytes(a->ab_dtype);
+}
+
 size_t ag_ws(const tpg_ag_args* a) {
-  if (!a || a->P < 1 || a->M < 0 || a->K < 0 || (a->flags & TPG_NO_COPY)) return 0;
-  const size_t m = size_t(a->M) / a->P;
-  const size_t slice = m * a->K * elem_bytes(a->ab_dtype);
+  if (!a || a->P < 1 || a->M < 0 || a->N < 0 || a->K < 0 || (a->flags & TPG_NO_COPY)) return 0;
+  const size_t slice = ag_slice_bytes(a);
   if (a->flags & TPG_UNSTAGED) return slice * a->P;
   return slice * (a->P - 1);
 }
@@ -334,11 +364,155 @@ tpg::GemmParams base_params() {
   std::memset(&p, 0, sizeof(p));
   p.add_row0 = 0;
   p.add_row1 = 0;
+  p.add_col0 = 0;
+  p.add_col1 = std::numeric_limits<int>::max();   // addends (when any) span every column
   p.batch = 1;
   return p;
 }
 
+// All-gather with rotating B (TPG_ROTATE_B): the column dual of enqueue_ag.
+// A is local; stage t multiplies slice s = (rank + t) mod P of B and writes
+// columns [s*n, (s+1)*n) of D. Receive slots: (N, K) layout, slot j holds the
+// (n, K) rows of one slice, back to back; (K, N) layout, one (K, W*n)
+// matrix whose column block j holds one slice (W = P-1 staged, P unstaged),
+// filled with 2-D copies. Stream roles, runs, gates and CU budgets are those
+// of the rotating-A form.
+tpg_status enqueue_ag_rotb(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
+  const int P = a.P, r = a.rank;
+  const int eb = elem_bytes(a.ab_dtype);
+  const bool kn = a.b_layout == TPG_B_KN;
+  const int64_t n = a.N / P;
+  const size_t slice_b = size_t(n) * a.K * eb;
+  const bool copies = !(a.flags & TPG_NO_COPY) && slice_b > 0 && (P > 1 || (a.flags & TPG_UNSTAGED));
+  const hipMemcpyKind kind = copy_kind(a.flags, false);
+  char* ws = static_cast<char*>(a.workspace);
+  uint16_t* D = static_cast<uint16_t*>(a.d);
+  const uint16_t* C = static_cast<const uint16_t*>(a.c);
+
+  tpg::GemmParams p = base_params();
+  p.a = a.a_slices[0];
+  p.lda = a.K;
+  p.ldc = a.N;
+  p.ldd = a.N;
+  p.M = static_cast<int>(a.M);
+  p.K = static_cast<int>(a.K);
+  p.alpha = a.alpha;
+  p.beta = a.beta;
+  p.vec_ok = (a.N % 8) == 0;
+  const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
+  const int layout = kn ? tpg::kKN : tpg::kNK;
+
+  // slice s into receive slot j of a W-slot receive area
+  auto deliver = [&](int j, int s, int W) -> tpg_status {
+    if (!kn) {
+      HIP_TRY(hipMemcpyAsync(ws + j * slice_b, a.b_slices[s], slice_b, kind, L.root));
+    } else {
+      HIP_TRY(hipMemcpy2DAsync(ws + size_t(j) * n * eb, size_t(W) * n * eb, a.b_slices[s], size_t(n) * eb,
+                               size_t(n) * eb, a.K, kind, L.root));
+    }
+    return TPG_OK;
+  };
+  // columns [s*n, (s+run)*n) of D from B at Bp (row stride ldb elements)
+  auto launch_cols = [&](hipStream_t cs, const void* Bp, int64_t ldb, int s, int run, int cus) {
+    tpg::GemmParams q = p;
+    q.b = Bp;
+    q.ldb = ldb;
+    q.N = static_cast<int>(run * n);
+    q.d = D + s * n;
+    q.c = C ? C + s * n : nullptr;
+    q.cu_budget = cus;
+    return gemm_on(cx, L, cs, q, dtype, layout, tpg::kEpiAlphaBeta);
+  };
+
+  if (a.flags & TPG_UNSTAGED) {
+    // single stage: gather every slice (rank order) into B, then one GEMM
+    const void* Bp = a.b_slices[0];
+    int64_t ldb = a.K;                  // NO_COPY: contiguous (N, K) slices (validated)
+    if (copies) {
+      tpg_status hs = hold_deliveries(a.flags, L.root);
+      if (hs != TPG_OK) return hs;
+      for (int s = 0; s < P; ++s) {
+        hs = deliver(s, s, P);
+        if (hs != TPG_OK) return hs;
+      }
+      Bp = ws;
+      ldb = kn ? a.N : a.K;
+    }
+    return launch_cols(L.root, Bp, ldb, 0, P, 0);
+  }
+
+  const int remote = P - 1;
+  const int G = remote == 0 ? 0 : (a.groups > 0 ? std::min(a.groups, remote) : auto_groups(remote));
+  auto t0 = [&](int g) { return 1 + (g * remote) / G; };
+  auto adjacent = [&](int s, int run) {   // NK slices s .. s+run back to back in memory
+    if (kn) return run == 1;
+    for (int i = 1; i < run; ++i)
+      if (static_cast<const char*>(a.b_slices[s + i]) != static_cast<const char*>(a.b_slices[s]) + i * slice_b)
+        return false;
+    return true;
+  };
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(G + 1, kStreams);
+  hipStream_t st[kStreams];
+  tpg_status stat = fork_streams(cx, L.root, ns, st);
+  if (stat != TPG_OK) return stat;
+  const int stack = (G + 1 + ns - 1) / ns;
+  auto budget = [&](int stages) {
+    if (ns == 1) return 0;
+    return static_cast<int>(std::min<int64_t>(tpg::device_cus(),
+                                              std::max<int64_t>(8, int64_t(tpg::device_cus()) * stages * stack / P)));
+  };
+  auto side = [&](int i) { return ns > 1 ? st[1 + i % (ns - 1)] : L.root; };
+  stat = launch_cols(side(0), a.b_slices[r], kn ? n : a.K, r, 1, budget(1));   // the local slice
+  if (stat != TPG_OK) return stat;
+  if (copies) {
+    stat = hold_deliveries(a.flags, L.root);
+    if (stat != TPG_OK) return stat;
+  }
+  for (int g = 0; g < G; ++g) {
+    if (copies) {
+      for (int t = t0(g); t < t0(g + 1);) {
+        const int s = (r + t) % P;
+        int run = 1;
+        while (t + run < t0(g + 1) && s + run < P && adjacent(s, run + 1)) ++run;
+        if (run > 1) {
+          HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.b_slices[s], run * slice_b, kind, L.root));
+        } else {
+          stat = deliver(t - 1, s, remote);
+          if (stat != TPG_OK) return stat;
+        }
+        t += run;
+      }
+    }
+    const bool last = g == G - 1;
+    hipStream_t cs = last ? L.root : side(g + 1);
+    if (!last && copies && ns > 1) {
+      HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
+      HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
+    }
+    for (int t = t0(g); t < t0(g + 1);) {
+      const int s = (r + t) % P;
+      int run = std::min(t0(g + 1) - t, P - s);
+      if (!copies)
+        while (run > 1 && !adjacent(s, run)) --run;      // in place: one launch per adjacent stretch
+      const void* Bp;
+      int64_t ldb;
+      if (copies) {
+        Bp = kn ? static_cast<const void*>(ws + size_t(t - 1) * n * eb) : static_cast<const void*>(ws + (t - 1) * slice_b);
+        ldb = kn ? int64_t(remote) * n : a.K;
+      } else {
+        Bp = a.b_slices[s];
+        ldb = kn ? n : a.K;
+      }
+      stat = launch_cols(cs, Bp, ldb, s, run, budget(t0(g + 1) - t0(g)));
+      if (stat != TPG_OK) return stat;
+      t += run;
+    }
+  }
+  return join_streams(cx, L.root, ns, st);
+}
+
 tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
+  if (a.schedule == TPG_ROTATE_B) return enqueue_ag_rotb(cx, a, L);
   const int P = a.P, r = a.rank;
   const int eb = elem_bytes(a.ab_dtype);
   const int64_t m = a.M / P;
@@ -466,12 +640,21 @@ std::string ag_key(const tpg_ag_args& a) {
   put(os, a.M); put(os, a.N); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.ab_dtype);
   put(os, a.b_layout); put(os, a.epilogue); put(os, a.b); put(os, a.c); put(os, a.d);
   put(os, a.alpha); put(os, a.beta); put(os, a.workspace); put(os, a.flags); put(os, a.groups);
-  for (int s = 0; s < a.P && a.a_slices; ++s) put(os, a.a_slices[s]);
+  put(os, a.schedule);
+  const int na = a.schedule == TPG_ROTATE_B ? 1 : a.P;
+  for (int s = 0; s < na && a.a_slices; ++s) put(os, a.a_slices[s]);
+  for (int s = 0; a.schedule == TPG_ROTATE_B && s < a.P && a.b_slices; ++s) put(os, a.b_slices[s]);
   return os.str();
 }
 
 // ---------------------------------------------------------------- reduce-scatter
-size_t rs_slot(const tpg_rs_args* a) { return round_up(size_t(a->M / a->P) * a->N * 2, 256); }
+// One incoming partial: an (m, N) row block, or with TPG_TILE_B an (M, n)
+// column block, bf16.
+size_t rs_part_bytes(const tpg_rs_args* a) {
+  return a->schedule == TPG_TILE_B ? size_t(a->M) * (a->N / a->P) * 2 : size_t(a->M / a->P) * a->N * 2;
+}
+
+size_t rs_slot(const tpg_rs_args* a) { return round_up(rs_part_bytes(a), 256); }
 
 size_t rs_ws(const tpg_rs_args* a) {
   if (!a || a->P < 1 || a->M < 0 || a->N < 0 || !a->incoming || (a->flags & TPG_NO_COPY)) return 0;
@@ -483,7 +666,11 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
   if (a->P < 1 || a->P > kMaxP) return fail(TPG_ERR_INVALID, "P must be in [1, 64]");
   if (a->rank < 0 || a->rank >= a->P) return fail(TPG_ERR_INVALID, "rank must be in [0, P)");
   if (a->M < 0 || a->N < 0 || a->K < 0) return fail(TPG_ERR_INVALID, "negative dimension");
-  if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
+  if (a->schedule != TPG_TILE_A && a->schedule != TPG_TILE_B) return fail(TPG_ERR_INVALID, "bad schedule");
+  const bool tileb = a->schedule == TPG_TILE_B;
+  if (!tileb && a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
+  if (tileb && a->N % a->P) return fail(TPG_ERR_INVALID, "TPG_TILE_B: N must be a multiple of P");
+  if (tileb && (a->N / a->P) % 8) return fail(TPG_ERR_UNSUPPORTED, "TPG_TILE_B: N/P must be a multiple of 8");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
   if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
@@ -497,7 +684,6 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
     return fail(TPG_ERR_UNSUPPORTED, "K must be a multiple of 8 (bf16) or 16 (e4m3)");
   if (a->b_layout == TPG_B_KN && a->N % 8) return fail(TPG_ERR_UNSUPPORTED, "KN layout needs N % 8 == 0");
   const int eb = elem_bytes(a->ab_dtype);
-  const int64_t m = a->M / a->P;
   std::vector<Range> inputs;
   const size_t a_b = size_t(a->M) * a->K * eb, b_b = size_t(a->N) * a->K * eb;
   if (!a->a && a_b) return fail(TPG_ERR_INVALID, "A is NULL");
@@ -506,7 +692,7 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
   inputs.push_back({a->a, a_b});
   inputs.push_back({a->b, b_b});
   int n_in = 0;
-  const size_t part_b = size_t(m) * a->N * 2;
+  const size_t part_b = rs_part_bytes(a);
   if (a->incoming) {
     for (int j = 0; j < a->P; ++j) {
       if (j == a->rank || !a->incoming[j]) continue;
@@ -535,8 +721,10 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
 tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   const int P = a.P, r = a.rank;
   const int eb = elem_bytes(a.ab_dtype);
-  const int64_t m = a.M / P;
-  const size_t part_b = size_t(m) * a.N * 2;
+  const bool tileb = a.schedule == TPG_TILE_B;
+  const int64_t m = a.M / P;          // TPG_TILE_A: rows per block
+  const int64_t n = a.N / P;          // TPG_TILE_B: columns per block
+  const size_t part_b = rs_part_bytes(&a);
   const size_t slot = rs_slot(&a);
   char* ws = static_cast<char*>(a.workspace);
   const hipMemcpyKind kind = copy_kind(a.flags, true);
@@ -555,7 +743,7 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   p.ldb = a.b_layout == TPG_B_NK ? a.K : a.N;
   p.lda = a.K;
   p.ldd = a.N;
-  p.ld_add = a.N;
+  p.ld_add = tileb ? n : a.N;
   p.N = static_cast<int>(a.N);
   p.K = static_cast<int>(a.K);
   p.alpha = a.alpha;
@@ -603,8 +791,15 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     p.a = a.a;
     p.d = static_cast<uint16_t*>(a.d);
     p.M = static_cast<int>(a.M);
-    p.add_row0 = static_cast<int>(r * m);
-    p.add_row1 = static_cast<int>((r + 1) * m);
+    if (!tileb) {
+      p.add_row0 = static_cast<int>(r * m);
+      p.add_row1 = static_cast<int>((r + 1) * m);
+    } else {
+      p.add_row0 = 0;
+      p.add_row1 = static_cast<int>(a.M);
+      p.add_col0 = static_cast<int>(r * n);
+      p.add_col1 = static_cast<int>((r + 1) * n);
+    }
     set_adds(p);
     return gemm_on(cx, L, L.root, p, dtype, layout, tpg::kEpiAlphaBeta);
   }
@@ -627,12 +822,20 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   int64_t emitted_tiles = 0;
   auto launch_blocks = [&](hipStream_t cs, int blk, int run, bool own) {
     tpg::GemmParams q = p;
-    q.M = static_cast<int>(run * m);
-    q.a = static_cast<const char*>(a.a) + size_t(blk) * m * a.K * eb;
-    q.d = static_cast<uint16_t*>(a.d) + blk * m * a.N;
+    if (!tileb) {     // row blocks: rows of A and D
+      q.M = static_cast<int>(run * m);
+      q.a = static_cast<const char*>(a.a) + size_t(blk) * m * a.K * eb;
+      q.d = static_cast<uint16_t*>(a.d) + blk * m * a.N;
+    } else {          // column blocks: rows of B (NK) or its columns (KN), columns of D
+      q.M = static_cast<int>(a.M);
+      q.a = a.a;
+      q.N = static_cast<int>(run * n);
+      q.b = static_cast<const char*>(a.b) + size_t(blk) * n * (a.b_layout == TPG_B_NK ? a.K : 1) * eb;
+      q.d = static_cast<uint16_t*>(a.d) + blk * n;
+    }
     if (own) {
       q.add_row0 = 0;
-      q.add_row1 = static_cast<int>(m);
+      q.add_row1 = q.M;
       set_adds(q);
       const int cus = tpg::device_cus();
       const int rem = static_cast<int>(emitted_tiles % cus);
@@ -667,7 +870,7 @@ std::string rs_key(const tpg_rs_args& a) {
   os << "rs|";
   put(os, a.M); put(os, a.N); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.ab_dtype);
   put(os, a.b_layout); put(os, a.a); put(os, a.b); put(os, a.d); put(os, a.alpha);
-  put(os, a.workspace); put(os, a.flags); put(os, a.groups);
+  put(os, a.workspace); put(os, a.flags); put(os, a.groups); put(os, a.schedule);
   for (int j = 0; a.incoming && j < a.P; ++j) put(os, a.incoming[j]);
   return os.str();
 }

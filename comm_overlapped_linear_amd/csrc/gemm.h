@@ -19,8 +19,11 @@ struct GemmParams {
   int64_t lda, ldb, ldc, ldd;  // in elements
   int M, N, K;                 // N = accumulator columns (2n for swiglu)
   float alpha, beta;
-  // extra bf16 addends summed into rows [add_row0, add_row1) of the output
-  // (the reduce-scatter incoming partials), fp32 accumulate:
+  // extra bf16 addends summed into rows [add_row0, add_row1) and columns
+  // [add_col0, add_col1) of the output (the reduce-scatter incoming
+  // partials), fp32 accumulate; addend element (r, c) of output (row, col)
+  // is at (row - add_row0) * ld_add + (col - add_col0). Column bounds are
+  // multiples of 8. Addends:
   //   add_list[0..n_add_list) and add_base + i * add_stride (i < n_add_strided)
   const uint16_t* add_list[kMaxAddList];
   int n_add_list;
@@ -29,6 +32,7 @@ struct GemmParams {
   int n_add_strided;
   int64_t ld_add;              // row stride of every addend (elements)
   int add_row0, add_row1;
+  int add_col0, add_col1;
   int vec_ok;                  // 1 if ldc, ldd and ld_add are multiples of 8 (16-byte row vectors)
   // batched launch (blockIdx.y = batch index): element strides between the
   // operands of consecutive batches (0 = shared); C and addends unbatched

@@ -142,8 +142,8 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPt
   const bool vec = p.vec_ok && n == 8;
   if (p.beta != 0.0f) add_row8(p.c, static_cast<int64_t>(row) * p.ldc + col, vec, n, p.beta, x);
   if (bp.bias) add_row8(bp.bias, col, n == 8, n, 1.0f, x);
-  if (row >= p.add_row0 && row < p.add_row1) {
-    const int64_t off = static_cast<int64_t>(row - p.add_row0) * p.ld_add + col;
+  if (row >= p.add_row0 && row < p.add_row1 && col >= p.add_col0 && col < p.add_col1) {
+    const int64_t off = static_cast<int64_t>(row - p.add_row0) * p.ld_add + (col - p.add_col0);
     for (int t = 0; t < p.n_add_list; ++t) add_row8(p.add_list[t], off, vec, n, 1.0f, x);
     for (int t = 0; t < p.n_add_strided; ++t) add_row8(p.add_base + t * p.add_stride, off, vec, n, 1.0f, x);
   }
@@ -205,16 +205,17 @@ __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchP
     for (int u = 0; u < NV; ++u) add_vec8(c[u], 1.0f, x[u]);
   }
   const int nadd = p.n_add_list + p.n_add_strided;
-  if (nadd > 0 && p.add_row1 > p.add_row0) {
-    // rows outside [add_row0, add_row1) take no addends; their (clamped,
+  if (nadd > 0 && p.add_row1 > p.add_row0 && p.add_col1 > p.add_col0) {
+    // vectors outside the addend rectangle take no addends; their (clamped,
     // valid) loads are discarded
     bool in[NV];
     int64_t off[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      in[u] = row[u] >= p.add_row0 && row[u] < p.add_row1;
+      in[u] = row[u] >= p.add_row0 && row[u] < p.add_row1 && col[u] >= p.add_col0 && col[u] < p.add_col1;
       const int ra = min(max(row[u] - p.add_row0, 0), max(p.add_row1 - p.add_row0 - 1, 0));
-      off[u] = int64_t(ra) * p.ld_add + col[u];
+      const int ca = min(max(col[u] - p.add_col0, 0), max(p.add_col1 - p.add_col0 - 8, 0));
+      off[u] = int64_t(ra) * p.ld_add + ca;
     }
     for (int t = 0; t < nadd; ++t) {
       const uint16_t* src = t < p.n_add_list ? p.add_list[t] : p.add_base + (t - p.n_add_list) * p.add_stride;

@@ -124,11 +124,26 @@ enum {
  *                (contiguous) receive slots, and deliveries of slices that are
  *                adjacent in memory are merged into one copy. groups = P-1 is
  *                one gate per stage; 1 runs the local stage while everything
- *                else is delivered; 0 lets the library choose from the tile
- *                count. Values above P-1 are clamped. The result does not
- *                depend on it.
+ *                else is delivered; 0 lets the library choose (one gate).
+ *                Values above P-1 are clamped. The result does not depend on
+ *                it.
+ *   schedule     TPG_ROTATE_A (the above) or TPG_ROTATE_B, the column dual
+ *                (Approach: schedule AllGather1D_TilingCD_RotatingB; its
+ *                layout is the plain reading stated here): A (M, K) is local,
+ *                B arrives as P slices of n = N/P rows (NK: (n, K) each; KN:
+ *                the (K, n) column block of B^T each), slice s from rank s,
+ *                and stage t computes columns [s*n, (s+1)*n) of D (and reads
+ *                those of C) from slice s = (rank + t) mod P, local first.
+ *                TPG_ROTATE_B needs N % P == 0, n % 8 == 0 and
+ *                TPG_EPI_ALPHA_BETA; a_slices[0] is then the whole A (the
+ *                other entries are not read), b is not read, and b_slices
+ *                holds the P slices. Receive slots then hold B slices (NK:
+ *                back to back; KN: one (K, (P-1)*n) matrix).
+ *   b_slices     TPG_ROTATE_B: host array of P device pointers; else unused.
  * All device pointers must be 16-byte aligned.
  * ---------------------------------------------------------------------- */
+enum { TPG_ROTATE_A = 0, TPG_ROTATE_B = 1 };
+
 typedef struct {
   int64_t M, N, K;
   int32_t P, rank;
@@ -144,6 +159,8 @@ typedef struct {
   size_t workspace_bytes;
   uint32_t flags;
   int32_t groups;
+  int32_t schedule;
+  const void* const* b_slices;
 } tpg_ag_args;
 
 size_t tpgemm_stage_ag_workspace_size(const tpg_ag_args* args);
@@ -159,7 +176,7 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream);
  * emitted partial alpha * E_b; block rank receives
  * alpha * E_rank + sum_{j != rank} incoming[j], accumulated in fp32 and
  * rounded once to bf16. The incoming partials are delivered into the
- * workspace by the copy stream and gate the last stage only.
+ * workspace and gate the last stage only.
  *
  *   M, N, K      M % P == 0; K % 8 == 0 (bf16) or 16 (e4m3, NK only).
  *   a            (M, K) row-major.   b  (N, K) or (K, N) row-major.
@@ -171,7 +188,16 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream);
  *                `groups` launches of consecutive blocks (0: library choice;
  *                clamped to [1, P-1]); the own block is always its own launch,
  *                gated on every delivery. The result does not depend on it.
+ *   schedule     TPG_TILE_A (the above: row blocks) or TPG_TILE_B, the column
+ *                dual (Approach: schedule ReduceScatter1D_TilingB_RotatingC;
+ *                its layout is the plain reading stated here): the blocks
+ *                are the P column blocks of n = N/P columns of E, block b
+ *                owed to rank b, and the incoming partials are bf16 (M, n).
+ *                TPG_TILE_B needs N % P == 0 and n % 8 == 0 (M % P is then
+ *                not required).
  * ---------------------------------------------------------------------- */
+enum { TPG_TILE_A = 0, TPG_TILE_B = 1 };
+
 typedef struct {
   int64_t M, N, K;
   int32_t P, rank;
@@ -186,6 +212,7 @@ typedef struct {
   size_t workspace_bytes;
   uint32_t flags;
   int32_t groups;
+  int32_t schedule;
 } tpg_rs_args;
 
 size_t tpgemm_stage_rs_workspace_size(const tpg_rs_args* args);

@@ -78,6 +78,27 @@ def ag_inputs(case: AgCase, seed: int = SEED):
     return dict(a_slices=a_slices, b=b, c=c)
 
 
+def ag_rotb_inputs(case: AgCase, seed: int = SEED):
+    """Rotating-B all-gather: dict(a=(M, K), b_slices=[P x (n, K) or (K, n)],
+    c=(M, N) or None), n = N/P; slice s is rank s's shard of B."""
+    n, K = case.N // case.P, case.K
+
+    def operand(key, shape):
+        if case.dist == "u11":
+            return uniform_bf16(key, shape, -1.0, 1.0)
+        if case.dtype == "e4m3":
+            return normal_e4m3(key, shape, scale=0.5, clip=448.0)
+        return normal_bf16(key, shape, 0.0, 0.5)
+
+    a = operand(stream_key(seed + case.rank, "agb.a"), (case.M, K))
+    shape = (n, K) if case.b_layout == "nk" else (K, n)
+    b_slices = [operand(stream_key(seed + s, "agb.b"), shape) for s in range(case.P)]
+    c = None
+    if case.beta != 0.0:
+        c = normal_bf16(stream_key(seed + case.rank, "agb.c"), (case.M, case.N), 0.0, 1.0)
+    return dict(a=a, b_slices=b_slices, c=c)
+
+
 # --------------------------------------------------------------------------
 # staged GEMM + reduce-scatter dual
 # --------------------------------------------------------------------------
@@ -114,6 +135,34 @@ def rs_inputs(case: RsCase, seed: int = SEED):
             if j != case.rank:
                 incoming[j] = normal_bf16(stream_key(seed + j, "rs.in"), (case.m, case.N), 0.0, 1.0)
     return dict(a=a, b=b, incoming=incoming)
+
+
+def rs_tileb_inputs(case: RsCase, seed: int = SEED):
+    """Tiled-B reduce-scatter: dict(a, b, incoming) with (M, N/P) partials."""
+    a = normal_bf16(stream_key(seed + case.rank, "rsb.a"), (case.M, case.K), 0.0, case.std)
+    bshape = (case.N, case.K) if case.b_layout == "nk" else (case.K, case.N)
+    b = normal_bf16(stream_key(seed + case.rank, "rsb.b"), bshape, 0.0, case.std)
+    incoming = [None] * case.P
+    if case.incoming:
+        for j in range(case.P):
+            if j != case.rank:
+                incoming[j] = normal_bf16(stream_key(seed + j, "rsb.in"), (case.M, case.N // case.P), 0.0, 1.0)
+    return dict(a=a, b=b, incoming=incoming)
+
+
+# small parity cases of the column-dual schedules (N/P a multiple of 8)
+SMALL_AG_ROTB = [
+    AgCase("agb_bf16_p4_small", M=200, N=4 * 64, K=264, P=4, rank=1, dist="u11"),
+    AgCase("agb_bf16_p8_kn_small", M=136, N=8 * 40, K=192, P=8, rank=5, b_layout="kn", dist="n05"),
+    AgCase("agb_e4m3_p4_small", M=96, N=4 * 56, K=512, P=4, rank=3, dtype="e4m3", dist="n05", beta=0.0),
+    AgCase("agb_bf16_p2_medium", M=3000, N=2 * 1024, K=512, P=2, rank=0, dist="u11", alpha=0.5),
+    AgCase("agb_bf16_p4_kn_medium", M=2048, N=4 * 512, K=1024, P=4, rank=2, b_layout="kn", dist="n05"),
+]
+SMALL_RS_TILEB = [
+    RsCase("rsb_bf16_p4_small", M=136, N=4 * 64, K=264, P=4, rank=2, std=0.5),
+    RsCase("rsb_bf16_p8_kn_small", M=100, N=8 * 48, K=192, P=8, rank=7, b_layout="kn", std=0.5),
+    RsCase("rsb_bf16_p4_medium", M=2000, N=4 * 768, K=512, P=4, rank=1, std=0.5),
+]
 
 
 # --------------------------------------------------------------------------

@@ -59,6 +59,11 @@ def ag(**kw):
     (dict(workspace_bytes=10), tp.ERR_WORKSPACE),
     (dict(flags=1 << 20), tp.ERR_INVALID),
     (dict(flags=tp.COPY_SDMA | tp.COPY_SHADER), tp.ERR_INVALID),
+    (dict(schedule=2), tp.ERR_INVALID),
+    (dict(schedule=tp.ROTATE_B), tp.ERR_INVALID),                   # b_slices NULL
+    (dict(schedule=tp.ROTATE_B, N=255), tp.ERR_INVALID),            # N % P
+    (dict(schedule=tp.ROTATE_B, N=2 * 12), tp.ERR_UNSUPPORTED),     # N/P % 8
+    (dict(schedule=tp.ROTATE_B, epilogue=tp.EPI_SWIGLU), tp.ERR_UNSUPPORTED),
     (dict(epilogue=tp.EPI_SWIGLU, N=255), tp.ERR_INVALID),
 ])
 def test_ag_validation_rejects_before_enqueue(kw, status):
@@ -98,3 +103,27 @@ def test_rs_and_ffn_and_permute_validation():
     assert tp.lib().combine_permute(sp, FAKE + 0x200000, 2, 2, 1, 2, 4, 2, None) == tp.ERR_INVALID   # rank
     assert tp.lib().dispatch_permute(sp, FAKE, 2, 0, 1, 2, 4, 2, None) == tp.ERR_INVALID             # aliasing
     assert tp.lib().dispatch_permute(sp, FAKE + 0x200000, 2, 0, 1, 2, 4, 3, None) == tp.ERR_INVALID  # elem size
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of tpg_ag_args / tpg_rs_args / tpg_ffn_args have
+    the C header's field offsets and sizes (compiled with the host gcc)."""
+    import subprocess
+    structs = {"tpg_ag_args": tp.AgArgs, "tpg_rs_args": tp.RsArgs, "tpg_ffn_args": tp.FfnArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tpgemm.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.split("\n") if l)
+    for cname, cls in structs.items():
+        assert int(out[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(out[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
