@@ -308,6 +308,35 @@ def bench_swiglu(case, args):
     return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1))
 
 
+def bench_column_duals(args):
+    """The column-dual schedules at the e4m3 AG and bf16 RS workload shapes:
+    rotating B (A local 8192 x 8192, B as 8 slices of 128 x 8192) and tiled B
+    (8 column blocks of 1024 of the 8192 x 8192 x 3584 partial)."""
+    out = {}
+    c2 = W.AgCase("agb", M=8192, N=1024, K=8192, P=8, dtype="e4m3", dist="n05", beta=1.0)
+    inp = W.ag_rotb_inputs(c2)
+    a, bs, c = dev(inp["a"]), [dev(x) for x in inp["b_slices"]], dev(inp["c"])
+    d = torch.empty((c2.M, c2.N), dtype=torch.int16, device="cuda")
+    ag = tp.prepare_stage_ag(a, bs, c, d, M=c2.M, N=c2.N, K=c2.K, dtype=tp.E4M3, schedule=tp.ROTATE_B,
+                             flags=tp.UNSTAGED)
+    ms = time_steps(lambda: ag(flags=0), args.steps, args.warmup)
+    mu = time_steps(lambda: ag(flags=tp.UNSTAGED), args.steps, args.warmup)
+    out["ag_e4m3_rotb_p8_8192x1024x8192"] = dict(us=round(ms * 1e3, 1), tflops=round(c2.flop / (ms * 1e-3) / 1e12, 1),
+                                                 us_unstaged=round(mu * 1e3, 1))
+    c3 = W.RsCase("rsb", M=8192, N=8192, K=3584, P=8)
+    inp = W.rs_tileb_inputs(c3)
+    a, b = dev(inp["a"]), dev(inp["b"])
+    inc = [dev(x) if x is not None else None for x in inp["incoming"]]
+    d = torch.empty((c3.M, c3.N), dtype=torch.int16, device="cuda")
+    rs = tp.prepare_stage_rs(a, b, inc, d, M=c3.M, N=c3.N, K=c3.K, P=c3.P, schedule=tp.TILE_B, flags=tp.UNSTAGED)
+    steps = max(5, args.steps // 2)
+    ms = time_steps(lambda: rs(flags=0), steps, 3)
+    mu = time_steps(lambda: rs(flags=tp.UNSTAGED), steps, 3)
+    out["rs_bf16_tileb_p8_8192x8192x3584"] = dict(us=round(ms * 1e3, 1), tflops=round(c3.flop / (ms * 1e-3) / 1e12, 1),
+                                                  us_unstaged=round(mu * 1e3, 1))
+    return out
+
+
 def bench_small_ag(case, args):
     inp, call, _, _ = setup_ag(case)
     ms = time_steps(lambda: call(0), args.steps, args.warmup)
@@ -365,6 +394,7 @@ def main():
         detail["ag_bf16_p2_256x256x512"] = bench_small_ag(W.C1, args)
         detail["rs_bf16_p8_8192x8192x3584"] = bench_rs(W.C3, args)
         detail["swiglu_p8_s1024_d4096_f1792"] = bench_swiglu(W.C5, args)
+        detail.update(bench_column_duals(args))
         log(f"[other] {json.dumps({k: detail[k] for k in ('ag_bf16_p2_256x256x512', 'rs_bf16_p8_8192x8192x3584', 'swiglu_p8_s1024_d4096_f1792')})}")
 
     cpu = None
