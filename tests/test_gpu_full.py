@@ -120,3 +120,57 @@ def test_full_swiglu_block():
     assert_parity(host_f64(h)[rows], h_ref, "h")
     out_ref = h_ref @ oracle.decode_bf16(inp["w2"])
     assert_parity(host_f64(out)[rows], out_ref, "partial blocks")
+
+
+def test_full_ag_rotb_e4m3():
+    """Rotating B at the e4m3 all-gather shape: A local (8192 x 8192), B as 8
+    slices of (128 x 8192); every output column block comes from its own
+    slice."""
+    case = W.AgCase("agb_e4m3_p8_8192x1024x8192", M=8192, N=1024, K=8192, P=8, rank=5, dtype="e4m3",
+                    dist="n05", beta=1.0)
+    say(f"full: {case.name} generate")
+    inp = W.ag_rotb_inputs(case)
+    a, bs, c = dev(inp["a"]), [dev(x) for x in inp["b_slices"]], dev(inp["c"])
+    kw = dict(M=case.M, N=case.N, K=case.K, rank=case.rank, dtype=tp.E4M3, alpha=case.alpha, beta=case.beta,
+              schedule=tp.ROTATE_B)
+    d = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} staged")
+    tp.stage_ag(a, bs, c, d, **kw)
+    torch.cuda.synchronize()
+    rows = sample_rows(case.M, 1024)
+    ref = oracle.gemm_ag_rotb_rows(inp["a"], inp["b_slices"], inp["c"], case.alpha, case.beta, "e4m3", "nk", rows)
+    assert_parity(host_f64(d)[rows], ref, case.name)
+    d2 = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} unstaged")
+    tp.stage_ag(a, bs, c, d2, flags=tp.UNSTAGED, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(d, d2)
+
+
+def test_full_rs_tileb_bf16():
+    """Tiled B at the bf16 reduce-scatter shape: 8 column blocks of 1024 of
+    the (8192 x 8192) partial, K = 3584; the incoming partials land on the
+    own column block only."""
+    case = W.RsCase("rsb_bf16_p8_8192x8192x3584", M=8192, N=8192, K=3584, P=8, rank=6)
+    say(f"full: {case.name} generate")
+    inp = W.rs_tileb_inputs(case)
+    a, b = dev(inp["a"]), dev(inp["b"])
+    inc = [dev(x) if x is not None else None for x in inp["incoming"]]
+    kw = dict(M=case.M, N=case.N, K=case.K, P=case.P, rank=case.rank, schedule=tp.TILE_B)
+    d = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} staged")
+    tp.stage_rs(a, b, inc, d, **kw)
+    torch.cuda.synchronize()
+    rows = sample_rows(case.M, 1024)
+    ref = oracle.gemm_rs_tileb_rows(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P, "nk", rows)
+    got = host_f64(d)[rows]
+    n = case.N // case.P
+    own = slice(case.rank * n, (case.rank + 1) * n)
+    emitted = np.r_[0:case.rank * n, (case.rank + 1) * n:case.N]
+    assert_parity(got[:, emitted], ref[:, emitted], "emitted column blocks")
+    assert_parity(got[:, own], ref[:, own], "own column block")
+    d2 = bf16_empty(case.M, case.N)
+    say(f"full: {case.name} unstaged")
+    tp.stage_rs(a, b, inc, d2, flags=tp.UNSTAGED, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(d, d2)
