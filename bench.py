@@ -103,6 +103,53 @@ def time_flushed(fn, steps, warmup, scratch):
                 median=float(np.median(times)))
 
 
+def time_sustained(fn, seconds=1.0, batch=50):
+    """Throughput of back-to-back calls held for about `seconds` (the clocks
+    the chip settles at under sustained load): ms per call over the whole run."""
+    fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    calls, t0 = 0, time.perf_counter()
+    s.record()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn()
+        calls += batch
+        torch.cuda.synchronize()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / calls, calls
+
+
+def measure_mfma_peaks():
+    """The matrix cores' attainable rate on this chip: a register-only MFMA
+    loop over every CU (no memory traffic), timed with events, plus the
+    engine clock it ran at (shader-clock over wall-clock ticks)."""
+    cus, clk_khz, wall_khz = tp.device_info()
+    blocks = 2 * cus                       # 16 waves per CU
+    sink = torch.zeros(blocks * 8 * 2, dtype=torch.int64, device="cuda")
+    out = dict(cus=cus, spec_clock_mhz=round(clk_khz / 1e3), wall_clock_mhz=round(wall_khz / 1e3, 1))
+    for name, dt, iters in (("e4m3", tp.E4M3, 16000), ("bf16", tp.BF16, 32000)):
+        tp.mfma_probe(dt, iters // 2, blocks, sink)              # clocks settle
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            flop = tp.mfma_probe(dt, iters, blocks, sink)
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e)
+            if best is None or ms < best[0]:
+                ticks = sink.view(-1, 2).cpu().numpy().astype(np.float64)
+                best = (ms, flop, float(np.median(ticks[:, 0] / ticks[:, 1])) * wall_khz / 1e3)
+        ms, flop, mhz = best
+        spec = PEAK_TFLOPS["fp8_e4m3" if name == "e4m3" else "bf16"]
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = dict(tflops=round(tf, 1), frac_of_spec=round(tf / spec, 3), clock_mhz=round(mhz))
+    return out
+
+
 def stored_traffic(case_name):
     """HBM bytes per stage-GEMM launch from the committed rocprofv3 counter
     summary, or None when the kernel source changed since it was taken."""
@@ -240,9 +287,11 @@ def bench_ag(case, args, detail):
         hidden = 1.0 - (ms - t_compute) / t_copy if t_copy > 0 else None
         hidden_sdma = 1.0 - (t_sdma - t_compute) / t_copy_sdma if t_copy_sdma > 0 else None
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        flushed = time_flushed(lambda: call(0), max(args.steps, 10), 2, scratch)
+        flushed = time_flushed(lambda: call(0), max(args.steps, 100), 2, scratch)
         del scratch
+        t_sus, n_sus = time_sustained(lambda: call(0))
         detail.update({
+            "sustained_1s": dict(calls=n_sus, us=round(t_sus * 1e3, 2), tflops=round(flop / (t_sus * 1e-3) / 1e12, 1)),
             "us_staged": round(ms * 1e3, 2),
             "us_compute_only": round(t_compute * 1e3, 2),
             "us_deliveries_alone": round(t_copy * 1e3, 2),
@@ -387,6 +436,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst, evict
     r = bench_ag(case, args, detail)
+    probe = measure_mfma_peaks()
+    detail["mfma_probe"] = probe
+    log(f"[probe] {json.dumps(probe)}")
+    measured = probe["e4m3" if r["dtype"] == "fp8_e4m3" else "bf16"]["tflops"]
+    r["roofline"]["measured_peak"] = measured
+    r["roofline"]["frac_of_measured_peak"] = round(r["roofline"]["achieved"] / measured, 4)
     if not args.no_ffn and not args.quick:
         detail["ffn_layer"] = bench_ffn(W.C4, args)
         log(f"[ffn] {detail['ffn_layer']}")
@@ -418,7 +473,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": case.name, "M": case.M, "N": case.N, "K": case.K, "P": case.P,
                    "rank": case.rank, "alpha": case.alpha, "beta": case.beta, "b_layout": case.b_layout,
-                   "pct_mfma_peak": round(100.0 * r["value"] / peak, 2), "parallelism": "tp8 rank share"},
+                   "pct_mfma_peak": round(100.0 * r["value"] / peak, 2),
+                   "pct_measured_mfma_peak": round(100.0 * r["value"] / measured, 2),
+                   "parallelism": "tp8 rank share"},
         "roofline": r["roofline"],
         "cpu_baseline": cpu,
         "detail": detail,

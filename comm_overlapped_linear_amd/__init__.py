@@ -94,6 +94,8 @@ def lib():
             ("tpg_last_error", [], ctypes.c_char_p),
             ("tpg_release_caches", [], None),
             ("tpg_profile_read", [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double), i32], i32),
+            ("tpg_device_info", [ctypes.POINTER(i32)] * 3, i32),
+            ("tpg_mfma_probe", [i32, i32, i32, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double), vp], i32),
         ]:
             fn = getattr(L, name)
             fn.argtypes = argt
@@ -315,3 +317,19 @@ def profile_read(cap=4096):
     fl = (ctypes.c_double * cap)()
     n = lib().tpg_profile_read(ms, fl, cap)
     return [(ms[i], fl[i]) for i in range(n)]
+
+
+def device_info():
+    """(compute units, peak engine clock kHz, wall-clock counter kHz) of the current device."""
+    v = [ctypes.c_int32() for _ in range(3)]
+    _check(lib().tpg_device_info(*[ctypes.byref(x) for x in v]))
+    return tuple(x.value for x in v)
+
+
+def mfma_probe(dtype, iters, blocks, sink, stream=None):
+    """Enqueues the register-only MFMA loop; returns its algorithmic flop
+    count. `sink` is a device tensor of at least blocks * 8 * 16 bytes."""
+    flop = ctypes.c_double()
+    _check(lib().tpg_mfma_probe(dtype, iters, blocks, _ptr(sink), sink.numel() * sink.element_size(),
+                                ctypes.byref(flop), _stream(stream)))
+    return flop.value

@@ -1099,6 +1099,39 @@ tpg_status combine_permute(const void* const* src, void* dst, int32_t P, int32_t
   return guarded([&]() { return permute_common(false, src, dst, P, rank, B, T, D, elem_bytes, stream); });
 }
 
+tpg_status tpg_device_info(int32_t* cus, int32_t* clock_khz, int32_t* wall_clock_khz) {
+  return guarded([&]() -> tpg_status {
+    int dev = 0, v = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (cus) *cus = tpg::device_cus();
+    if (clock_khz) {
+      HIP_TRY(hipDeviceGetAttribute(&v, hipDeviceAttributeClockRate, dev));
+      *clock_khz = v;
+    }
+    if (wall_clock_khz) {
+      HIP_TRY(hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev));
+      *wall_clock_khz = v;
+    }
+    return TPG_OK;
+  });
+}
+
+tpg_status tpg_mfma_probe(int32_t dtype, int32_t iters, int32_t blocks, uint64_t* sink, size_t sink_bytes,
+                          double* flop, void* stream) {
+  return guarded([&]() -> tpg_status {
+    if (dtype != TPG_BF16 && dtype != TPG_E4M3) return fail(TPG_ERR_UNSUPPORTED, "mfma probe: dtype must be bf16 or e4m3");
+    if (iters < 1 || iters > (1 << 24)) return fail(TPG_ERR_INVALID, "mfma probe: iters must be in [1, 2^24]");
+    if (blocks < 1 || blocks > 65536) return fail(TPG_ERR_INVALID, "mfma probe: blocks must be in [1, 65536]");
+    const size_t need = size_t(blocks) * (tpg::kProbeThreads / 64) * 2 * sizeof(uint64_t);
+    if (!sink || sink_bytes < need) return fail(TPG_ERR_WORKSPACE, "mfma probe: sink needs " + std::to_string(need) + " bytes");
+    if (reinterpret_cast<uintptr_t>(sink) % 8) return fail(TPG_ERR_UNSUPPORTED, "mfma probe: sink must be 8-byte aligned");
+    if (flop) *flop = tpg::probe_flop_per_iter(dtype) * double(blocks) * iters;
+    HIP_TRY(tpg::launch_mfma_probe(dtype, iters, blocks, reinterpret_cast<unsigned long long*>(sink),
+                                   static_cast<hipStream_t>(stream)));
+    return TPG_OK;
+  });
+}
+
 const char* tpg_last_error(void) { return g_err.c_str(); }
 
 void tpg_release_caches(void) {

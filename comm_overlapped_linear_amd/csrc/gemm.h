@@ -58,6 +58,13 @@ int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget);
 // shapes and alignment are the caller's job (api.cpp validates every call).
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);
 
+// Register-only MFMA rate probe: `blocks` workgroups of kProbeThreads, each
+// wave running `iters` iterations of four independent MFMAs; sink holds two
+// uint64 per wave (shader-clock ticks, wall-clock ticks over the loop).
+constexpr int kProbeThreads = 512;
+double probe_flop_per_iter(int dtype);    // per workgroup and iteration
+hipError_t launch_mfma_probe(int dtype, int iters, int blocks, unsigned long long* sink, hipStream_t s);
+
 // Row-wise LayerNorm(u) * silu(LayerNorm(g)) over z = [u | g] (each H wide).
 hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t ldh, int rows, int H,
                           const uint16_t* gx, const uint16_t* bx, const uint16_t* gg,

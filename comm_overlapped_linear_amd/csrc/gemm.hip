@@ -879,9 +879,60 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   }
 }
 
+// Register-only MFMA loop: the matrix cores' attainable rate at the clocks
+// the chip holds under this load, with no memory traffic. Each wave keeps
+// four independent accumulators in flight, so the MFMA pipe never waits on
+// a result. Lane 0 of every wave records its shader-clock and wall-clock
+// ticks over the loop (the wall clock runs at a fixed rate), from which the
+// host derives the engine clock.
+template <typename Op>
+__global__ void __launch_bounds__(kProbeThreads) mfma_probe_kernel(unsigned long long* sink, int iters) {
+  typedef typename Op::frag_t frag_t;
+  struct Words { unsigned v[sizeof(frag_t) / 4]; };
+  const int lane = threadIdx.x & 63;
+  Words wx, wy;
+  for (int i = 0; i < int(sizeof(frag_t) / 4); ++i) {
+    // small nonzero operands (bf16 pairs near 2^-7, e4m3 bytes 0.5 .. 0.875)
+    const unsigned w = Op::kElemBytes == 2 ? 0x3C003C00u + (lane & 15) * 0x00010001u
+                                           : 0x30303030u + (lane & 7) * 0x01010101u;
+    wx.v[i] = w;
+    wy.v[i] = w ^ 0x00010001u;
+  }
+  const frag_t x = __builtin_bit_cast(frag_t, wx), y = __builtin_bit_cast(frag_t, wy);
+  f32x16_t a0 = {}, a1 = {}, a2 = {}, a3 = {};
+  const unsigned long long c0 = clock64(), r0 = wall_clock64();
+  for (int it = 0; it < iters; ++it) {
+    a0 = Op::mma(x, y, a0);
+    a1 = Op::mma(y, x, a1);
+    a2 = Op::mma(x, x, a2);
+    a3 = Op::mma(y, y, a3);
+  }
+  const unsigned long long c1 = clock64(), r1 = wall_clock64();
+  float acc = 0.0f;
+  for (int e = 0; e < 16; ++e) acc += a0[e] + a1[e] + a2[e] + a3[e];
+  const int wave = blockIdx.x * (kProbeThreads / 64) + threadIdx.x / 64;
+  if (lane == 0) {
+    sink[2 * wave] = c1 - c0;
+    sink[2 * wave + 1] = r1 - r0;
+  }
+  if (acc == -1.0f) sink[2 * wave] = 0;   // keeps every accumulator live
+}
+
 }  // namespace
 
 int device_cus() { return cu_count(); }
+
+double probe_flop_per_iter(int dtype) {
+  return double(kProbeThreads / 64) * 4 * (dtype == kE4m3 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16);
+}
+
+hipError_t launch_mfma_probe(int dtype, int iters, int blocks, unsigned long long* sink, hipStream_t s) {
+  if (dtype == kE4m3)
+    hipLaunchKernelGGL(mfma_probe_kernel<OpE4m3>, dim3(blocks), dim3(kProbeThreads), 0, s, sink, iters);
+  else
+    hipLaunchKernelGGL(mfma_probe_kernel<OpBf16>, dim3(blocks), dim3(kProbeThreads), 0, s, sink, iters);
+  return hipGetLastError();
+}
 
 int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget) {
   const int t = pick_tile(M, N, epi, batch, cu_budget);

@@ -270,6 +270,29 @@ tpg_status combine_permute(const void* const* src, void* dst, int32_t P, int32_t
                            int64_t B, int64_t T, int64_t D, int32_t elem_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Measurement aids, outside the staged GEMM: the rate the matrix cores
+ * reach on this chip, against which the stage GEMMs' percent-of-peak figures
+ * (the pages' measurement of GEMM efficiency as a fraction of the MMA peak)
+ * can also be read.
+ * tpg_device_info: compute units, peak engine clock and wall-clock counter
+ *   rate (both kHz) of the current device; any pointer may be NULL.
+ * tpg_mfma_probe: enqueues on `stream` `blocks` workgroups of 512 threads
+ *   whose waves run `iters` iterations of four independent 32x32 MFMAs of
+ *   `dtype` (TPG_BF16: 32x32x16, TPG_E4M3: 32x32x64) on register operands,
+ *   with no memory traffic. *flop (if not NULL) receives the algorithmic
+ *   flop count of the launch; the caller times it. `sink` is a device buffer
+ *   of at least blocks * 8 * 16 bytes, 8-byte aligned: wave w writes
+ *   sink[2w] = shader-clock ticks and sink[2w+1] = wall-clock ticks over its
+ *   loop (their ratio times the wall-clock rate is the engine clock).
+ *   Errors: TPG_ERR_UNSUPPORTED (dtype, alignment), TPG_ERR_INVALID (iters
+ *   outside [1, 2^24], blocks outside [1, 65536]), TPG_ERR_WORKSPACE (sink
+ *   too small or NULL).
+ * ---------------------------------------------------------------------- */
+tpg_status tpg_device_info(int32_t* cus, int32_t* clock_khz, int32_t* wall_clock_khz);
+tpg_status tpg_mfma_probe(int32_t dtype, int32_t iters, int32_t blocks, uint64_t* sink, size_t sink_bytes,
+                          double* flop, void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * tpg_last_error: message of the last failing call on this host thread
  *   (empty string if none); valid until the next call on the thread.

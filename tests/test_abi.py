@@ -127,3 +127,15 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert int(out[cname]) == ctypes.sizeof(cls), cname
         for f, _ in cls._fields_:
             assert int(out[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
+
+
+def test_mfma_probe_validation():
+    L = tp.lib()
+    flop = ctypes.c_double()
+    call = lambda dt, it, bl, sink, nb: L.tpg_mfma_probe(dt, it, bl, sink, nb, ctypes.byref(flop), None)
+    assert call(7, 10, 1, FAKE, 1 << 20) == tp.ERR_UNSUPPORTED
+    assert call(tp.BF16, 0, 1, FAKE, 1 << 20) == tp.ERR_INVALID
+    assert call(tp.BF16, 10, 0, FAKE, 1 << 20) == tp.ERR_INVALID
+    assert call(tp.E4M3, 10, 4, FAKE, 4 * 8 * 16 - 8) == tp.ERR_WORKSPACE
+    assert call(tp.E4M3, 10, 4, None, 1 << 20) == tp.ERR_WORKSPACE
+    assert call(tp.E4M3, 10, 4, FAKE + 4, 1 << 20) == tp.ERR_UNSUPPORTED
