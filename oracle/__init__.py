@@ -20,7 +20,8 @@ Sources (pages of the reference set, cited by title and section):
     dispatch/combine and its P=2 worked example).
   * "Add dist GEMM attention and FFN backend" (torchtitan PR #4044),
     Structure: AllGatherLinear / LinearReduceScatter / AllGatherLinearMulti
-    for the SwiGLU w1/w3 pair; gathered rows ordered (rank, batch, seq).
+    for the SwiGLU w1/w3 pair; gathered rows ordered (rank, batch, seq);
+    the backward of the two linears (backward.py).
 
 Every function is pinned by a CPU test against something other than itself
 (closed forms, brute-force loops, library routines, the pages' worked
@@ -32,3 +33,4 @@ from .gemm import (ag_stage_order, rs_block_order, gemm_ag, gemm_ag_rows, gemm_r
 from .ffn import layer_norm, silu, ffn_slot_forward, ffn_slot_rows
 from .swiglu import swiglu_hidden, swiglu_hidden_rows, swiglu_block
 from .permute import dispatch, combine
+from .backward import wgrad, wgrad_staged, wgrad_rows

@@ -276,6 +276,53 @@ def swiglu_inputs(case: SwigluCase, seed: int = SEED):
 
 
 # --------------------------------------------------------------------------
+# weight gradient of the all-gather / reduce-scatter linears
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class WgCase:
+    name: str
+    M: int          # contraction rows (tokens): P slices of m = M/P
+    N: int          # output rows (columns of G)
+    K: int          # output columns (columns of X)
+    P: int
+    rank: int = 0
+    gathered: str = "x"     # which operand arrives as P row slices: "x" or "g"
+    alpha: float = 1.0
+
+    @property
+    def m(self):
+        return self.M // self.P
+
+    @property
+    def flop(self):
+        return 2.0 * self.M * self.N * self.K
+
+
+def wgrad_inputs(case: WgCase, seed: int = SEED):
+    """dict(local, slices): with gathered "x", local is G (M, N) (the output
+    gradient, this rank's stream) and slices are X's P row slices (m, K),
+    slice s from rank s's stream; with gathered "g", local is X (M, K) and
+    slices are G's (m, N). All N(0, 1), bf16."""
+    if case.gathered == "x":
+        local = normal_bf16(stream_key(seed + case.rank, "wg.g"), (case.M, case.N))
+        slices = [normal_bf16(stream_key(seed + s, "wg.x"), (case.m, case.K)) for s in range(case.P)]
+    else:
+        local = normal_bf16(stream_key(seed + case.rank, "wg.x"), (case.M, case.K))
+        slices = [normal_bf16(stream_key(seed + s, "wg.g"), (case.m, case.N)) for s in range(case.P)]
+    return dict(local=local, slices=slices)
+
+
+# small parity cases (m a multiple of 64; N and K multiples of 8 with ragged tiles)
+SMALL_WGRAD = [
+    WgCase("wg_p4_x_small", M=4 * 64, N=200, K=264, P=4, rank=1),
+    WgCase("wg_p8_g_small", M=8 * 64, N=136, K=328, P=8, rank=5, gathered="g", alpha=0.5),
+    WgCase("wg_p8_x_wrap", M=8 * 128, N=520, K=264, P=8, rank=3),
+    WgCase("wg_p2_x_medium", M=2 * 1024, N=1120, K=2088, P=2, rank=1),
+    WgCase("wg_p4_g_medium", M=4 * 512, N=1032, K=1536, P=4, rank=2, gathered="g"),
+]
+
+
+# --------------------------------------------------------------------------
 # the five workloads at full size, and small parity variants with ragged tails
 # --------------------------------------------------------------------------
 C1 = AgCase("ag_bf16_p2_256x256x512", M=256, N=256, K=512, P=2, dtype="bf16",
