@@ -7,8 +7,9 @@ tensors may be torch.bfloat16 or raw int16/uint16 bits, e4m3 tensors
 torch.float8_e4m3fn or raw uint8 bits.
 
 The names follow the C ABI in include/tpgemm.h:
-    stage_ag, stage_rs, ffn_slot_forward, dispatch_permute, combine_permute
-(plus the *_workspace_size queries, last_error, release_caches, profile_read).
+    stage_ag, stage_rs, stage_wgrad, ffn_slot_forward, dispatch_permute, combine_permute
+(plus the *_workspace_size queries, last_error, release_caches, profile_read,
+device_info, mfma_probe).
 """
 import ctypes
 import os
@@ -24,6 +25,7 @@ B_NK, B_KN = 0, 1
 EPI_ALPHA_BETA, EPI_SWIGLU = 0, 1
 ROTATE_A, ROTATE_B = 0, 1       # all-gather schedules
 TILE_A, TILE_B = 0, 1           # reduce-scatter schedules
+GATHER_X, GATHER_G = 0, 1       # weight gradient: which operand arrives as slices
 UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE, FORCE_GRAPH = 1, 2, 4, 8, 16, 32, 64
 DEBUG_HOLD_DELIVERIES, COPY_SHADER = 128, 256
 
@@ -60,6 +62,15 @@ class RsArgs(ctypes.Structure):
                 ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
+class WgArgs(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("P", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("gathered", ctypes.c_int32), ("groups", ctypes.c_int32),
+                ("local", ctypes.c_void_p), ("slices", ctypes.POINTER(ctypes.c_void_p)),
+                ("d", ctypes.c_void_p), ("alpha", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class FfnArgs(ctypes.Structure):
     _fields_ = [("PB", ctypes.c_int64), ("L", ctypes.c_int64), ("D", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("x", ctypes.c_void_p), ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
@@ -87,6 +98,8 @@ def lib():
             ("tpgemm_stage_ag_workspace_size", [ctypes.POINTER(AgArgs)], ctypes.c_size_t),
             ("tpgemm_stage_rs", [ctypes.POINTER(RsArgs), vp], i32),
             ("tpgemm_stage_rs_workspace_size", [ctypes.POINTER(RsArgs)], ctypes.c_size_t),
+            ("tpgemm_stage_wgrad", [ctypes.POINTER(WgArgs), vp], i32),
+            ("tpgemm_stage_wgrad_workspace_size", [ctypes.POINTER(WgArgs)], ctypes.c_size_t),
             ("ffn_slot_forward", [ctypes.POINTER(FfnArgs), vp], i32),
             ("ffn_slot_forward_workspace_size", [ctypes.POINTER(FfnArgs)], ctypes.c_size_t),
             ("dispatch_permute", [ctypes.POINTER(vp), vp, i32, i32, i64, i64, i64, i32, vp], i32),
@@ -234,6 +247,33 @@ def stage_rs(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK
     _check(lib().tpgemm_stage_rs(ctypes.byref(args), _stream(stream)))
 
 
+def wgrad_args(local, slices, d, *, M, N, K, rank=0, gathered=None, alpha=1.0, flags=0, groups=0):
+    """Argument struct of tpgemm_stage_wgrad: d (N, K) = alpha * G^T X over
+    M token rows; `slices` are the P row slices of the gathered operand."""
+    sl = _ptr_array(slices)
+    args = WgArgs(M=M, N=N, K=K, P=len(slices), rank=rank, gathered=GATHER_X if gathered is None else gathered,
+                  groups=groups, local=_ptr(local), slices=ctypes.cast(sl, ctypes.POINTER(ctypes.c_void_p)),
+                  d=_ptr(d), alpha=alpha, flags=flags)
+    args._keep = sl
+    return args
+
+
+def stage_wgrad_workspace_size(args):
+    return lib().tpgemm_stage_wgrad_workspace_size(ctypes.byref(args))
+
+
+def stage_wgrad(local, slices, d, *, M, N, K, rank=0, gathered=None, alpha=1.0, flags=0, groups=0,
+                workspace=None, stream=None):
+    """Staged weight gradient d = alpha * G^T X (see tpgemm.h and wgrad_args)."""
+    args = wgrad_args(local, slices, d, M=M, N=N, K=K, rank=rank, gathered=gathered, alpha=alpha,
+                      flags=flags, groups=groups)
+    need = stage_wgrad_workspace_size(args)
+    ws = _workspace(workspace, need)
+    args.workspace = _ptr(ws) if ws is not None else None
+    args.workspace_bytes = ws.numel() if ws is not None else 0
+    _check(lib().tpgemm_stage_wgrad(ctypes.byref(args), _stream(stream)))
+
+
 def ffn_args(x, w1, b1, wout, bout, gx, bx, gg, bg, y, *, PB, L, D, H, eps=1e-5, flags=0):
     return FfnArgs(PB=PB, L=L, D=D, H=H, x=_ptr(x), w1=_ptr(w1), b1=_ptr(b1), wout=_ptr(wout),
                    bout=_ptr(bout), gx=_ptr(gx), bx=_ptr(bx), gg=_ptr(gg), bg=_ptr(bg), eps=eps,
@@ -300,6 +340,12 @@ def prepare_stage_rs(a, b, incoming, d, *, workspace=None, **kw):
     args = rs_args(a, b, incoming, d, **kw)
     ws = _attach_workspace(args, stage_rs_workspace_size, workspace)
     return Prepared(lib().tpgemm_stage_rs, args, (a, b, incoming, d, ws))
+
+
+def prepare_stage_wgrad(local, slices, d, *, workspace=None, **kw):
+    args = wgrad_args(local, slices, d, **kw)
+    ws = _attach_workspace(args, stage_wgrad_workspace_size, workspace)
+    return Prepared(lib().tpgemm_stage_wgrad, args, (local, slices, d, ws))
 
 
 def prepare_ffn_slot_forward(x, w1, b1, wout, bout, gx, bx, gg, bg, y, *, workspace=None, **kw):

@@ -145,6 +145,9 @@ int elem_bytes(int32_t dt) { return dt == TPG_E4M3 ? 1 : 2; }
 
 bool fits_int(int64_t v) { return v >= 0 && v < (int64_t(1) << 31); }
 
+// gemm_on layout of the weight gradient: A and B both contraction-major.
+constexpr int kLayoutAT = 2;
+
 struct Launch {
   hipStream_t root;
   bool profile;
@@ -164,7 +167,7 @@ tpg_status gemm_on(Ctx& cx, const Launch& L, hipStream_t s, const tpg::GemmParam
     }
     HIP_TRY(hipEventRecord(rec.a, s));
   }
-  hipError_t e = tpg::launch_gemm(p, dtype, layout, epi, s);
+  hipError_t e = layout == kLayoutAT ? tpg::launch_gemm_at(p, s) : tpg::launch_gemm(p, dtype, layout, epi, s);
   if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("gemm launch failed: ") + hipGetErrorString(e));
   if (L.profile) {
     HIP_TRY(hipEventRecord(rec.b, s));
@@ -875,6 +878,208 @@ std::string rs_key(const tpg_rs_args& a) {
   return os.str();
 }
 
+// ---------------------------------------------------------------- weight gradient
+// d (N, K) = alpha * sum_i G[i, n] X[i, k] over M token rows, one operand
+// arriving as P row slices. On the kernel: D rows = n, D columns = k, the
+// contraction runs over token rows; A = G read contraction-major (row stride
+// N), B = X in the (K, N) layout (row stride K).
+int64_t wg_width(const tpg_wg_args* a) { return a->gathered == TPG_GATHER_X ? a->K : a->N; }
+
+size_t wg_slice_bytes(const tpg_wg_args* a) { return size_t(a->M / a->P) * wg_width(a) * 2; }
+
+// Receive slots: (P-1) slices in ring order staged, P in rank order unstaged.
+size_t wg_recv(const tpg_wg_args* a) {
+  if (a->flags & TPG_NO_COPY) return 0;
+  return round_up(wg_slice_bytes(a) * ((a->flags & TPG_UNSTAGED) ? a->P : a->P - 1), 256);
+}
+
+// The fp32 partial exists when the call makes more than one launch: staged
+// with P > 1.
+bool wg_chain(const tpg_wg_args* a) { return !(a->flags & TPG_UNSTAGED) && a->P > 1; }
+
+size_t wg_ws(const tpg_wg_args* a) {
+  if (!a || a->P < 1 || a->P > kMaxP || a->M <= 0 || a->N <= 0 || a->K <= 0 || a->M % a->P) return 0;
+  return wg_recv(a) + (wg_chain(a) ? size_t(a->N) * a->K * 4 : 0);
+}
+
+tpg_status validate_wg(const tpg_wg_args* a, size_t need) {
+  if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
+  if (a->P < 1 || a->P > kMaxP) return fail(TPG_ERR_INVALID, "P must be in [1, 64]");
+  if (a->rank < 0 || a->rank >= a->P) return fail(TPG_ERR_INVALID, "rank must be in [0, P)");
+  if (a->M < 0 || a->N < 0 || a->K < 0) return fail(TPG_ERR_INVALID, "negative dimension");
+  if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
+  if (a->gathered != TPG_GATHER_X && a->gathered != TPG_GATHER_G) return fail(TPG_ERR_INVALID, "bad gathered");
+  if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
+    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
+  if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
+    return fail(TPG_ERR_UNSUPPORTED, "dimensions must be below 2^31");
+  const int64_t m = a->M / a->P;
+  if (m % 64) return fail(TPG_ERR_UNSUPPORTED, "M/P must be a multiple of 64");
+  if (a->N % 8 || a->K % 8) return fail(TPG_ERR_UNSUPPORTED, "N and K must be multiples of 8");
+  // the kernel's 31-bit offsets: 64 contraction rows of either operand plus one tile row
+  if (int64_t(64) * a->N * 2 + a->N * 2 >= (int64_t(1) << 31) || int64_t(64) * a->K * 2 + a->K * 2 >= (int64_t(1) << 31))
+    return fail(TPG_ERR_UNSUPPORTED, "N or K too large for the kernel's 31-bit offsets");
+  if (!a->d && a->N && a->K) return fail(TPG_ERR_INVALID, "D is NULL");
+  if (!aligned16(a->d)) return fail(TPG_ERR_UNSUPPORTED, "D not 16-byte aligned");
+  const size_t d_b = size_t(a->N) * a->K * 2;
+  std::vector<Range> inputs;
+  if (a->M > 0 && a->N > 0 && a->K > 0) {
+    const size_t local_b = size_t(a->M) * (a->gathered == TPG_GATHER_X ? a->N : a->K) * 2;
+    if (!a->local) return fail(TPG_ERR_INVALID, "local is NULL");
+    if (!aligned16(a->local)) return fail(TPG_ERR_UNSUPPORTED, "local not 16-byte aligned");
+    inputs.push_back({a->local, local_b});
+    if (!a->slices) return fail(TPG_ERR_INVALID, "slices is NULL");
+    const size_t slice_b = wg_slice_bytes(a);
+    for (int s = 0; s < a->P; ++s) {
+      if (!a->slices[s]) return fail(TPG_ERR_INVALID, "NULL slice");
+      if (!aligned16(a->slices[s])) return fail(TPG_ERR_UNSUPPORTED, "slice not 16-byte aligned");
+      inputs.push_back({a->slices[s], slice_b});
+    }
+  }
+  if (need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_wgrad_workspace_size()");
+  const Range dr{a->d, d_b}, wr{a->workspace, need};
+  for (const auto& r : inputs) {
+    if (overlaps(dr, r)) return fail(TPG_ERR_INVALID, "D overlaps an input");
+    if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
+  }
+  if (overlaps(dr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps D");
+  if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  if ((a->flags & TPG_UNSTAGED) && (a->flags & TPG_NO_COPY) && a->M > 0) {
+    const size_t slice_b = wg_slice_bytes(a);
+    for (int s = 1; s < a->P; ++s)
+      if (static_cast<const char*>(a->slices[s]) != static_cast<const char*>(a->slices[0]) + s * slice_b)
+        return fail(TPG_ERR_UNSUPPORTED, "UNSTAGED|NO_COPY needs the slices to be contiguous");
+  }
+  return TPG_OK;
+}
+
+// Launch chain. The local stage comes first, then the P-1 remote stages in
+// `groups` runs; every launch but the last writes the fp32 partial, every
+// launch but the first adds it (in place: each element is read and written
+// by the same thread). The chain runs on one compute stream; the deliveries
+// run on the root, each run gated by one event after its slices. With
+// TPG_NO_COPY the slices are read in place, one launch per stretch that is
+// contiguous in memory and does not wrap past slice P-1.
+tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
+  const int P = a.P, r = a.rank;
+  const int64_t m = a.M / P;
+  const bool gx = a.gathered == TPG_GATHER_X;
+  const int64_t lw = gx ? a.N : a.K;              // row width of the local operand
+  const size_t slice_b = wg_slice_bytes(&a);
+  const bool copies = !(a.flags & TPG_NO_COPY);
+  const hipMemcpyKind kind = copy_kind(a.flags, false);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  float* part = wg_chain(&a) ? reinterpret_cast<float*>(ws + wg_recv(&a)) : nullptr;
+  const char* loc = static_cast<const char*>(a.local);
+
+  tpg::GemmParams p = base_params();
+  p.M = static_cast<int>(a.N);
+  p.N = static_cast<int>(a.K);
+  p.lda = a.N;
+  p.ldb = a.K;
+  p.ldd = a.K;
+  p.ld_acc = a.K;
+  p.d = static_cast<uint16_t*>(a.d);
+  p.alpha = a.alpha;
+  p.beta = 0.0f;
+  p.vec_ok = 1;                                   // K % 8 == 0 (validated)
+  p.kwrap_rows = a.M;
+  // One launch: contraction over `rows` token rows, the gathered operand's
+  // rows contiguous at g, the local operand's from token row l0 on (wrapping
+  // past M back to row 0).
+  auto launch = [&](hipStream_t s, const void* g, int64_t l0, int64_t rows, bool first, bool last) {
+    tpg::GemmParams q = p;
+    q.K = static_cast<int>(rows);
+    const void* lp = loc + l0 * lw * 2;
+    const int wrap = l0 + rows > a.M ? static_cast<int>(a.M - l0) : 0;
+    if (gx) {
+      q.a = lp;
+      q.b = g;
+      q.a_kwrap = wrap;
+    } else {
+      q.a = g;
+      q.b = lp;
+      q.b_kwrap = wrap;
+    }
+    q.acc_in = first ? nullptr : part;
+    q.acc_out = last ? nullptr : part;
+    return gemm_on(cx, L, s, q, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA);
+  };
+
+  if (a.flags & TPG_UNSTAGED) {
+    const void* g = a.slices[0];
+    if (copies) {
+      for (int s = 0; s < P; ++s) HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.slices[s], slice_b, kind, L.root));
+      g = ws;
+    }
+    return launch(L.root, g, 0, a.M, true, true);
+  }
+  if (P == 1) return launch(L.root, a.slices[0], 0, m, true, true);
+
+  const int remote = P - 1;
+  const int G = a.groups > 0 ? std::min(a.groups, remote) : 1;
+  auto t0 = [&](int g) { return 1 + (g * remote) / G; };
+  auto adjacent = [&](int s, int run) {
+    for (int i = 1; i < run; ++i)
+      if (static_cast<const char*>(a.slices[s + i]) != static_cast<const char*>(a.slices[s]) + i * slice_b)
+        return false;
+    return true;
+  };
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : 2;
+  hipStream_t st[kStreams];
+  tpg_status stat = fork_streams(cx, L.root, ns, st);
+  if (stat != TPG_OK) return stat;
+  hipStream_t cs = st[ns - 1];                    // the chain's stream
+  // the local stage: no delivery needed
+  stat = launch(cs, a.slices[r], r * m, m, true, false);
+  if (stat != TPG_OK) return stat;
+  if (copies) {
+    stat = hold_deliveries(a.flags, L.root);
+    if (stat != TPG_OK) return stat;
+  }
+  for (int g = 0; g < G; ++g) {
+    const bool last_run = g == G - 1;
+    if (copies) {
+      for (int t = t0(g); t < t0(g + 1);) {
+        const int s = (r + t) % P;
+        int run = 1;
+        while (t + run < t0(g + 1) && s + run < P && adjacent(s, run + 1)) ++run;
+        HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.slices[s], run * slice_b, kind, L.root));
+        t += run;
+      }
+      if (ns > 1) {
+        HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
+        HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
+      }
+      const int s0 = (r + t0(g)) % P;
+      stat = launch(cs, ws + (t0(g) - 1) * slice_b, s0 * m, (t0(g + 1) - t0(g)) * m, false, last_run);
+      if (stat != TPG_OK) return stat;
+    } else {
+      for (int t = t0(g); t < t0(g + 1);) {
+        const int s = (r + t) % P;
+        int run = std::min(t0(g + 1) - t, P - s);
+        while (run > 1 && !adjacent(s, run)) --run;
+        const bool last = last_run && t + run == t0(g + 1);
+        stat = launch(cs, a.slices[s], s * m, run * m, false, last);
+        if (stat != TPG_OK) return stat;
+        t += run;
+      }
+    }
+  }
+  return join_streams(cx, L.root, ns, st);
+}
+
+std::string wg_key(const tpg_wg_args& a) {
+  std::ostringstream os;
+  os << "wg|";
+  put(os, a.M); put(os, a.N); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.gathered);
+  put(os, a.groups); put(os, a.local); put(os, a.d); put(os, a.alpha); put(os, a.flags); put(os, a.workspace);
+  for (int s = 0; a.slices && s < a.P; ++s) put(os, a.slices[s]);
+  return os.str();
+}
+
 // ---------------------------------------------------------------- FFN
 // Slots are pipelined over two compute streams, each with its own z / h
 // buffers: the LayerNorm pass of one slot (HBM-bound) overlaps the GEMMs of
@@ -1069,6 +1274,29 @@ tpg_status tpgemm_stage_rs(const tpg_rs_args* args, void* stream) {
       a.flags |= TPG_SERIAL_STAGES;
     return run_call(*cx, a.flags, rs_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_rs(*cx, a, L); });
+  });
+}
+
+size_t tpgemm_stage_wgrad_workspace_size(const tpg_wg_args* args) { return wg_ws(args); }
+
+tpg_status tpgemm_stage_wgrad(const tpg_wg_args* args, void* stream) {
+  return guarded([&]() -> tpg_status {
+    std::lock_guard<std::mutex> lk(g_mu);
+    tpg_status st = validate_wg(args, wg_ws(args));
+    if (st != TPG_OK) return st;
+    if (args->N == 0 || args->K == 0) return TPG_OK;       // empty output: nothing to enqueue
+    if (args->M == 0) {                                    // an empty sum
+      HIP_TRY(tpg::launch_fill_zero16(args->d, size_t(args->N) * args->K * 2, static_cast<hipStream_t>(stream)));
+      return TPG_OK;
+    }
+    Ctx* cx = nullptr;
+    st = get_ctx(&cx);
+    if (st != TPG_OK) return st;
+    tpg_wg_args a = *args;
+    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+      a.flags |= TPG_SERIAL_STAGES;
+    return run_call(*cx, a.flags, wg_key(a), static_cast<hipStream_t>(stream),
+                    [&](const Launch& L) { return enqueue_wg(*cx, a, L); });
   });
 }
 

@@ -42,6 +42,19 @@ struct GemmParams {
   // that run side by side each get their share, so that together they make
   // one wave of tiles instead of each sizing its tiles for the whole chip.
   int cu_budget;
+  // Contraction-major A (the weight gradient, launch_gemm_at): A is stored
+  // (K, M) row-major with row stride lda, B is (K, N). Contraction rows wrap:
+  // K-steps at contraction index >= a_kwrap (if > 0) read the A rows
+  // kwrap_rows earlier, and likewise b_kwrap for B, so a run of stages in
+  // ring order over one (tokens, .) tensor is one launch.
+  int a_kwrap, b_kwrap;
+  int64_t kwrap_rows;
+  // fp32 chains between launches that split one contraction (weight
+  // gradient only): acc_in (if set) is added before rounding, and acc_out (if
+  // set) receives the fp32 result instead of bf16 d. Row stride ld_acc.
+  const float* acc_in;
+  float* acc_out;
+  int64_t ld_acc;
 };
 
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };
@@ -58,6 +71,12 @@ int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget);
 // shapes and alignment are the caller's job (api.cpp validates every call).
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);
 
+// D (M, N) = alpha * A^T B with A (K, M) and B (K, N), both bf16 row-major
+// (contraction over their rows), on the direct-to-LDS kernel; needs
+// K % 64 == 0, M % 8 == 0 and N % 8 == 0 (checked by the caller).
+hipError_t launch_gemm_at(const GemmParams& p, hipStream_t s);
+bool gemm_at_supported(const GemmParams& p);
+
 // Register-only MFMA rate probe: `blocks` workgroups of kProbeThreads, each
 // wave running `iters` iterations of four independent MFMAs; sink holds two
 // uint64 per wave (shader-clock ticks, wall-clock ticks over the loop).
@@ -69,6 +88,10 @@ hipError_t launch_mfma_probe(int dtype, int iters, int blocks, unsigned long lon
 hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t ldh, int rows, int H,
                           const uint16_t* gx, const uint16_t* bx, const uint16_t* gg,
                           const uint16_t* bg, float eps, hipStream_t s);
+
+// Zeroes `bytes` (a multiple of 16) at p (16-byte aligned) with a kernel, so
+// the fill may sit in a captured graph.
+hipError_t launch_fill_zero16(void* p, size_t bytes, hipStream_t s);
 
 // Bit-exact run permute used by dispatch / combine.
 struct PermuteParams {

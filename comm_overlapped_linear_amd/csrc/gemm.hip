@@ -136,16 +136,41 @@ __device__ __forceinline__ void add_row8(const uint16_t* src, int64_t off, bool 
   }
 }
 
+template <bool F32IO>
 __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPtrs& bp, int row, int col, int nout,
                                               float* x) {
   const int n = min(8, nout - col);
   const bool vec = p.vec_ok && n == 8;
+  if constexpr (F32IO) {
+    if (p.acc_in) {
+      const float* src = p.acc_in + static_cast<int64_t>(row) * p.ld_acc + col;
+      if (vec) {
+        const float4 lo = *reinterpret_cast<const float4*>(src), hi = *reinterpret_cast<const float4*>(src + 4);
+        x[0] += lo.x; x[1] += lo.y; x[2] += lo.z; x[3] += lo.w;
+        x[4] += hi.x; x[5] += hi.y; x[6] += hi.z; x[7] += hi.w;
+      } else {
+        for (int e = 0; e < n; ++e) x[e] += src[e];
+      }
+    }
+  }
   if (p.beta != 0.0f) add_row8(p.c, static_cast<int64_t>(row) * p.ldc + col, vec, n, p.beta, x);
   if (bp.bias) add_row8(bp.bias, col, n == 8, n, 1.0f, x);
   if (row >= p.add_row0 && row < p.add_row1 && col >= p.add_col0 && col < p.add_col1) {
     const int64_t off = static_cast<int64_t>(row - p.add_row0) * p.ld_add + (col - p.add_col0);
     for (int t = 0; t < p.n_add_list; ++t) add_row8(p.add_list[t], off, vec, n, 1.0f, x);
     for (int t = 0; t < p.n_add_strided; ++t) add_row8(p.add_base + t * p.add_stride, off, vec, n, 1.0f, x);
+  }
+  if constexpr (F32IO) {
+    if (p.acc_out) {
+      float* dst = p.acc_out + static_cast<int64_t>(row) * p.ld_acc + col;
+      if (vec) {
+        *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+      } else {
+        for (int e = 0; e < n; ++e) dst[e] = x[e];
+      }
+      return;
+    }
   }
   uint16_t* dst = bp.d + static_cast<int64_t>(row) * p.ldd + col;
   if (vec) {
@@ -174,7 +199,7 @@ __device__ __forceinline__ void add_vec8(const uint4 c, float scale, float* x) {
 // then each addend in order) the loads of all NV vectors of a thread are
 // issued together before any is used. The arithmetic, and so the result, is
 // that of epilogue_vec8; only the memory latency is overlapped.
-template <int NV>
+template <int NV, bool F32IO>
 __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchPtrs& bp, const float* stage,
                                                int sld, int tid, int nt, int vec_per_row, int row0, int wtm,
                                                int tcol0) {
@@ -190,6 +215,22 @@ __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchP
     const float4 hi = *reinterpret_cast<const float4*>(stage + sr * sld + sc + 4);
     x[u][0] = lo.x; x[u][1] = lo.y; x[u][2] = lo.z; x[u][3] = lo.w;
     x[u][4] = hi.x; x[u][5] = hi.y; x[u][6] = hi.z; x[u][7] = hi.w;
+  }
+  if constexpr (F32IO) {
+    if (p.acc_in) {
+      float4 f[NV][2];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const float* src = p.acc_in + int64_t(row[u]) * p.ld_acc + col[u];
+        f[u][0] = *reinterpret_cast<const float4*>(src);
+        f[u][1] = *reinterpret_cast<const float4*>(src + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        x[u][0] += f[u][0].x; x[u][1] += f[u][0].y; x[u][2] += f[u][0].z; x[u][3] += f[u][0].w;
+        x[u][4] += f[u][1].x; x[u][5] += f[u][1].y; x[u][6] += f[u][1].z; x[u][7] += f[u][1].w;
+      }
+    }
   }
   uint4 c[NV];
   if (p.beta != 0.0f) {
@@ -226,6 +267,17 @@ __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchP
         if (in[u]) add_vec8(c[u], 1.0f, x[u]);
     }
   }
+  if constexpr (F32IO) {
+    if (p.acc_out) {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        float* dst = p.acc_out + int64_t(row[u]) * p.ld_acc + col[u];
+        *reinterpret_cast<float4*>(dst) = make_float4(x[u][0], x[u][1], x[u][2], x[u][3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(x[u][4], x[u][5], x[u][6], x[u][7]);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     uint4 o;
@@ -243,7 +295,7 @@ __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchP
 // threads sweep that block in 8-column vectors: + beta * C, + bias, + addends,
 // one bf16 rounding, 16-byte coalesced stores. The caller has synchronised
 // the workgroup, so the LDS is free.
-template <int BM, int BN, int WM, int WN, bool SWIGLU>
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool F32IO = false>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs& bp,
                                            const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32], uint8_t* smem,
                                            int tm, int tn) {
@@ -292,12 +344,14 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs&
     }
     __syncthreads();
     if (interior) {
-      // at most four vectors in flight per thread (register budget)
-      constexpr int G = NV < 4 ? NV : 4;
+      // at most four vectors in flight per thread (two with the fp32 chain,
+      // whose inputs are twice as wide): register budget
+      constexpr int GMAX = F32IO ? 2 : 4;
+      constexpr int G = NV < GMAX ? NV : GMAX;
       static_assert(NV % G == 0, "vector groups");
 #pragma unroll
       for (int g0 = 0; g0 < NV; g0 += G)
-        sweep_interior<G>(p, bp, stage, SLD, tid + g0 * NT, NT, VEC_PER_ROW, m0 + i * 32, WTM, tcol0);
+        sweep_interior<G, F32IO>(p, bp, stage, SLD, tid + g0 * NT, NT, VEC_PER_ROW, m0 + i * 32, WTM, tcol0);
     } else {
       for (int v = tid; v < VEC_PASS; v += NT) {
         const int sr = v / VEC_PER_ROW, sc = (v % VEC_PER_ROW) * 8;
@@ -309,7 +363,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs&
         const float4 hi = *reinterpret_cast<const float4*>(stage + sr * SLD + sc + 4);
         x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
         x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
-        epilogue_vec8(p, bp, row, col, nout, x);
+        epilogue_vec8<F32IO>(p, bp, row, col, nout, x);
       }
     }
     __syncthreads();
@@ -518,11 +572,12 @@ __device__ __forceinline__ void tile_of_block(int vt, int nt, int ntm, int& tm, 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // Whether a DMA tile shape runs as persistent workgroups. The fp8 256 x 256
-// tile does not: its 256 registers per lane leave no room for the tile loop
-// (the loop would spill), so it keeps one workgroup per tile.
-template <typename Op, int BM, int BN>
+// tile and the contraction-major-A 256 x 256 tile do not: their registers
+// leave no room for the tile loop (the loop would spill), so they keep one
+// workgroup per tile.
+template <typename Op, int BM, int BN, bool AT = false>
 constexpr bool persistent_tiles() {
-  return !(Op::kElemBytes == 1 && BM == 256 && BN == 256);
+  return !((Op::kElemBytes == 1 || AT) && BM == 256 && BN == 256);
 }
 
 // 16 bytes per lane from base + voff (a uniform 64-bit base in SGPRs and a
@@ -579,7 +634,7 @@ struct Interleave {
   }
 };
 
-template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU>
+template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(const GemmParams p) {
   const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
   constexpr int NW = WM * WN;                  // waves: 4 (one per SIMD) or 8 (two per SIMD)
@@ -600,6 +655,13 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   // transposing fragment reads of four consecutive k-rows hit distinct banks
   constexpr int CPRB = BN * 2 / 16;            // chunks per k-row
   constexpr int RPIB = 64 / CPRB;              // k-rows per DMA instruction
+  // Contraction-major A (AT): the A tile sits in LDS as [64 k-rows][BM m],
+  // swizzled and read like a (K, N) B tile; 64 k-rows of BM columns take as
+  // many DMA instructions as BM rows of 128 bytes.
+  static_assert(!AT || (KN && !SWIGLU && Op::kElemBytes == 2 && ROWB == 128 && BM >= 128),
+                "contraction-major A: bf16 weight-gradient tiles");
+  constexpr int CPRA = BM * 2 / 16;
+  constexpr int RPIA = 64 / CPRA;
   static_assert(WM * 32 * ((SWIGLU ? BN / 2 : BN) + 4) * 4 <= STAGES * STAGE, "epilogue stage fits in LDS");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -644,9 +706,17 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   uint32_t boff[B_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
-    const int r = (j * NW + wave) * RPI + rsub;
-    const int grow = min(m0 + r, p.M - 1);
-    aoff[j] = static_cast<uint32_t>(int64_t(grow - m0) * lda_b + swz<ROWB>(r, pc) * 16);
+    if constexpr (!AT) {
+      const int r = (j * NW + wave) * RPI + rsub;
+      const int grow = min(m0 + r, p.M - 1);
+      aoff[j] = static_cast<uint32_t>(int64_t(grow - m0) * lda_b + swz<ROWB>(r, pc) * 16);
+    } else {
+      const int kr = (j * NW + wave) * RPIA + lane / CPRA;
+      const int c = (lane % CPRA) ^ kn_swz(kr);
+      int mc = m0 + c * 8;
+      if (mc >= p.M) mc = 0;
+      aoff[j] = static_cast<uint32_t>(int64_t(kr) * lda_b + mc * 2);
+    }
   }
 #pragma unroll
   for (int j = 0; j < B_INSTR; ++j) {
@@ -666,8 +736,22 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
 
   auto issue = [&](int kt, int buf) {
     const uint32_t sb = lds0 + buf * STAGE;
-    const uint8_t* ab = a_tile + int64_t(kt) * ROWB;
-    const uint8_t* bb = Bp + int64_t(kt) * b_step;
+    const uint8_t* ab;
+    if constexpr (AT) {
+      int64_t k0 = int64_t(kt) * 64;
+      if (p.a_kwrap > 0 && k0 >= p.a_kwrap) k0 -= p.kwrap_rows;
+      ab = A + k0 * lda_b;
+    } else {
+      ab = a_tile + int64_t(kt) * ROWB;
+    }
+    const uint8_t* bb;
+    if constexpr (KN) {
+      int64_t k0 = int64_t(kt) * 64;
+      if (p.b_kwrap > 0 && k0 >= p.b_kwrap) k0 -= p.kwrap_rows;
+      bb = Bp + k0 * ldb_b;
+    } else {
+      bb = Bp + int64_t(kt) * b_step;
+    }
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
       dma16(ab, aoff[j], __builtin_amdgcn_readfirstlane(sb + (j * NW + wave) * 1024));
@@ -702,7 +786,16 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   auto load_frags = [&](int set, const uint8_t* la, int kk) {
     const uint8_t* lb = la + A_BYTES;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[set][i] = Op::template load<ROWB>(la, wm * WTM + i * 32 + l32, kk, half);
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (!AT) {
+        fa[set][i] = Op::template load<ROWB>(la, wm * WTM + i * 32 + l32, kk, half);
+      } else {
+        // the transposing read of the (K, N) B tile, over A's m columns
+        const int g = lane >> 4, lq = lane & 15;
+        const int kr = kk * 16 + 8 * (g >> 1) + (lq >> 2);
+        fa[set][i] = load_kn_frag<BM>(la, kr, wm * WTM + i * 32 + 16 * (g & 1) + 4 * (lq & 3));
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       if constexpr (!KN) {
@@ -762,9 +855,9 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   }
   wait_vmcnt<0>();
   __syncthreads();
-  store_tile<BM, BN, WM, WN, SWIGLU>(p, bp, acc, smem, tm, tn);   // ends with a barrier: LDS free
+  store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm, tn);   // ends with a barrier: LDS free
   };
-  if constexpr (persistent_tiles<Op, BM, BN>()) {
+  if constexpr (persistent_tiles<Op, BM, BN, AT>()) {
     for (int vt = blockIdx.x; vt < ntiles; vt += gridDim.x) run_tile(vt);
   } else {
     run_tile(blockIdx.x);
@@ -773,11 +866,11 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
 
 int cu_count();
 
-template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU>
+template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT = false>
 hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   constexpr int smem = STAGES * (BM + BN) * ROWB;
   constexpr int nt = 64 * WM * WN;
-  auto kern = gemm_dma_kernel<Op, BM, BN, WM, WN, ROWB, STAGES, KN, SWIGLU>;
+  auto kern = gemm_dma_kernel<Op, BM, BN, WM, WN, ROWB, STAGES, KN, SWIGLU, AT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -791,7 +884,7 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   // at most one persistent workgroup per CU (all tiles when batched). The
   // CU budget shaped the tiles only: once launches beside this one finish,
   // their CUs are this launch's to use.
-  const int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN>()) ? std::min(tiles, cu_count()) : tiles;
+  const int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) ? std::min(tiles, cu_count()) : tiles;
   hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }
@@ -879,6 +972,21 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   }
 }
 
+// Contraction-major A (the weight gradient): bf16, B in (K, N), the DMA
+// kernel only. The same cost model picks the tile.
+bool at_offsets_fit(const GemmParams& p) {
+  return int64_t(64) * p.lda * 2 + int64_t(p.M) * 2 < (int64_t(1) << 31) &&
+         int64_t(64) * p.ldb * 2 + int64_t(p.N) * 2 < (int64_t(1) << 31);
+}
+
+hipError_t dispatch_at(const GemmParams& p, hipStream_t s) {
+  switch (pick_tile(p.M, p.N, kEpiAlphaBeta, p.batch, p.cu_budget)) {
+    case 0: return launch_dma_tile<OpBf16, 256, 256, 2, 4, 128, 2, true, false, true>(p, s);
+    case 1: return launch_dma_tile<OpBf16, 128, 256, 2, 4, 128, 3, true, false, true>(p, s);
+    default: return launch_dma_tile<OpBf16, 128, 128, 2, 4, 128, 4, true, false, true>(p, s);
+  }
+}
+
 // Register-only MFMA loop: the matrix cores' attainable rate at the clocks
 // the chip holds under this load, with no memory traffic. Each wave keeps
 // four independent accumulators in flight, so the MFMA pipe never waits on
@@ -921,6 +1029,16 @@ __global__ void __launch_bounds__(kProbeThreads) mfma_probe_kernel(unsigned long
 }  // namespace
 
 int device_cus() { return cu_count(); }
+
+bool gemm_at_supported(const GemmParams& p) {
+  return p.M > 0 && p.N > 0 && p.K > 0 && p.K % 64 == 0 && p.M % 8 == 0 && p.N % 8 == 0 && p.lda % 8 == 0 &&
+         p.ldb % 8 == 0 && p.batch == 1 && at_offsets_fit(p);
+}
+
+hipError_t launch_gemm_at(const GemmParams& p, hipStream_t s) {
+  if (!gemm_at_supported(p)) return hipErrorInvalidValue;
+  return dispatch_at(p, s);
+}
 
 double probe_flop_per_iter(int dtype) {
   return double(kProbeThreads / 64) * 4 * (dtype == kE4m3 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16);

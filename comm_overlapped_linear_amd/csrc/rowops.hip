@@ -152,7 +152,21 @@ __global__ __launch_bounds__(kPermThreads) void permute1_kernel(const PermutePar
     dst[i] = src[i];
 }
 
+// Zero fill in 16-byte vector stores (used where a result is an empty sum).
+__global__ __launch_bounds__(256) void fill_zero16_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
 }  // namespace
+
+hipError_t launch_fill_zero16(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = int64_t(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_zero16_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t ldh, int rows, int H,
                           const uint16_t* gx, const uint16_t* bx, const uint16_t* gg,

@@ -219,6 +219,65 @@ size_t tpgemm_stage_rs_workspace_size(const tpg_rs_args* args);
 tpg_status tpgemm_stage_rs(const tpg_rs_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Weight gradient of the all-gather / reduce-scatter linears, staged over
+ * the gathered token rows ("Add dist GEMM attention and FFN backend",
+ * Structure: the backward of AllGatherLinear and LinearReduceScatter needs
+ * the same two collectives; their data gradients are this library's RS and
+ * AG calls with the weight read in the (K, N) layout, and their weight
+ * gradients are this call):
+ *   d (N, K) = alpha * sum_{i < M} G[i, n] * X[i, k]
+ * with the M token rows split into P slices of m = M/P, one operand local
+ * (all M rows) and the other arriving as the P slices (the all-gathered
+ * operand: X = the gathered input for AllGatherLinear, G = the gathered
+ * output gradient for LinearReduceScatter). Stage t contributes the rows of
+ * slice (rank + t) mod P, local first, as in the all-gather form
+ * ("Distributed GEMM", Background, Figures 3-4). The stages split the
+ * contraction, so they add into one fp32 partial in the workspace and the
+ * last launch rounds once to bf16.
+ *
+ *   M, N, K      M % P == 0, m % 64 == 0; N % 8 == 0; K % 8 == 0.
+ *                M == 0 writes zeros to d.
+ *   gathered     TPG_GATHER_X: local is G (M, N), slices are X's (m, K);
+ *                TPG_GATHER_G: local is X (M, K), slices are G's (m, N).
+ *   local        bf16 row-major, all M rows (never modified).
+ *   slices       host array of P device pointers to bf16 row-major slices;
+ *                slice s holds rows [s*m, (s+1)*m) of the gathered operand,
+ *                [rank] is this rank's own (never modified).
+ *   d            bf16 (N, K) row-major output; must not overlap any input.
+ *   workspace    >= tpgemm_stage_wgrad_workspace_size() bytes: receive slots
+ *                ((P-1) slices staged, P unstaged, none with TPG_NO_COPY)
+ *                and, when the call makes more than one launch, the fp32
+ *                (N, K) partial.
+ *   groups       the P-1 remote stages form `groups` launches (0: library
+ *                choice, one), each gated by its own deliveries; the result
+ *                does not depend on it beyond fp32 rounding order.
+ *   flags        as for tpgemm_stage_ag. TPG_UNSTAGED gathers all P slices
+ *                in rank order first and makes one launch; with
+ *                TPG_NO_COPY it needs the slices contiguous in rank order.
+ * Errors: TPG_ERR_INVALID (P, rank, M % P, NULL pointers, overlaps, flags,
+ * gathered), TPG_ERR_UNSUPPORTED (m % 64, N % 8, K % 8, alignment, sizes
+ * past the kernel's 31-bit offsets), TPG_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+enum { TPG_GATHER_X = 0, TPG_GATHER_G = 1 };
+
+typedef struct {
+  int64_t M, N, K;
+  int32_t P, rank;
+  int32_t gathered;
+  int32_t groups;
+  const void* local;
+  const void* const* slices;
+  void* d;
+  float alpha;
+  uint32_t flags;
+  void* workspace;
+  size_t workspace_bytes;
+} tpg_wg_args;
+
+size_t tpgemm_stage_wgrad_workspace_size(const tpg_wg_args* args);
+tpg_status tpgemm_stage_wgrad(const tpg_wg_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * Per-token-slot FFN, compute-only part of the p04 layer ("Computation and
  * communication example"; comp_only in "Interface, layout, and parameters").
  * For n < PB = P*B rows and slot l < L = T/P, with H the hidden width:

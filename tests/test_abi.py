@@ -109,7 +109,8 @@ def test_struct_layouts_match_the_header(tmp_path):
     """The ctypes mirrors of tpg_ag_args / tpg_rs_args / tpg_ffn_args have
     the C header's field offsets and sizes (compiled with the host gcc)."""
     import subprocess
-    structs = {"tpg_ag_args": tp.AgArgs, "tpg_rs_args": tp.RsArgs, "tpg_ffn_args": tp.FfnArgs}
+    structs = {"tpg_ag_args": tp.AgArgs, "tpg_rs_args": tp.RsArgs, "tpg_ffn_args": tp.FfnArgs,
+               "tpg_wg_args": tp.WgArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tpgemm.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
@@ -139,3 +140,56 @@ def test_mfma_probe_validation():
     assert call(tp.E4M3, 10, 4, FAKE, 4 * 8 * 16 - 8) == tp.ERR_WORKSPACE
     assert call(tp.E4M3, 10, 4, None, 1 << 20) == tp.ERR_WORKSPACE
     assert call(tp.E4M3, 10, 4, FAKE + 4, 1 << 20) == tp.ERR_UNSUPPORTED
+
+
+def wg(**kw):
+    P = kw.pop("P", 4)
+    M, N, K = kw.pop("M", 4 * 64), kw.pop("N", 128), kw.pop("K", 256)
+    gathered = kw.get("gathered", tp.GATHER_X)
+    width = K if gathered == tp.GATHER_X else N
+    slice_b = (M // max(P, 1)) * width * 2
+    slices = (ctypes.c_void_p * max(P, 1))(*[FAKE + 0x10000000 + i * slice_b for i in range(max(P, 1))])
+    base = dict(M=M, N=N, K=K, P=P, rank=0, gathered=tp.GATHER_X, groups=0, local=FAKE,
+                slices=ctypes.cast(slices, ctypes.POINTER(ctypes.c_void_p)), d=FAKE + 0x40000000, alpha=1.0,
+                flags=tp.NO_COPY | tp.UNSTAGED, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    a = tp.WgArgs(**base)
+    a._keep = slices
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), tp.ERR_INVALID),
+    (dict(rank=4), tp.ERR_INVALID),
+    (dict(M=4 * 64 + 2), tp.ERR_INVALID),                 # M % P
+    (dict(M=4 * 32), tp.ERR_UNSUPPORTED),                 # m % 64
+    (dict(N=100), tp.ERR_UNSUPPORTED),                    # N % 8
+    (dict(K=260), tp.ERR_UNSUPPORTED),                    # K % 8
+    (dict(gathered=2), tp.ERR_INVALID),
+    (dict(local=None), tp.ERR_INVALID),
+    (dict(local=FAKE + 8), tp.ERR_UNSUPPORTED),
+    (dict(d=FAKE), tp.ERR_INVALID),                       # D overlaps local
+    (dict(flags=1 << 20), tp.ERR_INVALID),
+    (dict(flags=tp.COPY_SDMA | tp.COPY_SHADER), tp.ERR_INVALID),
+    (dict(flags=0), tp.ERR_WORKSPACE),                    # staged needs slots and the fp32 partial
+])
+def test_wgrad_validation_rejects_before_enqueue(kw, status):
+    assert tp.lib().tpgemm_stage_wgrad(ctypes.byref(wg(**kw)), None) == status
+
+
+def test_wgrad_workspace_sizes():
+    P, m, N, K = 4, 128, 136, 264
+    a = wg(P=P, M=P * m, N=N, K=K, flags=0)
+    f32 = N * K * 4
+    slot = lambda n: -(-(n * m * K * 2) // 256) * 256
+    assert tp.stage_wgrad_workspace_size(a) == slot(P - 1) + f32
+    a.flags = tp.UNSTAGED
+    assert tp.stage_wgrad_workspace_size(a) == slot(P)
+    a.flags = tp.UNSTAGED | tp.NO_COPY
+    assert tp.stage_wgrad_workspace_size(a) == 0
+    a.flags = tp.NO_COPY
+    assert tp.stage_wgrad_workspace_size(a) == f32
+    a.gathered = tp.GATHER_G
+    a.flags = 0
+    assert tp.stage_wgrad_workspace_size(a) == -(-(3 * m * N * 2) // 256) * 256 + f32
+    assert tp.stage_wgrad_workspace_size(wg(P=1, M=64, flags=0)) == 0
