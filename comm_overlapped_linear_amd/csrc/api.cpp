@@ -887,15 +887,26 @@ int64_t wg_width(const tpg_wg_args* a) { return a->gathered == TPG_GATHER_X ? a-
 
 size_t wg_slice_bytes(const tpg_wg_args* a) { return size_t(a->M / a->P) * wg_width(a) * 2; }
 
+// Library choice (groups == 0): one gathered launch. Measured on MI355X at
+// the weight gradients of the e4m3 all-gather shape (1024 x 8192 over 8192
+// token rows, X gathered) and of the SwiGLU block (w13: 4096 x 3584, G
+// gathered; w2: 1792 x 4096, X gathered), in us, staged with one run / two
+// runs / unstaged: 233 / 233 / 212, 278 / 301 / 252, 181 / 196 / 162. Every
+// stage here spans the whole output, so a split contraction pays a second
+// prologue and epilogue and an fp32 round trip of the output, and the local
+// stage (1/8 of the work) takes longer than its share while the deliveries
+// compete with it for the chip.
+bool wg_unstaged(const tpg_wg_args* a) { return (a->flags & TPG_UNSTAGED) || a->groups == 0; }
+
 // Receive slots: (P-1) slices in ring order staged, P in rank order unstaged.
 size_t wg_recv(const tpg_wg_args* a) {
   if (a->flags & TPG_NO_COPY) return 0;
-  return round_up(wg_slice_bytes(a) * ((a->flags & TPG_UNSTAGED) ? a->P : a->P - 1), 256);
+  return round_up(wg_slice_bytes(a) * (wg_unstaged(a) ? a->P : a->P - 1), 256);
 }
 
 // The fp32 partial exists when the call makes more than one launch: staged
 // with P > 1.
-bool wg_chain(const tpg_wg_args* a) { return !(a->flags & TPG_UNSTAGED) && a->P > 1; }
+bool wg_chain(const tpg_wg_args* a) { return !wg_unstaged(a) && a->P > 1; }
 
 size_t wg_ws(const tpg_wg_args* a) {
   if (!a || a->P < 1 || a->P > kMaxP || a->M <= 0 || a->N <= 0 || a->K <= 0 || a->M % a->P) return 0;
@@ -946,7 +957,7 @@ tpg_status validate_wg(const tpg_wg_args* a, size_t need) {
   }
   if (overlaps(dr, wr)) return fail(TPG_ERR_INVALID, "workspace overlaps D");
   if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
-  if ((a->flags & TPG_UNSTAGED) && (a->flags & TPG_NO_COPY) && a->M > 0) {
+  if (wg_unstaged(a) && (a->flags & TPG_NO_COPY) && a->M > 0) {
     const size_t slice_b = wg_slice_bytes(a);
     for (int s = 1; s < a->P; ++s)
       if (static_cast<const char*>(a->slices[s]) != static_cast<const char*>(a->slices[0]) + s * slice_b)
@@ -958,10 +969,13 @@ tpg_status validate_wg(const tpg_wg_args* a, size_t need) {
 // Launch chain. The local stage comes first, then the P-1 remote stages in
 // `groups` runs; every launch but the last writes the fp32 partial, every
 // launch but the first adds it (in place: each element is read and written
-// by the same thread). The chain runs on one compute stream; the deliveries
-// run on the root, each run gated by one event after its slices. With
-// TPG_NO_COPY the slices are read in place, one launch per stretch that is
-// contiguous in memory and does not wrap past slice P-1.
+// by the same thread). Stream roles as in the all-gather: the deliveries run
+// back to back on the root and the last run follows them there, after one
+// wait for the chain's previous link, so the critical path (last delivery,
+// then the last run) waits on no other queue; the local stage and earlier
+// runs go to one side stream, each run gated by one event after its slices.
+// With TPG_NO_COPY the slices are read in place, one launch per stretch that
+// is contiguous in memory and does not wrap past slice P-1.
 tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
   const int P = a.P, r = a.rank;
   const int64_t m = a.M / P;
@@ -1007,11 +1021,26 @@ tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
     q.acc_out = last ? nullptr : part;
     return gemm_on(cx, L, s, q, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA);
   };
+  // deliveries of stages [t_begin, t_end) into their ring-order slots on the
+  // root, adjacent slices merged into one copy
+  auto adjacent = [&](int s, int run) {
+    for (int i = 1; i < run; ++i)
+      if (static_cast<const char*>(a.slices[s + i]) != static_cast<const char*>(a.slices[s]) + i * slice_b)
+        return false;
+    return true;
+  };
 
-  if (a.flags & TPG_UNSTAGED) {
+  if (wg_unstaged(&a)) {
     const void* g = a.slices[0];
     if (copies) {
-      for (int s = 0; s < P; ++s) HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.slices[s], slice_b, kind, L.root));
+      tpg_status hs = hold_deliveries(a.flags, L.root);
+      if (hs != TPG_OK) return hs;
+      for (int s = 0; s < P;) {                   // rank order
+        int run = 1;
+        while (s + run < P && adjacent(s, run + 1)) ++run;
+        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.slices[s], run * slice_b, kind, L.root));
+        s += run;
+      }
       g = ws;
     }
     return launch(L.root, g, 0, a.M, true, true);
@@ -1019,21 +1048,14 @@ tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
   if (P == 1) return launch(L.root, a.slices[0], 0, m, true, true);
 
   const int remote = P - 1;
-  const int G = a.groups > 0 ? std::min(a.groups, remote) : 1;
+  const int G = std::min(a.groups, remote);       // >= 1 here
   auto t0 = [&](int g) { return 1 + (g * remote) / G; };
-  auto adjacent = [&](int s, int run) {
-    for (int i = 1; i < run; ++i)
-      if (static_cast<const char*>(a.slices[s + i]) != static_cast<const char*>(a.slices[s]) + i * slice_b)
-        return false;
-    return true;
-  };
   const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : 2;
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, ns, st);
   if (stat != TPG_OK) return stat;
-  hipStream_t cs = st[ns - 1];                    // the chain's stream
-  // the local stage: no delivery needed
-  stat = launch(cs, a.slices[r], r * m, m, true, false);
+  hipStream_t cs = st[ns - 1];                    // the chain's side stream
+  stat = launch(cs, a.slices[r], r * m, m, true, false);   // the local stage: no delivery needed
   if (stat != TPG_OK) return stat;
   if (copies) {
     stat = hold_deliveries(a.flags, L.root);
@@ -1049,12 +1071,17 @@ tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
         HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.slices[s], run * slice_b, kind, L.root));
         t += run;
       }
-      if (ns > 1) {
+      hipStream_t rs = cs;
+      if (ns > 1 && !last_run) {
         HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
         HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
+      } else if (ns > 1) {                        // the last run: on the root, after the chain's last link
+        HIP_TRY(hipEventRecord(cx.ev_copy[G], cs));
+        HIP_TRY(hipStreamWaitEvent(L.root, cx.ev_copy[G], 0));
+        rs = L.root;
       }
       const int s0 = (r + t0(g)) % P;
-      stat = launch(cs, ws + (t0(g) - 1) * slice_b, s0 * m, (t0(g + 1) - t0(g)) * m, false, last_run);
+      stat = launch(rs, ws + (t0(g) - 1) * slice_b, s0 * m, (t0(g + 1) - t0(g)) * m, false, last_run);
       if (stat != TPG_OK) return stat;
     } else {
       for (int t = t0(g); t < t0(g + 1);) {
@@ -1292,9 +1319,7 @@ tpg_status tpgemm_stage_wgrad(const tpg_wg_args* args, void* stream) {
     Ctx* cx = nullptr;
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
-    tpg_wg_args a = *args;
-    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
-      a.flags |= TPG_SERIAL_STAGES;
+    const tpg_wg_args& a = *args;
     return run_call(*cx, a.flags, wg_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_wg(*cx, a, L); });
   });

@@ -42,6 +42,9 @@ struct GemmParams {
   // that run side by side each get their share, so that together they make
   // one wave of tiles instead of each sizing its tiles for the whole chip.
   int cu_budget;
+  // Upper bound on the persistent grid (0: none): workgroups beyond it would
+  // hold CUs that work beside this launch (shader-copy deliveries) needs.
+  int grid_cap;
   // Contraction-major A (the weight gradient, launch_gemm_at): A is stored
   // (K, M) row-major with row stride lda, B is (K, N). Contraction rows wrap:
   // K-steps at contraction index >= a_kwrap (if > 0) read the A rows

@@ -884,7 +884,8 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   // at most one persistent workgroup per CU (all tiles when batched). The
   // CU budget shaped the tiles only: once launches beside this one finish,
   // their CUs are this launch's to use.
-  const int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) ? std::min(tiles, cu_count()) : tiles;
+  int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) ? std::min(tiles, cu_count()) : tiles;
+  if (p.grid_cap >= 8 && p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) grid = std::min(grid, p.grid_cap & ~7);
   hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }

@@ -179,17 +179,19 @@ def test_wgrad_validation_rejects_before_enqueue(kw, status):
 
 def test_wgrad_workspace_sizes():
     P, m, N, K = 4, 128, 136, 264
-    a = wg(P=P, M=P * m, N=N, K=K, flags=0)
+    a = wg(P=P, M=P * m, N=N, K=K, flags=0, groups=1)
     f32 = N * K * 4
     slot = lambda n: -(-(n * m * K * 2) // 256) * 256
-    assert tp.stage_wgrad_workspace_size(a) == slot(P - 1) + f32
+    assert tp.stage_wgrad_workspace_size(a) == slot(P - 1) + f32          # staged
     a.flags = tp.UNSTAGED
+    assert tp.stage_wgrad_workspace_size(a) == slot(P)
+    a.flags, a.groups = 0, 0                                             # library choice: one gathered launch
     assert tp.stage_wgrad_workspace_size(a) == slot(P)
     a.flags = tp.UNSTAGED | tp.NO_COPY
     assert tp.stage_wgrad_workspace_size(a) == 0
-    a.flags = tp.NO_COPY
+    a.flags, a.groups = tp.NO_COPY, 3
     assert tp.stage_wgrad_workspace_size(a) == f32
     a.gathered = tp.GATHER_G
     a.flags = 0
     assert tp.stage_wgrad_workspace_size(a) == -(-(3 * m * N * 2) // 256) * 256 + f32
-    assert tp.stage_wgrad_workspace_size(wg(P=1, M=64, flags=0)) == 0
+    assert tp.stage_wgrad_workspace_size(wg(P=1, M=64, flags=0, groups=1)) == 0

@@ -26,6 +26,8 @@ def gathered_of(case):
 
 def run(case, inp, flags=0, groups=0, workspace=None, local=None, slices=None):
     local = dev(inp["local"]) if local is None else local
+    if slices is None and (flags & tp.NO_COPY) and (groups == 0 or flags & tp.UNSTAGED):
+        _, slices = contiguous_slices(inp)      # one launch in place needs the slices in one buffer
     slices = [dev(s) for s in inp["slices"]] if slices is None else slices
     d = bf16_empty(case.N, case.K)
     tp.stage_wgrad(local, slices, d, M=case.M, N=case.N, K=case.K, rank=case.rank, gathered=gathered_of(case),
@@ -43,14 +45,17 @@ def contiguous_slices(inp):
 
 @pytest.mark.parametrize("case", W.SMALL_WGRAD, ids=lambda c: c.name)
 def test_wgrad_parity_all_modes(case):
+    """Every issue mode, both with the library's choice (one gathered launch)
+    and staged (groups >= 1)."""
     inp = W.wgrad_inputs(case)
     ref = oracle.wgrad_staged(inp["local"], inp["slices"], case.gathered, case.rank, case.alpha)
     outs = {}
     for name, flags in MODES.items():
-        say(f"wgrad: {case.name} mode={name}")
-        outs[name] = run(case, inp, flags)
-        assert_parity(host_f64(outs[name]), ref, f"{case.name}/{name}")
-    for groups in sorted({1, 2, case.P - 1}):
+        for groups in (0, 1):
+            say(f"wgrad: {case.name} mode={name} groups={groups}")
+            outs[name, groups] = run(case, inp, flags, groups)
+            assert_parity(host_f64(outs[name, groups]), ref, f"{case.name}/{name}/{groups}")
+    for groups in sorted({2, case.P - 1}):
         if groups > case.P - 1:
             continue
         say(f"wgrad: {case.name} groups={groups}")
@@ -60,10 +65,12 @@ def test_wgrad_parity_all_modes(case):
     _, sl = contiguous_slices(inp)
     d = run(case, inp, tp.UNSTAGED | tp.NO_COPY, slices=sl)
     assert_parity(host_f64(d), ref, f"{case.name}/unstaged in place")
-    # the same launch chain gives the same bits whatever the issue mode
+    # the same launches give the same bits whatever the issue mode
     for name in ("graph", "eager", "serial", "sdma"):
-        assert torch.equal(outs[name], outs["default"]), name
-    assert torch.equal(d, outs["unstaged"])
+        assert torch.equal(outs[name, 1], outs["default", 1]), name
+        assert torch.equal(outs[name, 0], outs["default", 0]), name
+    assert torch.equal(outs["unstaged", 1], outs["default", 0])
+    assert torch.equal(d, outs["default", 0])
 
 
 def test_wgrad_integer_inputs_are_exact():
