@@ -386,6 +386,41 @@ def bench_column_duals(args):
     return out
 
 
+WGRAD_BENCH = [W.WgCase("wgrad_bf16_p8_1024x8192_c8192", M=8192, N=1024, K=8192, P=8, gathered="x"),
+               W.WgCase("wgrad_bf16_p8_w13_4096x3584_c8192", M=8192, N=4096, K=3584, P=8, gathered="g"),
+               W.WgCase("wgrad_bf16_p8_w2_1792x4096_c8192", M=8192, N=1792, K=4096, P=8, gathered="x")]
+
+
+def bench_wgrad(args):
+    """Weight gradients of the backward pass: of the e4m3 all-gather shape
+    (in bf16, X gathered) and of the SwiGLU block's w13 (G gathered) and w2
+    (X gathered). Default call (one gathered launch), the staged chain
+    (groups=1) and the GEMM alone over slices already in one buffer."""
+    out = {}
+    for case in WGRAD_BENCH:
+        inp = W.wgrad_inputs(case)
+        local, sl = dev(inp["local"]), [dev(x) for x in inp["slices"]]
+        big = torch.cat(sl)
+        whole = [big[i * case.m:(i + 1) * case.m] for i in range(case.P)]
+        d = torch.empty((case.N, case.K), dtype=torch.int16, device="cuda")
+        g = tp.GATHER_X if case.gathered == "x" else tp.GATHER_G
+        kw = dict(M=case.M, N=case.N, K=case.K, gathered=g)
+        need = max(tp.stage_wgrad_workspace_size(tp.wgrad_args(local, sl, d, groups=gr, **kw)) for gr in (0, 1))
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        call = tp.prepare_stage_wgrad(local, sl, d, workspace=ws, **kw)
+        staged = tp.prepare_stage_wgrad(local, sl, d, workspace=ws, groups=1, **kw)
+        gemm = tp.prepare_stage_wgrad(local, whole, d, flags=tp.UNSTAGED | tp.NO_COPY, **kw)
+        steps = max(5, args.steps // 2)
+        ms = time_steps(lambda: call(flags=0), steps, 3)
+        ms_staged = time_steps(lambda: staged(flags=0), steps, 3)
+        ms_gemm = time_steps(lambda: gemm(flags=tp.UNSTAGED | tp.NO_COPY), steps, 3)
+        out[case.name] = dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1),
+                              us_staged=round(ms_staged * 1e3, 1), us_gemm_only=round(ms_gemm * 1e3, 1),
+                              tflops_gemm_only=round(case.flop / (ms_gemm * 1e-3) / 1e12, 1))
+        del big, whole, local, sl, ws
+    return out
+
+
 def bench_small_ag(case, args):
     inp, call, _, _ = setup_ag(case)
     ms = time_steps(lambda: call(0), args.steps, args.warmup)
@@ -450,6 +485,7 @@ def main():
         detail["rs_bf16_p8_8192x8192x3584"] = bench_rs(W.C3, args)
         detail["swiglu_p8_s1024_d4096_f1792"] = bench_swiglu(W.C5, args)
         detail.update(bench_column_duals(args))
+        detail.update(bench_wgrad(args))
         log(f"[other] {json.dumps({k: detail[k] for k in ('ag_bf16_p2_256x256x512', 'rs_bf16_p8_8192x8192x3584', 'swiglu_p8_s1024_d4096_f1792')})}")
 
     cpu = None

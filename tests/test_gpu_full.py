@@ -174,3 +174,27 @@ def test_full_rs_tileb_bf16():
     tp.stage_rs(a, b, inc, d2, flags=tp.UNSTAGED, **kw)
     torch.cuda.synchronize()
     assert torch.equal(d, d2)
+
+
+WGRAD_FULL = [W.WgCase("wg_x_1024x8192_c8192", M=8192, N=1024, K=8192, P=8, rank=3, gathered="x"),
+              W.WgCase("wg_g_w13_4096x3584_c8192", M=8192, N=4096, K=3584, P=8, rank=6, gathered="g")]
+
+
+@pytest.mark.parametrize("case", WGRAD_FULL, ids=lambda c: c.name)
+def test_full_wgrad(case):
+    """Weight gradients at full size: of the e4m3 all-gather shape (in bf16, X
+    gathered) and of the SwiGLU block's w13 (G = the gathered input), both
+    the library's single gathered launch and the staged chain, on sampled
+    output rows."""
+    say(f"full: {case.name} generate")
+    inp = W.wgrad_inputs(case)
+    local, sl = dev(inp["local"]), [dev(x) for x in inp["slices"]]
+    g = tp.GATHER_X if case.gathered == "x" else tp.GATHER_G
+    rows = sorted(set([0, case.N - 1] + np.random.default_rng(2).integers(0, case.N, 30).tolist()))
+    ref = oracle.wgrad_rows(inp["local"], inp["slices"], case.gathered, rows)
+    for groups in (0, 1):
+        d = bf16_empty(case.N, case.K)
+        say(f"full: {case.name} groups={groups}")
+        tp.stage_wgrad(local, sl, d, M=case.M, N=case.N, K=case.K, rank=case.rank, gathered=g, groups=groups)
+        torch.cuda.synchronize()
+        assert_parity(host_f64(d)[rows], ref, f"{case.name}/groups={groups}")
