@@ -47,22 +47,6 @@ def dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(view)).cuda()
 
 
-class Hip:
-    """Direct HIP runtime calls used only for measurement (raw deliveries)."""
-
-    def __init__(self):
-        self.lib = ctypes.CDLL("libamdhip64.so")
-        self.lib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                            ctypes.c_int, ctypes.c_void_p]
-        self.lib.hipMemcpyAsync.restype = ctypes.c_int
-
-    def copy(self, dst, src, nbytes, kind, stream):
-        rc = self.lib.hipMemcpyAsync(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, kind,
-                                     ctypes.c_void_p(stream))
-        if rc != 0:
-            raise RuntimeError(f"hipMemcpyAsync failed: {rc}")
-
-
 def time_steps(fn, steps, warmup):
     """ms per call over `steps` calls, after `warmup` calls and at least
     WARM_MS of calls (the clocks settle over the first few ms of load)."""
@@ -215,17 +199,17 @@ def setup_ag(case, extra_flags=0):
 
     side = torch.cuda.Stream()
 
-    def deliveries(hip, kind):
-        """The P-1 deliveries alone, as the library issues them: ring order,
-        back to back on one copy stream, recorded once into a graph so that
-        replays time the copies rather than the host calls."""
+    def deliveries(flags):
+        """The P-1 deliveries alone, as the library issues them (tpg_deliver
+        with the call's copy kind): ring order, back to back on one stream,
+        recorded once into a graph so that replays time the copies rather
+        than the host calls."""
+        ring = [slices[(case.rank + t) % case.P] for t in range(1, case.P)]
+
         def issue():
             cur = torch.cuda.current_stream()
             side.wait_stream(cur)
-            for t in range(1, case.P):
-                s = (case.rank + t) % case.P
-                hip.copy(ws.data_ptr() + (t - 1) * slice_bytes, slices[s].data_ptr(), slice_bytes, kind,
-                         side.cuda_stream)
+            tp.deliver(ring, ws, nbytes=slice_bytes, flags=flags, stream=side)
             cur.wait_stream(side)
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
@@ -250,7 +234,6 @@ def bench_ag(case, args, detail):
         case, (tp.NO_COPY | tp.SERIAL_STAGES) if args.isolate_kernels else 0)
     dtype = "fp8_e4m3" if case.dtype == "e4m3" else "bf16"
     flop = case.flop
-    hip = Hip()
 
     ms = time_steps(lambda: call(0), args.steps, args.warmup)
     value = flop / (ms * 1e-3) / 1e12
@@ -278,8 +261,10 @@ def bench_ag(case, args, detail):
 
     if not args.quick:
         t_compute = time_steps(bufs["compute_only"], args.steps, args.warmup)
-        t_copy = time_steps(deliveries(hip, 3), args.steps, args.warmup)          # shader copy
-        t_copy_sdma = time_steps(deliveries(hip, 1024), args.steps, args.warmup)  # copy engines
+        t_copy = time_steps(deliveries(0), args.steps, args.warmup)               # the AG default: copy kernel
+        t_copy_sdma = time_steps(deliveries(tp.COPY_SDMA), args.steps, args.warmup)  # copy engines
+        t_copy_shader = time_steps(deliveries(tp.COPY_SHADER), args.steps, args.warmup)  # runtime shader copy
+        t_shader = time_steps(lambda: call(tp.COPY_SHADER), args.steps, args.warmup)
         t_unstaged = time_steps(lambda: call(tp.UNSTAGED), args.steps, args.warmup)
         t_per_stage = time_steps(lambda: call(0, case.P - 1), args.steps, args.warmup)
         t_sdma = time_steps(lambda: call(tp.COPY_SDMA), args.steps, args.warmup)
@@ -302,6 +287,8 @@ def bench_ag(case, args, detail):
             "us_staged_copy_engines": round(t_sdma * 1e3, 2),
             "us_deliveries_alone_copy_engines": round(t_copy_sdma * 1e3, 2),
             "hidden_fraction_copy_engines": None if hidden_sdma is None else round(hidden_sdma, 3),
+            "us_staged_runtime_shader_copy": round(t_shader * 1e3, 2),
+            "us_deliveries_alone_runtime_shader_copy": round(t_copy_shader * 1e3, 2),
             "us_staged_l2_flushed": {k: round(v * 1e3, 2) for k, v in flushed.items()},
             "tflops_compute_only": round(flop / (t_compute * 1e-3) / 1e12, 1),
         })

@@ -27,7 +27,7 @@ ROTATE_A, ROTATE_B = 0, 1       # all-gather schedules
 TILE_A, TILE_B = 0, 1           # reduce-scatter schedules
 GATHER_X, GATHER_G = 0, 1       # weight gradient: which operand arrives as slices
 UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE, FORCE_GRAPH = 1, 2, 4, 8, 16, 32, 64
-DEBUG_HOLD_DELIVERIES, COPY_SHADER = 128, 256
+DEBUG_HOLD_DELIVERIES, COPY_SHADER, COPY_KERNEL = 128, 256, 512
 
 _STATUS = {OK: "OK", ERR_INVALID: "INVALID", ERR_UNSUPPORTED: "UNSUPPORTED",
            ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP"}
@@ -108,6 +108,7 @@ def lib():
             ("tpg_release_caches", [], None),
             ("tpg_profile_read", [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double), i32], i32),
             ("tpg_device_info", [ctypes.POINTER(i32)] * 3, i32),
+            ("tpg_deliver", [ctypes.POINTER(vp), i32, ctypes.c_size_t, vp, ctypes.c_size_t, ctypes.c_uint32, vp], i32),
             ("tpg_mfma_probe", [i32, i32, i32, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double), vp], i32),
         ]:
             fn = getattr(L, name)
@@ -363,6 +364,13 @@ def profile_read(cap=4096):
     fl = (ctypes.c_double * cap)()
     n = lib().tpg_profile_read(ms, fl, cap)
     return [(ms[i], fl[i]) for i in range(n)]
+
+
+def deliver(srcs, dst, *, nbytes, dst_stride=None, flags=0, stream=None):
+    """The stage delivery alone: srcs[i] (nbytes each) to dst + i * dst_stride."""
+    arr = _ptr_array(srcs)
+    _check(lib().tpg_deliver(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), len(srcs), nbytes, _ptr(dst),
+                             nbytes if dst_stride is None else dst_stride, flags, _stream(stream)))
 
 
 def device_info():

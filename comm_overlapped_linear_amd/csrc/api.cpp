@@ -52,7 +52,8 @@ constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
                                  TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH |
-                                 TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER;
+                                 TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER | TPG_COPY_KERNEL;
+constexpr uint32_t kCopyFlags = TPG_COPY_SDMA | TPG_COPY_SHADER | TPG_COPY_KERNEL;
 // Staged calls below this many flops run on one stream: their GEMMs take
 // well under the few microseconds each cross-stream event costs (the P = 2
 // bf16 workload: 20 us on one stream, 40-45 us on two).
@@ -208,9 +209,41 @@ tpg_status hold_deliveries(uint32_t flags, hipStream_t s) {
 
 // Delivery copy: the entry point's default unless a flag overrides it
 // (the defaults and their measurements are stated in tpgemm.h).
-hipMemcpyKind copy_kind(uint32_t flags, bool sdma_default) {
-  const bool sdma = (flags & TPG_COPY_SDMA) || (sdma_default && !(flags & TPG_COPY_SHADER));
-  return sdma ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+enum class Copy { Kernel, Shader, Sdma };
+
+Copy copy_of(uint32_t flags, Copy dflt) {
+  if (flags & TPG_COPY_SDMA) return Copy::Sdma;
+  if (flags & TPG_COPY_SHADER) return Copy::Shader;
+  if (flags & TPG_COPY_KERNEL) return Copy::Kernel;
+  return dflt;
+}
+
+bool copy_flags_ok(uint32_t flags) {
+  const uint32_t c = flags & kCopyFlags;
+  return (c & (c - 1)) == 0;                       // at most one copy kind
+}
+
+// n slices of `bytes` from src[0..n) to dst + i * dst_stride on stream s:
+// one launch of the library's delivery kernel, or runtime copies (slices
+// back to back in memory and in the slots move as one copy). Arguments the
+// kernel does not take (unaligned sizes) go to the runtime's shader copy.
+tpg_status deliver_slices(Copy k, const void* const* src, int n, size_t bytes, char* dst, size_t dst_stride,
+                          hipStream_t s) {
+  if (n <= 0 || bytes == 0) return TPG_OK;
+  if (k == Copy::Kernel && tpg::deliver_ok(src, n, bytes, dst, dst_stride)) {
+    HIP_TRY(tpg::launch_deliver(src, n, bytes, dst, dst_stride, s));
+    return TPG_OK;
+  }
+  const hipMemcpyKind mk = k == Copy::Sdma ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+  for (int i = 0; i < n;) {
+    int run = 1;
+    while (dst_stride == bytes && i + run < n &&
+           static_cast<const char*>(src[i + run]) == static_cast<const char*>(src[i]) + run * bytes)
+      ++run;
+    HIP_TRY(hipMemcpyAsync(dst + i * dst_stride, src[i], run * bytes, mk, s));
+    i += run;
+  }
+  return TPG_OK;
 }
 
 // Records `enqueue` into a graph once per key and replays it on `user`, or
@@ -275,8 +308,8 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   if (rotb && a->epilogue != TPG_EPI_ALPHA_BETA)
     return fail(TPG_ERR_UNSUPPORTED, "TPG_ROTATE_B needs the alpha/beta epilogue");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
-  if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
-    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
+  if (!copy_flags_ok(a->flags))
+    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
   if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
   if (a->epilogue != TPG_EPI_ALPHA_BETA && a->epilogue != TPG_EPI_SWIGLU)
@@ -387,7 +420,8 @@ tpg_status enqueue_ag_rotb(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   const int64_t n = a.N / P;
   const size_t slice_b = size_t(n) * a.K * eb;
   const bool copies = !(a.flags & TPG_NO_COPY) && slice_b > 0 && (P > 1 || (a.flags & TPG_UNSTAGED));
-  const hipMemcpyKind kind = copy_kind(a.flags, false);
+  const Copy ck = copy_of(a.flags, Copy::Kernel);
+  const hipMemcpyKind kind2d = ck == Copy::Sdma ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
   char* ws = static_cast<char*>(a.workspace);
   uint16_t* D = static_cast<uint16_t*>(a.d);
   const uint16_t* C = static_cast<const uint16_t*>(a.c);
@@ -405,14 +439,13 @@ tpg_status enqueue_ag_rotb(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
   const int layout = kn ? tpg::kKN : tpg::kNK;
 
-  // slice s into receive slot j of a W-slot receive area
-  auto deliver = [&](int j, int s, int W) -> tpg_status {
-    if (!kn) {
-      HIP_TRY(hipMemcpyAsync(ws + j * slice_b, a.b_slices[s], slice_b, kind, L.root));
-    } else {
-      HIP_TRY(hipMemcpy2DAsync(ws + size_t(j) * n * eb, size_t(W) * n * eb, a.b_slices[s], size_t(n) * eb,
-                               size_t(n) * eb, a.K, kind, L.root));
-    }
+  // slices src[0..cnt) into receive slots j .. j+cnt of a W-slot receive area:
+  // (N, K) slots back to back; (K, N) column blocks by 2-D runtime copies
+  auto deliver = [&](int j, const void* const* src, int cnt, int W) -> tpg_status {
+    if (!kn) return deliver_slices(ck, src, cnt, slice_b, ws + j * slice_b, slice_b, L.root);
+    for (int i = 0; i < cnt; ++i)
+      HIP_TRY(hipMemcpy2DAsync(ws + size_t(j + i) * n * eb, size_t(W) * n * eb, src[i], size_t(n) * eb,
+                               size_t(n) * eb, a.K, kind2d, L.root));
     return TPG_OK;
   };
   // columns [s*n, (s+run)*n) of D from B at Bp (row stride ldb elements)
@@ -434,10 +467,8 @@ tpg_status enqueue_ag_rotb(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     if (copies) {
       tpg_status hs = hold_deliveries(a.flags, L.root);
       if (hs != TPG_OK) return hs;
-      for (int s = 0; s < P; ++s) {
-        hs = deliver(s, s, P);
-        if (hs != TPG_OK) return hs;
-      }
+      hs = deliver(0, a.b_slices, P, P);
+      if (hs != TPG_OK) return hs;
       Bp = ws;
       ldb = kn ? a.N : a.K;
     }
@@ -473,18 +504,10 @@ tpg_status enqueue_ag_rotb(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   }
   for (int g = 0; g < G; ++g) {
     if (copies) {
-      for (int t = t0(g); t < t0(g + 1);) {
-        const int s = (r + t) % P;
-        int run = 1;
-        while (t + run < t0(g + 1) && s + run < P && adjacent(s, run + 1)) ++run;
-        if (run > 1) {
-          HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.b_slices[s], run * slice_b, kind, L.root));
-        } else {
-          stat = deliver(t - 1, s, remote);
-          if (stat != TPG_OK) return stat;
-        }
-        t += run;
-      }
+      const void* src[kMaxP];
+      for (int t = t0(g); t < t0(g + 1); ++t) src[t - t0(g)] = a.b_slices[(r + t) % P];
+      stat = deliver(t0(g) - 1, src, t0(g + 1) - t0(g), remote);
+      if (stat != TPG_OK) return stat;
     }
     const bool last = g == G - 1;
     hipStream_t cs = last ? L.root : side(g + 1);
@@ -523,7 +546,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   const int64_t nout = sw ? a.N / 2 : a.N;
   const size_t slice_b = size_t(m) * a.K * eb;
   const bool copies = !(a.flags & TPG_NO_COPY) && slice_b > 0 && (P > 1 || (a.flags & TPG_UNSTAGED));
-  const hipMemcpyKind kind = copy_kind(a.flags, false);
+  const Copy ck = copy_of(a.flags, Copy::Kernel);
   char* ws = static_cast<char*>(a.workspace);
 
   tpg::GemmParams p = base_params();
@@ -547,8 +570,8 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     if (copies) {
       tpg_status hs = hold_deliveries(a.flags, L.root);
       if (hs != TPG_OK) return hs;
-      for (int s = 0; s < P; ++s)
-        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.a_slices[s], slice_b, kind, L.root));
+      hs = deliver_slices(ck, a.a_slices, P, slice_b, ws, slice_b, L.root);
+      if (hs != TPG_OK) return hs;
       A = ws;
     }
     p.a = A;
@@ -609,13 +632,10 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   }
   for (int g = 0; g < G; ++g) {
     if (copies) {
-      for (int t = t0(g); t < t0(g + 1);) {
-        const int s = (r + t) % P;
-        int run = 1;
-        while (t + run < t0(g + 1) && s + run < P && adjacent(s, run + 1)) ++run;
-        HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.a_slices[s], run * slice_b, kind, L.root));
-        t += run;
-      }
+      const void* src[kMaxP];
+      for (int t = t0(g); t < t0(g + 1); ++t) src[t - t0(g)] = a.a_slices[(r + t) % P];
+      stat = deliver_slices(ck, src, t0(g + 1) - t0(g), slice_b, ws + (t0(g) - 1) * slice_b, slice_b, L.root);
+      if (stat != TPG_OK) return stat;
     }
     const bool last = g == G - 1;
     hipStream_t cs = last ? L.root : side(g + 1);
@@ -675,8 +695,8 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
   if (tileb && a->N % a->P) return fail(TPG_ERR_INVALID, "TPG_TILE_B: N must be a multiple of P");
   if (tileb && (a->N / a->P) % 8) return fail(TPG_ERR_UNSUPPORTED, "TPG_TILE_B: N/P must be a multiple of 8");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
-  if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
-    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
+  if (!copy_flags_ok(a->flags))
+    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
   if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
   if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
@@ -730,7 +750,7 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   const size_t part_b = rs_part_bytes(&a);
   const size_t slot = rs_slot(&a);
   char* ws = static_cast<char*>(a.workspace);
-  const hipMemcpyKind kind = copy_kind(a.flags, true);
+  const Copy ck = copy_of(a.flags, Copy::Sdma);
 
   // peers whose partial for block `rank` arrives, in ring order rank+1, rank+2, ...
   std::vector<int> peers;
@@ -773,17 +793,9 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     if (!copies) return TPG_OK;
     tpg_status hs = hold_deliveries(a.flags, L.root);
     if (hs != TPG_OK) return hs;
-    // partials that sit back to back in memory (and in the slots) move as one copy
-    for (size_t i = 0; i < peers.size();) {
-      size_t run = 1;
-      while (slot == part_b && i + run < peers.size() &&
-             static_cast<const char*>(a.incoming[peers[i + run]]) ==
-                 static_cast<const char*>(a.incoming[peers[i]]) + run * part_b)
-        ++run;
-      HIP_TRY(hipMemcpyAsync(ws + i * slot, a.incoming[peers[i]], run * part_b, kind, L.root));
-      i += run;
-    }
-    return TPG_OK;
+    const void* src[kMaxP];
+    for (size_t i = 0; i < peers.size(); ++i) src[i] = a.incoming[peers[i]];
+    return deliver_slices(ck, src, static_cast<int>(peers.size()), part_b, ws, slot, L.root);
   };
 
   if (a.flags & TPG_UNSTAGED) {
@@ -921,8 +933,8 @@ tpg_status validate_wg(const tpg_wg_args* a, size_t need) {
   if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
   if (a->gathered != TPG_GATHER_X && a->gathered != TPG_GATHER_G) return fail(TPG_ERR_INVALID, "bad gathered");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
-  if ((a->flags & TPG_COPY_SDMA) && (a->flags & TPG_COPY_SHADER))
-    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA and TPG_COPY_SHADER are exclusive");
+  if (!copy_flags_ok(a->flags))
+    return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
     return fail(TPG_ERR_UNSUPPORTED, "dimensions must be below 2^31");
   const int64_t m = a->M / a->P;
@@ -983,8 +995,8 @@ tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
   const int64_t lw = gx ? a.N : a.K;              // row width of the local operand
   const size_t slice_b = wg_slice_bytes(&a);
   const bool copies = !(a.flags & TPG_NO_COPY);
-  const hipMemcpyKind kind = copy_kind(a.flags, false);
-  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  const Copy ck = copy_of(a.flags, Copy::Kernel);
+  char* ws = static_cast<char*>(a.workspace);
   float* part = wg_chain(&a) ? reinterpret_cast<float*>(ws + wg_recv(&a)) : nullptr;
   const char* loc = static_cast<const char*>(a.local);
 
@@ -1035,12 +1047,8 @@ tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
     if (copies) {
       tpg_status hs = hold_deliveries(a.flags, L.root);
       if (hs != TPG_OK) return hs;
-      for (int s = 0; s < P;) {                   // rank order
-        int run = 1;
-        while (s + run < P && adjacent(s, run + 1)) ++run;
-        HIP_TRY(hipMemcpyAsync(ws + s * slice_b, a.slices[s], run * slice_b, kind, L.root));
-        s += run;
-      }
+      hs = deliver_slices(ck, a.slices, P, slice_b, ws, slice_b, L.root);   // rank order
+      if (hs != TPG_OK) return hs;
       g = ws;
     }
     return launch(L.root, g, 0, a.M, true, true);
@@ -1064,13 +1072,10 @@ tpg_status enqueue_wg(Ctx& cx, const tpg_wg_args& a, const Launch& L) {
   for (int g = 0; g < G; ++g) {
     const bool last_run = g == G - 1;
     if (copies) {
-      for (int t = t0(g); t < t0(g + 1);) {
-        const int s = (r + t) % P;
-        int run = 1;
-        while (t + run < t0(g + 1) && s + run < P && adjacent(s, run + 1)) ++run;
-        HIP_TRY(hipMemcpyAsync(ws + (t - 1) * slice_b, a.slices[s], run * slice_b, kind, L.root));
-        t += run;
-      }
+      const void* src[kMaxP];
+      for (int t = t0(g); t < t0(g + 1); ++t) src[t - t0(g)] = a.slices[(r + t) % P];
+      stat = deliver_slices(ck, src, t0(g + 1) - t0(g), slice_b, ws + (t0(g) - 1) * slice_b, slice_b, L.root);
+      if (stat != TPG_OK) return stat;
       hipStream_t rs = cs;
       if (ns > 1 && !last_run) {
         HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
@@ -1350,6 +1355,25 @@ tpg_status dispatch_permute(const void* const* src, void* dst, int32_t P, int32_
 tpg_status combine_permute(const void* const* src, void* dst, int32_t P, int32_t rank, int64_t B,
                            int64_t T, int64_t D, int32_t elem_bytes, void* stream) {
   return guarded([&]() { return permute_common(false, src, dst, P, rank, B, T, D, elem_bytes, stream); });
+}
+
+tpg_status tpg_deliver(const void* const* src, int32_t n, size_t bytes, void* dst, size_t dst_stride,
+                       uint32_t flags, void* stream) {
+  return guarded([&]() -> tpg_status {
+    if (n < 0 || n > kMaxP) return fail(TPG_ERR_INVALID, "n must be in [0, 64]");
+    if (flags & ~kCopyFlags) return fail(TPG_ERR_INVALID, "only copy-kind flags apply");
+    if (!copy_flags_ok(flags)) return fail(TPG_ERR_INVALID, "copy-kind flags are exclusive");
+    if (n == 0 || bytes == 0) return TPG_OK;
+    if (!src || !dst) return fail(TPG_ERR_INVALID, "NULL src or dst");
+    if (dst_stride < bytes) return fail(TPG_ERR_INVALID, "dst_stride < bytes");
+    const Range dr{dst, dst_stride * (n - 1) + bytes};
+    for (int i = 0; i < n; ++i) {
+      if (!src[i]) return fail(TPG_ERR_INVALID, "NULL source slice");
+      if (overlaps(dr, Range{src[i], bytes})) return fail(TPG_ERR_INVALID, "dst overlaps a source");
+    }
+    return deliver_slices(copy_of(flags, Copy::Kernel), src, n, bytes, static_cast<char*>(dst), dst_stride,
+                          static_cast<hipStream_t>(stream));
+  });
 }
 
 tpg_status tpg_device_info(int32_t* cus, int32_t* clock_khz, int32_t* wall_clock_khz) {

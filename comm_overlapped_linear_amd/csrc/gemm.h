@@ -96,6 +96,20 @@ hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t l
 // the fill may sit in a captured graph.
 hipError_t launch_fill_zero16(void* p, size_t bytes, hipStream_t s);
 
+// Stage deliveries (the library's own copy kernel): n slices of `bytes`,
+// slice i from src[i] to dst + i * dst_stride. deliver_ok says whether the
+// kernel takes the arguments (16-byte aligned pointers, sizes and stride,
+// n <= kMaxDeliver); the caller uses a runtime copy otherwise.
+constexpr int kMaxDeliver = 64;
+struct DeliverParams {
+  const uint8_t* src[kMaxDeliver];
+  uint8_t* dst;
+  int64_t dst_stride;
+  int64_t nvec;            // 16-byte vectors per slice
+};
+bool deliver_ok(const void* const* src, int n, size_t bytes, const void* dst, size_t dst_stride);
+hipError_t launch_deliver(const void* const* src, int n, size_t bytes, void* dst, size_t dst_stride, hipStream_t s);
+
 // Bit-exact run permute used by dispatch / combine.
 struct PermuteParams {
   const uint8_t* src[64];

@@ -12,6 +12,9 @@
 // layout, and parameters") are unions of contiguous runs (one per source rank
 // and batch row, L*D elements long); each workgroup copies 16-byte chunks of
 // one run, bit-exactly.
+#include <algorithm>
+#include <cstring>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -152,6 +155,37 @@ __global__ __launch_bounds__(kPermThreads) void permute1_kernel(const PermutePar
     dst[i] = src[i];
 }
 
+// Stage deliveries: n slices of nvec 16-byte vectors, slice s from src[s] to
+// dst + s * dst_stride. blockIdx.y picks the slice; the x blocks stride over
+// it, eight vectors in flight per thread. The loads are non-temporal (the
+// sources are read once); the stores are ordinary, so the receive slots stay
+// in L2 and the Infinity Cache for the stage GEMM that reads them next.
+// Measured on MI355X, 7 x 8 MiB with cold caches: 22.8 us (5.1 TB/s read +
+// write), against 40 us for seven runtime copies and 34 us for the same
+// kernel with ordinary loads.
+constexpr int kDelThreads = 256;
+constexpr int kDelUnroll = 8;
+
+__global__ __launch_bounds__(kDelThreads) void deliver16_kernel(const DeliverParams p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* src = reinterpret_cast<const u32x4*>(p.src[blockIdx.y]);
+  u32x4* dst = reinterpret_cast<u32x4*>(p.dst + int64_t(blockIdx.y) * p.dst_stride);
+  const int64_t step = int64_t(gridDim.x) * kDelThreads * kDelUnroll;
+  for (int64_t base = int64_t(blockIdx.x) * kDelThreads * kDelUnroll + threadIdx.x; base < p.nvec; base += step) {
+    u32x4 v[kDelUnroll];
+#pragma unroll
+    for (int u = 0; u < kDelUnroll; ++u) {
+      const int64_t i = base + u * kDelThreads;
+      if (i < p.nvec) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kDelUnroll; ++u) {
+      const int64_t i = base + u * kDelThreads;
+      if (i < p.nvec) dst[i] = v[u];
+    }
+  }
+}
+
 // Zero fill in 16-byte vector stores (used where a result is an empty sum).
 __global__ __launch_bounds__(256) void fill_zero16_kernel(uint4* p, int64_t n16) {
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256)
@@ -165,6 +199,33 @@ hipError_t launch_fill_zero16(void* p, size_t bytes, hipStream_t s) {
   if (n16 == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 4096);
   hipLaunchKernelGGL(fill_zero16_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+bool deliver_ok(const void* const* src, int n, size_t bytes, const void* dst, size_t dst_stride) {
+  if (n < 1 || n > kMaxDeliver || bytes % 16 || dst_stride % 16 || dst_stride < bytes ||
+      reinterpret_cast<uintptr_t>(dst) % 16)
+    return false;
+  for (int i = 0; i < n; ++i)
+    if (!src[i] || reinterpret_cast<uintptr_t>(src[i]) % 16) return false;
+  return true;
+}
+
+hipError_t launch_deliver(const void* const* src, int n, size_t bytes, void* dst, size_t dst_stride, hipStream_t s) {
+  if (n == 0 || bytes == 0) return hipSuccess;
+  if (!deliver_ok(src, n, bytes, dst, dst_stride)) return hipErrorInvalidValue;
+  DeliverParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int i = 0; i < n; ++i) p.src[i] = static_cast<const uint8_t*>(src[i]);
+  p.dst = static_cast<uint8_t*>(dst);
+  p.dst_stride = static_cast<int64_t>(dst_stride);
+  p.nvec = static_cast<int64_t>(bytes / 16);
+  // about eight workgroups per CU over all slices (measured best), none idle
+  const int64_t per_slice = (p.nvec + kDelThreads * kDelUnroll - 1) / (kDelThreads * kDelUnroll);
+  const int64_t want = std::max<int64_t>(1, (int64_t(8) * device_cus() + n - 1) / n);
+  const int64_t bx = std::min(per_slice, want);
+  hipLaunchKernelGGL(deliver16_kernel, dim3(static_cast<unsigned>(bx), static_cast<unsigned>(n)), dim3(kDelThreads),
+                     0, s, p);
   return hipGetLastError();
 }
 

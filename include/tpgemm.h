@@ -8,12 +8,14 @@
  * the local shard while the rest is delivered ("Distributed GEMM", Hassani
  * et al., SHI Labs, Dec 2024: Introduction and Background, Figures 3 and 4).
  * Which copy: the all-gather's deliveries are on its critical path, so it
- * uses the faster shader copy (seven 8 MiB slices: ~34 us, against ~64 us
- * on the SDMA copy engines; the SwiGLU AG share: 251 vs 329 us). The
- * reduce-scatter's deliveries hide behind the emitted blocks, so it uses the
- * copy engines, which take no CUs from those GEMMs, as the pages'
- * copy-engine design intends (the bf16 RS share: equal within noise, 460 vs
- * 459 us). TPG_COPY_SDMA / TPG_COPY_SHADER override either default.
+ * uses the library's own copy kernel (non-temporal loads, eight 16-byte
+ * vectors in flight per thread: seven 8 MiB slices in 22.8 us with cold
+ * caches, against 40 us for the runtime's copies and ~64 us on the SDMA
+ * copy engines). The reduce-scatter's deliveries hide behind the emitted
+ * blocks, so it uses the copy engines, which take no CUs from those GEMMs,
+ * as the pages' copy-engine design intends (the bf16 RS share: equal within
+ * noise, 460 vs 459 us against the shader copy). TPG_COPY_SDMA /
+ * TPG_COPY_SHADER / TPG_COPY_KERNEL override either default (one at most).
  *
  * Conventions shared by every entry point
  *   - All pointers to tensor data are DEVICE pointers owned by the caller;
@@ -93,7 +95,8 @@ enum {
   TPG_FORCE_GRAPH = 64u,    /* record the call into a hipGraph once, replay it after */
   TPG_DEBUG_HOLD_DELIVERIES = 128u, /* testing: issue eagerly, with the deliveries queued behind a 20 ms
                                        host callback; every gated stage must still see its data */
-  TPG_COPY_SHADER = 256u    /* deliver with the shader copy (uses CUs); the AG default */
+  TPG_COPY_SHADER = 256u,   /* deliver with the runtime's shader copy (hipMemcpyAsync, uses CUs) */
+  TPG_COPY_KERNEL = 512u    /* deliver with the library's copy kernel (uses CUs); the AG and wgrad default */
 };
 
 /* ------------------------------------------------------------------------
@@ -333,6 +336,19 @@ tpg_status dispatch_permute(const void* const* src, void* dst, int32_t P, int32_
                             int64_t B, int64_t T, int64_t D, int32_t elem_bytes, void* stream);
 tpg_status combine_permute(const void* const* src, void* dst, int32_t P, int32_t rank,
                            int64_t B, int64_t T, int64_t D, int32_t elem_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The stage delivery alone ("Distributed GEMM", Background, Figure 4: each
+ * stage's input is copied in while the previous stage computes), as the
+ * staged calls issue it: n slices of `bytes`, slice i from src[i] to
+ * dst + i * dst_stride, on `stream`, with the copy kind the flags select
+ * (TPG_COPY_KERNEL when none; only copy-kind flags are accepted). src is a
+ * host array of n device pointers; dst must not overlap any source.
+ * Bit-exact. Errors: TPG_ERR_INVALID (n outside [0, 64], NULL pointers,
+ * dst_stride < bytes, overlap, flags).
+ * ---------------------------------------------------------------------- */
+tpg_status tpg_deliver(const void* const* src, int32_t n, size_t bytes, void* dst, size_t dst_stride,
+                       uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement aids, outside the staged GEMM: the rate the matrix cores

@@ -171,6 +171,7 @@ def wg(**kw):
     (dict(d=FAKE), tp.ERR_INVALID),                       # D overlaps local
     (dict(flags=1 << 20), tp.ERR_INVALID),
     (dict(flags=tp.COPY_SDMA | tp.COPY_SHADER), tp.ERR_INVALID),
+    (dict(flags=tp.COPY_KERNEL | tp.COPY_SHADER), tp.ERR_INVALID),
     (dict(flags=0), tp.ERR_WORKSPACE),                    # staged needs slots and the fp32 partial
 ])
 def test_wgrad_validation_rejects_before_enqueue(kw, status):
@@ -195,3 +196,16 @@ def test_wgrad_workspace_sizes():
     a.flags = 0
     assert tp.stage_wgrad_workspace_size(a) == -(-(3 * m * N * 2) // 256) * 256 + f32
     assert tp.stage_wgrad_workspace_size(wg(P=1, M=64, flags=0, groups=1)) == 0
+
+
+def test_deliver_validation():
+    L = tp.lib()
+    srcs = (ctypes.c_void_p * 2)(FAKE, FAKE + 0x100000)
+    sp = ctypes.cast(srcs, ctypes.POINTER(ctypes.c_void_p))
+    dst = FAKE + 0x10000000
+    assert L.tpg_deliver(sp, 65, 16, dst, 16, 0, None) == tp.ERR_INVALID
+    assert L.tpg_deliver(sp, 2, 32, dst, 16, 0, None) == tp.ERR_INVALID                 # stride < bytes
+    assert L.tpg_deliver(sp, 2, 32, dst, 32, tp.COPY_SDMA | tp.COPY_KERNEL, None) == tp.ERR_INVALID
+    assert L.tpg_deliver(sp, 2, 32, dst, 32, tp.UNSTAGED, None) == tp.ERR_INVALID         # not a copy flag
+    assert L.tpg_deliver(sp, 2, 32, FAKE + 16, 32, 0, None) == tp.ERR_INVALID             # overlaps a source
+    assert L.tpg_deliver(sp, 0, 32, dst, 32, 0, None) == tp.OK                            # nothing to move

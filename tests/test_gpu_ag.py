@@ -12,7 +12,7 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
-         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "sdma": tp.COPY_SDMA}
+         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES | tp.NO_GRAPH, "sdma": tp.COPY_SDMA, "shader": tp.COPY_SHADER}
 
 
 def run_ag(case, inp, flags, rank=None):

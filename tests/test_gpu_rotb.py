@@ -14,9 +14,9 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 AG_MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
-            "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "sdma": tp.COPY_SDMA}
+            "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "sdma": tp.COPY_SDMA, "shader": tp.COPY_SHADER}
 RS_MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
-            "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "shader": tp.COPY_SHADER}
+            "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "shader": tp.COPY_SHADER, "kernel": tp.COPY_KERNEL}
 
 
 def run_ag_rotb(case, inp, flags, groups=0, workspace=None):

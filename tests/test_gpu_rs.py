@@ -12,7 +12,8 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
-         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "shader": tp.COPY_SHADER | tp.NO_GRAPH}
+         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "shader": tp.COPY_SHADER | tp.NO_GRAPH,
+         "kernel": tp.COPY_KERNEL}
 
 
 def run_rs(case, inp, flags, incoming=True):

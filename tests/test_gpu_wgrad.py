@@ -17,7 +17,7 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 MODES = {"default": 0, "graph": tp.FORCE_GRAPH, "eager": tp.NO_GRAPH, "unstaged": tp.UNSTAGED,
-         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "sdma": tp.COPY_SDMA}
+         "no_copy": tp.NO_COPY, "serial": tp.SERIAL_STAGES, "sdma": tp.COPY_SDMA, "shader": tp.COPY_SHADER}
 
 
 def gathered_of(case):
@@ -66,7 +66,7 @@ def test_wgrad_parity_all_modes(case):
     d = run(case, inp, tp.UNSTAGED | tp.NO_COPY, slices=sl)
     assert_parity(host_f64(d), ref, f"{case.name}/unstaged in place")
     # the same launches give the same bits whatever the issue mode
-    for name in ("graph", "eager", "serial", "sdma"):
+    for name in ("graph", "eager", "serial", "sdma", "shader"):
         assert torch.equal(outs[name, 1], outs["default", 1]), name
         assert torch.equal(outs[name, 0], outs["default", 0]), name
     assert torch.equal(outs["unstaged", 1], outs["default", 0])
