@@ -212,3 +212,22 @@ def gemm_rs_tileb_rows(a, b, incoming, alpha, rank, P, b_layout, rows):
             if j != rank and incoming[j] is not None:
                 out[:, cols] = out[:, cols] + decode_bf16(incoming[j][np.asarray(rows)])
     return out
+
+
+def gemm_ag_multi(a_slices, bs, alpha, rank, dtype="bf16"):
+    """Several column-parallel projections sharing one all-gathered input
+    ("Add dist GEMM attention and FFN backend", Structure: AllGatherLinearMulti
+    serves several linears that share one input, one all-gather for all;
+    AllGatherFusedQKVLinear is the three-way case, wq / wk / wv in their own
+    (N_i, K) layouts). Returns [alpha * A @ B_i^T for each B_i], A the slices
+    gathered in rank order; stage t multiplies slice (rank + t) mod P by every
+    B_i."""
+    P = len(a_slices)
+    m = a_slices[0].shape[0]
+    outs = [np.empty((P * m, b.shape[0]), dtype=np.float64) for b in bs]
+    Bs = [decode(b, dtype) for b in bs]
+    for s in ag_stage_order(P, rank):
+        As = decode(a_slices[s], dtype)
+        for o, Bm in zip(outs, Bs):
+            o[s * m:(s + 1) * m] = alpha * (As @ Bm.T)
+    return outs

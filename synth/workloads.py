@@ -276,6 +276,53 @@ def swiglu_inputs(case: SwigluCase, seed: int = SEED):
 
 
 # --------------------------------------------------------------------------
+# several column-parallel projections of one gathered input (fused QKV)
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class AgmCase:
+    name: str
+    M: int          # gathered rows: P slices of m = M/P
+    K: int
+    P: int
+    ns: tuple       # output widths of the projections, e.g. (Nq, Nk, Nv)
+    rank: int = 0
+    dtype: str = "bf16"
+    alpha: float = 1.0
+
+    @property
+    def m(self):
+        return self.M // self.P
+
+    @property
+    def flop(self):
+        return 2.0 * self.M * sum(self.ns) * self.K
+
+
+def ag_multi_inputs(case: AgmCase, seed: int = SEED):
+    """dict(a_slices=[P x (m, K)], bs=[(N_i, K)]): the sequence shards N(0, 1)
+    (slice s from rank s's stream) and the projection weights N(0, 0.02)
+    (this rank's shards), bf16; e4m3 operands from clip(0.5 N(0,1))."""
+    def op(key, shape, std):
+        if case.dtype == "e4m3":
+            return normal_e4m3(key, shape, scale=0.5, clip=448.0)
+        return normal_bf16(key, shape, 0.0, std)
+    slices = [op(stream_key(seed + s, "agm.x"), (case.m, case.K), 1.0) for s in range(case.P)]
+    bs = [op(stream_key(seed + case.rank, f"agm.w{i}"), (n, case.K), 0.02) for i, n in enumerate(case.ns)]
+    return dict(a_slices=slices, bs=bs)
+
+
+SMALL_AGM = [
+    AgmCase("agm_bf16_p4_qkv_small", M=4 * 96, K=264, P=4, ns=(136, 40, 40), rank=1),
+    AgmCase("agm_e4m3_p8_qkv_small", M=8 * 64, K=512, P=8, ns=(256, 64, 64), rank=6, dtype="e4m3", alpha=0.5),
+    AgmCase("agm_bf16_p2_two_medium", M=2 * 1024, K=1024, P=2, ns=(1032, 520), rank=1),
+    AgmCase("agm_bf16_p8_qkv_medium", M=8 * 256, K=2048, P=8, ns=(512, 128, 128), rank=3),
+]
+# the fused QKV projection of an 8B-class model (32 query heads, 8 KV heads,
+# head dim 128, D = 4096) at TP = 8: per rank 512 + 128 + 128 columns, 8192 tokens
+QKV = AgmCase("ag_qkv_bf16_p8_8192x768x4096", M=8192, K=4096, P=8, ns=(512, 128, 128))
+
+
+# --------------------------------------------------------------------------
 # weight gradient of the all-gather / reduce-scatter linears
 # --------------------------------------------------------------------------
 @dataclass(frozen=True)

@@ -271,3 +271,27 @@ def test_rs_tileb_distributed_identity(P):
         incoming = [None if j == r else bf16_bits(emitted[j][:, r * n:(r + 1) * n]) for j in range(P)]
         out = oracle.gemm_rs_tileb(A[r], Bs[r], incoming, 1.0, r, P)
         assert np.array_equal(out[:, r * n:(r + 1) * n], full[:, r * n:(r + 1) * n])
+
+
+def test_ag_multi_brute_force_and_concatenation():
+    """Several projections of one gathered input: brute force on a tiny case,
+    and the concatenation identity [A Bq^T | A Bk^T | A Bv^T] = A [Bq; Bk; Bv]^T
+    against the single-B all-gather oracle."""
+    rng = np.random.default_rng(21)
+    P, m, K = 2, 2, 3
+    slices = [rand_int_bf16(rng, (m, K)) for _ in range(P)]
+    bs = [rand_int_bf16(rng, (n, K)) for n in (3, 1, 2)]
+    outs = oracle.gemm_ag_multi(slices, bs, 0.5, rank=1)
+    A = [[oracle.decode_bf16(v) for v in row] for s in slices for row in s]
+    for o, b in zip(outs, bs):
+        for i in range(P * m):
+            for j in range(b.shape[0]):
+                ref = 0.5 * sum(A[i][k] * oracle.decode_bf16(b[j, k]) for k in range(K))
+                assert o[i, j] == ref
+    rng = np.random.default_rng(22)
+    P, m, K = 4, 3, 16
+    slices = [rand_int_bf16(rng, (m, K)) for _ in range(P)]
+    bs = [rand_int_bf16(rng, (n, K)) for n in (8, 4, 4)]
+    outs = oracle.gemm_ag_multi(slices, bs, 1.0, rank=2, dtype="bf16")
+    whole = oracle.gemm_ag(slices, np.concatenate(bs, axis=0), None, 1.0, 0.0, rank=0)
+    np.testing.assert_array_equal(np.concatenate(outs, axis=1), whole)
