@@ -408,6 +408,34 @@ def bench_wgrad(args):
     return out
 
 
+def bench_qkv(args):
+    """The fused QKV projection (several projections of one gathered input)
+    of an 8B-class model at TP = 8: 8192 tokens, K = 4096, 512 + 128 + 128
+    output columns per rank, bf16; weights apart (copied side by side each
+    call) and back to back (read in place)."""
+    case = W.QKV
+    inp = W.ag_multi_inputs(case)
+    slices = [dev(s) for s in inp["a_slices"]]
+    apart = [dev(b) for b in inp["bs"]]
+    whole = dev(np.concatenate(inp["bs"], axis=0))
+    offs = np.cumsum([0] + list(case.ns))
+    adjacent = [whole[offs[i]:offs[i + 1]] for i in range(len(case.ns))]
+    ds = [torch.empty((case.M, n), dtype=torch.int16, device="cuda") for n in case.ns]
+    kw = dict(M=case.M, K=case.K)
+
+    def prepared(bs):
+        need = max(tp.stage_ag_multi_workspace_size(tp.ag_multi_args(slices, bs, ds, flags=f, **kw))
+                   for f in (0, tp.UNSTAGED))
+        return tp.prepare_stage_ag_multi(slices, bs, ds, workspace=torch.empty(need, dtype=torch.uint8,
+                                                                                device="cuda"), **kw)
+    call, inplace = prepared(apart), prepared(adjacent)
+    ms = time_steps(lambda: call(flags=0), args.steps, args.warmup)
+    ms_in = time_steps(lambda: inplace(flags=0), args.steps, args.warmup)
+    ms_un = time_steps(lambda: inplace(flags=tp.UNSTAGED), args.steps, args.warmup)
+    return {case.name: dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1),
+                            us_weights_adjacent=round(ms_in * 1e3, 1), us_unstaged=round(ms_un * 1e3, 1))}
+
+
 def bench_small_ag(case, args):
     inp, call, _, _ = setup_ag(case)
     ms = time_steps(lambda: call(0), args.steps, args.warmup)
@@ -473,6 +501,7 @@ def main():
         detail["swiglu_p8_s1024_d4096_f1792"] = bench_swiglu(W.C5, args)
         detail.update(bench_column_duals(args))
         detail.update(bench_wgrad(args))
+        detail.update(bench_qkv(args))
         log(f"[other] {json.dumps({k: detail[k] for k in ('ag_bf16_p2_256x256x512', 'rs_bf16_p8_8192x8192x3584', 'swiglu_p8_s1024_d4096_f1792')})}")
 
     cpu = None

@@ -7,7 +7,7 @@ tensors may be torch.bfloat16 or raw int16/uint16 bits, e4m3 tensors
 torch.float8_e4m3fn or raw uint8 bits.
 
 The names follow the C ABI in include/tpgemm.h:
-    stage_ag, stage_rs, stage_wgrad, ffn_slot_forward, dispatch_permute, combine_permute
+    stage_ag, stage_ag_multi, stage_rs, stage_wgrad, ffn_slot_forward, dispatch_permute, combine_permute
 (plus the *_workspace_size queries, last_error, release_caches, profile_read,
 device_info, mfma_probe).
 """
@@ -62,6 +62,19 @@ class RsArgs(ctypes.Structure):
                 ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
+MAX_PROJ = 4
+
+
+class AgmArgs(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("P", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("ab_dtype", ctypes.c_int32), ("n_out", ctypes.c_int32),
+                ("a_slices", ctypes.POINTER(ctypes.c_void_p)),
+                ("b", ctypes.c_void_p * MAX_PROJ), ("n", ctypes.c_int64 * MAX_PROJ), ("d", ctypes.c_void_p * MAX_PROJ),
+                ("alpha", ctypes.c_float), ("flags", ctypes.c_uint32), ("groups", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class WgArgs(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("P", ctypes.c_int32), ("rank", ctypes.c_int32),
@@ -98,6 +111,8 @@ def lib():
             ("tpgemm_stage_ag_workspace_size", [ctypes.POINTER(AgArgs)], ctypes.c_size_t),
             ("tpgemm_stage_rs", [ctypes.POINTER(RsArgs), vp], i32),
             ("tpgemm_stage_rs_workspace_size", [ctypes.POINTER(RsArgs)], ctypes.c_size_t),
+            ("tpgemm_stage_ag_multi", [ctypes.POINTER(AgmArgs), vp], i32),
+            ("tpgemm_stage_ag_multi_workspace_size", [ctypes.POINTER(AgmArgs)], ctypes.c_size_t),
             ("tpgemm_stage_wgrad", [ctypes.POINTER(WgArgs), vp], i32),
             ("tpgemm_stage_wgrad_workspace_size", [ctypes.POINTER(WgArgs)], ctypes.c_size_t),
             ("ffn_slot_forward", [ctypes.POINTER(FfnArgs), vp], i32),
@@ -246,6 +261,45 @@ def stage_rs(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK
     args.workspace = _ptr(ws) if ws is not None else None
     args.workspace_bytes = ws.numel() if ws is not None else 0
     _check(lib().tpgemm_stage_rs(ctypes.byref(args), _stream(stream)))
+
+
+def ag_multi_args(a_slices, bs, ds, *, M, K, ns=None, rank=0, dtype=BF16, alpha=1.0, flags=0, groups=0):
+    """Argument struct of tpgemm_stage_ag_multi: ds[i] = alpha * A bs[i]^T for
+    up to four weights bs[i] (n[i], K) sharing the gathered A."""
+    if not 1 <= len(bs) == len(ds) <= MAX_PROJ:
+        raise ValueError("one to four weights, one output each")
+    sl = _ptr_array(a_slices)
+    ns = [b.shape[0] for b in bs] if ns is None else list(ns)
+    args = AgmArgs(M=M, K=K, P=len(a_slices), rank=rank, ab_dtype=dtype, n_out=len(bs),
+                   a_slices=ctypes.cast(sl, ctypes.POINTER(ctypes.c_void_p)), alpha=alpha, flags=flags, groups=groups)
+    for i, (b, d, n) in enumerate(zip(bs, ds, ns)):
+        args.b[i] = _ptr(b)
+        args.d[i] = _ptr(d)
+        args.n[i] = n
+    args._keep = sl
+    return args
+
+
+def stage_ag_multi_workspace_size(args):
+    return lib().tpgemm_stage_ag_multi_workspace_size(ctypes.byref(args))
+
+
+def stage_ag_multi(a_slices, bs, ds, *, M, K, ns=None, rank=0, dtype=BF16, alpha=1.0, flags=0, groups=0,
+                   workspace=None, stream=None):
+    """Several projections of one all-gathered input (the fused QKV form; see tpgemm.h)."""
+    args = ag_multi_args(a_slices, bs, ds, M=M, K=K, ns=ns, rank=rank, dtype=dtype, alpha=alpha, flags=flags,
+                         groups=groups)
+    need = stage_ag_multi_workspace_size(args)
+    ws = _workspace(workspace, need)
+    args.workspace = _ptr(ws) if ws is not None else None
+    args.workspace_bytes = ws.numel() if ws is not None else 0
+    _check(lib().tpgemm_stage_ag_multi(ctypes.byref(args), _stream(stream)))
+
+
+def prepare_stage_ag_multi(a_slices, bs, ds, *, workspace=None, **kw):
+    args = ag_multi_args(a_slices, bs, ds, **kw)
+    ws = _attach_workspace(args, stage_ag_multi_workspace_size, workspace)
+    return Prepared(lib().tpgemm_stage_ag_multi, args, (a_slices, bs, ds, ws))
 
 
 def wgrad_args(local, slices, d, *, M, N, K, rank=0, gathered=None, alpha=1.0, flags=0, groups=0):

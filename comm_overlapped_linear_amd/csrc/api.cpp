@@ -537,7 +537,32 @@ tpg_status enqueue_ag_rotb(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
   return join_streams(cx, L.root, ns, st);
 }
 
-tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
+// Column-segmented output of the all-gather (several projections sharing
+// the gathered input): output columns [col[i], col[i+1]) go to d[i], row
+// stride ld[i].
+struct OutSegs {
+  int n = 0;
+  int col[tpg::kMaxSeg] = {};
+  uint16_t* d[tpg::kMaxSeg] = {};
+  int64_t ld[tpg::kMaxSeg] = {};
+};
+
+// Points q's output at global output row `row0`: d, or every segment.
+void set_out_rows(tpg::GemmParams& q, const tpg_ag_args& a, const OutSegs* segs, int64_t row0, int64_t nout) {
+  if (!segs) {
+    q.d = static_cast<uint16_t*>(a.d) + row0 * nout;
+    return;
+  }
+  q.n_seg = segs->n;
+  for (int i = 0; i < segs->n; ++i) {
+    q.seg_col[i] = segs->col[i];
+    q.seg_d[i] = segs->d[i] + row0 * segs->ld[i];
+    q.seg_ld[i] = segs->ld[i];
+  }
+  q.d = q.seg_d[0];
+}
+
+tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutSegs* segs = nullptr) {
   if (a.schedule == TPG_ROTATE_B) return enqueue_ag_rotb(cx, a, L);
   const int P = a.P, r = a.rank;
   const int eb = elem_bytes(a.ab_dtype);
@@ -576,7 +601,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     }
     p.a = A;
     p.c = static_cast<const uint16_t*>(a.c);
-    p.d = static_cast<uint16_t*>(a.d);
+    set_out_rows(p, a, segs, 0, nout);
     p.M = static_cast<int>(a.M);
     return gemm_on(cx, L, L.root, p, dtype, layout, epi);
   }
@@ -612,7 +637,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     q.a = A;
     q.M = static_cast<int>(run * m);
     q.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
-    q.d = static_cast<uint16_t*>(a.d) + s * m * nout;
+    set_out_rows(q, a, segs, s * m, nout);
     q.cu_budget = cus;
     return gemm_on(cx, L, cs, q, dtype, layout, epi);
   };
@@ -667,6 +692,160 @@ std::string ag_key(const tpg_ag_args& a) {
   const int na = a.schedule == TPG_ROTATE_B ? 1 : a.P;
   for (int s = 0; s < na && a.a_slices; ++s) put(os, a.a_slices[s]);
   for (int s = 0; a.schedule == TPG_ROTATE_B && s < a.P && a.b_slices; ++s) put(os, a.b_slices[s]);
+  return os.str();
+}
+
+// ---------------------------------------------------------------- several projections
+// The projections of one gathered input run as one all-gather GEMM over the
+// weights side by side (N = sum n[i]); the epilogue stores each column block
+// to its own output. Weights already back to back in memory are read in
+// place; otherwise they are copied side by side into the workspace (after
+// the all-gather's receive slots) on the root stream first.
+int64_t agm_ntot(const tpg_agm_args* a) {
+  int64_t t = 0;
+  for (int i = 0; i < a->n_out && i < TPG_MAX_PROJ; ++i) t += a->n[i];
+  return t;
+}
+
+bool agm_weights_adjacent(const tpg_agm_args* a) {
+  const int eb = elem_bytes(a->ab_dtype);
+  const char* at = static_cast<const char*>(a->b[0]);
+  for (int i = 0; i < a->n_out; ++i) {
+    if (a->n[i] == 0) continue;
+    if (static_cast<const char*>(a->b[i]) != at) return false;
+    at += size_t(a->n[i]) * a->K * eb;
+  }
+  return true;
+}
+
+// The equivalent single-B all-gather call (B and D filled in by the caller).
+tpg_ag_args agm_as_ag(const tpg_agm_args* a) {
+  tpg_ag_args g;
+  std::memset(&g, 0, sizeof(g));
+  g.M = a->M;
+  g.N = agm_ntot(a);
+  g.K = a->K;
+  g.P = a->P;
+  g.rank = a->rank;
+  g.ab_dtype = a->ab_dtype;
+  g.b_layout = TPG_B_NK;
+  g.epilogue = TPG_EPI_ALPHA_BETA;
+  g.a_slices = a->a_slices;
+  g.alpha = a->alpha;
+  g.beta = 0.0f;
+  g.flags = a->flags;
+  g.groups = a->groups;
+  g.schedule = TPG_ROTATE_A;
+  return g;
+}
+
+size_t agm_ws(const tpg_agm_args* a) {
+  if (!a || a->n_out < 1 || a->n_out > TPG_MAX_PROJ || a->P < 1 || a->M < 0 || a->K < 0) return 0;
+  for (int i = 0; i < a->n_out; ++i)
+    if (a->n[i] < 0) return 0;
+  const tpg_ag_args g = agm_as_ag(a);
+  size_t need = round_up(ag_ws(&g), 256);
+  if (!agm_weights_adjacent(a)) need += round_up(size_t(g.N) * a->K * elem_bytes(a->ab_dtype), 256);
+  return need;
+}
+
+tpg_status validate_agm(const tpg_agm_args* a, size_t need) {
+  if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
+  if (a->n_out < 1 || a->n_out > TPG_MAX_PROJ) return fail(TPG_ERR_INVALID, "n_out must be in [1, 4]");
+  int64_t ntot = 0;
+  for (int i = 0; i < a->n_out; ++i) {
+    if (a->n[i] < 0 || a->n[i] % 8) return fail(TPG_ERR_INVALID, "every n[i] must be a non-negative multiple of 8");
+    ntot += a->n[i];
+  }
+  if (!fits_int(ntot)) return fail(TPG_ERR_UNSUPPORTED, "sum of n[i] must be below 2^31");
+  // the shared checks (P, rank, M, K, dtype, slices, flags) on an equivalent
+  // call with one 8-column projection (the weights and outputs are checked
+  // below, each with its own size)
+  tpg_ag_args g = agm_as_ag(a);
+  g.N = 0;
+  for (int i = 0; i < a->n_out; ++i)
+    if (a->n[i] > 0) {
+      g.N = 8;
+      g.b = a->b[i];
+      g.d = a->d[i];
+      break;
+    }
+  tpg_status st = validate_ag(&g, 0);
+  if (st != TPG_OK) return st;
+  const int eb = elem_bytes(a->ab_dtype);
+  std::vector<Range> ins, outs;
+  for (int s = 0; a->M > 0 && s < a->P; ++s) ins.push_back({a->a_slices[s], size_t(a->M / a->P) * a->K * eb});
+  for (int i = 0; i < a->n_out; ++i) {
+    if (a->n[i] == 0) continue;
+    if ((!a->b[i] && a->K) || (!a->d[i] && a->M)) return fail(TPG_ERR_INVALID, "NULL weight or output");
+    if (!aligned16(a->b[i]) || !aligned16(a->d[i])) return fail(TPG_ERR_UNSUPPORTED, "weights and outputs must be 16-byte aligned");
+    ins.push_back({a->b[i], size_t(a->n[i]) * a->K * eb});
+    outs.push_back({a->d[i], size_t(a->M) * a->n[i] * 2});
+  }
+  if (need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than tpgemm_stage_ag_multi_workspace_size()");
+  const Range wr{a->workspace, need};
+  if (need && !aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const auto& r : ins)
+      if (overlaps(outs[i], r)) return fail(TPG_ERR_INVALID, "an output overlaps an input");
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlaps(outs[i], outs[j])) return fail(TPG_ERR_INVALID, "outputs overlap each other");
+    if (overlaps(outs[i], wr)) return fail(TPG_ERR_INVALID, "workspace overlaps an output");
+  }
+  for (const auto& r : ins)
+    if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
+  return TPG_OK;
+}
+
+tpg_status enqueue_agm(Ctx& cx, const tpg_agm_args& a, const Launch& L) {
+  tpg_ag_args g = agm_as_ag(&a);
+  const int eb = elem_bytes(a.ab_dtype);
+  char* ws = static_cast<char*>(a.workspace);
+  g.workspace = ws;
+  g.workspace_bytes = a.workspace_bytes;
+  OutSegs segs;
+  int col = 0;
+  for (int i = 0; i < a.n_out; ++i) {
+    if (a.n[i] == 0) continue;
+    segs.col[segs.n] = col;
+    segs.d[segs.n] = static_cast<uint16_t*>(a.d[i]);
+    segs.ld[segs.n] = a.n[i];
+    ++segs.n;
+    col += static_cast<int>(a.n[i]);
+  }
+  g.d = segs.d[0];
+  if (agm_weights_adjacent(&a)) {
+    for (int i = 0; i < a.n_out; ++i)
+      if (a.n[i] > 0) {
+        g.b = a.b[i];
+        break;
+      }
+  } else {
+    // weights side by side after the receive slots, on the root before any stage
+    char* wb = ws + round_up(ag_ws(&g), 256);
+    size_t off = 0;
+    for (int i = 0; i < a.n_out; ++i) {
+      if (a.n[i] == 0) continue;
+      const size_t bytes = size_t(a.n[i]) * a.K * eb;
+      tpg_status st = deliver_slices(Copy::Kernel, &a.b[i], 1, bytes, wb + off, bytes, L.root);
+      if (st != TPG_OK) return st;
+      off += bytes;
+    }
+    g.b = wb;
+  }
+  return enqueue_ag(cx, g, L, &segs);
+}
+
+std::string agm_key(const tpg_agm_args& a) {
+  std::ostringstream os;
+  os << "agm|";
+  put(os, a.M); put(os, a.K); put(os, a.P); put(os, a.rank); put(os, a.ab_dtype); put(os, a.n_out);
+  for (int i = 0; i < a.n_out; ++i) {
+    put(os, a.b[i]); put(os, a.n[i]); put(os, a.d[i]);
+  }
+  put(os, a.alpha); put(os, a.flags); put(os, a.groups); put(os, a.workspace);
+  for (int s = 0; a.a_slices && s < a.P; ++s) put(os, a.a_slices[s]);
   return os.str();
 }
 
@@ -1287,6 +1466,25 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
       a.flags |= TPG_SERIAL_STAGES;
     return run_call(*cx, a.flags, ag_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ag(*cx, a, L); });
+  });
+}
+
+size_t tpgemm_stage_ag_multi_workspace_size(const tpg_agm_args* args) { return agm_ws(args); }
+
+tpg_status tpgemm_stage_ag_multi(const tpg_agm_args* args, void* stream) {
+  return guarded([&]() -> tpg_status {
+    std::lock_guard<std::mutex> lk(g_mu);
+    tpg_status st = validate_agm(args, agm_ws(args));
+    if (st != TPG_OK) return st;
+    if (args->M == 0 || agm_ntot(args) == 0) return TPG_OK;   // empty outputs: nothing to enqueue
+    Ctx* cx = nullptr;
+    st = get_ctx(&cx);
+    if (st != TPG_OK) return st;
+    tpg_agm_args a = *args;
+    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(agm_ntot(&a)) * a.K < kLatencyBoundFlop)
+      a.flags |= TPG_SERIAL_STAGES;
+    return run_call(*cx, a.flags, agm_key(a), static_cast<hipStream_t>(stream),
+                    [&](const Launch& L) { return enqueue_agm(*cx, a, L); });
   });
 }
 

@@ -10,6 +10,8 @@ constexpr int kMaxAddList = 16;
 // One GEMM launch: D = epilogue(alpha * A * B^T) over an (M, Ncols) block.
 // A (M, K) with row stride lda elements; B (N, K) (nk) or (K, N) (kn) with
 // row stride ldb. C / D / bias / addends are bf16 bit patterns.
+constexpr int kMaxSeg = 4;
+
 struct GemmParams {
   const void* a;
   const void* b;
@@ -58,6 +60,14 @@ struct GemmParams {
   const float* acc_in;
   float* acc_out;
   int64_t ld_acc;
+  // Column-segmented output (several projections of one input): with
+  // n_seg > 0, output columns [seg_col[i], seg_col[i+1]) go to seg_d[i] (row
+  // stride seg_ld[i], column 0 = seg_col[i]) instead of d; seg_col[0] == 0,
+  // boundaries multiples of 8. beta must be 0 and there is no bias.
+  int n_seg;
+  int seg_col[kMaxSeg];
+  uint16_t* seg_d[kMaxSeg];
+  int64_t seg_ld[kMaxSeg];
 };
 
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };

@@ -136,6 +136,23 @@ __device__ __forceinline__ void add_row8(const uint16_t* src, int64_t off, bool 
   }
 }
 
+// Destination of output vector (row, col .. col + 7): d, or with a
+// column-segmented output the segment holding col (uniform selects; segment
+// boundaries are multiples of 8, so a vector never straddles two).
+__device__ __forceinline__ uint16_t* out_at(const GemmParams& p, const BatchPtrs& bp, int row, int col) {
+  if (p.n_seg == 0) return bp.d + static_cast<int64_t>(row) * p.ldd + col;
+  // the segment index, then its fields by a per-lane index into the
+  // parameter block (memory loads, not SGPRs that would stay live over the
+  // whole kernel)
+  int t = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSeg; ++i) t += (i < p.n_seg && col >= p.seg_col[i]) ? 1 : 0;
+  uint16_t* base = p.seg_d[t];
+  const int64_t ld = p.seg_ld[t];
+  const int c0 = p.seg_col[t];
+  return base + static_cast<int64_t>(row) * ld + (col - c0);
+}
+
 template <bool F32IO>
 __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPtrs& bp, int row, int col, int nout,
                                               float* x) {
@@ -172,7 +189,7 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPt
       return;
     }
   }
-  uint16_t* dst = bp.d + static_cast<int64_t>(row) * p.ldd + col;
+  uint16_t* dst = out_at(p, bp, row, col);
   if (vec) {
     uint4 o;
     o.x = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
@@ -285,7 +302,7 @@ __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchP
     o.y = f32_to_bf16(x[u][2]) | (static_cast<uint32_t>(f32_to_bf16(x[u][3])) << 16);
     o.z = f32_to_bf16(x[u][4]) | (static_cast<uint32_t>(f32_to_bf16(x[u][5])) << 16);
     o.w = f32_to_bf16(x[u][6]) | (static_cast<uint32_t>(f32_to_bf16(x[u][7])) << 16);
-    *reinterpret_cast<uint4*>(bp.d + int64_t(row[u]) * p.ldd + col[u]) = o;
+    *reinterpret_cast<uint4*>(out_at(p, bp, row[u], col[u])) = o;
   }
 }
 

@@ -170,6 +170,52 @@ size_t tpgemm_stage_ag_workspace_size(const tpg_ag_args* args);
 tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Several column-parallel projections sharing one all-gathered input
+ * ("Add dist GEMM attention and FFN backend", Structure: AllGatherLinearMulti
+ * serves several linears that share one input with one all-gather;
+ * AllGatherFusedQKVLinear is the three-way case with wq, wk and wv in their
+ * stock layouts). For i < n_out:
+ *   d[i] = alpha * A * b[i]^T,   A = the P row slices gathered in rank order,
+ * staged exactly as tpgemm_stage_ag (stage t multiplies slice (rank + t) mod
+ * P, local first, deliveries gated by events). The projections run as one
+ * GEMM over the weights side by side, each output column block stored to
+ * its own d[i]; weights that do not already sit back to back in memory are
+ * copied side by side into the workspace first.
+ *
+ *   M, K         M % P == 0; K % 8 == 0 (bf16) or 16 (e4m3).
+ *   n_out        1..4; n[i] % 8 == 0 (n[i] == 0 allowed: that output is
+ *                untouched).
+ *   a_slices     host array of P device pointers, (m, K) row-major each.
+ *   b[i]         (n[i], K) row-major weights, ab_dtype.
+ *   d[i]         bf16 (M, n[i]) row-major outputs; no overlaps with inputs
+ *                or with each other.
+ *   alpha        scale of every product (no C term, no bias).
+ *   workspace    >= tpgemm_stage_ag_multi_workspace_size() bytes.
+ *   flags, groups as for tpgemm_stage_ag (rotating A only).
+ * Errors: as tpgemm_stage_ag, plus TPG_ERR_INVALID for n_out or an n[i].
+ * ---------------------------------------------------------------------- */
+enum { TPG_MAX_PROJ = 4 };
+
+typedef struct {
+  int64_t M, K;
+  int32_t P, rank;
+  int32_t ab_dtype;
+  int32_t n_out;
+  const void* const* a_slices;
+  const void* b[TPG_MAX_PROJ];
+  int64_t n[TPG_MAX_PROJ];
+  void* d[TPG_MAX_PROJ];
+  float alpha;
+  uint32_t flags;
+  int32_t groups;
+  void* workspace;
+  size_t workspace_bytes;
+} tpg_agm_args;
+
+size_t tpgemm_stage_ag_multi_workspace_size(const tpg_agm_args* args);
+tpg_status tpgemm_stage_ag_multi(const tpg_agm_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * Reduce-scatter staged GEMM (the dual).
  * A (M, K) is this rank's K shard, so E = alpha * A * B^T is a partial sum
  * whose P row blocks of m = M/P belong to the P ranks ("Distributed GEMM",

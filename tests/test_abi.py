@@ -110,7 +110,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     the C header's field offsets and sizes (compiled with the host gcc)."""
     import subprocess
     structs = {"tpg_ag_args": tp.AgArgs, "tpg_rs_args": tp.RsArgs, "tpg_ffn_args": tp.FfnArgs,
-               "tpg_wg_args": tp.WgArgs}
+               "tpg_wg_args": tp.WgArgs, "tpg_agm_args": tp.AgmArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tpgemm.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
@@ -209,3 +209,55 @@ def test_deliver_validation():
     assert L.tpg_deliver(sp, 2, 32, dst, 32, tp.UNSTAGED, None) == tp.ERR_INVALID         # not a copy flag
     assert L.tpg_deliver(sp, 2, 32, FAKE + 16, 32, 0, None) == tp.ERR_INVALID             # overlaps a source
     assert L.tpg_deliver(sp, 0, 32, dst, 32, 0, None) == tp.OK                            # nothing to move
+
+
+def agm(**kw):
+    P = kw.pop("P", 4)
+    M, K = kw.pop("M", 4 * 64), kw.pop("K", 256)
+    ns = kw.pop("ns", (64, 16, 16))
+    m = M // max(P, 1)
+    slices = (ctypes.c_void_p * max(P, 1))(*[FAKE + i * m * K * 2 for i in range(max(P, 1))])
+    a = tp.AgmArgs(M=M, K=K, P=P, rank=kw.pop("rank", 0), ab_dtype=kw.pop("ab_dtype", tp.BF16), n_out=len(ns),
+                   a_slices=ctypes.cast(slices, ctypes.POINTER(ctypes.c_void_p)), alpha=1.0,
+                   flags=kw.pop("flags", tp.NO_COPY | tp.UNSTAGED), groups=0)
+    wbase, dbase = FAKE + 0x10000000, FAKE + 0x20000000
+    for i, n in enumerate(ns):             # weights back to back: read in place, no workspace
+        a.n[i] = n
+        a.b[i] = wbase + sum(ns[:i]) * K * 2
+        a.d[i] = dbase + i * 0x1000000
+    for k, v in kw.items():
+        if k in ("b", "d", "n"):
+            for i, x in v.items():
+                getattr(a, k)[i] = x
+        else:
+            setattr(a, k, v)
+    a._keep = slices
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_out=0), tp.ERR_INVALID),
+    (dict(n_out=5), tp.ERR_INVALID),
+    (dict(ns=(64, 12, 16)), tp.ERR_INVALID),             # n[i] % 8
+    (dict(M=4 * 64 + 2), tp.ERR_INVALID),                # M % P
+    (dict(K=260), tp.ERR_UNSUPPORTED),                   # K % 8
+    (dict(d={1: FAKE + 0x20000000 + 8}), tp.ERR_UNSUPPORTED),     # unaligned output
+    (dict(d={1: FAKE + 0x20000000}), tp.ERR_INVALID),    # outputs 0 and 1 overlap
+    (dict(d={2: FAKE}), tp.ERR_INVALID),                 # an output overlaps a slice
+    (dict(b={1: None}), tp.ERR_INVALID),
+    (dict(flags=0), tp.ERR_WORKSPACE),
+])
+def test_ag_multi_validation(kw, status):
+    assert tp.lib().tpgemm_stage_ag_multi(ctypes.byref(agm(**kw)), None) == status
+
+
+def test_ag_multi_workspace_sizes():
+    P, m, K, ns = 4, 64, 256, (64, 16, 16)
+    a = agm(P=P, M=P * m, K=K, ns=ns, flags=0)
+    slots = -(-((P - 1) * m * K * 2) // 256) * 256
+    concat = -(-(sum(ns) * K * 2) // 256) * 256
+    assert tp.stage_ag_multi_workspace_size(a) == slots                   # weights back to back: in place
+    a.b[1] = FAKE + 0x30000000                                           # apart: copied side by side
+    assert tp.stage_ag_multi_workspace_size(a) == slots + concat
+    a.flags = tp.NO_COPY
+    assert tp.stage_ag_multi_workspace_size(a) == concat                  # slices in place, weights copied

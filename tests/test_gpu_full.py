@@ -198,3 +198,27 @@ def test_full_wgrad(case):
         tp.stage_wgrad(local, sl, d, M=case.M, N=case.N, K=case.K, rank=case.rank, gathered=g, groups=groups)
         torch.cuda.synchronize()
         assert_parity(host_f64(d)[rows], ref, f"{case.name}/groups={groups}")
+
+
+def test_full_qkv():
+    """The fused QKV projection at full size (8192 tokens, K = 4096, 512 + 128
+    + 128 columns per rank), weights apart, staged and unstaged, on sampled
+    rows."""
+    case = W.QKV
+    say(f"full: {case.name} generate")
+    inp = W.ag_multi_inputs(case)
+    slices = [dev(s) for s in inp["a_slices"]]
+    bs = [dev(b) for b in inp["bs"]]
+    rows = sample_rows(case.M, case.m)
+    A = np.stack([oracle.decode_bf16(inp["a_slices"][r // case.m][r % case.m]) for r in rows])
+    outs = {}
+    for flags in (0, tp.UNSTAGED):
+        ds = [bf16_empty(case.M, n) for n in case.ns]
+        say(f"full: {case.name} flags={flags}")
+        tp.stage_ag_multi(slices, bs, ds, M=case.M, K=case.K, rank=case.rank, flags=flags)
+        torch.cuda.synchronize()
+        for i, (d, b) in enumerate(zip(ds, inp["bs"])):
+            assert_parity(host_f64(d)[rows], A @ oracle.decode_bf16(b).T, f"{case.name}/{flags}/out{i}")
+        outs[flags] = [d.cpu() for d in ds]
+    for x, y in zip(outs[0], outs[tp.UNSTAGED]):
+        assert torch.equal(x, y)
