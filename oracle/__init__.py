@@ -30,7 +30,7 @@ example); see tests/test_oracle_*.py.
 from .formats import decode_bf16, decode_e4m3, decode
 from .gemm import (ag_stage_order, rs_block_order, gemm_ag, gemm_ag_rows, gemm_rs, gemm_rs_rows,
                    gemm_ag_rotb, gemm_ag_rotb_rows, gemm_rs_tileb, gemm_rs_tileb_rows, gemm_ag_multi)
-from .ffn import layer_norm, silu, ffn_slot_forward, ffn_slot_rows
+from .ffn import layer_norm, silu, ffn_slot_forward, ffn_slot_rows, ffn_slot_backward
 from .swiglu import swiglu_hidden, swiglu_hidden_rows, swiglu_block
 from .permute import dispatch, combine
 from .backward import wgrad, wgrad_staged, wgrad_rows

@@ -230,6 +230,13 @@ def ffn_inputs(case: FfnCase, seed: int = SEED):
     return dict(x=x, w1=w1, b1=b1, wout=wout, bout=bout, gx=gx, bx=bx, gg=gg, bg=bg)
 
 
+def ffn_upstream_grad(case: FfnCase, seed: int = SEED):
+    """The upstream gradient dY [P*B, L, D], N(0, 1) bf16, from its own stream
+    (the p04 statement draws the backward check's gradient from a separate
+    generator seeded seed + 7)."""
+    return normal_bf16(stream_key(seed + 7 + case.rank, "ffn.dy"), (case.PB, case.L, case.D), 0.0, 1.0)
+
+
 def permute_sources(B, T, D, P, seed: int = SEED, dtype="bf16"):
     """Per-rank layer inputs [B, T, D] for ranks 0..P-1 (rank s uses seed + s)."""
     if dtype == "bf16":
