@@ -307,6 +307,26 @@ def bench_ffn(case, args):
     return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1))
 
 
+def bench_ffn_backward(case, args):
+    """Backward of the per-slot FFN layer at the workload size: every
+    gradient (recomputes z and h, then dh, the LayerNorm / SiLU backward, the
+    bias sums and the weight / input gradient GEMMs). Algorithmic flops: the
+    recomputed first GEMM plus the four gradient GEMMs (2 x 2PB D 2H + 3 x 2PB D H
+    per slot)."""
+    inp = W.ffn_inputs(case)
+    t = {k: dev(v) for k, v in inp.items()}
+    dy = dev(W.ffn_upstream_grad(case))
+    shapes = dict(dx=(case.PB, case.L, case.D), dw1=(case.L, case.D, 2 * case.H), db1=(case.L, 2 * case.H),
+                  dwout=(case.L, case.H, case.D), dbout=(case.L, case.D), dgx=(case.H,), dbx=(case.H,),
+                  dgg=(case.H,), dbg=(case.H,))
+    grads = {k: torch.empty(s, dtype=torch.int16, device="cuda") for k, s in shapes.items()}
+    call = tp.prepare_ffn_slot_backward(t["x"], t["w1"], t["b1"], t["wout"], t["gx"], t["bx"], t["gg"], t["bg"], dy,
+                                        grads, PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps)
+    ms = time_steps(call, max(3, args.steps // 5), 2)
+    flop = case.L * (3 * 2.0 * case.PB * case.D * 2 * case.H + 2 * 2.0 * case.PB * case.D * case.H)
+    return dict(us=round(ms * 1e3, 1), tflops=round(flop / (ms * 1e-3) / 1e12, 1), gflop=round(flop / 1e9, 1))
+
+
 def bench_rs(case, args):
     inp = W.rs_inputs(case)
     a, b = dev(inp["a"]), dev(inp["b"])
@@ -494,6 +514,8 @@ def main():
     r["roofline"]["frac_of_measured_peak"] = round(r["roofline"]["achieved"] / measured, 4)
     if not args.no_ffn and not args.quick:
         detail["ffn_layer"] = bench_ffn(W.C4, args)
+        if args.all:
+            detail["ffn_layer_backward"] = bench_ffn_backward(W.C4, args)
         log(f"[ffn] {detail['ffn_layer']}")
     if args.all:
         detail["ag_bf16_p2_256x256x512"] = bench_small_ag(W.C1, args)

@@ -7,7 +7,8 @@ tensors may be torch.bfloat16 or raw int16/uint16 bits, e4m3 tensors
 torch.float8_e4m3fn or raw uint8 bits.
 
 The names follow the C ABI in include/tpgemm.h:
-    stage_ag, stage_ag_multi, stage_rs, stage_wgrad, ffn_slot_forward, dispatch_permute, combine_permute
+    stage_ag, stage_ag_multi, stage_rs, stage_wgrad, ffn_slot_forward, ffn_slot_backward,
+    dispatch_permute, combine_permute
 (plus the *_workspace_size queries, last_error, release_caches, profile_read,
 device_info, mfma_probe).
 """
@@ -75,6 +76,17 @@ class AgmArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class FfnbArgs(ctypes.Structure):
+    _fields_ = [("PB", ctypes.c_int64), ("L", ctypes.c_int64), ("D", ctypes.c_int64), ("H", ctypes.c_int64)] + \
+               [(k, ctypes.c_void_p) for k in ("x", "w1", "b1", "wout", "gx", "bx", "gg", "bg")] + \
+               [("eps", ctypes.c_float), ("dy", ctypes.c_void_p)] + \
+               [(k, ctypes.c_void_p) for k in ("dx", "dw1", "db1", "dwout", "dbout", "dgx", "dbx", "dgg", "dbg")] + \
+               [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32)]
+
+
+FFN_GRADS = ("dx", "dw1", "db1", "dwout", "dbout", "dgx", "dbx", "dgg", "dbg")
+
+
 class WgArgs(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("P", ctypes.c_int32), ("rank", ctypes.c_int32),
@@ -116,6 +128,8 @@ def lib():
             ("tpgemm_stage_wgrad", [ctypes.POINTER(WgArgs), vp], i32),
             ("tpgemm_stage_wgrad_workspace_size", [ctypes.POINTER(WgArgs)], ctypes.c_size_t),
             ("ffn_slot_forward", [ctypes.POINTER(FfnArgs), vp], i32),
+            ("ffn_slot_backward", [ctypes.POINTER(FfnbArgs), vp], i32),
+            ("ffn_slot_backward_workspace_size", [ctypes.POINTER(FfnbArgs)], ctypes.c_size_t),
             ("ffn_slot_forward_workspace_size", [ctypes.POINTER(FfnArgs)], ctypes.c_size_t),
             ("dispatch_permute", [ctypes.POINTER(vp), vp, i32, i32, i64, i64, i64, i32, vp], i32),
             ("combine_permute", [ctypes.POINTER(vp), vp, i32, i32, i64, i64, i64, i32, vp], i32),
@@ -360,6 +374,38 @@ def combine_permute(srcs, dst, *, rank, B, T, D, elem_bytes, stream=None):
     arr = _ptr_array(srcs)
     _check(lib().combine_permute(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), _ptr(dst), len(srcs),
                                  rank, B, T, D, elem_bytes, _stream(stream)))
+
+
+def ffn_backward_args(x, w1, b1, wout, gx, bx, gg, bg, dy, grads, *, PB, L, D, H, eps=1e-5, flags=0):
+    """Argument struct of ffn_slot_backward; `grads` maps each name of
+    FFN_GRADS to its output tensor."""
+    args = FfnbArgs(PB=PB, L=L, D=D, H=H, x=_ptr(x), w1=_ptr(w1), b1=_ptr(b1), wout=_ptr(wout), gx=_ptr(gx),
+                    bx=_ptr(bx), gg=_ptr(gg), bg=_ptr(bg), eps=eps, dy=_ptr(dy), flags=flags)
+    for k in FFN_GRADS:
+        setattr(args, k, _ptr(grads[k]))
+    return args
+
+
+def ffn_slot_backward_workspace_size(args):
+    return lib().ffn_slot_backward_workspace_size(ctypes.byref(args))
+
+
+def ffn_slot_backward(x, w1, b1, wout, gx, bx, gg, bg, dy, grads, *, PB, L, D, H, eps=1e-5, flags=0,
+                      workspace=None, stream=None):
+    """Backward of the per-slot FFN (see tpgemm.h): fills the tensors of `grads`."""
+    args = ffn_backward_args(x, w1, b1, wout, gx, bx, gg, bg, dy, grads, PB=PB, L=L, D=D, H=H, eps=eps,
+                             flags=flags)
+    need = ffn_slot_backward_workspace_size(args)
+    ws = _workspace(workspace, need)
+    args.workspace = _ptr(ws) if ws is not None else None
+    args.workspace_bytes = ws.numel() if ws is not None else 0
+    _check(lib().ffn_slot_backward(ctypes.byref(args), _stream(stream)))
+
+
+def prepare_ffn_slot_backward(x, w1, b1, wout, gx, bx, gg, bg, dy, grads, *, workspace=None, **kw):
+    args = ffn_backward_args(x, w1, b1, wout, gx, bx, gg, bg, dy, grads, **kw)
+    ws = _attach_workspace(args, ffn_slot_backward_workspace_size, workspace)
+    return Prepared(lib().ffn_slot_backward, args, (x, w1, b1, wout, gx, bx, gg, bg, dy, grads, ws))
 
 
 class Prepared:

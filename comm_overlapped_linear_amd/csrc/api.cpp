@@ -1395,6 +1395,179 @@ std::string ffn_key(const tpg_ffn_args& a) {
   return os.str();
 }
 
+// ---------------------------------------------------------------- FFN backward
+// One slot after another on the caller's stream: recompute z and h, then
+// dh, the row backward (dz and the column partials), the bias reductions and
+// the three weight / input gradient GEMMs. Workspace layout (bytes):
+// z [PB][2H] bf16, h [PB][H], dh [PB][H], dz [PB][2H], then fp32 partials:
+// gamma/beta [nblk][4H], b1 [nblk][2H], bout [nblk][D].
+constexpr int kBwdBlocks = 256;
+
+struct FfnbLayout {
+  size_t z, h, dh, dz, pgb, pb1, pbo, total;
+};
+
+FfnbLayout ffnb_layout(const tpg_ffnb_args* a) {
+  FfnbLayout o{};
+  const size_t PB = a->PB, D = a->D, H = a->H;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t p = at;
+    at += round_up(bytes, 256);
+    return p;
+  };
+  o.z = take(PB * 2 * H * 2);
+  o.h = take(PB * H * 2);
+  o.dh = take(PB * H * 2);
+  o.dz = take(PB * 2 * H * 2);
+  o.pgb = take(size_t(kBwdBlocks) * 4 * H * 4);
+  o.pb1 = take(size_t(kBwdBlocks) * 2 * H * 4);
+  o.pbo = take(size_t(kBwdBlocks) * D * 4);
+  o.total = at;
+  return o;
+}
+
+size_t ffnb_ws(const tpg_ffnb_args* a) {
+  if (!a || a->PB <= 0 || a->L <= 0 || a->D <= 0 || a->H <= 0) return 0;
+  return ffnb_layout(a).total;
+}
+
+tpg_status validate_ffnb(const tpg_ffnb_args* a, size_t need) {
+  if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
+  if (a->PB < 0 || a->L < 0 || a->D < 0 || a->H < 0) return fail(TPG_ERR_INVALID, "negative dimension");
+  if (a->flags & ~(TPG_PROFILE | TPG_NO_GRAPH | TPG_FORCE_GRAPH)) return fail(TPG_ERR_INVALID, "unsupported flag bits");
+  if (!fits_int(a->PB) || !fits_int(a->L * a->D) || !fits_int(2 * a->H))
+    return fail(TPG_ERR_UNSUPPORTED, "dimensions too large");
+  if (a->D % 8 || a->H % 8) return fail(TPG_ERR_UNSUPPORTED, "D and H must be multiples of 8");
+  if (a->H > 8192) return fail(TPG_ERR_UNSUPPORTED, "H above 8192");
+  if (a->PB % 64) return fail(TPG_ERR_UNSUPPORTED, "PB must be a multiple of 64");
+  if (!(a->eps >= 0.0f)) return fail(TPG_ERR_INVALID, "eps must be >= 0");
+  const size_t PB = a->PB, L = a->L, D = a->D, H = a->H;
+  const bool work = PB * L * D * H > 0;
+  const Range in[] = {{a->x, PB * L * D * 2}, {a->w1, L * D * 2 * H * 2}, {a->b1, L * 2 * H * 2},
+                      {a->wout, L * H * D * 2}, {a->gx, H * 2}, {a->bx, H * 2}, {a->gg, H * 2},
+                      {a->bg, H * 2}, {a->dy, PB * L * D * 2}};
+  const Range out[] = {{a->dx, PB * L * D * 2}, {a->dw1, L * D * 2 * H * 2}, {a->db1, L * 2 * H * 2},
+                       {a->dwout, L * H * D * 2}, {a->dbout, L * D * 2}, {a->dgx, H * 2},
+                       {a->dbx, H * 2}, {a->dgg, H * 2}, {a->dbg, H * 2}};
+  for (const auto& r : in) {
+    if (work && !r.p) return fail(TPG_ERR_INVALID, "NULL FFN input");
+    if (!aligned16(r.p)) return fail(TPG_ERR_UNSUPPORTED, "FFN input not 16-byte aligned");
+  }
+  for (const auto& r : out) {
+    if (work && !r.p) return fail(TPG_ERR_INVALID, "NULL gradient output");
+    if (!aligned16(r.p)) return fail(TPG_ERR_UNSUPPORTED, "gradient output not 16-byte aligned");
+  }
+  if (work && need && (!a->workspace || a->workspace_bytes < need))
+    return fail(TPG_ERR_WORKSPACE, "workspace smaller than ffn_slot_backward_workspace_size()");
+  if (!aligned16(a->workspace)) return fail(TPG_ERR_UNSUPPORTED, "workspace not 16-byte aligned");
+  const Range wr{a->workspace, need};
+  const int nout = sizeof(out) / sizeof(out[0]);
+  for (int i = 0; i < nout; ++i) {
+    for (const auto& r : in)
+      if (overlaps(out[i], r)) return fail(TPG_ERR_INVALID, "a gradient output overlaps an input");
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(out[i], out[j])) return fail(TPG_ERR_INVALID, "gradient outputs overlap each other");
+    if (overlaps(out[i], wr)) return fail(TPG_ERR_INVALID, "workspace overlaps a gradient output");
+  }
+  for (const auto& r : in)
+    if (overlaps(wr, r)) return fail(TPG_ERR_INVALID, "workspace overlaps an input");
+  return TPG_OK;
+}
+
+tpg_status enqueue_ffnb(Ctx& cx, const tpg_ffnb_args& a, const Launch& L) {
+  const int64_t PB = a.PB, Ls = a.L, D = a.D, H = a.H;
+  const FfnbLayout o = ffnb_layout(&a);
+  char* ws = static_cast<char*>(a.workspace);
+  uint16_t* z = reinterpret_cast<uint16_t*>(ws + o.z);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + o.h);
+  uint16_t* dh = reinterpret_cast<uint16_t*>(ws + o.dh);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + o.dz);
+  float* pgb = reinterpret_cast<float*>(ws + o.pgb);
+  float* pb1 = reinterpret_cast<float*>(ws + o.pb1);
+  float* pbo = reinterpret_cast<float*>(ws + o.pbo);
+  auto bf = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  auto bfm = [](void* p) { return static_cast<uint16_t*>(p); };
+  const hipStream_t s = L.root;
+  auto hip = [&](hipError_t e, const char* what) -> tpg_status {
+    if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string(what) + " launch failed: " + hipGetErrorString(e));
+    return TPG_OK;
+  };
+#define TPG_STEP(expr)                 \
+  do {                                 \
+    tpg_status st_ = (expr);           \
+    if (st_ != TPG_OK) return st_;     \
+  } while (0)
+  for (int64_t l = 0; l < Ls; ++l) {
+    // z = X_l w1[l] + b1[l]; h = LN_x(u) silu(LN_gate(g))   (recomputed)
+    tpg::GemmParams g1 = base_params();
+    g1.a = bf(a.x) + l * D;  g1.lda = Ls * D;
+    g1.b = bf(a.w1) + l * D * 2 * H;  g1.ldb = 2 * H;
+    g1.bias = bf(a.b1) + l * 2 * H;
+    g1.d = z;  g1.ldd = 2 * H;
+    g1.M = int(PB);  g1.N = int(2 * H);  g1.K = int(D);
+    g1.alpha = 1.0f;  g1.vec_ok = 1;
+    TPG_STEP(gemm_on(cx, L, s, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta));
+    TPG_STEP(hip(tpg::launch_ln_silu(z, 2 * H, h, H, int(PB), int(H), bf(a.gx), bf(a.bx), bf(a.gg), bf(a.bg), a.eps, s),
+                 "ln_silu"));
+    // dh = dY_l wout[l]^T   (wout[l] is (H, D): the (N, K) layout)
+    tpg::GemmParams g2 = base_params();
+    g2.a = bf(a.dy) + l * D;  g2.lda = Ls * D;
+    g2.b = bf(a.wout) + l * H * D;  g2.ldb = D;
+    g2.d = dh;  g2.ldd = H;
+    g2.M = int(PB);  g2.N = int(H);  g2.K = int(D);
+    g2.alpha = 1.0f;  g2.vec_ok = 1;
+    TPG_STEP(gemm_on(cx, L, s, g2, tpg::kBf16, tpg::kNK, tpg::kEpiAlphaBeta));
+    // dz and the column partials; db1[l]
+    TPG_STEP(hip(tpg::launch_ffn_bwd_rows(z, 2 * H, dh, H, dz, 2 * H, int(PB), int(H), bf(a.gx), bf(a.bx), bf(a.gg),
+                                          bf(a.bg), a.eps, pgb, l > 0 ? 1 : 0, pb1, kBwdBlocks, s),
+                 "ffn_bwd_rows"));
+    TPG_STEP(hip(tpg::launch_colsum_f32(pb1, kBwdBlocks, 2 * H, int(2 * H), bfm(a.db1) + l * 2 * H, s), "colsum"));
+    // dwout[l] = h^T dY_l;  dbout[l] = sum_n dY_l
+    tpg::GemmParams g3 = base_params();
+    g3.a = h;  g3.lda = H;
+    g3.b = bf(a.dy) + l * D;  g3.ldb = Ls * D;
+    g3.d = bfm(a.dwout) + l * H * D;  g3.ldd = D;
+    g3.M = int(H);  g3.N = int(D);  g3.K = int(PB);
+    g3.alpha = 1.0f;  g3.vec_ok = 1;
+    TPG_STEP(gemm_on(cx, L, s, g3, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA));
+    TPG_STEP(hip(tpg::launch_colsum_bf16(bf(a.dy) + l * D, int(PB), int(D), Ls * D, pbo, kBwdBlocks, s), "colsum"));
+    TPG_STEP(hip(tpg::launch_colsum_f32(pbo, kBwdBlocks, D, int(D), bfm(a.dbout) + l * D, s), "colsum"));
+    // dw1[l] = X_l^T dz;  dx[:, l, :] = dz w1[l]^T   (w1[l] is (D, 2H): the (N, K) layout)
+    tpg::GemmParams g4 = base_params();
+    g4.a = bf(a.x) + l * D;  g4.lda = Ls * D;
+    g4.b = dz;  g4.ldb = 2 * H;
+    g4.d = bfm(a.dw1) + l * D * 2 * H;  g4.ldd = 2 * H;
+    g4.M = int(D);  g4.N = int(2 * H);  g4.K = int(PB);
+    g4.alpha = 1.0f;  g4.vec_ok = 1;
+    TPG_STEP(gemm_on(cx, L, s, g4, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA));
+    tpg::GemmParams g5 = base_params();
+    g5.a = dz;  g5.lda = 2 * H;
+    g5.b = bf(a.w1) + l * D * 2 * H;  g5.ldb = 2 * H;
+    g5.d = bfm(a.dx) + l * D;  g5.ldd = Ls * D;
+    g5.M = int(PB);  g5.N = int(D);  g5.K = int(2 * H);
+    g5.alpha = 1.0f;  g5.vec_ok = 1;
+    TPG_STEP(gemm_on(cx, L, s, g5, tpg::kBf16, tpg::kNK, tpg::kEpiAlphaBeta));
+  }
+  // the LayerNorm parameter gradients: sums over every slot's row blocks
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb, kBwdBlocks, 4 * H, int(H), bfm(a.dgx), s), "colsum"));
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + H, kBwdBlocks, 4 * H, int(H), bfm(a.dbx), s), "colsum"));
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + 2 * H, kBwdBlocks, 4 * H, int(H), bfm(a.dgg), s), "colsum"));
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + 3 * H, kBwdBlocks, 4 * H, int(H), bfm(a.dbg), s), "colsum"));
+#undef TPG_STEP
+  return TPG_OK;
+}
+
+std::string ffnb_key(const tpg_ffnb_args& a) {
+  std::ostringstream os;
+  os << "ffnb|";
+  put(os, a.PB); put(os, a.L); put(os, a.D); put(os, a.H); put(os, a.x); put(os, a.w1); put(os, a.b1);
+  put(os, a.wout); put(os, a.gx); put(os, a.bx); put(os, a.gg); put(os, a.bg); put(os, a.eps); put(os, a.dy);
+  put(os, a.dx); put(os, a.dw1); put(os, a.db1); put(os, a.dwout); put(os, a.dbout); put(os, a.dgx);
+  put(os, a.dbx); put(os, a.dgg); put(os, a.dbg); put(os, a.workspace); put(os, a.flags);
+  return os.str();
+}
+
 // ---------------------------------------------------------------- permutes
 tpg_status permute_common(bool dispatch, const void* const* src, void* dst, int32_t P, int32_t rank,
                           int64_t B, int64_t T, int64_t D, int32_t eb, void* stream) {
@@ -1525,6 +1698,33 @@ tpg_status tpgemm_stage_wgrad(const tpg_wg_args* args, void* stream) {
     const tpg_wg_args& a = *args;
     return run_call(*cx, a.flags, wg_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_wg(*cx, a, L); });
+  });
+}
+
+size_t ffn_slot_backward_workspace_size(const tpg_ffnb_args* args) { return ffnb_ws(args); }
+
+tpg_status ffn_slot_backward(const tpg_ffnb_args* args, void* stream) {
+  return guarded([&]() -> tpg_status {
+    std::lock_guard<std::mutex> lk(g_mu);
+    tpg_status st = validate_ffnb(args, ffnb_ws(args));
+    if (st != TPG_OK) return st;
+    if (args->PB == 0 || args->L == 0 || args->D == 0 || args->H == 0) {
+      // empty sums: every parameter gradient that has elements is zero
+      const hipStream_t hs = static_cast<hipStream_t>(stream);
+      const size_t L = args->L, D = args->D, H = args->H;
+      const std::pair<void*, size_t> zero[] = {{args->dw1, L * D * 2 * H * 2}, {args->db1, L * 2 * H * 2},
+                                               {args->dwout, L * H * D * 2}, {args->dbout, L * D * 2},
+                                               {args->dgx, H * 2}, {args->dbx, H * 2}, {args->dgg, H * 2},
+                                               {args->dbg, H * 2}};
+      for (const auto& zb : zero)
+        if (zb.first && zb.second) HIP_TRY(tpg::launch_fill_zero16(zb.first, zb.second, hs));
+      return TPG_OK;
+    }
+    Ctx* cx = nullptr;
+    st = get_ctx(&cx);
+    if (st != TPG_OK) return st;
+    return run_call(*cx, args->flags, ffnb_key(*args), static_cast<hipStream_t>(stream),
+                    [&](const Launch& L) { return enqueue_ffnb(*cx, *args, L); });
   });
 }
 

@@ -102,6 +102,21 @@ hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t l
                           const uint16_t* gx, const uint16_t* bx, const uint16_t* gg,
                           const uint16_t* bg, float eps, hipStream_t s);
 
+// FFN backward, row part: dz = [du | dg] from z = [u | g] and dh, plus fp32
+// column partials (one block of rows per workgroup, nblk workgroups):
+// part_gb [nblk][4][H] = (da xu, da, db xg, db), added to the buffer's
+// contents when accumulate != 0; part_b1 [nblk][2H] = (du, dg).
+hipError_t launch_ffn_bwd_rows(const uint16_t* z, int64_t ldz, const uint16_t* dh, int64_t lddh, uint16_t* dz,
+                               int64_t lddz, int rows, int H, const uint16_t* gx, const uint16_t* bx,
+                               const uint16_t* gg, const uint16_t* bg, float eps, float* part_gb, int accumulate,
+                               float* part_b1, int nblk, hipStream_t s);
+// out[c] = bf16(sum over nblk blocks of part[b * blk_stride + c]).
+hipError_t launch_colsum_f32(const float* part, int nblk, int64_t blk_stride, int ncols, uint16_t* out,
+                             hipStream_t s);
+// part[b][c] = fp32 sum of src[row * ld + c] over the b-th block of rows.
+hipError_t launch_colsum_bf16(const uint16_t* src, int rows, int cols, int64_t ld, float* part, int nblk,
+                              hipStream_t s);
+
 // Zeroes `bytes` (a multiple of 16) at p (16-byte aligned) with a kernel, so
 // the fill may sit in a captured graph.
 hipError_t launch_fill_zero16(void* p, size_t bytes, hipStream_t s);

@@ -119,6 +119,217 @@ __global__ __launch_bounds__(kRowThreads) void ln_silu_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// FFN backward, row part. For each row of z = [u | g] with upstream gradient
+// dh (the gradient of h = LN_x(u) * silu(LN_gate(g))):
+//   a = LN_x(u), b = LN_gate(g), s = silu(b), sg = logistic(b)
+//   da = dh * s,  db = dh * a * sg * (1 + b (1 - sg))
+//   du = (da gx - mean(da gx) - xu mean(da gx xu)) * ru   (xu = (u - mu) ru)
+//   dg likewise;  dz = [du | dg] (bf16)
+// and, summed over the workgroup's rows in fp32 registers, the column
+// partials of the LayerNorm parameter gradients (da xu, da, db xg, db) and of
+// the first bias gradient (du, dg). Workgroup w takes rows [w R, (w+1) R) and
+// writes its partials to block w of two fp32 buffers; the gamma / beta
+// partials are added to what the block already holds when `accumulate` is
+// set (they sum over slots). Three workgroup reductions per row (means,
+// centred second moments, the two backward means). HBM-bound: 10H bytes per
+// row (z and dh in, dz out).
+constexpr int kBwdThreads = 512;
+
+__device__ __forceinline__ float4 block_sum4(float a, float b, float c, float d, float4* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_sum(c);
+  d = wave_sum(d);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = make_float4(a, b, c, d);
+  __syncthreads();
+  float4 s = red[0];
+#pragma unroll
+  for (int w = 1; w < kBwdThreads / 64; ++w) {
+    s.x += red[w].x;
+    s.y += red[w].y;
+    s.z += red[w].z;
+    s.w += red[w].w;
+  }
+  return s;
+}
+
+__device__ __forceinline__ void store8_bf16(uint16_t* dst, const float* f) {
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = f32_to_bf16(f[2 * e]) | (static_cast<uint32_t>(f32_to_bf16(f[2 * e + 1])) << 16);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// CH = 8-element chunks per thread per half (H <= 8 * kBwdThreads * CH).
+template <int CH>
+__global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
+    const uint16_t* __restrict__ z, int64_t ldz, const uint16_t* __restrict__ dh, int64_t lddh,
+    uint16_t* __restrict__ dz, int64_t lddz, int rows, int rows_per_block, int H,
+    const uint16_t* __restrict__ gx, const uint16_t* __restrict__ bx, const uint16_t* __restrict__ gg,
+    const uint16_t* __restrict__ bg, float eps, float* __restrict__ part_gb, int accumulate,
+    float* __restrict__ part_b1) {
+  __shared__ float4 red[kBwdThreads / 64];
+  const int nchunk = H >> 3;
+  const float inv_h = 1.0f / static_cast<float>(H);
+  float p_gx[CH][8], p_bx[CH][8], p_gg[CH][8], p_bg[CH][8], p_du[CH][8], p_dg[CH][8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p_gx[c][e] = p_bx[c][e] = p_gg[c][e] = p_bg[c][e] = p_du[c][e] = p_dg[c][e] = 0.f;
+  const int r0 = blockIdx.x * rows_per_block;
+  const int r1 = min(rows, r0 + rows_per_block);
+  for (int row = r0; row < r1; ++row) {
+    const uint16_t* zu = z + int64_t(row) * ldz;
+    const uint16_t* zg = zu + H;
+    const uint16_t* dhr = dh + int64_t(row) * lddh;
+    float u[CH][8], g[CH][8], d[CH][8];
+    float su = 0.f, sg = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = c * kBwdThreads + threadIdx.x;
+      if (ch < nchunk) {
+        unpack8(*reinterpret_cast<const uint4*>(zu + ch * 8), u[c]);
+        unpack8(*reinterpret_cast<const uint4*>(zg + ch * 8), g[c]);
+        unpack8(*reinterpret_cast<const uint4*>(dhr + ch * 8), d[c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          su += u[c][e];
+          sg += g[c][e];
+        }
+      }
+    }
+    float4 s4 = block_sum4(su, sg, 0.f, 0.f, red);
+    const float mu = s4.x * inv_h, mg = s4.y * inv_h;
+    float qu = 0.f, qg = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = c * kBwdThreads + threadIdx.x;
+      if (ch < nchunk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          u[c][e] -= mu;
+          g[c][e] -= mg;
+          qu += u[c][e] * u[c][e];
+          qg += g[c][e] * g[c][e];
+        }
+      }
+    }
+    s4 = block_sum4(qu, qg, 0.f, 0.f, red);
+    const float ru = rsqrtf(s4.x * inv_h + eps), rg = rsqrtf(s4.y * inv_h + eps);
+    float xu_m = 0.f, xu_x = 0.f, xg_m = 0.f, xg_x = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = c * kBwdThreads + threadIdx.x;
+      if (ch < nchunk) {
+        float a_g[8], b_x[8], c_g[8], c_b[8];
+        unpack8(*reinterpret_cast<const uint4*>(gx + ch * 8), a_g);
+        unpack8(*reinterpret_cast<const uint4*>(bx + ch * 8), b_x);
+        unpack8(*reinterpret_cast<const uint4*>(gg + ch * 8), c_g);
+        unpack8(*reinterpret_cast<const uint4*>(bg + ch * 8), c_b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xu = u[c][e] * ru, xg = g[c][e] * rg;
+          const float a = xu * a_g[e] + b_x[e];
+          const float b = xg * c_g[e] + c_b[e];
+          const float sgm = 1.0f / (1.0f + __expf(-b));
+          const float da = d[c][e] * (b * sgm);
+          const float db = d[c][e] * a * sgm * (1.0f + b * (1.0f - sgm));
+          p_gx[c][e] += da * xu;
+          p_bx[c][e] += da;
+          p_gg[c][e] += db * xg;
+          p_bg[c][e] += db;
+          const float dxu = da * a_g[e], dxg = db * c_g[e];
+          xu_m += dxu;
+          xu_x += dxu * xu;
+          xg_m += dxg;
+          xg_x += dxg * xg;
+          u[c][e] = xu;            // u, g now hold the normalised rows,
+          g[c][e] = xg;            // d holds da * gx; da * ... * gg is recomputed
+          d[c][e] = dxu;           // below from dh (cheaper than registers)
+        }
+      }
+    }
+    s4 = block_sum4(xu_m, xu_x, xg_m, xg_x, red);
+    const float mdu = s4.x * inv_h, mdux = s4.y * inv_h, mdg = s4.z * inv_h, mdgx = s4.w * inv_h;
+    uint16_t* dzr = dz + int64_t(row) * lddz;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = c * kBwdThreads + threadIdx.x;
+      if (ch < nchunk) {
+        float a_g[8], b_x[8], c_g[8], c_b[8], dhv[8];
+        unpack8(*reinterpret_cast<const uint4*>(gx + ch * 8), a_g);
+        unpack8(*reinterpret_cast<const uint4*>(bx + ch * 8), b_x);
+        unpack8(*reinterpret_cast<const uint4*>(gg + ch * 8), c_g);
+        unpack8(*reinterpret_cast<const uint4*>(bg + ch * 8), c_b);
+        unpack8(*reinterpret_cast<const uint4*>(dhr + ch * 8), dhv);
+        float ou[8], og[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xu = u[c][e], xg = g[c][e];
+          const float a = xu * a_g[e] + b_x[e];
+          const float b = xg * c_g[e] + c_b[e];
+          const float sgm = 1.0f / (1.0f + __expf(-b));
+          const float dxg = dhv[e] * a * sgm * (1.0f + b * (1.0f - sgm)) * c_g[e];
+          ou[e] = (d[c][e] - mdu - xu * mdux) * ru;
+          og[e] = (dxg - mdg - xg * mdgx) * rg;
+          p_du[c][e] += ou[e];
+          p_dg[c][e] += og[e];
+        }
+        store8_bf16(dzr + ch * 8, ou);
+        store8_bf16(dzr + H + ch * 8, og);
+      }
+    }
+  }
+  // partials of this block: gamma/beta [4][H] (accumulated over slots), b1 [2H]
+  float* pgb = part_gb + int64_t(blockIdx.x) * 4 * H;
+  float* pb1 = part_b1 + int64_t(blockIdx.x) * 2 * H;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = c * kBwdThreads + threadIdx.x;
+    if (ch < nchunk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int col = ch * 8 + e;
+        const float add0 = accumulate ? pgb[col] : 0.f, add1 = accumulate ? pgb[H + col] : 0.f;
+        const float add2 = accumulate ? pgb[2 * H + col] : 0.f, add3 = accumulate ? pgb[3 * H + col] : 0.f;
+        pgb[col] = add0 + p_gx[c][e];
+        pgb[H + col] = add1 + p_bx[c][e];
+        pgb[2 * H + col] = add2 + p_gg[c][e];
+        pgb[3 * H + col] = add3 + p_bg[c][e];
+        pb1[col] = p_du[c][e];
+        pb1[H + col] = p_dg[c][e];
+      }
+    }
+  }
+}
+
+// Column sums of fp32 partials: out[c] = bf16(sum_b part[b * blk_stride + c]),
+// blocks in order (deterministic).
+__global__ __launch_bounds__(256) void colsum_f32_kernel(const float* __restrict__ part, int nblk, int64_t blk_stride,
+                                                          int ncols, uint16_t* __restrict__ out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= ncols) return;
+  float s = 0.f;
+  for (int b = 0; b < nblk; ++b) s += part[int64_t(b) * blk_stride + c];
+  out[c] = f32_to_bf16(s);
+}
+
+// fp32 column partials of a bf16 matrix, one per block of rows:
+// part[blk][c] = sum over rows [blk R, (blk+1) R) of src[row * ld + c].
+__global__ __launch_bounds__(256) void colsum_bf16_kernel(const uint16_t* __restrict__ src, int rows, int cols,
+                                                           int64_t ld, int rows_per_block, float* __restrict__ part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int r0 = blockIdx.y * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  float s = 0.f;
+  for (int r = r0; r < r1; ++r) s += bf16_to_f32(src[int64_t(r) * ld + c]);
+  part[int64_t(blockIdx.y) * cols + c] = s;
+}
+
 constexpr int kPermThreads = 256;
 constexpr int kPermUnroll = 4;
 
@@ -246,6 +457,41 @@ hipError_t launch_ln_silu(const uint16_t* z, int64_t ldz, uint16_t* h, int64_t l
     hipLaunchKernelGGL(ln_silu_kernel<8>, grid, block, 0, s, z, ldz, h, ldh, H, gx, bx, gg, bg, eps);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_bwd_rows(const uint16_t* z, int64_t ldz, const uint16_t* dh, int64_t lddh, uint16_t* dz,
+                               int64_t lddz, int rows, int H, const uint16_t* gx, const uint16_t* bx,
+                               const uint16_t* gg, const uint16_t* bg, float eps, float* part_gb, int accumulate,
+                               float* part_b1, int nblk, hipStream_t s) {
+  if (rows == 0 || H == 0) return hipSuccess;
+  if (nblk < 1 || H % 8) return hipErrorInvalidValue;
+  const int per = (H / 8 + kBwdThreads - 1) / kBwdThreads;
+  const int rpb = (rows + nblk - 1) / nblk;
+  dim3 grid(nblk), block(kBwdThreads);
+#define TPG_BWD(CH) hipLaunchKernelGGL(ffn_bwd_rows_kernel<CH>, grid, block, 0, s, z, ldz, dh, lddh, dz, lddz, rows, \
+                                       rpb, H, gx, bx, gg, bg, eps, part_gb, accumulate, part_b1)
+  if (per <= 1) TPG_BWD(1);
+  else if (per <= 2) TPG_BWD(2);     // H <= 8192 (more would spill at 512 threads)
+  else return hipErrorInvalidValue;
+#undef TPG_BWD
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_f32(const float* part, int nblk, int64_t blk_stride, int ncols, uint16_t* out,
+                             hipStream_t s) {
+  if (ncols == 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_f32_kernel, dim3((ncols + 255) / 256), dim3(256), 0, s, part, nblk, blk_stride, ncols,
+                     out);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_bf16(const uint16_t* src, int rows, int cols, int64_t ld, float* part, int nblk,
+                              hipStream_t s) {
+  if (cols == 0 || nblk < 1) return hipSuccess;
+  const int rpb = (rows + nblk - 1) / nblk;
+  hipLaunchKernelGGL(colsum_bf16_kernel, dim3((cols + 255) / 256, nblk), dim3(256), 0, s, src, rows, cols, ld, rpb,
+                     part);
   return hipGetLastError();
 }
 

@@ -368,6 +368,58 @@ size_t ffn_slot_forward_workspace_size(const tpg_ffn_args* args);
 tpg_status ffn_slot_forward(const tpg_ffn_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Backward of the per-token-slot FFN (p04 statement, "Interface, layout, and
+ * parameters": autograd propagates through the layer to its input and every
+ * parameter). With the forward's tensors and notation and the upstream
+ * gradient dy = dL/dY [PB, L, D], for every slot l (a, b the two LayerNorm
+ * outputs, s = silu(b)):
+ *   dwout[l] = h^T dY_l;  dbout[l] = sum_n dY_l;  dh = dY_l wout[l]^T
+ *   da = dh s;  db = dh a silu'(b);  dz = [LN_x^T(da) | LN_gate^T(db)]
+ *   dw1[l] = X_l^T dz;  db1[l] = sum_n dz;  dx[:, l, :] = dz w1[l]^T
+ *   dgx = sum over slots and rows of da * (u - mean u) / sqrt(var u + eps),
+ *   dbx = sum of da; dgg, dbg likewise for the gate half
+ * where LN^T is the LayerNorm input gradient. z and h are recomputed from x
+ * (no activations are kept by the forward call). Products accumulate in fp32;
+ * dh and dz are stored bf16 between the steps; column sums are fp32 in a
+ * fixed block order (deterministic). Outputs are bf16 with the parameter
+ * shapes: dx [PB, L, D], dw1 [L, D, 2H], db1 [L, 2H], dwout [L, H, D],
+ * dbout [L, D], dgx, dbx, dgg, dbg [H].
+ *   PB % 64 == 0 (the weight gradients contract over the PB rows), D % 8 == 0,
+ *   H % 8 == 0, H <= 8192. Inputs are never modified; outputs must not
+ *   overlap inputs or each other. workspace >=
+ *   ffn_slot_backward_workspace_size() bytes. flags: TPG_PROFILE only
+ *   (besides TPG_NO_GRAPH / TPG_FORCE_GRAPH).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t PB, L, D, H;
+  const void* x;
+  const void* w1;
+  const void* b1;
+  const void* wout;
+  const void* gx;
+  const void* bx;
+  const void* gg;
+  const void* bg;
+  float eps;
+  const void* dy;
+  void* dx;
+  void* dw1;
+  void* db1;
+  void* dwout;
+  void* dbout;
+  void* dgx;
+  void* dbx;
+  void* dgg;
+  void* dbg;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+} tpg_ffnb_args;
+
+size_t ffn_slot_backward_workspace_size(const tpg_ffnb_args* args);
+tpg_status ffn_slot_backward(const tpg_ffnb_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * All-to-All dispatch / combine as single-GPU layout permutes (p04 statement,
  * "Interface, layout, and parameters" and "Computation and communication
  * example"). With L = T/P (T % P == 0):

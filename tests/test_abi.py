@@ -110,7 +110,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     the C header's field offsets and sizes (compiled with the host gcc)."""
     import subprocess
     structs = {"tpg_ag_args": tp.AgArgs, "tpg_rs_args": tp.RsArgs, "tpg_ffn_args": tp.FfnArgs,
-               "tpg_wg_args": tp.WgArgs, "tpg_agm_args": tp.AgmArgs}
+               "tpg_wg_args": tp.WgArgs, "tpg_agm_args": tp.AgmArgs, "tpg_ffnb_args": tp.FfnbArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tpgemm.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
@@ -261,3 +261,38 @@ def test_ag_multi_workspace_sizes():
     assert tp.stage_ag_multi_workspace_size(a) == slots + concat
     a.flags = tp.NO_COPY
     assert tp.stage_ag_multi_workspace_size(a) == concat                  # slices in place, weights copied
+
+
+def ffnb(**kw):
+    PB, L, D, H = kw.pop("PB", 128), kw.pop("L", 2), kw.pop("D", 64), kw.pop("H", 128)
+    a = tp.FfnbArgs(PB=PB, L=L, D=D, H=H, eps=1e-5, flags=0, workspace=FAKE + 0x80000000, workspace_bytes=1 << 32)
+    for i, k in enumerate(("x", "w1", "b1", "wout", "gx", "bx", "gg", "bg", "dy") + tp.FFN_GRADS):
+        setattr(a, k, FAKE + i * 0x1000000)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(PB=100), tp.ERR_UNSUPPORTED),                   # PB % 64
+    (dict(H=8200), tp.ERR_UNSUPPORTED),                   # H > 8192
+    (dict(D=60), tp.ERR_UNSUPPORTED),
+    (dict(eps=-1.0), tp.ERR_INVALID),
+    (dict(dx=None), tp.ERR_INVALID),
+    (dict(dgx=FAKE + 8), tp.ERR_UNSUPPORTED),
+    (dict(dgx=FAKE), tp.ERR_INVALID),                     # a gradient over an input
+    (dict(dbg=FAKE + 13 * 0x1000000), tp.ERR_INVALID),    # two gradients overlap
+    (dict(flags=tp.UNSTAGED), tp.ERR_INVALID),
+    (dict(workspace=None, workspace_bytes=0), tp.ERR_WORKSPACE),
+    (dict(workspace=FAKE + 0x1000000), tp.ERR_INVALID),   # workspace over an input
+])
+def test_ffn_backward_validation(kw, status):
+    assert tp.lib().ffn_slot_backward(ctypes.byref(ffnb(**kw)), None) == status
+
+
+def test_ffn_backward_workspace_size():
+    PB, L, D, H = 128, 2, 64, 128
+    r = lambda n: -(-n // 256) * 256
+    want = r(PB * 2 * H * 2) + 2 * r(PB * H * 2) + r(PB * 2 * H * 2) + r(256 * 4 * H * 4) + r(256 * 2 * H * 4) + \
+        r(256 * D * 4)
+    assert tp.ffn_slot_backward_workspace_size(ffnb(PB=PB, L=L, D=D, H=H)) == want

@@ -222,3 +222,36 @@ def test_full_qkv():
         outs[flags] = [d.cpu() for d in ds]
     for x, y in zip(outs[0], outs[tp.UNSTAGED]):
         assert torch.equal(x, y)
+
+
+def test_full_ffn_backward_one_slot():
+    """The FFN backward at the workload size (PB = 4096, L = 8, D = 1280,
+    H = 7680): every gradient of one slot against the oracle run on that
+    slot alone (the LayerNorm parameter gradients sum over slots and are
+    covered at small sizes), with the p04 backward rule for bf16 (per-gradient
+    Frobenius relative error <= 2e-2)."""
+    case, l = W.C4, 5
+    say(f"full: ffn backward generate")
+    inp = W.ffn_inputs(case)
+    dy = W.ffn_upstream_grad(case)
+    t = {k: dev(v) for k, v in inp.items()}
+    shapes = dict(dx=(case.PB, case.L, case.D), dw1=(case.L, case.D, 2 * case.H), db1=(case.L, 2 * case.H),
+                  dwout=(case.L, case.H, case.D), dbout=(case.L, case.D), dgx=(case.H,), dbx=(case.H,),
+                  dgg=(case.H,), dbg=(case.H,))
+    grads = {k: bf16_empty(*s) for k, s in shapes.items()}
+    say("full: ffn backward run")
+    tp.ffn_slot_backward(t["x"], t["w1"], t["b1"], t["wout"], t["gx"], t["bx"], t["gg"], t["bg"], dev(dy), grads,
+                         PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps)
+    torch.cuda.synchronize()
+    say("full: ffn backward oracle (one slot)")
+    from oracle import ffn as F
+    q = {k: oracle.decode_bf16(inp[k]) for k in ("w1", "b1", "wout", "bout", "gx", "bx", "gg", "bg")}
+    q1 = dict(q, w1=q["w1"][l:l + 1], b1=q["b1"][l:l + 1], wout=q["wout"][l:l + 1], bout=q["bout"][l:l + 1])
+    X = oracle.decode_bf16(inp["x"][:, l:l + 1])
+    ref = F.backward_f64(X, q1, oracle.decode_bf16(dy[:, l:l + 1]), case.eps)
+    pairs = dict(dx=(host_f64(grads["dx"])[:, l], ref["x"][:, 0]), dw1=(host_f64(grads["dw1"])[l], ref["w1"][0]),
+                 db1=(host_f64(grads["db1"])[l], ref["b1"][0]), dwout=(host_f64(grads["dwout"])[l], ref["wout"][0]),
+                 dbout=(host_f64(grads["dbout"])[l], ref["bout"][0]))
+    errs = {k: float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-12)) for k, (g, r) in pairs.items()}
+    say(f"full: ffn backward slot {l} frobenius {errs}")
+    assert all(e <= 2e-2 for e in errs.values()), errs
