@@ -1396,11 +1396,17 @@ std::string ffn_key(const tpg_ffn_args& a) {
 }
 
 // ---------------------------------------------------------------- FFN backward
-// One slot after another on the caller's stream: recompute z and h, then
-// dh, the row backward (dz and the column partials), the bias reductions and
-// the three weight / input gradient GEMMs. Workspace layout (bytes):
-// z [PB][2H] bf16, h [PB][H], dh [PB][H], dz [PB][2H], then fp32 partials:
-// gamma/beta [nblk][4H], b1 [nblk][2H], bout [nblk][D].
+// Per slot: recompute z and h, then dh, the row backward (dz and the column
+// partials), the bias reductions and the three weight / input gradient
+// GEMMs, over two streams so that independent steps share the chip:
+//   s0: z = GEMM1, h = ln_silu -> [h ready] -> wait dh -> rows -> [dz ready]
+//       -> dw1, db1
+//   s1: dh -> [dh ready] -> wait h -> dwout, dbout -> wait dz -> dx
+// (dh beside GEMM1, dwout beside the row backward, dx beside dw1). h is
+// double-buffered; z, dh and dz are reused in stream order (each next
+// writer follows the last reader through the events above). Workspace
+// layout (bytes): z [PB][2H] bf16, h [2][PB][H], dh [PB][H], dz [PB][2H],
+// then fp32 partials: gamma/beta [nblk][4H], b1 [nblk][2H], bout [nblk][D].
 constexpr int kBwdBlocks = 256;
 
 struct FfnbLayout {
@@ -1417,7 +1423,7 @@ FfnbLayout ffnb_layout(const tpg_ffnb_args* a) {
     return p;
   };
   o.z = take(PB * 2 * H * 2);
-  o.h = take(PB * H * 2);
+  o.h = take(2 * PB * H * 2);                  // two buffers: slot l uses l % 2
   o.dh = take(PB * H * 2);
   o.dz = take(PB * 2 * H * 2);
   o.pgb = take(size_t(kBwdBlocks) * 4 * H * 4);
@@ -1435,7 +1441,8 @@ size_t ffnb_ws(const tpg_ffnb_args* a) {
 tpg_status validate_ffnb(const tpg_ffnb_args* a, size_t need) {
   if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
   if (a->PB < 0 || a->L < 0 || a->D < 0 || a->H < 0) return fail(TPG_ERR_INVALID, "negative dimension");
-  if (a->flags & ~(TPG_PROFILE | TPG_NO_GRAPH | TPG_FORCE_GRAPH)) return fail(TPG_ERR_INVALID, "unsupported flag bits");
+  if (a->flags & ~(TPG_PROFILE | TPG_NO_GRAPH | TPG_FORCE_GRAPH | TPG_SERIAL_STAGES))
+    return fail(TPG_ERR_INVALID, "unsupported flag bits");
   if (!fits_int(a->PB) || !fits_int(a->L * a->D) || !fits_int(2 * a->H))
     return fail(TPG_ERR_UNSUPPORTED, "dimensions too large");
   if (a->D % 8 || a->H % 8) return fail(TPG_ERR_UNSUPPORTED, "D and H must be multiples of 8");
@@ -1480,7 +1487,6 @@ tpg_status enqueue_ffnb(Ctx& cx, const tpg_ffnb_args& a, const Launch& L) {
   const FfnbLayout o = ffnb_layout(&a);
   char* ws = static_cast<char*>(a.workspace);
   uint16_t* z = reinterpret_cast<uint16_t*>(ws + o.z);
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + o.h);
   uint16_t* dh = reinterpret_cast<uint16_t*>(ws + o.dh);
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + o.dz);
   float* pgb = reinterpret_cast<float*>(ws + o.pgb);
@@ -1488,9 +1494,23 @@ tpg_status enqueue_ffnb(Ctx& cx, const tpg_ffnb_args& a, const Launch& L) {
   float* pbo = reinterpret_cast<float*>(ws + o.pbo);
   auto bf = [](const void* p) { return static_cast<const uint16_t*>(p); };
   auto bfm = [](void* p) { return static_cast<uint16_t*>(p); };
-  const hipStream_t s = L.root;
   auto hip = [&](hipError_t e, const char* what) -> tpg_status {
     if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string(what) + " launch failed: " + hipGetErrorString(e));
+    return TPG_OK;
+  };
+  const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : 2;
+  hipStream_t st[kStreams];
+  tpg_status fs = fork_streams(cx, L.root, ns, st);
+  if (fs != TPG_OK) return fs;
+  const hipStream_t s0 = st[0], s1 = st[ns - 1];
+  // slot l's events: ev_copy[3 (l mod 21) + {0: h ready, 1: dh ready, 2: dz ready}]
+  auto ev = [&](int64_t l, int k) { return cx.ev_copy[3 * (l % 21) + k]; };
+  auto record = [&](hipStream_t from, hipEvent_t e) -> tpg_status {
+    if (ns > 1) HIP_TRY(hipEventRecord(e, from));
+    return TPG_OK;
+  };
+  auto wait = [&](hipStream_t to, hipEvent_t e) -> tpg_status {
+    if (ns > 1) HIP_TRY(hipStreamWaitEvent(to, e, 0));
     return TPG_OK;
   };
 #define TPG_STEP(expr)                 \
@@ -1499,7 +1519,17 @@ tpg_status enqueue_ffnb(Ctx& cx, const tpg_ffnb_args& a, const Launch& L) {
     if (st_ != TPG_OK) return st_;     \
   } while (0)
   for (int64_t l = 0; l < Ls; ++l) {
-    // z = X_l w1[l] + b1[l]; h = LN_x(u) silu(LN_gate(g))   (recomputed)
+    uint16_t* h = reinterpret_cast<uint16_t*>(ws + o.h) + (l % 2) * PB * H;
+    // s1: dh = dY_l wout[l]^T   (wout[l] is (H, D): the (N, K) layout)
+    tpg::GemmParams g2 = base_params();
+    g2.a = bf(a.dy) + l * D;  g2.lda = Ls * D;
+    g2.b = bf(a.wout) + l * H * D;  g2.ldb = D;
+    g2.d = dh;  g2.ldd = H;
+    g2.M = int(PB);  g2.N = int(H);  g2.K = int(D);
+    g2.alpha = 1.0f;  g2.vec_ok = 1;
+    TPG_STEP(gemm_on(cx, L, s1, g2, tpg::kBf16, tpg::kNK, tpg::kEpiAlphaBeta));
+    TPG_STEP(record(s1, ev(l, 1)));
+    // s0: z = X_l w1[l] + b1[l]; h = LN_x(u) silu(LN_gate(g))   (recomputed)
     tpg::GemmParams g1 = base_params();
     g1.a = bf(a.x) + l * D;  g1.lda = Ls * D;
     g1.b = bf(a.w1) + l * D * 2 * H;  g1.ldb = 2 * H;
@@ -1507,55 +1537,52 @@ tpg_status enqueue_ffnb(Ctx& cx, const tpg_ffnb_args& a, const Launch& L) {
     g1.d = z;  g1.ldd = 2 * H;
     g1.M = int(PB);  g1.N = int(2 * H);  g1.K = int(D);
     g1.alpha = 1.0f;  g1.vec_ok = 1;
-    TPG_STEP(gemm_on(cx, L, s, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta));
-    TPG_STEP(hip(tpg::launch_ln_silu(z, 2 * H, h, H, int(PB), int(H), bf(a.gx), bf(a.bx), bf(a.gg), bf(a.bg), a.eps, s),
+    TPG_STEP(gemm_on(cx, L, s0, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta));
+    TPG_STEP(hip(tpg::launch_ln_silu(z, 2 * H, h, H, int(PB), int(H), bf(a.gx), bf(a.bx), bf(a.gg), bf(a.bg),
+                                     a.eps, s0),
                  "ln_silu"));
-    // dh = dY_l wout[l]^T   (wout[l] is (H, D): the (N, K) layout)
-    tpg::GemmParams g2 = base_params();
-    g2.a = bf(a.dy) + l * D;  g2.lda = Ls * D;
-    g2.b = bf(a.wout) + l * H * D;  g2.ldb = D;
-    g2.d = dh;  g2.ldd = H;
-    g2.M = int(PB);  g2.N = int(H);  g2.K = int(D);
-    g2.alpha = 1.0f;  g2.vec_ok = 1;
-    TPG_STEP(gemm_on(cx, L, s, g2, tpg::kBf16, tpg::kNK, tpg::kEpiAlphaBeta));
-    // dz and the column partials; db1[l]
-    TPG_STEP(hip(tpg::launch_ffn_bwd_rows(z, 2 * H, dh, H, dz, 2 * H, int(PB), int(H), bf(a.gx), bf(a.bx), bf(a.gg),
-                                          bf(a.bg), a.eps, pgb, l > 0 ? 1 : 0, pb1, kBwdBlocks, s),
+    TPG_STEP(record(s0, ev(l, 0)));
+    // s0: dz and the column partials (needs dh), then dw1[l] = X_l^T dz and db1[l]
+    TPG_STEP(wait(s0, ev(l, 1)));
+    TPG_STEP(hip(tpg::launch_ffn_bwd_rows(z, 2 * H, dh, H, dz, 2 * H, int(PB), int(H), bf(a.gx), bf(a.bx),
+                                          bf(a.gg), bf(a.bg), a.eps, pgb, l > 0 ? 1 : 0, pb1, kBwdBlocks, s0),
                  "ffn_bwd_rows"));
-    TPG_STEP(hip(tpg::launch_colsum_f32(pb1, kBwdBlocks, 2 * H, int(2 * H), bfm(a.db1) + l * 2 * H, s), "colsum"));
-    // dwout[l] = h^T dY_l;  dbout[l] = sum_n dY_l
-    tpg::GemmParams g3 = base_params();
-    g3.a = h;  g3.lda = H;
-    g3.b = bf(a.dy) + l * D;  g3.ldb = Ls * D;
-    g3.d = bfm(a.dwout) + l * H * D;  g3.ldd = D;
-    g3.M = int(H);  g3.N = int(D);  g3.K = int(PB);
-    g3.alpha = 1.0f;  g3.vec_ok = 1;
-    TPG_STEP(gemm_on(cx, L, s, g3, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA));
-    TPG_STEP(hip(tpg::launch_colsum_bf16(bf(a.dy) + l * D, int(PB), int(D), Ls * D, pbo, kBwdBlocks, s), "colsum"));
-    TPG_STEP(hip(tpg::launch_colsum_f32(pbo, kBwdBlocks, D, int(D), bfm(a.dbout) + l * D, s), "colsum"));
-    // dw1[l] = X_l^T dz;  dx[:, l, :] = dz w1[l]^T   (w1[l] is (D, 2H): the (N, K) layout)
+    TPG_STEP(record(s0, ev(l, 2)));
     tpg::GemmParams g4 = base_params();
     g4.a = bf(a.x) + l * D;  g4.lda = Ls * D;
     g4.b = dz;  g4.ldb = 2 * H;
     g4.d = bfm(a.dw1) + l * D * 2 * H;  g4.ldd = 2 * H;
     g4.M = int(D);  g4.N = int(2 * H);  g4.K = int(PB);
     g4.alpha = 1.0f;  g4.vec_ok = 1;
-    TPG_STEP(gemm_on(cx, L, s, g4, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA));
+    TPG_STEP(gemm_on(cx, L, s0, g4, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA));
+    TPG_STEP(hip(tpg::launch_colsum_f32(pb1, kBwdBlocks, 2 * H, int(2 * H), bfm(a.db1) + l * 2 * H, s0), "colsum"));
+    // s1: dwout[l] = h^T dY_l and dbout[l] (need h), then dx[:, l, :] = dz w1[l]^T (needs dz)
+    TPG_STEP(wait(s1, ev(l, 0)));
+    tpg::GemmParams g3 = base_params();
+    g3.a = h;  g3.lda = H;
+    g3.b = bf(a.dy) + l * D;  g3.ldb = Ls * D;
+    g3.d = bfm(a.dwout) + l * H * D;  g3.ldd = D;
+    g3.M = int(H);  g3.N = int(D);  g3.K = int(PB);
+    g3.alpha = 1.0f;  g3.vec_ok = 1;
+    TPG_STEP(gemm_on(cx, L, s1, g3, TPG_BF16, kLayoutAT, TPG_EPI_ALPHA_BETA));
+    TPG_STEP(hip(tpg::launch_colsum_bf16(bf(a.dy) + l * D, int(PB), int(D), Ls * D, pbo, kBwdBlocks, s1), "colsum"));
+    TPG_STEP(hip(tpg::launch_colsum_f32(pbo, kBwdBlocks, D, int(D), bfm(a.dbout) + l * D, s1), "colsum"));
+    TPG_STEP(wait(s1, ev(l, 2)));
     tpg::GemmParams g5 = base_params();
     g5.a = dz;  g5.lda = 2 * H;
     g5.b = bf(a.w1) + l * D * 2 * H;  g5.ldb = 2 * H;
     g5.d = bfm(a.dx) + l * D;  g5.ldd = Ls * D;
     g5.M = int(PB);  g5.N = int(D);  g5.K = int(2 * H);
     g5.alpha = 1.0f;  g5.vec_ok = 1;
-    TPG_STEP(gemm_on(cx, L, s, g5, tpg::kBf16, tpg::kNK, tpg::kEpiAlphaBeta));
+    TPG_STEP(gemm_on(cx, L, s1, g5, tpg::kBf16, tpg::kNK, tpg::kEpiAlphaBeta));
   }
   // the LayerNorm parameter gradients: sums over every slot's row blocks
-  TPG_STEP(hip(tpg::launch_colsum_f32(pgb, kBwdBlocks, 4 * H, int(H), bfm(a.dgx), s), "colsum"));
-  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + H, kBwdBlocks, 4 * H, int(H), bfm(a.dbx), s), "colsum"));
-  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + 2 * H, kBwdBlocks, 4 * H, int(H), bfm(a.dgg), s), "colsum"));
-  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + 3 * H, kBwdBlocks, 4 * H, int(H), bfm(a.dbg), s), "colsum"));
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb, kBwdBlocks, 4 * H, int(H), bfm(a.dgx), s0), "colsum"));
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + H, kBwdBlocks, 4 * H, int(H), bfm(a.dbx), s0), "colsum"));
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + 2 * H, kBwdBlocks, 4 * H, int(H), bfm(a.dgg), s0), "colsum"));
+  TPG_STEP(hip(tpg::launch_colsum_f32(pgb + 3 * H, kBwdBlocks, 4 * H, int(H), bfm(a.dbg), s0), "colsum"));
 #undef TPG_STEP
-  return TPG_OK;
+  return join_streams(cx, L.root, ns, st);
 }
 
 std::string ffnb_key(const tpg_ffnb_args& a) {

@@ -164,7 +164,25 @@ __device__ __forceinline__ void store8_bf16(uint16_t* dst, const float* f) {
   *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// CH = 8-element chunks per thread per half (H <= 8 * kBwdThreads * CH).
+__device__ __forceinline__ void put8(float* at, const float* v, int accumulate) {
+  float4* dst = reinterpret_cast<float4*>(at);
+  float4 lo = make_float4(v[0], v[1], v[2], v[3]);
+  float4 hi = make_float4(v[4], v[5], v[6], v[7]);
+  if (accumulate) {
+    const float4 ol = dst[0], oh = dst[1];
+    lo.x += ol.x; lo.y += ol.y; lo.z += ol.z; lo.w += ol.w;
+    hi.x += oh.x; hi.y += oh.y; hi.z += oh.z; hi.w += oh.w;
+  }
+  dst[0] = lo;
+  dst[1] = hi;
+}
+
+// CH = 8-column chunks per thread and half (H <= 8 * kBwdThreads * CH). The
+// next row's z chunks are loaded while the current row is reduced, so a
+// workgroup keeps a row of loads in flight behind its barriers. The row
+// statistics come from one reduction of sums shifted by the row's first
+// element (sum (v - v0), sum (v - v0)^2), which keeps the variance free of
+// cancellation for rows whose mean is large against their spread.
 template <int CH>
 __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
     const uint16_t* __restrict__ z, int64_t ldz, const uint16_t* __restrict__ dh, int64_t lddh,
@@ -173,107 +191,143 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
     const uint16_t* __restrict__ bg, float eps, float* __restrict__ part_gb, int accumulate,
     float* __restrict__ part_b1) {
   __shared__ float4 red[kBwdThreads / 64];
+  // the gamma / beta partials [4][H] live in LDS (each thread owns its
+  // columns, so there are no conflicts); the b1 partials in registers
+  extern __shared__ __attribute__((aligned(16))) float lds_gb[];
   const int nchunk = H >> 3;
   const float inv_h = 1.0f / static_cast<float>(H);
-  float p_gx[CH][8], p_bx[CH][8], p_gg[CH][8], p_bg[CH][8], p_du[CH][8], p_dg[CH][8];
+  float p_du[CH][8], p_dg[CH][8];
 #pragma unroll
   for (int c = 0; c < CH; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p_gx[c][e] = p_bx[c][e] = p_gg[c][e] = p_bg[c][e] = p_du[c][e] = p_dg[c][e] = 0.f;
+    for (int e = 0; e < 8; ++e) p_du[c][e] = p_dg[c][e] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = c * kBwdThreads + threadIdx.x;
+    if (ch < nchunk)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        reinterpret_cast<float4*>(lds_gb + q * H + ch * 8)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        reinterpret_cast<float4*>(lds_gb + q * H + ch * 8)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+  }
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(rows, r0 + rows_per_block);
+  uint4 nu[CH], ng[CH];
+  auto fetch = [&](int row) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = c * kBwdThreads + threadIdx.x;
+      nu[c] = ng[c] = make_uint4(0, 0, 0, 0);
+      if (ch < nchunk && row < r1) {
+        const uint16_t* zr = z + int64_t(row) * ldz;
+        nu[c] = *reinterpret_cast<const uint4*>(zr + ch * 8);
+        ng[c] = *reinterpret_cast<const uint4*>(zr + H + ch * 8);
+      }
+    }
+  };
+  fetch(r0);
   for (int row = r0; row < r1; ++row) {
-    const uint16_t* zu = z + int64_t(row) * ldz;
-    const uint16_t* zg = zu + H;
-    const uint16_t* dhr = dh + int64_t(row) * lddh;
+    const uint16_t* zr = z + int64_t(row) * ldz;
+    const float u0 = bf16_to_f32(zr[0]), g0 = bf16_to_f32(zr[H]);
     float u[CH][8], g[CH][8], d[CH][8];
-    float su = 0.f, sg = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      unpack8(nu[c], u[c]);
+      unpack8(ng[c], g[c]);
+    }
+    fetch(row + 1);                            // lands while this row is reduced
+    const uint16_t* dhr = dh + int64_t(row) * lddh;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {             // dh: needed after the first reduction
+      const int ch = c * kBwdThreads + threadIdx.x;
+      unpack8(ch < nchunk ? *reinterpret_cast<const uint4*>(dhr + ch * 8) : make_uint4(0, 0, 0, 0), d[c]);
+    }
+    float su = 0.f, sg = 0.f, qu = 0.f, qg = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const bool on = c * kBwdThreads + int(threadIdx.x) < nchunk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = on ? u[c][e] - u0 : 0.f, b = on ? g[c][e] - g0 : 0.f;
+        su += a;
+        sg += b;
+        qu += a * a;
+        qg += b * b;
+      }
+    }
+    float4 s4 = block_sum4(su, sg, qu, qg, red);
+    const float du0 = s4.x * inv_h, dg0 = s4.y * inv_h;   // mean - v0
+    const float mu = u0 + du0, mg = g0 + dg0;
+    const float ru = rsqrtf(fmaxf(s4.z * inv_h - du0 * du0, 0.f) + eps);
+    const float rg = rsqrtf(fmaxf(s4.w * inv_h - dg0 * dg0, 0.f) + eps);
+    float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = c * kBwdThreads + threadIdx.x;
-      if (ch < nchunk) {
-        unpack8(*reinterpret_cast<const uint4*>(zu + ch * 8), u[c]);
-        unpack8(*reinterpret_cast<const uint4*>(zg + ch * 8), g[c]);
-        unpack8(*reinterpret_cast<const uint4*>(dhr + ch * 8), d[c]);
+      const bool on = ch < nchunk;
+      float ag[8], ab[8], cg[8], cb[8];
+      const uint4 zero4 = make_uint4(0, 0, 0, 0);
+      unpack8(on ? *reinterpret_cast<const uint4*>(gx + ch * 8) : zero4, ag);
+      unpack8(on ? *reinterpret_cast<const uint4*>(bx + ch * 8) : zero4, ab);
+      unpack8(on ? *reinterpret_cast<const uint4*>(gg + ch * 8) : zero4, cg);
+      unpack8(on ? *reinterpret_cast<const uint4*>(bg + ch * 8) : zero4, cb);
+      float t_gx[8], t_bx[8], t_gg[8], t_bg[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          su += u[c][e];
-          sg += g[c][e];
+      for (int e = 0; e < 8; ++e) {
+        const float xu = on ? (u[c][e] - mu) * ru : 0.f, xg = on ? (g[c][e] - mg) * rg : 0.f;
+        const float a = xu * ag[e] + ab[e];
+        const float b = xg * cg[e] + cb[e];
+        const float sgm = 1.0f / (1.0f + __expf(-b));
+        const float da = d[c][e] * (b * sgm);
+        const float db = d[c][e] * a * sgm * (1.0f + b * (1.0f - sgm));
+        t_gx[e] = da * xu;
+        t_bx[e] = da;
+        t_gg[e] = db * xg;
+        t_bg[e] = db;
+        const float dxu = da * ag[e], dxg = db * cg[e];
+        m0 += dxu;
+        m1 += dxu * xu;
+        m2 += dxg;
+        m3 += dxg * xg;
+        u[c][e] = xu;          // u, g: the normalised rows; d: da * gx, g's
+        g[c][e] = xg;          // partner db * gg kept in the gate slot of d
+        d[c][e] = dxu;         // is recomputed below from dh (fewer registers)
+      }
+      if (on) {
+        float* lp = lds_gb + ch * 8;
+        const float* t[4] = {t_gx, t_bx, t_gg, t_bg};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float4* v = reinterpret_cast<float4*>(lp + q * H);
+          float4 lo = v[0], hi = v[1];
+          lo.x += t[q][0]; lo.y += t[q][1]; lo.z += t[q][2]; lo.w += t[q][3];
+          hi.x += t[q][4]; hi.y += t[q][5]; hi.z += t[q][6]; hi.w += t[q][7];
+          v[0] = lo;
+          v[1] = hi;
         }
       }
     }
-    float4 s4 = block_sum4(su, sg, 0.f, 0.f, red);
-    const float mu = s4.x * inv_h, mg = s4.y * inv_h;
-    float qu = 0.f, qg = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = c * kBwdThreads + threadIdx.x;
-      if (ch < nchunk) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          u[c][e] -= mu;
-          g[c][e] -= mg;
-          qu += u[c][e] * u[c][e];
-          qg += g[c][e] * g[c][e];
-        }
-      }
-    }
-    s4 = block_sum4(qu, qg, 0.f, 0.f, red);
-    const float ru = rsqrtf(s4.x * inv_h + eps), rg = rsqrtf(s4.y * inv_h + eps);
-    float xu_m = 0.f, xu_x = 0.f, xg_m = 0.f, xg_x = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = c * kBwdThreads + threadIdx.x;
-      if (ch < nchunk) {
-        float a_g[8], b_x[8], c_g[8], c_b[8];
-        unpack8(*reinterpret_cast<const uint4*>(gx + ch * 8), a_g);
-        unpack8(*reinterpret_cast<const uint4*>(bx + ch * 8), b_x);
-        unpack8(*reinterpret_cast<const uint4*>(gg + ch * 8), c_g);
-        unpack8(*reinterpret_cast<const uint4*>(bg + ch * 8), c_b);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xu = u[c][e] * ru, xg = g[c][e] * rg;
-          const float a = xu * a_g[e] + b_x[e];
-          const float b = xg * c_g[e] + c_b[e];
-          const float sgm = 1.0f / (1.0f + __expf(-b));
-          const float da = d[c][e] * (b * sgm);
-          const float db = d[c][e] * a * sgm * (1.0f + b * (1.0f - sgm));
-          p_gx[c][e] += da * xu;
-          p_bx[c][e] += da;
-          p_gg[c][e] += db * xg;
-          p_bg[c][e] += db;
-          const float dxu = da * a_g[e], dxg = db * c_g[e];
-          xu_m += dxu;
-          xu_x += dxu * xu;
-          xg_m += dxg;
-          xg_x += dxg * xg;
-          u[c][e] = xu;            // u, g now hold the normalised rows,
-          g[c][e] = xg;            // d holds da * gx; da * ... * gg is recomputed
-          d[c][e] = dxu;           // below from dh (cheaper than registers)
-        }
-      }
-    }
-    s4 = block_sum4(xu_m, xu_x, xg_m, xg_x, red);
+    s4 = block_sum4(m0, m1, m2, m3, red);
     const float mdu = s4.x * inv_h, mdux = s4.y * inv_h, mdg = s4.z * inv_h, mdgx = s4.w * inv_h;
     uint16_t* dzr = dz + int64_t(row) * lddz;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = c * kBwdThreads + threadIdx.x;
       if (ch < nchunk) {
-        float a_g[8], b_x[8], c_g[8], c_b[8], dhv[8];
-        unpack8(*reinterpret_cast<const uint4*>(gx + ch * 8), a_g);
-        unpack8(*reinterpret_cast<const uint4*>(bx + ch * 8), b_x);
-        unpack8(*reinterpret_cast<const uint4*>(gg + ch * 8), c_g);
-        unpack8(*reinterpret_cast<const uint4*>(bg + ch * 8), c_b);
+        float ag[8], ab[8], cg[8], cb[8], dhv[8], ou[8], og[8];
+        unpack8(*reinterpret_cast<const uint4*>(gx + ch * 8), ag);
+        unpack8(*reinterpret_cast<const uint4*>(bx + ch * 8), ab);
+        unpack8(*reinterpret_cast<const uint4*>(gg + ch * 8), cg);
+        unpack8(*reinterpret_cast<const uint4*>(bg + ch * 8), cb);
         unpack8(*reinterpret_cast<const uint4*>(dhr + ch * 8), dhv);
-        float ou[8], og[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xu = u[c][e], xg = g[c][e];
-          const float a = xu * a_g[e] + b_x[e];
-          const float b = xg * c_g[e] + c_b[e];
+          const float a = xu * ag[e] + ab[e];
+          const float b = xg * cg[e] + cb[e];
           const float sgm = 1.0f / (1.0f + __expf(-b));
-          const float dxg = dhv[e] * a * sgm * (1.0f + b * (1.0f - sgm)) * c_g[e];
+          const float dxg = dhv[e] * a * sgm * (1.0f + b * (1.0f - sgm)) * cg[e];
           ou[e] = (d[c][e] - mdu - xu * mdux) * ru;
           og[e] = (dxg - mdg - xg * mdgx) * rg;
           p_du[c][e] += ou[e];
@@ -292,30 +346,35 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
     const int ch = c * kBwdThreads + threadIdx.x;
     if (ch < nchunk) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = ch * 8 + e;
-        const float add0 = accumulate ? pgb[col] : 0.f, add1 = accumulate ? pgb[H + col] : 0.f;
-        const float add2 = accumulate ? pgb[2 * H + col] : 0.f, add3 = accumulate ? pgb[3 * H + col] : 0.f;
-        pgb[col] = add0 + p_gx[c][e];
-        pgb[H + col] = add1 + p_bx[c][e];
-        pgb[2 * H + col] = add2 + p_gg[c][e];
-        pgb[3 * H + col] = add3 + p_bg[c][e];
-        pb1[col] = p_du[c][e];
-        pb1[H + col] = p_dg[c][e];
-      }
+      for (int q = 0; q < 4; ++q) put8(pgb + q * H + ch * 8, lds_gb + q * H + ch * 8, accumulate);
+      put8(pb1 + ch * 8, p_du[c], 0);
+      put8(pb1 + H + ch * 8, p_dg[c], 0);
     }
   }
 }
 
-// Column sums of fp32 partials: out[c] = bf16(sum_b part[b * blk_stride + c]),
-// blocks in order (deterministic).
+// Column sums of fp32 partials: out[c] = bf16(sum_b part[b * blk_stride + c]).
+// A 256-thread workgroup takes 32 columns; its 8 row groups each sum a
+// fixed, interleaved eighth of the blocks, and the 8 group sums are added in
+// group order (deterministic).
+constexpr int kSumCols = 32;
+
 __global__ __launch_bounds__(256) void colsum_f32_kernel(const float* __restrict__ part, int nblk, int64_t blk_stride,
                                                           int ncols, uint16_t* __restrict__ out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= ncols) return;
+  __shared__ float acc[256 / kSumCols][kSumCols];
+  const int cl = threadIdx.x % kSumCols, grp = threadIdx.x / kSumCols;
+  const int c = blockIdx.x * kSumCols + cl;
   float s = 0.f;
-  for (int b = 0; b < nblk; ++b) s += part[int64_t(b) * blk_stride + c];
-  out[c] = f32_to_bf16(s);
+  if (c < ncols)
+    for (int b = grp; b < nblk; b += 256 / kSumCols) s += part[int64_t(b) * blk_stride + c];
+  acc[grp][cl] = s;
+  __syncthreads();
+  if (grp == 0 && c < ncols) {
+    float t = acc[0][cl];
+#pragma unroll
+    for (int g = 1; g < 256 / kSumCols; ++g) t += acc[g][cl];
+    out[c] = f32_to_bf16(t);
+  }
 }
 
 // fp32 column partials of a bf16 matrix, one per block of rows:
@@ -469,20 +528,31 @@ hipError_t launch_ffn_bwd_rows(const uint16_t* z, int64_t ldz, const uint16_t* d
   const int per = (H / 8 + kBwdThreads - 1) / kBwdThreads;
   const int rpb = (rows + nblk - 1) / nblk;
   dim3 grid(nblk), block(kBwdThreads);
-#define TPG_BWD(CH) hipLaunchKernelGGL(ffn_bwd_rows_kernel<CH>, grid, block, 0, s, z, ldz, dh, lddh, dz, lddz, rows, \
-                                       rpb, H, gx, bx, gg, bg, eps, part_gb, accumulate, part_b1)
-  if (per <= 1) TPG_BWD(1);
-  else if (per <= 2) TPG_BWD(2);     // H <= 8192 (more would spill at 512 threads)
-  else return hipErrorInvalidValue;
-#undef TPG_BWD
+  const size_t lds = size_t(4) * H * sizeof(float);
+  static bool attr_set[2] = {false, false};
+  const void* kern = per <= 1 ? reinterpret_cast<const void*>(ffn_bwd_rows_kernel<1>)
+                              : reinterpret_cast<const void*>(ffn_bwd_rows_kernel<2>);
+  if (per <= 2 && !attr_set[per - 1]) {
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 8192 * 4);
+    if (e != hipSuccess) return e;
+    attr_set[per - 1] = true;
+  }
+  if (per <= 1)
+    hipLaunchKernelGGL(ffn_bwd_rows_kernel<1>, grid, block, lds, s, z, ldz, dh, lddh, dz, lddz, rows, rpb, H, gx, bx,
+                       gg, bg, eps, part_gb, accumulate, part_b1);
+  else if (per <= 2)      // H <= 8192 (more would spill at 512 threads)
+    hipLaunchKernelGGL(ffn_bwd_rows_kernel<2>, grid, block, lds, s, z, ldz, dh, lddh, dz, lddz, rows, rpb, H, gx, bx,
+                       gg, bg, eps, part_gb, accumulate, part_b1);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_colsum_f32(const float* part, int nblk, int64_t blk_stride, int ncols, uint16_t* out,
                              hipStream_t s) {
   if (ncols == 0) return hipSuccess;
-  hipLaunchKernelGGL(colsum_f32_kernel, dim3((ncols + 255) / 256), dim3(256), 0, s, part, nblk, blk_stride, ncols,
-                     out);
+  hipLaunchKernelGGL(colsum_f32_kernel, dim3((ncols + kSumCols - 1) / kSumCols), dim3(256), 0, s, part, nblk,
+                     blk_stride, ncols, out);
   return hipGetLastError();
 }
 

@@ -293,6 +293,6 @@ def test_ffn_backward_validation(kw, status):
 def test_ffn_backward_workspace_size():
     PB, L, D, H = 128, 2, 64, 128
     r = lambda n: -(-n // 256) * 256
-    want = r(PB * 2 * H * 2) + 2 * r(PB * H * 2) + r(PB * 2 * H * 2) + r(256 * 4 * H * 4) + r(256 * 2 * H * 4) + \
-        r(256 * D * 4)
+    want = r(PB * 2 * H * 2) + r(2 * PB * H * 2) + r(PB * H * 2) + r(PB * 2 * H * 2) + r(256 * 4 * H * 4) + \
+        r(256 * 2 * H * 4) + r(256 * D * 4)
     assert tp.ffn_slot_backward_workspace_size(ffnb(PB=PB, L=L, D=D, H=H)) == want

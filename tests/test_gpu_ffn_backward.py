@@ -27,11 +27,11 @@ SHAPES = lambda c: dict(dx=(c.PB, c.L, c.D), dw1=(c.L, c.D, 2 * c.H), db1=(c.L, 
 ORACLE_KEY = dict(dx="x", dw1="w1", db1="b1", dwout="wout", dbout="bout", dgx="gx", dbx="bx", dgg="gg", dbg="bg")
 
 
-def run_backward(case, inp, dy):
+def run_backward(case, inp, dy, flags=0):
     t = {k: dev(v) for k, v in inp.items()}
     grads = {k: bf16_empty(*shape) for k, shape in SHAPES(case).items()}
     tp.ffn_slot_backward(t["x"], t["w1"], t["b1"], t["wout"], t["gx"], t["bx"], t["gg"], t["bg"], dev(dy), grads,
-                         PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps)
+                         PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps, flags=flags)
     torch.cuda.synchronize()
     return grads
 
@@ -51,8 +51,12 @@ def test_ffn_backward_parity(case):
     say(f"ffn backward: {case.name} frobenius {errs}")
     assert all(e <= BWD_TOL for e in errs.values()), errs
     again = run_backward(case, inp, dy)
-    for k in grads:                      # fixed reduction order: the same bits every run
+    serial = run_backward(case, inp, dy, tp.SERIAL_STAGES)
+    graph = run_backward(case, inp, dy, tp.FORCE_GRAPH)
+    for k in grads:                      # fixed reduction order: the same bits every run and issue mode
         assert torch.equal(grads[k], again[k]), k
+        assert torch.equal(grads[k], serial[k]), k
+        assert torch.equal(grads[k], graph[k]), k
 
 
 def test_ffn_backward_empty_batch_zeroes_parameter_grads():
