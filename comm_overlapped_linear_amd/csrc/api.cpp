@@ -1364,7 +1364,7 @@ tpg_status enqueue_ffn(Ctx& cx, const tpg_ffn_args& a, const Launch& L) {
       g1.bias = b1 + l * 2 * H;
       g1.d = z;  g1.ldd = 2 * H;
       g1.M = static_cast<int>(PB);  g1.N = static_cast<int>(2 * H);  g1.K = static_cast<int>(D);
-      g1.alpha = 1.0f;  g1.vec_ok = 1;
+      g1.alpha = 1.0f;  g1.vec_ok = 1;  g1.keep_out = 1;   // z: read next by the LayerNorm pass
       stat = gemm_on(cx, L, cs, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
       if (stat != TPG_OK) return stat;
       hipError_t e = tpg::launch_ln_silu(z, 2 * H, h, H, static_cast<int>(PB), static_cast<int>(H),
@@ -1526,7 +1526,7 @@ tpg_status enqueue_ffnb(Ctx& cx, const tpg_ffnb_args& a, const Launch& L) {
     g2.b = bf(a.wout) + l * H * D;  g2.ldb = D;
     g2.d = dh;  g2.ldd = H;
     g2.M = int(PB);  g2.N = int(H);  g2.K = int(D);
-    g2.alpha = 1.0f;  g2.vec_ok = 1;
+    g2.alpha = 1.0f;  g2.vec_ok = 1;  g2.keep_out = 1;   // dh: read next by the row backward
     TPG_STEP(gemm_on(cx, L, s1, g2, tpg::kBf16, tpg::kNK, tpg::kEpiAlphaBeta));
     TPG_STEP(record(s1, ev(l, 1)));
     // s0: z = X_l w1[l] + b1[l]; h = LN_x(u) silu(LN_gate(g))   (recomputed)
@@ -1536,7 +1536,7 @@ tpg_status enqueue_ffnb(Ctx& cx, const tpg_ffnb_args& a, const Launch& L) {
     g1.bias = bf(a.b1) + l * 2 * H;
     g1.d = z;  g1.ldd = 2 * H;
     g1.M = int(PB);  g1.N = int(2 * H);  g1.K = int(D);
-    g1.alpha = 1.0f;  g1.vec_ok = 1;
+    g1.alpha = 1.0f;  g1.vec_ok = 1;  g1.keep_out = 1;   // z: read next by the LayerNorm pass
     TPG_STEP(gemm_on(cx, L, s0, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta));
     TPG_STEP(hip(tpg::launch_ln_silu(z, 2 * H, h, H, int(PB), int(H), bf(a.gx), bf(a.bx), bf(a.gg), bf(a.bg),
                                      a.eps, s0),

@@ -302,7 +302,14 @@ __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchP
     o.y = f32_to_bf16(x[u][2]) | (static_cast<uint32_t>(f32_to_bf16(x[u][3])) << 16);
     o.z = f32_to_bf16(x[u][4]) | (static_cast<uint32_t>(f32_to_bf16(x[u][5])) << 16);
     o.w = f32_to_bf16(x[u][6]) | (static_cast<uint32_t>(f32_to_bf16(x[u][7])) << 16);
-    *reinterpret_cast<uint4*>(out_at(p, bp, row[u], col[u])) = o;
+    uint4* dst = reinterpret_cast<uint4*>(out_at(p, bp, row[u], col[u]));
+    if (p.keep_out) {
+      *dst = o;
+    } else {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 v = {o.x, o.y, o.z, o.w};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+    }
   }
 }
 
