@@ -649,25 +649,26 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
   // slices. (With the local stage on the root and the deliveries on a side
   // stream, the first delivery started ~17 us late and the call took ~127 us.)
   auto side = [&](int i) { return ns > 1 ? st[1 + i % (ns - 1)] : L.root; };
-  stat = launch_rows(side(0), a.a_slices[r], r, 1, budget(1));   // stage 0: the local slice
-  if (stat != TPG_OK) return stat;
+  // Issue order: every delivery first (they are the critical path; issued
+  // after the local stage's launch, the first started ~10 us late), then
+  // the local stage, then the runs.
   if (copies) {
     stat = hold_deliveries(a.flags, L.root);
     if (stat != TPG_OK) return stat;
-  }
-  for (int g = 0; g < G; ++g) {
-    if (copies) {
+    for (int g = 0; g < G; ++g) {
       const void* src[kMaxP];
       for (int t = t0(g); t < t0(g + 1); ++t) src[t - t0(g)] = a.a_slices[(r + t) % P];
       stat = deliver_slices(ck, src, t0(g + 1) - t0(g), slice_b, ws + (t0(g) - 1) * slice_b, slice_b, L.root);
       if (stat != TPG_OK) return stat;
+      if (g < G - 1 && ns > 1) HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
     }
+  }
+  stat = launch_rows(side(0), a.a_slices[r], r, 1, budget(1));   // stage 0: the local slice
+  if (stat != TPG_OK) return stat;
+  for (int g = 0; g < G; ++g) {
     const bool last = g == G - 1;
     hipStream_t cs = last ? L.root : side(g + 1);
-    if (!last && copies && ns > 1) {
-      HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
-      HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
-    }
+    if (!last && copies && ns > 1) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
     for (int t = t0(g); t < t0(g + 1);) {
       const int s = (r + t) % P;
       int run = std::min(t0(g + 1) - t, P - s);
