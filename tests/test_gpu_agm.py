@@ -74,3 +74,22 @@ def test_ag_multi_empty_projection_is_untouched():
     assert_parity(host_f64(ds[0]), refs[0], "out0")
     assert_parity(host_f64(ds[2]), refs[1], "out2")
     assert bool((ds[1] == 0x7FC0).all())                    # still the NaN fill
+
+
+def test_ag_multi_graph_replay_sees_new_data():
+    case = W.SMALL_AGM[0]
+    inp = W.ag_multi_inputs(case)
+    slices = [dev(s) for s in inp["a_slices"]]
+    bs = [dev(b) for b in inp["bs"]]
+    ds = [bf16_empty(case.M, n) for n in case.ns]
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    for it in range(3):
+        say(f"ag multi: graph replay {it}")
+        tp.stage_ag_multi(slices, bs, ds, M=case.M, K=case.K, rank=case.rank, flags=tp.FORCE_GRAPH, workspace=ws)
+        torch.cuda.synchronize()
+        refs = oracle.gemm_ag_multi([s.cpu().numpy().view(np.uint16) for s in slices],
+                                    [b.cpu().numpy().view(np.uint16) for b in bs], 1.0, case.rank)
+        for d, ref in zip(ds, refs):
+            assert_parity(host_f64(d), ref, f"replay {it}")
+        for s in slices:
+            s.copy_(torch.roll(s, 1, dims=0))

@@ -69,3 +69,26 @@ def test_ffn_backward_empty_batch_zeroes_parameter_grads():
     for k, g in grads.items():
         if k != "dx":
             assert torch.count_nonzero(g).item() == 0, k
+
+
+def test_ffn_backward_graph_replay_sees_new_data():
+    """The recorded backward replayed three times with a new upstream gradient
+    in place and eager work between: each replay equals the eager call."""
+    case = CASES[1]
+    inp = W.ffn_inputs(case)
+    t = {k: dev(v) for k, v in inp.items()}
+    dy = dev(W.ffn_upstream_grad(case))
+    g_rep = {k: bf16_empty(*shape) for k, shape in SHAPES(case).items()}
+    g_eag = {k: bf16_empty(*shape) for k, shape in SHAPES(case).items()}
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    args = (t["x"], t["w1"], t["b1"], t["wout"], t["gx"], t["bx"], t["gg"], t["bg"], dy)
+    kw = dict(PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps, workspace=ws)
+    for it in range(3):
+        say(f"ffn backward: graph replay {it}")
+        tp.ffn_slot_backward(*args, g_rep, flags=tp.FORCE_GRAPH, **kw)
+        torch.cuda.synchronize()
+        tp.ffn_slot_backward(*args, g_eag, flags=tp.NO_GRAPH, **kw)
+        torch.cuda.synchronize()
+        for k in g_rep:
+            assert torch.equal(g_rep[k], g_eag[k]), (it, k)
+        dy.copy_(torch.roll(dy, 1, dims=0))
