@@ -226,7 +226,18 @@ def cpu_baseline_ag(case, inp):
                    case.dtype, case.b_layout, swiglu=case.swiglu)
     dt = time.perf_counter() - t0
     return dict(value=case.flop / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
-                sample=f"the whole workload once ({case.flop / 1e9:.1f} GFLOP, float64 numpy), {dt:.2f} s")
+                sample=f"the whole workload once ({case.flop / 1e9:.1f} GFLOP, float64 numpy), {dt:.2f} s",
+                cpu=cpu_model(), host_cpus=os.cpu_count())
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_ag(case, args, detail):
@@ -470,7 +481,7 @@ WORKLOADS = {"ag_e4m3_p8": W.C2, "ag_e4m3_p8_beta0": W.C2_BETA0, "ag_bf16_p2": W
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ag_e4m3_p8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -553,6 +564,7 @@ def main():
         "roofline": r["roofline"],
         "cpu_baseline": cpu,
         "detail": detail,
+        "args": vars(args),
     }
     print(json.dumps(out), flush=True)
 
