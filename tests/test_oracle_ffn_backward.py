@@ -75,3 +75,20 @@ def test_bias_gradient_is_the_row_sum():
     dY = rng.normal(0, 1, (PB, L, D))
     g = F.backward_f64(rng.normal(0, 1, (PB, L, D)), params(rng, L, D, H), dY, 1e-5)
     np.testing.assert_allclose(g["bout"], dY.sum(axis=0), rtol=0, atol=1e-12)
+
+
+def test_bit_array_entry_point_decodes_every_tensor():
+    """ffn_slot_backward takes the storage formats (bf16 bits) of the
+    forward's inputs and the upstream gradient: its gradients equal those of
+    backward_f64 on the decoded values, key for key."""
+    from synth import workloads as W
+    case = W.FfnCase("tiny", B=2, T=4, D=8, k=2, P=2, affine=True, big_bias=True)
+    inp = W.ffn_inputs(case)
+    dy = W.ffn_upstream_grad(case)
+    got = oracle.ffn_slot_backward(inp, dy, case.eps)
+    q = {k: oracle.decode_bf16(inp[k]) for k in ("w1", "b1", "wout", "bout", "gx", "bx", "gg", "bg")}
+    ref = F.backward_f64(oracle.decode_bf16(inp["x"]), q, oracle.decode_bf16(dy), case.eps)
+    assert sorted(got) == sorted(ref) == sorted(["x", "w1", "b1", "wout", "bout", "gx", "bx", "gg", "bg"])
+    for k in ref:
+        np.testing.assert_array_equal(got[k], ref[k])
+        assert got[k].shape == (inp[k].shape if k != "x" else inp["x"].shape)
