@@ -18,7 +18,10 @@ from .formats import decode_bf16
 
 
 def silu(t):
-    return t / (1.0 + np.exp(-t))
+    # e^-t overflows to inf for t below about -709; t / inf is then the exact
+    # limit -0.0, so the overflow warning is silenced, not the value changed
+    with np.errstate(over="ignore"):
+        return t / (1.0 + np.exp(-t))
 
 
 def layer_norm(v, gamma, beta, eps):
