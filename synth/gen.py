@@ -151,3 +151,20 @@ def normal_e4m3(key, shape, scale=1.0, clip=448.0):
     n = int(np.prod(shape))
     v = np.clip(scale * normal(key, n), -clip, clip)
     return _encode_chunked(v, encode_e4m3, np.uint8).reshape(shape)
+
+
+def small_ints(key, n, lo, hi):
+    """n integers drawn uniformly from [lo, hi] (floor of a uniform draw)."""
+    return np.floor(uniform(key, n, lo, hi + 1)).astype(np.int64)
+
+
+def shifted_rows(key, rows, cols, lo, hi, encode, dtype, step=37):
+    """(rows, cols) storage codes whose row r is one seeded sequence of small
+    integers in [lo, hi], cyclically shifted by r * step places, and encoded
+    with `encode` (exact for small integers). Cheap at any size: only the one
+    sequence (2 * cols + 1 values) is drawn; every row is a copy of a window
+    of it, so tensors of several GiB are built by memory copies alone."""
+    period = 2 * cols + 1
+    seq = encode(small_ints(key, period, lo, hi).astype(np.float64)).astype(dtype)
+    windows = np.lib.stride_tricks.sliding_window_view(np.concatenate([seq, seq]), cols)
+    return windows[(np.arange(rows, dtype=np.int64) * step) % period]

@@ -74,3 +74,20 @@ def test_generator_is_counter_based_and_seeded():
     assert u.min() >= -1 and u.max() < 1 and abs(u.mean()) < 3e-3
     # SplitMix64 reference value: first output for state 0 (published test vector)
     assert int(gen._raw(np.uint64(0), 0, 1)[0]) == 0xE220A8397B1DCDAF
+
+
+def test_shifted_rows_are_windows_of_one_sequence():
+    """Row r of the large-tensor generator is the window of the seeded
+    sequence starting at r * step (cyclically), with every value an exact
+    small integer in [lo, hi] and all of them drawn."""
+    rows, cols, step = 300, 1000, 37
+    key = gen.stream_key(9, "shift")
+    codes = gen.shifted_rows(key, rows, cols, -2, 2, gen.encode_e4m3, np.uint8, step)
+    assert codes.shape == (rows, cols) and codes.flags["C_CONTIGUOUS"]
+    vals = oracle.decode_e4m3(codes)
+    assert set(np.unique(vals).tolist()) == {-2.0, -1.0, 0.0, 1.0, 2.0}
+    period = 2 * cols + 1
+    seq = gen.small_ints(key, period, -2, 2)
+    for r in (0, 1, 7, 54, 55, rows - 1):
+        idx = (r * step + np.arange(cols)) % period
+        assert np.array_equal(vals[r], seq[idx].astype(np.float64))
