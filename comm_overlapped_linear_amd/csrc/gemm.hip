@@ -192,10 +192,10 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, const BatchPt
   uint16_t* dst = out_at(p, bp, row, col);
   if (vec) {
     uint4 o;
-    o.x = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-    o.y = f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
-    o.z = f32_to_bf16(x[4]) | (static_cast<uint32_t>(f32_to_bf16(x[5])) << 16);
-    o.w = f32_to_bf16(x[6]) | (static_cast<uint32_t>(f32_to_bf16(x[7])) << 16);
+    o.x = pack_bf16x2(x[0], x[1]);
+    o.y = pack_bf16x2(x[2], x[3]);
+    o.z = pack_bf16x2(x[4], x[5]);
+    o.w = pack_bf16x2(x[6], x[7]);
     *reinterpret_cast<uint4*>(dst) = o;
   } else {
     for (int e = 0; e < n; ++e) dst[e] = f32_to_bf16(x[e]);
@@ -298,10 +298,10 @@ __device__ __forceinline__ void sweep_interior(const GemmParams& p, const BatchP
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     uint4 o;
-    o.x = f32_to_bf16(x[u][0]) | (static_cast<uint32_t>(f32_to_bf16(x[u][1])) << 16);
-    o.y = f32_to_bf16(x[u][2]) | (static_cast<uint32_t>(f32_to_bf16(x[u][3])) << 16);
-    o.z = f32_to_bf16(x[u][4]) | (static_cast<uint32_t>(f32_to_bf16(x[u][5])) << 16);
-    o.w = f32_to_bf16(x[u][6]) | (static_cast<uint32_t>(f32_to_bf16(x[u][7])) << 16);
+    o.x = pack_bf16x2(x[u][0], x[u][1]);
+    o.y = pack_bf16x2(x[u][2], x[u][3]);
+    o.z = pack_bf16x2(x[u][4], x[u][5]);
+    o.w = pack_bf16x2(x[u][6], x[u][7]);
     uint4* dst = reinterpret_cast<uint4*>(out_at(p, bp, row[u], col[u]));
     if (p.keep_out) {
       *dst = o;

@@ -111,8 +111,7 @@ __global__ __launch_bounds__(kRowThreads) void ln_silu_kernel(
         const float x1 = (u[c][e + 1] - mu) * ru * a[e + 1] + b[e + 1];
         const float y0 = (g[c][e] - mg) * rg * cc[e] + d[e];
         const float y1 = (g[c][e + 1] - mg) * rg * cc[e + 1] + d[e + 1];
-        o[e / 2] = f32_to_bf16(x0 * silu_f32(y0)) |
-                   (static_cast<uint32_t>(f32_to_bf16(x1 * silu_f32(y1))) << 16);
+        o[e / 2] = pack_bf16x2(x0 * silu_f32(y0), x1 * silu_f32(y1));
       }
       *reinterpret_cast<uint4*>(hr + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -131,18 +130,21 @@ __global__ __launch_bounds__(kRowThreads) void ln_silu_kernel(
 // the first bias gradient (du, dg). Workgroup w takes rows [w R, (w+1) R) and
 // writes its partials to block w of two fp32 buffers; the gamma / beta
 // partials are added to what the block already holds when `accumulate` is
-// set (they sum over slots). Three workgroup reductions per row (means,
-// centred second moments, the two backward means). HBM-bound: 10H bytes per
-// row (z and dh in, dz out).
+// set (they sum over slots). Two workgroup reductions per row (the shifted
+// first and second moments; the two backward means). HBM-bound: 10H bytes
+// per row (z and dh in, dz out).
 constexpr int kBwdThreads = 512;
 
+// Sum over the workgroup of four values; `red` alternates between two buffers
+// on consecutive calls, so one barrier suffices: a wave can only overwrite a
+// buffer two reductions later, after every wave has passed the barrier of the
+// reduction in between and so has finished reading it.
 __device__ __forceinline__ float4 block_sum4(float a, float b, float c, float d, float4* red) {
   a = wave_sum(a);
   b = wave_sum(b);
   c = wave_sum(c);
   d = wave_sum(d);
   const int wave = threadIdx.x >> 6;
-  __syncthreads();
   if ((threadIdx.x & 63) == 0) red[wave] = make_float4(a, b, c, d);
   __syncthreads();
   float4 s = red[0];
@@ -160,7 +162,7 @@ __device__ __forceinline__ void store8_bf16(uint16_t* dst, const float* f) {
   uint32_t o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    o[e] = f32_to_bf16(f[2 * e]) | (static_cast<uint32_t>(f32_to_bf16(f[2 * e + 1])) << 16);
+    o[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
   *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -177,11 +179,21 @@ __device__ __forceinline__ void put8(float* at, const float* v, int accumulate) 
   dst[1] = hi;
 }
 
-// CH = 8-column chunks per thread and half (H <= 8 * kBwdThreads * CH). The
-// next row's z chunks are loaded while the current row is reduced, so a
-// workgroup keeps a row of loads in flight behind its barriers. The row
-// statistics come from one reduction of sums shifted by the row's first
-// element (sum (v - v0), sum (v - v0)^2), which keeps the variance free of
+// One 16-byte load (a single dwordx4) of 8 bf16, or zeros when !on.
+__device__ __forceinline__ uint4 load16_or_zero(const uint16_t* p, bool on) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (on) v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// CH = 8-column chunks per thread and half (H <= 8 * kBwdThreads * CH).
+// Memory schedule: the four LayerNorm parameter vectors are read once, into
+// registers (packed bf16), and every global read of a row (z, dh and the
+// row's first elements, which shift the moment sums) is issued one row ahead,
+// so the only wait per row is for loads issued a whole row earlier. The row statistics come
+// from one reduction of sums shifted by the row's first element
+// (sum (v - v0), sum (v - v0)^2), which keeps the variance free of
 // cancellation for rows whose mean is large against their spread.
 template <int CH>
 __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
@@ -190,21 +202,26 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
     const uint16_t* __restrict__ gx, const uint16_t* __restrict__ bx, const uint16_t* __restrict__ gg,
     const uint16_t* __restrict__ bg, float eps, float* __restrict__ part_gb, int accumulate,
     float* __restrict__ part_b1) {
-  __shared__ float4 red[kBwdThreads / 64];
+  __shared__ float4 red[2][kBwdThreads / 64];
   // the gamma / beta partials [4][H] live in LDS (each thread owns its
   // columns, so there are no conflicts); the b1 partials in registers
   extern __shared__ __attribute__((aligned(16))) float lds_gb[];
   const int nchunk = H >> 3;
   const float inv_h = 1.0f / static_cast<float>(H);
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  uint4 q_gx[CH], q_bx[CH], q_gg[CH], q_bg[CH];   // this thread's parameter chunks
   float p_du[CH][8], p_dg[CH][8];
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p_du[c][e] = p_dg[c][e] = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int ch = c * kBwdThreads + threadIdx.x;
-    if (ch < nchunk)
+    const bool on = ch < nchunk;
+    q_gx[c] = load16_or_zero(gx + ch * 8, on);
+    q_bx[c] = load16_or_zero(bx + ch * 8, on);
+    q_gg[c] = load16_or_zero(gg + ch * 8, on);
+    q_bg[c] = load16_or_zero(bg + ch * 8, on);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p_du[c][e] = p_dg[c][e] = 0.f;
+    if (on)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         reinterpret_cast<float4*>(lds_gb + q * H + ch * 8)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -213,36 +230,36 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
   }
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(rows, r0 + rows_per_block);
-  uint4 nu[CH], ng[CH];
+  uint4 nu[CH], ng[CH], nd[CH];
+  uint16_t nu0 = 0, ng0 = 0;
   auto fetch = [&](int row) {
+    const bool live = row < r1;                // past the block's rows: nothing is read
+    const uint16_t* zr = z + int64_t(live ? row : 0) * ldz;
+    const uint16_t* dr = dh + int64_t(live ? row : 0) * lddh;
+    nu0 = live ? zr[0] : uint16_t(0);
+    ng0 = live ? zr[H] : uint16_t(0);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = c * kBwdThreads + threadIdx.x;
-      nu[c] = ng[c] = make_uint4(0, 0, 0, 0);
-      if (ch < nchunk && row < r1) {
-        const uint16_t* zr = z + int64_t(row) * ldz;
-        nu[c] = *reinterpret_cast<const uint4*>(zr + ch * 8);
-        ng[c] = *reinterpret_cast<const uint4*>(zr + H + ch * 8);
-      }
+      const bool on = live && ch < nchunk;
+      nu[c] = load16_or_zero(zr + ch * 8, on);
+      ng[c] = load16_or_zero(zr + H + ch * 8, on);
+      nd[c] = load16_or_zero(dr + ch * 8, on);
     }
   };
   fetch(r0);
+  int k = 0;                                   // reduction buffer
   for (int row = r0; row < r1; ++row) {
-    const uint16_t* zr = z + int64_t(row) * ldz;
-    const float u0 = bf16_to_f32(zr[0]), g0 = bf16_to_f32(zr[H]);
-    float u[CH][8], g[CH][8], d[CH][8];
+    const float u0 = bf16_to_f32(nu0), g0 = bf16_to_f32(ng0);
+    float u[CH][8], g[CH][8], d[CH][8], dg[CH][8];
+    uint4 dq[CH];                              // this row's dh, packed
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       unpack8(nu[c], u[c]);
       unpack8(ng[c], g[c]);
+      dq[c] = nd[c];
     }
-    fetch(row + 1);                            // lands while this row is reduced
-    const uint16_t* dhr = dh + int64_t(row) * lddh;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {             // dh: needed after the first reduction
-      const int ch = c * kBwdThreads + threadIdx.x;
-      unpack8(ch < nchunk ? *reinterpret_cast<const uint4*>(dhr + ch * 8) : make_uint4(0, 0, 0, 0), d[c]);
-    }
+    fetch(row + 1);                            // lands while this row is worked on
     float su = 0.f, sg = 0.f, qu = 0.f, qg = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -256,7 +273,8 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
         qg += b * b;
       }
     }
-    float4 s4 = block_sum4(su, sg, qu, qg, red);
+    float4 s4 = block_sum4(su, sg, qu, qg, red[k]);
+    k ^= 1;
     const float du0 = s4.x * inv_h, dg0 = s4.y * inv_h;   // mean - v0
     const float mu = u0 + du0, mg = g0 + dg0;
     const float ru = rsqrtf(fmaxf(s4.z * inv_h - du0 * du0, 0.f) + eps);
@@ -266,21 +284,21 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
     for (int c = 0; c < CH; ++c) {
       const int ch = c * kBwdThreads + threadIdx.x;
       const bool on = ch < nchunk;
-      float ag[8], ab[8], cg[8], cb[8];
-      const uint4 zero4 = make_uint4(0, 0, 0, 0);
-      unpack8(on ? *reinterpret_cast<const uint4*>(gx + ch * 8) : zero4, ag);
-      unpack8(on ? *reinterpret_cast<const uint4*>(bx + ch * 8) : zero4, ab);
-      unpack8(on ? *reinterpret_cast<const uint4*>(gg + ch * 8) : zero4, cg);
-      unpack8(on ? *reinterpret_cast<const uint4*>(bg + ch * 8) : zero4, cb);
+      float ag[8], ab[8], cg[8], cb[8], dhv[8];
+      unpack8(q_gx[c], ag);
+      unpack8(q_bx[c], ab);
+      unpack8(q_gg[c], cg);
+      unpack8(q_bg[c], cb);
+      unpack8(dq[c], dhv);
       float t_gx[8], t_bx[8], t_gg[8], t_bg[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float xu = on ? (u[c][e] - mu) * ru : 0.f, xg = on ? (g[c][e] - mg) * rg : 0.f;
         const float a = xu * ag[e] + ab[e];
         const float b = xg * cg[e] + cb[e];
-        const float sgm = 1.0f / (1.0f + __expf(-b));
-        const float da = d[c][e] * (b * sgm);
-        const float db = d[c][e] * a * sgm * (1.0f + b * (1.0f - sgm));
+        const float sgm = sigmoid_f32(b);
+        const float da = dhv[e] * (b * sgm);
+        const float db = dhv[e] * a * sgm * (1.0f + b * (1.0f - sgm));
         t_gx[e] = da * xu;
         t_bx[e] = da;
         t_gg[e] = db * xg;
@@ -290,9 +308,10 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
         m1 += dxu * xu;
         m2 += dxg;
         m3 += dxg * xg;
-        u[c][e] = xu;          // u, g: the normalised rows; d: da * gx, g's
-        g[c][e] = xg;          // partner db * gg kept in the gate slot of d
-        d[c][e] = dxu;         // is recomputed below from dh (fewer registers)
+        u[c][e] = xu;          // u, g: the normalised rows
+        g[c][e] = xg;
+        d[c][e] = dxu;         // da * gx and db * gg, for the last phase
+        dg[c][e] = dxg;
       }
       if (on) {
         float* lp = lds_gb + ch * 8;
@@ -308,28 +327,20 @@ __global__ __launch_bounds__(kBwdThreads) void ffn_bwd_rows_kernel(
         }
       }
     }
-    s4 = block_sum4(m0, m1, m2, m3, red);
+    s4 = block_sum4(m0, m1, m2, m3, red[k]);
+    k ^= 1;
     const float mdu = s4.x * inv_h, mdux = s4.y * inv_h, mdg = s4.z * inv_h, mdgx = s4.w * inv_h;
     uint16_t* dzr = dz + int64_t(row) * lddz;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = c * kBwdThreads + threadIdx.x;
       if (ch < nchunk) {
-        float ag[8], ab[8], cg[8], cb[8], dhv[8], ou[8], og[8];
-        unpack8(*reinterpret_cast<const uint4*>(gx + ch * 8), ag);
-        unpack8(*reinterpret_cast<const uint4*>(bx + ch * 8), ab);
-        unpack8(*reinterpret_cast<const uint4*>(gg + ch * 8), cg);
-        unpack8(*reinterpret_cast<const uint4*>(bg + ch * 8), cb);
-        unpack8(*reinterpret_cast<const uint4*>(dhr + ch * 8), dhv);
+        float ou[8], og[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xu = u[c][e], xg = g[c][e];
-          const float a = xu * ag[e] + ab[e];
-          const float b = xg * cg[e] + cb[e];
-          const float sgm = 1.0f / (1.0f + __expf(-b));
-          const float dxg = dhv[e] * a * sgm * (1.0f + b * (1.0f - sgm)) * cg[e];
           ou[e] = (d[c][e] - mdu - xu * mdux) * ru;
-          og[e] = (dxg - mdg - xg * mdgx) * rg;
+          og[e] = (dg[c][e] - mdg - xg * mdgx) * rg;
           p_du[c][e] += ou[e];
           p_dg[c][e] += og[e];
         }
