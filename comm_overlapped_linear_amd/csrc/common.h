@@ -35,11 +35,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ float silu_f32(float t) { return t / (1.0f + __expf(-t)); }
-
 // logistic(t) = 1 / (1 + e^-t) with the hardware reciprocal (v_rcp_f32, about
 // 1 ulp) in place of the correctly rounded division, which takes about ten
 // instructions; e^-t -> inf gives 0 and e^-t -> 0 gives 1.
 __device__ __forceinline__ float sigmoid_f32(float t) { return __builtin_amdgcn_rcpf(1.0f + __expf(-t)); }
+
+// silu(t) = t * logistic(t)
+__device__ __forceinline__ float silu_f32(float t) { return t * sigmoid_f32(t); }
 
 }  // namespace tpg
