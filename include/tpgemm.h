@@ -4,7 +4,8 @@
  * One GPU runs the rank-local share of a tensor-parallel GEMM as P ordered
  * stages. The peers' shards are ordinary device buffers in the same HBM;
  * each stage's input is delivered by an asynchronous device-to-device copy
- * (hipMemcpyAsync) and gated by a HIP event, so the matrix cores start on
+ * (the library's copy kernel, the runtime's shader copy or the SDMA copy
+ * engines, below) and gated by a HIP event, so the matrix cores start on
  * the local shard while the rest is delivered ("Distributed GEMM", Hassani
  * et al., SHI Labs, Dec 2024: Introduction and Background, Figures 3 and 4).
  * Which copy: the all-gather's deliveries are on its critical path, so it
