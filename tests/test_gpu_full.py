@@ -1,5 +1,6 @@
 """Full-size GPU parity: the five workloads at their real shapes, in the launch
-configuration the benchmark times (default issue, shader-copy deliveries).
+configuration the benchmark times (the library's default issue and copy kind
+for each call).
 
 The oracle computes sampled output rows one by one (every stage's first and
 last row plus seeded random rows); properties that hold at any size (staged
