@@ -5,10 +5,11 @@
 // matrix cores run the local stage, and the stage kernels need no
 // communication code of their own (Introduction; Approach, observations 2 and
 // 4; Background, Figure 4: local shard first, then rotate). On one MI355X the
-// peers' shards are buffers in the same HBM: each delivery is one
-// hipMemcpyAsync (the shader copy, or the SDMA copy engines with
-// TPG_COPY_SDMA), and one event after a run's deliveries gates exactly the
-// stage run that reads them. Stage launches fan out over up to four streams
+// peers' shards are buffers in the same HBM: a run's deliveries are one
+// launch of the library's copy kernel (the all-gather and weight-gradient
+// default), the runtime's shader copy, or the SDMA copy engines (the
+// reduce-scatter default), and one event after a run's deliveries gates
+// exactly the stage run that reads them. Stage launches fan out over up to four streams
 // forked from and joined back into the caller's stream. Calls are issued
 // eagerly; with TPG_FORCE_GRAPH one call is recorded once into a hipGraph and
 // replayed on request (launch gaps between stages are overhead, Approach
@@ -79,14 +80,26 @@ struct Ctx {
 std::mutex g_mu;
 std::unordered_map<int, Ctx*> g_ctx;
 
-tpg_status make_ctx(int dev, Ctx** out) {
-  Ctx* c = new Ctx();
-  c->device = dev;
+void destroy_ctx(Ctx* c);
+
+tpg_status make_ctx_into(Ctx* c) {
   for (int i = 1; i < kStreams; ++i) HIP_TRY(hipStreamCreateWithFlags(&c->comp[i], hipStreamNonBlocking));
   HIP_TRY(hipStreamCreateWithFlags(&c->capture, hipStreamNonBlocking));
   HIP_TRY(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming));
   for (int i = 0; i < kMaxP; ++i) HIP_TRY(hipEventCreateWithFlags(&c->ev_copy[i], hipEventDisableTiming));
   for (int i = 0; i < kStreams; ++i) HIP_TRY(hipEventCreateWithFlags(&c->ev_join[i], hipEventDisableTiming));
+  return TPG_OK;
+}
+
+// A context whose creation fails part way is released again (nothing leaks).
+tpg_status make_ctx(int dev, Ctx** out) {
+  Ctx* c = new Ctx();
+  c->device = dev;
+  const tpg_status st = make_ctx_into(c);
+  if (st != TPG_OK) {
+    destroy_ctx(c);
+    return st;
+  }
   *out = c;
   return TPG_OK;
 }
