@@ -497,7 +497,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures the rank-local share on ONE GPU; peers are buffers in the same HBM. "
-              "Multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+              "Runs on several GPUs are not supported: use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

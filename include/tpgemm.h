@@ -67,7 +67,7 @@ extern "C" {
 typedef enum {
   TPG_OK = 0,
   TPG_ERR_INVALID = 1,      /* bad shape, rank, NULL pointer, aliasing, beta != 0 without C */
-  TPG_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (dtype/layout/alignment) */
+  TPG_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement (dtype/layout/alignment) */
   TPG_ERR_WORKSPACE = 3,    /* workspace missing or smaller than *_workspace_size() */
   TPG_ERR_HIP = 4           /* a HIP runtime call failed; see tpg_last_error() */
 } tpg_status;
