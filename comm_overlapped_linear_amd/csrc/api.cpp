@@ -181,7 +181,9 @@ tpg_status gemm_on(Ctx& cx, const Launch& L, hipStream_t s, const tpg::GemmParam
     }
     HIP_TRY(hipEventRecord(rec.a, s));
   }
-  hipError_t e = layout == kLayoutAT ? tpg::launch_gemm_at(p, s) : tpg::launch_gemm(p, dtype, layout, epi, s);
+  hipError_t e = layout == kLayoutAT      ? tpg::launch_gemm_at(p, s)
+                 : p.cp_blocks > 0         ? tpg::launch_gemm_carrying_copy(p, dtype, layout, epi, s)
+                                           : tpg::launch_gemm(p, dtype, layout, epi, s);
   if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("gemm launch failed: ") + hipGetErrorString(e));
   if (L.profile) {
     HIP_TRY(hipEventRecord(rec.b, s));
@@ -647,15 +649,44 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
     return static_cast<int>(std::min<int64_t>(tpg::device_cus(),
                                               std::max<int64_t>(8, int64_t(tpg::device_cus()) * stages * stack / P)));
   };
-  auto launch_rows = [&](hipStream_t cs, const void* A, int s, int run, int cus) {
+  auto launch_rows = [&](hipStream_t cs, const void* A, int s, int run, int cus, const tpg::GemmParams* job) {
     tpg::GemmParams q = p;
     q.a = A;
     q.M = static_cast<int>(run * m);
     q.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
     set_out_rows(q, a, segs, s * m, nout);
     q.cu_budget = cus;
+    if (job) {
+      q.cp_blocks = job->cp_blocks;
+      q.cp_n = job->cp_n;
+      for (int i = 0; i < job->cp_n; ++i) q.cp_src[i] = job->cp_src[i];
+      q.cp_dst = job->cp_dst;
+      q.cp_dst_stride = job->cp_dst_stride;
+      q.cp_nvec = job->cp_nvec;
+    }
     return gemm_on(cx, L, cs, q, dtype, layout, epi);
   };
+  // On one stream (a latency-bound call) the local stage's launch carries
+  // the deliveries as extra workgroups: the local stage then runs beside
+  // them, as the staged schedule intends, with one launch fewer. The remote
+  // run follows in stream order. (Only with the library's copy kernel and
+  // a single remote run of at most kMaxCopySlices slices.)
+  tpg::GemmParams job = base_params();
+  bool carry = false;
+  if (copies && ns == 1 && G == 1 && ck == Copy::Kernel && remote <= tpg::kMaxCopySlices) {
+    const void* src[kMaxP];
+    for (int t = 1; t < P; ++t) src[t - 1] = a.a_slices[(r + t) % P];
+    if (tpg::deliver_ok(src, remote, slice_b, ws, slice_b)) {
+      carry = true;
+      job.cp_n = remote;
+      for (int i = 0; i < remote; ++i) job.cp_src[i] = static_cast<const uint8_t*>(src[i]);
+      job.cp_dst = reinterpret_cast<uint8_t*>(ws);
+      job.cp_dst_stride = static_cast<int64_t>(slice_b);
+      job.cp_nvec = static_cast<int64_t>(slice_b / 16);
+      const int64_t vecs = job.cp_nvec * remote;
+      job.cp_blocks = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (vecs + 2047) / 2048)));
+    }
+  }
   // Stream roles. The deliveries run back to back on the root and the last
   // run follows them there in stream order, so the call's critical path (last
   // delivery, then the last run) waits on no other queue. The local stage,
@@ -670,7 +701,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
   if (copies) {
     stat = hold_deliveries(a.flags, L.root);
     if (stat != TPG_OK) return stat;
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < G && !carry; ++g) {
       const void* src[kMaxP];
       for (int t = t0(g); t < t0(g + 1); ++t) src[t - t0(g)] = a.a_slices[(r + t) % P];
       stat = deliver_slices(ck, src, t0(g + 1) - t0(g), slice_b, ws + (t0(g) - 1) * slice_b, slice_b, L.root);
@@ -678,7 +709,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
       if (g < G - 1 && ns > 1) HIP_TRY(hipEventRecord(cx.ev_copy[g], L.root));
     }
   }
-  stat = launch_rows(side(0), a.a_slices[r], r, 1, budget(1));   // stage 0: the local slice
+  stat = launch_rows(side(0), a.a_slices[r], r, 1, budget(1), carry ? &job : nullptr);   // stage 0: the local slice
   if (stat != TPG_OK) return stat;
   for (int g = 0; g < G; ++g) {
     const bool last = g == G - 1;
@@ -690,7 +721,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
       if (!copies)
         while (run > 1 && !adjacent(s, run)) --run;      // in place: one launch per adjacent stretch
       const void* A = copies ? static_cast<const void*>(ws + (t - 1) * slice_b) : a.a_slices[s];
-      stat = launch_rows(cs, A, s, run, budget(t0(g + 1) - t0(g)));
+      stat = launch_rows(cs, A, s, run, budget(t0(g + 1) - t0(g)), nullptr);
       if (stat != TPG_OK) return stat;
       t += run;
     }

@@ -11,6 +11,7 @@ constexpr int kMaxAddList = 16;
 // A (M, K) with row stride lda elements; B (N, K) (nk) or (K, N) (kn) with
 // row stride ldb. C / D / bias / addends are bf16 bit patterns.
 constexpr int kMaxSeg = 4;
+constexpr int kMaxCopySlices = 8;
 
 struct GemmParams {
   const void* a;
@@ -73,6 +74,17 @@ struct GemmParams {
   int seg_col[kMaxSeg];
   uint16_t* seg_d[kMaxSeg];
   int64_t seg_ld[kMaxSeg];
+  // Stage deliveries carried by this launch (a latency-bound staged call on
+  // one stream): cp_blocks workgroups past the tile workgroups copy cp_n
+  // slices of cp_nvec 16-byte vectors, slice i from cp_src[i] to cp_dst +
+  // i * cp_dst_stride (16-byte aligned), and exit; 0 = none. Only the
+  // direct-to-LDS kernel takes them (launch_gemm_carrying_copy).
+  int cp_blocks;
+  int cp_n;
+  const uint8_t* cp_src[kMaxCopySlices];
+  uint8_t* cp_dst;
+  int64_t cp_dst_stride;
+  int64_t cp_nvec;
 };
 
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };
@@ -88,6 +100,12 @@ int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget);
 // Picks a tile shape for (M, N) and launches on `s`. Host-side checks of the
 // shapes and alignment are the caller's job (api.cpp validates every call).
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);
+
+// launch_gemm with the copy job of p (cp_n slices, see GemmParams) done by
+// extra workgroups of the same launch when the direct-to-LDS kernel runs the
+// GEMM; otherwise the copy runs as its own kernel right before the GEMM, in
+// stream order. Either way the copy and the GEMM share no data.
+hipError_t launch_gemm_carrying_copy(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);
 
 // D (M, N) = alpha * A^T B with A (K, M) and B (K, N), both bf16 row-major
 // (contraction over their rows), on the direct-to-LDS kernel; needs

@@ -658,8 +658,29 @@ struct Interleave {
   }
 };
 
+// The copy job of a launch that carries stage deliveries (GemmParams cp_*):
+// workgroup b of the p.cp_blocks copy workgroups strides over the vectors of
+// every slice.
+__device__ __forceinline__ void copy_job(const GemmParams& p, int b) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t total = int64_t(p.cp_n) * p.cp_nvec;
+  const int64_t step = int64_t(p.cp_blocks) * blockDim.x;
+  for (int64_t i = int64_t(b) * blockDim.x + threadIdx.x; i < total; i += step) {
+    const int sl = static_cast<int>(i / p.cp_nvec);
+    const int64_t v = i - sl * p.cp_nvec;
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cp_src[sl]) + v);
+    reinterpret_cast<u32x4*>(p.cp_dst + sl * p.cp_dst_stride)[v] = x;
+  }
+}
+
 template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(const GemmParams p) {
+  // workgroups past the tile workgroups carry the launch's copy job, if any
+  const int tile_grid = static_cast<int>(gridDim.x) - p.cp_blocks;
+  if (static_cast<int>(blockIdx.x) >= tile_grid) {
+    copy_job(p, static_cast<int>(blockIdx.x) - tile_grid);
+    return;
+  }
   const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
   constexpr int NW = WM * WN;                  // waves: 4 (one per SIMD) or 8 (two per SIMD)
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -882,7 +903,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm, tn);   // ends with a barrier: LDS free
   };
   if constexpr (persistent_tiles<Op, BM, BN, AT>()) {
-    for (int vt = blockIdx.x; vt < ntiles; vt += gridDim.x) run_tile(vt);
+    for (int vt = blockIdx.x; vt < ntiles; vt += tile_grid) run_tile(vt);
   } else {
     run_tile(blockIdx.x);
   }
@@ -910,7 +931,8 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   // their CUs are this launch's to use.
   int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) ? std::min(tiles, cu_count()) : tiles;
   if (p.grid_cap >= 8 && p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) grid = std::min(grid, p.grid_cap & ~7);
-  hipLaunchKernelGGL(kern, dim3(grid, p.batch), dim3(nt), smem, s, p);
+  if (p.cp_blocks > 0 && p.batch != 1) return hipErrorInvalidValue;   // a copy job needs a single batch
+  hipLaunchKernelGGL(kern, dim3(grid + p.cp_blocks, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }
 
@@ -970,16 +992,20 @@ int pick_tile(int M, int N, int epi, int batch, int budget) {
   return best;
 }
 
+// Whether a launch runs on the direct-to-LDS kernel: 128-byte K-steps, and a
+// tile's A rows and all of B addressable with 31-bit offsets.
+bool dma_path(const GemmParams& p, int64_t eb, bool kn) {
+  const bool offsets_fit = int64_t(256) * p.lda * eb < (int64_t(1) << 31) &&
+                           (kn ? int64_t(64) * p.ldb * eb + int64_t(p.N) * 2
+                               : int64_t(p.N) * p.ldb * eb) < (int64_t(1) << 31);
+  return p.M > 0 && p.N > 0 && p.K > 0 && (p.K * eb) % 128 == 0 && offsets_fit;
+}
+
 template <typename Op, bool KN, bool SW>
 hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   // direct-to-LDS mainloop: 128-byte K-steps (measured faster on gfx950 than
   // 64-byte K-steps with twice the ring depth: half the barriers per byte)
-  // the DMA path addresses a tile's A rows and all of B with 31-bit offsets
-  const int64_t eb = Op::kElemBytes;
-  const bool offsets_fit = int64_t(256) * p.lda * eb < (int64_t(1) << 31) &&
-                           (KN ? int64_t(64) * p.ldb * eb + int64_t(p.N) * 2
-                               : int64_t(p.N) * p.ldb * eb) < (int64_t(1) << 31);
-  const bool dma = p.M > 0 && p.N > 0 && p.K > 0 && (p.K * Op::kElemBytes) % 128 == 0 && offsets_fit;
+  const bool dma = dma_path(p, Op::kElemBytes, KN);
   const int epi = SW ? kEpiSwiglu : kEpiAlphaBeta;
   if (dma) {
     switch (pick_tile(p.M, p.N, epi, p.batch, p.cu_budget)) {
@@ -1093,6 +1119,20 @@ hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipS
   }
   if (kn) return hipErrorInvalidValue;     // fp8 is NK only (validated on the host)
   return sw ? dispatch_tile<OpE4m3, false, true>(p, s) : dispatch_tile<OpE4m3, false, false>(p, s);
+}
+
+hipError_t launch_gemm_carrying_copy(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s) {
+  if (p.cp_blocks <= 0) return launch_gemm(p, dtype, layout, epi, s);
+  if (p.cp_n < 1 || p.cp_n > kMaxCopySlices || p.batch != 1) return hipErrorInvalidValue;
+  if (dma_path(p, dtype == kE4m3 ? 1 : 2, layout == kKN)) return launch_gemm(p, dtype, layout, epi, s);
+  // the register-staged kernel takes no copy job: the copy goes first
+  GemmParams q = p;
+  q.cp_blocks = 0;
+  const void* src[kMaxCopySlices];
+  for (int i = 0; i < p.cp_n; ++i) src[i] = p.cp_src[i];
+  hipError_t e = launch_deliver(src, p.cp_n, size_t(p.cp_nvec) * 16, p.cp_dst, size_t(p.cp_dst_stride), s);
+  if (e != hipSuccess) return e;
+  return launch_gemm(q, dtype, layout, epi, s);
 }
 
 }  // namespace tpg
