@@ -278,6 +278,15 @@ def bench_ag(case, args, detail):
                     kernel="gemm_dma_kernel (stage runs of one call)", launches=len(recs),
                     launches_per_step=len(recs) // args.steps,
                     avg_launch_us=round(kms * 1e3, 2), flop_per_launch=kflop)
+    # the same launches by kind (the local stage beside the deliveries, the
+    # remote run over the delivered slices): flops, mean duration, rate
+    kinds = {}
+    for ms_, fl in recs:
+        kinds.setdefault(fl, []).append(ms_)
+    roofline["by_launch"] = [dict(gflop=round(fl / 1e9, 2), launches=len(v), avg_us=round(float(np.mean(v)) * 1e3, 2),
+                                  tflops=round(fl / (float(np.mean(v)) * 1e-3) / 1e12, 1),
+                                  frac=round(fl / (float(np.mean(v)) * 1e-3) / 1e12 / peak, 4))
+                             for fl, v in sorted(kinds.items())]
     log(f"[{case.name}] stage GEMM launches: {kms * 1e3:.1f} us avg, {achieved:.1f} TFLOP/s "
         f"({len(recs)} launches, eager, HIP events on each launch's stream)")
 
