@@ -85,6 +85,9 @@ struct GemmParams {
   uint8_t* cp_dst;
   int64_t cp_dst_stride;
   int64_t cp_nvec;
+  // Tile-rows per group of the direct-to-LDS kernel's tile order, set by its
+  // launcher (callers leave 0: the kernel's own power-of-two rule).
+  int tile_gm;
 };
 
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };

@@ -565,12 +565,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
 // tile order. The tile order walks groups of GM tile-rows column by column,
 // with GM chosen so that one XCD's run is a compact rectangle of tiles
 // (about sqrt(run) rows): its A rows and B columns are shared in its L2.
-__device__ __forceinline__ void tile_of_block(int vt, int nt, int ntm, int& tm, int& tn) {
+// The launcher may fix GM instead (gm_fixed > 0; see group_rows).
+__device__ __forceinline__ void tile_of_block(int vt, int nt, int ntm, int gm_fixed, int& tm, int& tn) {
   int bid = vt;
   if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);
   const int run = (nt & 7) == 0 ? (nt >> 3) : nt;
-  int gm = 1;
-  while ((gm * 2) * (gm * 2) <= run && gm * 2 <= ntm) gm *= 2;
+  int gm = gm_fixed;
+  if (gm <= 0) {
+    gm = 1;
+    while ((gm * 2) * (gm * 2) <= run && gm * 2 <= ntm) gm *= 2;
+  }
   const int ntn = nt / ntm;
   const int group = bid / (gm * ntn);
   const int first = group * gm;
@@ -740,7 +744,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   const int rsub = lane / CPR, pc = lane % CPR;
   auto run_tile = [&](int vt) {
   int tm, tn;
-  tile_of_block(vt, ntiles, ntm, tm, tn);
+  tile_of_block(vt, ntiles, ntm, p.tile_gm, tm, tn);
   const int m0 = tm * BM;
   // This lane's source chunk in each DMA instruction, as a 32-bit offset
   // from a uniform base (the tile's first A row; B itself), which the host
@@ -911,8 +915,45 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
 
 int cu_count();
 
+// Group height for tile_of_block when a launch is one round of tiles (every
+// tile has a workgroup at once, the tiles split evenly over the 8 XCDs): the
+// height, among those that make each XCD's run of tiles one whole rectangle,
+// with the fewest A rows plus B columns per XCD, i.e. the least L2 fill for
+// the tiles that run together. 0 (the kernel's power-of-two rule) otherwise,
+// or when no height gives whole rectangles. For 224 tiles of 128 x 256 over
+// 56 x 4 (the 7168-row stage run of 1024 columns) the power-of-two rule
+// groups 4 tile-rows, so most XCD runs straddle three groups and read 12 A
+// tile-rows; 7 gives each XCD 7 tile-rows by all 4 columns.
+int group_rows(int ntm, int ntn, int bm, int bn, int grid) {
+  const int64_t nt = int64_t(ntm) * ntn;
+  if (nt % 8 != 0 || nt > grid || nt > cu_count()) return 0;
+  const int64_t run = nt / 8;
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int gm = 1; gm <= std::min(ntm, 64); ++gm) {
+    if (ntm % gm != 0) continue;
+    const int64_t group = int64_t(gm) * ntn;
+    int64_t rows, cols;
+    if (run % group == 0) {                          // each XCD: whole groups
+      rows = run / ntn;
+      cols = ntn;
+    } else if (group % run == 0 && run % gm == 0) {  // each XCD: whole columns of one group
+      rows = gm;
+      cols = run / gm;
+    } else {
+      continue;
+    }
+    const int64_t cost = rows * bm + cols * bn;
+    if (best == 0 || cost < best_cost) {
+      best = gm;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT = false>
-hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
+hipError_t launch_dma_tile(const GemmParams& p_in, hipStream_t s) {
   constexpr int smem = STAGES * (BM + BN) * ROWB;
   constexpr int nt = 64 * WM * WN;
   auto kern = gemm_dma_kernel<Op, BM, BN, WM, WN, ROWB, STAGES, KN, SWIGLU, AT>;
@@ -923,6 +964,7 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  GemmParams p = p_in;
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int tiles = ((p.M + BM - 1) / BM) * nout_tiles;
   if (tiles == 0 || p.batch < 1) return hipSuccess;
@@ -932,6 +974,7 @@ hipError_t launch_dma_tile(const GemmParams& p, hipStream_t s) {
   int grid = (p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) ? std::min(tiles, cu_count()) : tiles;
   if (p.grid_cap >= 8 && p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) grid = std::min(grid, p.grid_cap & ~7);
   if (p.cp_blocks > 0 && p.batch != 1) return hipErrorInvalidValue;   // a copy job needs a single batch
+  p.tile_gm = p.batch == 1 ? group_rows((p.M + BM - 1) / BM, nout_tiles, BM, BN, grid) : 0;
   hipLaunchKernelGGL(kern, dim3(grid + p.cp_blocks, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }
