@@ -90,6 +90,20 @@ struct GemmParams {
   int tile_gm;
 };
 
+// Raises a kernel's dynamic-LDS limit on the current device the first time
+// it is launched there (the attribute may be per device); `done` holds one
+// bit per device. Callers hold the library's lock.
+inline hipError_t lds_limit_once(const void* kern, int bytes, uint64_t& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit != 0 && (done & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done |= bit;
+  return e;
+}
+
 enum GemmDtype { kBf16 = 0, kE4m3 = 1 };
 enum GemmLayout { kNK = 0, kKN = 1 };
 enum GemmEpi { kEpiAlphaBeta = 0, kEpiSwiglu = 1 };

@@ -26,6 +26,7 @@
 //    Accumulation is fp32; D is rounded once to bf16 (nearest even).
 #include "common.h"
 #include <algorithm>
+#include <atomic>
 
 #include "gemm.h"
 
@@ -957,13 +958,8 @@ hipError_t launch_dma_tile(const GemmParams& p_in, hipStream_t s) {
   constexpr int smem = STAGES * (BM + BN) * ROWB;
   constexpr int nt = 64 * WM * WN;
   auto kern = gemm_dma_kernel<Op, BM, BN, WM, WN, ROWB, STAGES, KN, SWIGLU, AT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static uint64_t lds_set = 0;
+  if (hipError_t e = lds_limit_once(reinterpret_cast<const void*>(kern), smem, lds_set); e != hipSuccess) return e;
   GemmParams p = p_in;
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int tiles = ((p.M + BM - 1) / BM) * nout_tiles;
@@ -983,13 +979,8 @@ template <typename Op, int BM, int BN, bool KN, bool SWIGLU>
 hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
   constexpr int smem = 2 * (BM + BN) * kRowBytes;
   auto kern = gemm_kernel<Op, BM, BN, KN, SWIGLU>;
-  static bool attr_set = false;   // per process; the attribute is per function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static uint64_t lds_set = 0;
+  if (hipError_t e = lds_limit_once(reinterpret_cast<const void*>(kern), smem, lds_set); e != hipSuccess) return e;
   const int nout_tiles = SWIGLU ? ((p.N / 2) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int grid = ((p.M + BM - 1) / BM) * nout_tiles;
   if (grid == 0 || p.batch < 1) return hipSuccess;
@@ -997,17 +988,18 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Number of compute units of the current device (cached per device).
+// Number of compute units of the current device (cached per device; read
+// also by calls that do not take the library's lock).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Tile choice by a small cost model: waves of workgroups over the CUs times

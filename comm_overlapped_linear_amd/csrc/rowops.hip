@@ -540,13 +540,11 @@ hipError_t launch_ffn_bwd_rows(const uint16_t* z, int64_t ldz, const uint16_t* d
   const int rpb = (rows + nblk - 1) / nblk;
   dim3 grid(nblk), block(kBwdThreads);
   const size_t lds = size_t(4) * H * sizeof(float);
-  static bool attr_set[2] = {false, false};
+  static uint64_t lds_set[2] = {0, 0};
   const void* kern = per <= 1 ? reinterpret_cast<const void*>(ffn_bwd_rows_kernel<1>)
                               : reinterpret_cast<const void*>(ffn_bwd_rows_kernel<2>);
-  if (per <= 2 && !attr_set[per - 1]) {
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 8192 * 4);
-    if (e != hipSuccess) return e;
-    attr_set[per - 1] = true;
+  if (per <= 2) {
+    if (hipError_t e = lds_limit_once(kern, 4 * 8192 * 4, lds_set[per - 1]); e != hipSuccess) return e;
   }
   if (per <= 1)
     hipLaunchKernelGGL(ffn_bwd_rows_kernel<1>, grid, block, lds, s, z, ldz, dh, lddh, dz, lddz, rows, rpb, H, gx, bx,
