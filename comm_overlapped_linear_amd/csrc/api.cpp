@@ -53,7 +53,8 @@ constexpr int kMaxP = 64;
 constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
                                  TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH |
-                                 TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER | TPG_COPY_KERNEL;
+                                 TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER | TPG_COPY_KERNEL |
+                                 TPG_DEBUG_NO_GATE;
 constexpr uint32_t kCopyFlags = TPG_COPY_SDMA | TPG_COPY_SHADER | TPG_COPY_KERNEL;
 // Staged calls below this many flops run on one stream: their GEMMs take
 // well under the few microseconds each cross-stream event costs (the P = 2
@@ -65,6 +66,13 @@ struct ProfRec {
   double flop;
 };
 
+// A recorded call: the executable graph and an event recorded after its
+// latest replay (a retired graph is destroyed once that event has completed).
+struct GraphEntry {
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;
+};
+
 struct Ctx {
   int device = -1;
   hipStream_t comp[kStreams] = {};   // comp[0] unused: the root stream takes its place
@@ -72,7 +80,8 @@ struct Ctx {
   hipEvent_t ev_fork = nullptr;
   hipEvent_t ev_copy[kMaxP] = {};
   hipEvent_t ev_join[kStreams] = {};
-  std::unordered_map<std::string, hipGraphExec_t> graphs;
+  std::unordered_map<std::string, GraphEntry> graphs;
+  std::vector<GraphEntry> retired;
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> prof_pool;
 };
@@ -120,8 +129,14 @@ tpg_status get_ctx(Ctx** out) {
   return TPG_OK;
 }
 
+void destroy_graph(const GraphEntry& g) {
+  if (g.exec) (void)hipGraphExecDestroy(g.exec);
+  if (g.done) (void)hipEventDestroy(g.done);
+}
+
 void destroy_ctx(Ctx* c) {
-  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : c->graphs) destroy_graph(kv.second);
+  for (auto& g : c->retired) destroy_graph(g);
   for (auto& r : c->prof) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
@@ -268,13 +283,23 @@ tpg_status deliver_slices(Copy k, const void* const* src, int n, size_t bytes, c
 tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t user,
                     const std::function<tpg_status(const Launch&)>& enqueue) {
   const bool eager = !(flags & TPG_FORCE_GRAPH) ||
-                     (flags & (TPG_NO_GRAPH | TPG_PROFILE | TPG_DEBUG_HOLD_DELIVERIES)) != 0;
+                     (flags & (TPG_NO_GRAPH | TPG_PROFILE | TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE)) != 0;
   if (eager) return enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
   auto it = cx.graphs.find(key);
   if (it == cx.graphs.end()) {
+    // retired graphs whose last replay has completed are destroyed; the
+    // others wait for a later call (no call blocks the host on the GPU)
+    for (size_t i = 0; i < cx.retired.size();) {
+      if (hipEventQuery(cx.retired[i].done) == hipSuccess) {
+        destroy_graph(cx.retired[i]);
+        cx.retired[i] = cx.retired.back();
+        cx.retired.pop_back();
+      } else {
+        ++i;
+      }
+    }
     if (cx.graphs.size() >= kMaxGraphs) {
-      HIP_TRY(hipDeviceSynchronize());
-      for (auto& kv : cx.graphs) (void)hipGraphExecDestroy(kv.second);
+      for (auto& kv : cx.graphs) cx.retired.push_back(kv.second);
       cx.graphs.clear();
     }
     HIP_TRY(hipStreamBeginCapture(cx.capture, hipStreamCaptureModeThreadLocal));
@@ -286,19 +311,35 @@ tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t
       return st;
     }
     if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("graph capture failed: ") + hipGetErrorString(e));
-    hipGraphExec_t ex = nullptr;
-    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    GraphEntry ge;
+    e = hipGraphInstantiate(&ge.exec, g, nullptr, nullptr, 0);
     (void)hipGraphDestroy(g);
     if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("graph instantiate failed: ") + hipGetErrorString(e));
-    it = cx.graphs.emplace(key, ex).first;
+    e = hipEventCreateWithFlags(&ge.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      destroy_graph(ge);
+      return fail(TPG_ERR_HIP, std::string("hipEventCreateWithFlags failed: ") + hipGetErrorString(e));
+    }
+    it = cx.graphs.emplace(key, ge).first;
   }
-  HIP_TRY(hipGraphLaunch(it->second, user));
+  HIP_TRY(hipGraphLaunch(it->second.exec, user));
+  HIP_TRY(hipEventRecord(it->second.done, user));
   return TPG_OK;
 }
 
 template <typename T>
 void put(std::ostringstream& os, const T& v) {
   os << v << '|';
+}
+
+// TPG_DEBUG_NO_GATE applies to staged calls of the entry points that
+// implement it (`supported`).
+tpg_status validate_no_gate(uint32_t flags, bool supported) {
+  if (!(flags & TPG_DEBUG_NO_GATE)) return TPG_OK;
+  if (!supported) return fail(TPG_ERR_UNSUPPORTED, "TPG_DEBUG_NO_GATE: not implemented by this call");
+  if (flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES))
+    return fail(TPG_ERR_INVALID, "TPG_DEBUG_NO_GATE needs a staged call on several streams");
+  return TPG_OK;
 }
 
 // ---------------------------------------------------------------- all-gather
@@ -327,6 +368,7 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
   if (!copy_flags_ok(a->flags))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
+  if (tpg_status ng = validate_no_gate(a->flags, !rotb); ng != TPG_OK) return ng;
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
   if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
   if (a->epilogue != TPG_EPI_ALPHA_BETA && a->epilogue != TPG_EPI_SWIGLU)
@@ -635,6 +677,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
         return false;
     return true;
   };
+  const bool no_gate = (a.flags & TPG_DEBUG_NO_GATE) != 0;
   const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(G + 1, kStreams);
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, ns, st);
@@ -676,15 +719,20 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
   if (copies && ns == 1 && G == 1 && ck == Copy::Kernel && remote <= tpg::kMaxCopySlices) {
     const void* src[kMaxP];
     for (int t = 1; t < P; ++t) src[t - 1] = a.a_slices[(r + t) % P];
-    if (tpg::deliver_ok(src, remote, slice_b, ws, slice_b)) {
+    const int64_t vecs = int64_t(slice_b / 16) * remote;
+    const int cp_blocks = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (vecs + 2047) / 2048)));
+    // the copy workgroups must find CUs of their own beside the local stage's
+    // tiles (the persistent grid holds one workgroup per CU): otherwise they
+    // would queue behind the tile loop and the deliveries run separately
+    const int local_tiles = tpg::gemm_tiles(static_cast<int>(m), static_cast<int>(a.N), dtype, epi, 1, 0);
+    if (tpg::deliver_ok(src, remote, slice_b, ws, slice_b) && local_tiles + cp_blocks <= tpg::device_cus()) {
       carry = true;
       job.cp_n = remote;
       for (int i = 0; i < remote; ++i) job.cp_src[i] = static_cast<const uint8_t*>(src[i]);
       job.cp_dst = reinterpret_cast<uint8_t*>(ws);
       job.cp_dst_stride = static_cast<int64_t>(slice_b);
       job.cp_nvec = static_cast<int64_t>(slice_b / 16);
-      const int64_t vecs = job.cp_nvec * remote;
-      job.cp_blocks = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (vecs + 2047) / 2048)));
+      job.cp_blocks = cp_blocks;
     }
   }
   // Stream roles. The deliveries run back to back on the root and the last
@@ -713,8 +761,9 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
   if (stat != TPG_OK) return stat;
   for (int g = 0; g < G; ++g) {
     const bool last = g == G - 1;
-    hipStream_t cs = last ? L.root : side(g + 1);
-    if (!last && copies && ns > 1) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
+    // TPG_DEBUG_NO_GATE: every run on a side stream, with no wait for its slices
+    hipStream_t cs = (last && !no_gate) ? L.root : side(g + 1);
+    if (!last && copies && ns > 1 && !no_gate) HIP_TRY(hipStreamWaitEvent(cs, cx.ev_copy[g], 0));
     for (int t = t0(g); t < t0(g + 1);) {
       const int s = (r + t) % P;
       int run = std::min(t0(g + 1) - t, P - s);
@@ -921,6 +970,7 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
   if (tileb && a->N % a->P) return fail(TPG_ERR_INVALID, "TPG_TILE_B: N must be a multiple of P");
   if (tileb && (a->N / a->P) % 8) return fail(TPG_ERR_UNSUPPORTED, "TPG_TILE_B: N/P must be a multiple of 8");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if (tpg_status ng = validate_no_gate(a->flags, true); ng != TPG_OK) return ng;
   if (!copy_flags_ok(a->flags))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
@@ -1101,7 +1151,8 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   }
   stat = deliver();
   if (stat != TPG_OK) return stat;
-  stat = launch_blocks(L.root, r, 1, true);
+  // TPG_DEBUG_NO_GATE: the own block on a side stream, not after the deliveries
+  stat = launch_blocks((a.flags & TPG_DEBUG_NO_GATE) ? side(G) : L.root, r, 1, true);
   if (stat != TPG_OK) return stat;
   return join_streams(cx, L.root, ns, st);
 }
@@ -1159,6 +1210,7 @@ tpg_status validate_wg(const tpg_wg_args* a, size_t need) {
   if (a->M % a->P) return fail(TPG_ERR_INVALID, "M must be a multiple of P");
   if (a->gathered != TPG_GATHER_X && a->gathered != TPG_GATHER_G) return fail(TPG_ERR_INVALID, "bad gathered");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if (tpg_status ng = validate_no_gate(a->flags, false); ng != TPG_OK) return ng;
   if (!copy_flags_ok(a->flags))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
@@ -1356,6 +1408,7 @@ tpg_status validate_ffn(const tpg_ffn_args* a, size_t need) {
   if (!a) return fail(TPG_ERR_INVALID, "args is NULL");
   if (a->PB < 0 || a->L < 0 || a->D < 0 || a->H < 0) return fail(TPG_ERR_INVALID, "negative dimension");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
+  if (tpg_status ng = validate_no_gate(a->flags, false); ng != TPG_OK) return ng;
   if (!fits_int(a->PB) || !fits_int(a->L * a->D) || !fits_int(2 * a->H))
     return fail(TPG_ERR_UNSUPPORTED, "dimensions too large");
   if (a->D % 8 || a->H % 8) return fail(TPG_ERR_UNSUPPORTED, "D and H must be multiples of 8");
@@ -1709,7 +1762,7 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
     tpg_ag_args a = *args;
-    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE)) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
     return run_call(*cx, a.flags, ag_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ag(*cx, a, L); });
@@ -1728,7 +1781,7 @@ tpg_status tpgemm_stage_ag_multi(const tpg_agm_args* args, void* stream) {
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
     tpg_agm_args a = *args;
-    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(agm_ntot(&a)) * a.K < kLatencyBoundFlop)
+    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE)) && a.groups == 0 && 2.0 * a.M * double(agm_ntot(&a)) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
     return run_call(*cx, a.flags, agm_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_agm(*cx, a, L); });
@@ -1747,7 +1800,7 @@ tpg_status tpgemm_stage_rs(const tpg_rs_args* args, void* stream) {
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
     tpg_rs_args a = *args;
-    if (!(a.flags & TPG_UNSTAGED) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE)) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
     return run_call(*cx, a.flags, rs_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_rs(*cx, a, L); });

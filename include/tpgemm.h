@@ -53,7 +53,10 @@
  *     pointers, scalars, flags). A changed pointer makes a new graph, never
  *     a stale replay. Freeing a buffer a cached graph refers to is safe as
  *     long as that exact argument set is not called again;
- *     tpg_release_caches() drops all graphs.
+ *     tpg_release_caches() drops all graphs. When the cache is full (512
+ *     graphs) its graphs are retired: each is destroyed by a later call once
+ *     an event recorded after its last replay has completed (polled, never
+ *     waited on).
  *   - Calls on one device serialise on an internal lock; two calls whose
  *     workspaces overlap must not be in flight at once on different streams.
  */
@@ -100,7 +103,16 @@ enum {
   TPG_DEBUG_HOLD_DELIVERIES = 128u, /* testing: issue eagerly, with the deliveries queued behind a 20 ms
                                        host callback; every gated stage must still see its data */
   TPG_COPY_SHADER = 256u,   /* deliver with the runtime's shader copy (hipMemcpyAsync, uses CUs) */
-  TPG_COPY_KERNEL = 512u    /* deliver with the library's copy kernel (uses CUs); the AG and wgrad default */
+  TPG_COPY_KERNEL = 512u,   /* deliver with the library's copy kernel (uses CUs); the AG and wgrad default */
+  TPG_DEBUG_NO_GATE = 1024u /* testing, the negative control of the gate tests: staged rotating-A
+                               all-gathers and reduce-scatters issue every stage run that reads
+                               delivered data on an internal stream WITHOUT waiting for its
+                               deliveries. With TPG_DEBUG_HOLD_DELIVERIES those runs read the
+                               receive slots before the deliveries land, so the result is wrong
+                               (never a fault: the slots are valid workspace memory). Issues
+                               eagerly; rejected with TPG_UNSTAGED or TPG_SERIAL_STAGES
+                               (TPG_ERR_INVALID) and by the other entry points
+                               (TPG_ERR_UNSUPPORTED). */
 };
 
 /* ------------------------------------------------------------------------

@@ -162,6 +162,8 @@ SMALL_RS_TILEB = [
     RsCase("rsb_bf16_p4_small", M=136, N=4 * 64, K=264, P=4, rank=2, std=0.5),
     RsCase("rsb_bf16_p8_kn_small", M=100, N=8 * 48, K=192, P=8, rank=7, b_layout="kn", std=0.5),
     RsCase("rsb_bf16_p4_medium", M=2000, N=4 * 768, K=512, P=4, rank=1, std=0.5),
+    # alpha != 1 with incoming partials: alpha scales the own product only
+    RsCase("rsb_bf16_p4_alpha_small", M=136, N=4 * 64, K=256, P=4, rank=1, std=0.5, alpha=0.75),
 ]
 
 
@@ -429,6 +431,10 @@ SMALL_RS = [
     RsCase("rs_bf16_p4_dma_medium", M=4 * 1000, N=4040, K=128, P=4, rank=1, std=0.5),
     RsCase("rs_bf16_p4_kn_dma_small", M=4 * 100, N=264, K=192, P=4, rank=0, b_layout="kn", std=0.5),
     RsCase("rs_bf16_p4_longk_medium", M=4 * 256, N=768, K=2048, P=4, rank=2, std=0.5),
+    # alpha != 1 with incoming partials: alpha scales the own product only
+    RsCase("rs_bf16_p4_alpha_small", M=4 * 136, N=264, K=256, P=4, rank=1, std=0.5, alpha=0.75),
+    RsCase("rs_bf16_p8_kn_alpha_medium", M=8 * 256, N=1032, K=512, P=8, rank=5, b_layout="kn", std=0.5,
+           alpha=-1.5),
 ]
 SMALL_FFN = [
     FfnCase("ffn_public_b4_t16_d128_k2_p2", B=4, T=16, D=128, k=2, P=2),

@@ -65,6 +65,9 @@ def ag(**kw):
     (dict(schedule=tp.ROTATE_B, N=2 * 12), tp.ERR_UNSUPPORTED),     # N/P % 8
     (dict(schedule=tp.ROTATE_B, epilogue=tp.EPI_SWIGLU), tp.ERR_UNSUPPORTED),
     (dict(epilogue=tp.EPI_SWIGLU, N=255), tp.ERR_INVALID),
+    (dict(flags=tp.DEBUG_NO_GATE | tp.UNSTAGED), tp.ERR_INVALID),         # the negative control is staged
+    (dict(flags=tp.DEBUG_NO_GATE | tp.SERIAL_STAGES), tp.ERR_INVALID),
+    (dict(flags=tp.DEBUG_NO_GATE, schedule=tp.ROTATE_B, N=2 * 64), tp.ERR_UNSUPPORTED),
 ])
 def test_ag_validation_rejects_before_enqueue(kw, status):
     a = ag(**kw)
@@ -97,6 +100,10 @@ def test_rs_and_ffn_and_permute_validation():
     f = tp.FfnArgs(PB=8, L=2, D=12, H=16, x=FAKE, w1=FAKE, b1=FAKE, wout=FAKE, bout=FAKE, gx=FAKE,
                    bx=FAKE, gg=FAKE, bg=FAKE, eps=1e-5, y=FAKE + 0x1000000, flags=0)
     assert tp.lib().ffn_slot_forward(ctypes.byref(f), None) == tp.ERR_UNSUPPORTED   # D % 8
+    f.D, f.flags = 16, tp.DEBUG_NO_GATE
+    assert tp.lib().ffn_slot_forward(ctypes.byref(f), None) == tp.ERR_UNSUPPORTED   # no gate to drop
+    r.M, r.flags = 8 * 64, tp.DEBUG_NO_GATE | tp.UNSTAGED
+    assert tp.lib().tpgemm_stage_rs(ctypes.byref(r), None) == tp.ERR_INVALID
     srcs = (ctypes.c_void_p * 2)(FAKE, FAKE + 0x100000)
     sp = ctypes.cast(srcs, ctypes.POINTER(ctypes.c_void_p))
     assert tp.lib().dispatch_permute(sp, FAKE + 0x200000, 2, 0, 1, 3, 4, 2, None) == tp.ERR_INVALID  # T % P

@@ -58,8 +58,8 @@ def run_rs_tileb(case, inp, flags, groups=0, workspace=None):
     inc = [dev(x) if x is not None else None for x in inp["incoming"]]
     d = bf16_empty(case.M, case.N)
     tp.stage_rs(a, b, inc, d, M=case.M, N=case.N, K=case.K, P=case.P, rank=case.rank,
-                b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK, flags=flags, groups=groups,
-                schedule=tp.TILE_B, workspace=workspace)
+                b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK, alpha=case.alpha, flags=flags,
+                groups=groups, schedule=tp.TILE_B, workspace=workspace)
     torch.cuda.synchronize()
     return d
 
@@ -67,7 +67,8 @@ def run_rs_tileb(case, inp, flags, groups=0, workspace=None):
 @pytest.mark.parametrize("case", W.SMALL_RS_TILEB, ids=lambda c: c.name)
 def test_rs_tileb_parity_all_modes(case):
     inp = W.rs_tileb_inputs(case)
-    ref = oracle.gemm_rs_tileb(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P, case.b_layout)
+    ref = oracle.gemm_rs_tileb(inp["a"], inp["b"], inp["incoming"], case.alpha, case.rank, case.P,
+                               case.b_layout)
     outs = {}
     for name, flags in RS_MODES.items():
         say(f"rs tileb: {case.name} mode={name}")
@@ -83,12 +84,21 @@ def test_rs_tileb_parity_all_modes(case):
     # the emitted column blocks are the plain partial: the incoming partials
     # touch the own block only
     n = case.N // case.P
-    plain = oracle.gemm_rs_tileb(inp["a"], inp["b"], None, 1.0, case.rank, case.P, case.b_layout)
+    plain = oracle.gemm_rs_tileb(inp["a"], inp["b"], None, case.alpha, case.rank, case.P, case.b_layout)
     got = host_f64(outs["default"])
     for blk in range(case.P):
         if blk != case.rank:
             cols = slice(blk * n, (blk + 1) * n)
             assert_parity(got[:, cols], plain[:, cols], f"emitted block {blk}")
+    # own column block minus the incoming partials ~ alpha * E_rank, at a
+    # tolerance scaled to that partial (the incoming sum dominates the block)
+    cols = slice(case.rank * n, (case.rank + 1) * n)
+    inc_sum = sum(oracle.decode_bf16(x) for x in inp["incoming"] if x is not None)
+    own = got[:, cols] - inc_sum
+    e_r = plain[:, cols]
+    rms_e = np.sqrt(np.mean(e_r ** 2))
+    ulp_out = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref[:, cols]), 1e-30))) - 7)
+    assert np.all(np.abs(own - e_r) <= 0.02 * rms_e + ulp_out), "own partial mis-scaled or missing"
 
 
 def test_column_duals_with_held_deliveries():

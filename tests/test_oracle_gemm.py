@@ -295,3 +295,100 @@ def test_ag_multi_brute_force_and_concatenation():
     outs = oracle.gemm_ag_multi(slices, bs, 1.0, rank=2, dtype="bf16")
     whole = oracle.gemm_ag(slices, np.concatenate(bs, axis=0), None, 1.0, 0.0, rank=0)
     np.testing.assert_array_equal(np.concatenate(outs, axis=1), whole)
+
+
+# ---- reduce-scatter with alpha != 1 and incoming partials: alpha scales the
+# own partial product only; the incoming partials are added as they arrive
+
+def brute_rs(a, b, incoming, alpha, rank, P, tile_b):
+    """Scalar loops over the definition: out = alpha * A B^T everywhere, plus,
+    on the own block (rows of block `rank`, or columns with tile_b), the sum
+    of the peers' bf16 partials, unscaled."""
+    A = oracle.decode_bf16(a)
+    Bv = oracle.decode_bf16(b)
+    M, K = A.shape
+    N = Bv.shape[0]
+    m, n = M // P, N // P
+    out = np.zeros((M, N))
+    for i in range(M):
+        for j in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(A[i, k]) * float(Bv[j, k])
+            v = alpha * acc
+            own = (j // n == rank) if tile_b else (i // m == rank)
+            if own:
+                for src in range(P):
+                    if src != rank and incoming[src] is not None:
+                        x = incoming[src][i, j - rank * n] if tile_b else incoming[src][i - rank * m, j]
+                        v += float(oracle.decode_bf16(x))
+            out[i, j] = v
+    return out
+
+
+@pytest.mark.parametrize("tile_b", [False, True])
+@pytest.mark.parametrize("P,rank", [(2, 1), (4, 2)])
+def test_rs_alpha_scales_own_partial_only(tile_b, P, rank):
+    """Integer data, alpha = 0.75: every sum is exact, so the oracle must
+    equal the scalar brute force bit for bit. Scaling the incoming partials
+    by alpha as well (a plausible mistake) moves the own block by
+    0.25 * sum(incoming), which is nonzero here."""
+    rng = np.random.default_rng(90 + P + 10 * tile_b)
+    m, n, K = 3, 2, 8
+    M, N = P * m, P * n
+    a = rand_int_bf16(rng, (M, K))
+    b = rand_int_bf16(rng, (N, K))
+    shape = (M, n) if tile_b else (m, N)
+    inc = [None if j == rank else rand_int_bf16(rng, shape, -3, 3) for j in range(P)]
+    assert any(np.any(oracle.decode_bf16(x) != 0) for x in inc if x is not None)
+    ref = brute_rs(a, b, inc, 0.75, rank, P, tile_b)
+    got = (oracle.gemm_rs_tileb if tile_b else oracle.gemm_rs)(a, b, inc, 0.75, rank, P)
+    assert np.array_equal(got, ref)
+    got_kn = (oracle.gemm_rs_tileb if tile_b else oracle.gemm_rs)(a, np.ascontiguousarray(b.T), inc, 0.75,
+                                                                  rank, P, b_layout="kn")
+    assert np.array_equal(got_kn, ref)
+
+
+@pytest.mark.parametrize("tile_b", [False, True])
+@pytest.mark.parametrize("P", [2, 4])
+def test_rs_distributed_identity_with_alpha(tile_b, P):
+    """Every rank runs with the same alpha and feeds on the partials its
+    peers emitted (already scaled by alpha): the own block must then be
+    alpha times the unsharded product, exactly (integer data, alpha = 0.75,
+    |partials| <= 16, so alpha * E is exact in bf16)."""
+    rng = np.random.default_rng(120 + P + 10 * tile_b)
+    m, n, Ks = 3, 2, 4
+    M, N = P * m, P * n
+    alpha = 0.75
+    A = [rand_int_bf16(rng, (M, Ks), -1, 1) for _ in range(P)]
+    Bs = [rand_int_bf16(rng, (N, Ks), -1, 1) for _ in range(P)]
+    fn = oracle.gemm_rs_tileb if tile_b else oracle.gemm_rs
+    emitted = [fn(A[r], Bs[r], None, alpha, r, P) for r in range(P)]
+    full = np.concatenate([oracle.decode_bf16(x) for x in A], axis=1) @ \
+        np.concatenate([oracle.decode_bf16(x) for x in Bs], axis=1).T
+    for r in range(P):
+        if tile_b:
+            blk = (slice(None), slice(r * n, (r + 1) * n))
+        else:
+            blk = (slice(r * m, (r + 1) * m), slice(None))
+        incoming = [None if j == r else bf16_bits(emitted[j][blk]) for j in range(P)]
+        out = fn(A[r], Bs[r], incoming, alpha, r, P)
+        assert np.array_equal(out[blk], alpha * full[blk])
+
+
+@pytest.mark.parametrize("tile_b", [False, True])
+def test_rs_planted_alpha_on_incoming_is_caught(tile_b):
+    """A copy of the reduce-scatter oracle that also scales the incoming
+    partials by alpha differs from the brute force: the alpha pins above can
+    fail."""
+    rng = np.random.default_rng(150 + tile_b)
+    P, rank, m, n, K = 4, 1, 3, 2, 8
+    a = rand_int_bf16(rng, (P * m, K))
+    b = rand_int_bf16(rng, (P * n, K))
+    shape = (P * m, n) if tile_b else (m, P * n)
+    inc = [None if j == rank else rand_int_bf16(rng, shape, -3, 3) for j in range(P)]
+    fn = oracle.gemm_rs_tileb if tile_b else oracle.gemm_rs
+    bad = fn(a, b, None, 0.75, rank, P)
+    blk = (slice(None), slice(rank * n, (rank + 1) * n)) if tile_b else (slice(rank * m, (rank + 1) * m), slice(None))
+    bad[blk] += 0.75 * sum(oracle.decode_bf16(x) for x in inc if x is not None)
+    assert not np.array_equal(bad, brute_rs(a, b, inc, 0.75, rank, P, tile_b))
