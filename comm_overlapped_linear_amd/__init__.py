@@ -120,6 +120,7 @@ def lib():
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         for name, argt, rest in [
             ("tpgemm_stage_ag", [ctypes.POINTER(AgArgs), vp], i32),
+            ("tpgemm_stage_ag_noalloc", [ctypes.POINTER(AgArgs), vp], i32),
             ("tpgemm_stage_ag_workspace_size", [ctypes.POINTER(AgArgs)], ctypes.c_size_t),
             ("tpgemm_stage_rs", [ctypes.POINTER(RsArgs), vp], i32),
             ("tpgemm_stage_rs_workspace_size", [ctypes.POINTER(RsArgs)], ctypes.c_size_t),
@@ -248,6 +249,15 @@ def stage_ag(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, e
     args.workspace = _ptr(ws) if ws is not None else None
     args.workspace_bytes = ws.numel() if ws is not None else 0
     _check(lib().tpgemm_stage_ag(ctypes.byref(args), _stream(stream)))
+
+
+def stage_ag_noalloc(a_slices, b, c, d, *, M, N, K, rank=0, dtype=BF16, b_layout=B_NK, epilogue=EPI_ALPHA_BETA,
+                     alpha=1.0, beta=1.0, flags=0, groups=0, schedule=None, stream=None):
+    """tpgemm_stage_ag with the library's static scratch in place of a
+    workspace (allocates nothing; see tpgemm.h)."""
+    args = ag_args(a_slices, b, c, d, M=M, N=N, K=K, rank=rank, dtype=dtype, b_layout=b_layout,
+                   epilogue=epilogue, alpha=alpha, beta=beta, flags=flags, groups=groups, schedule=schedule)
+    _check(lib().tpgemm_stage_ag_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def rs_args(a, b, incoming, d, *, M, N, K, P, rank=0, dtype=BF16, b_layout=B_NK, alpha=1.0, flags=0,

@@ -1769,6 +1769,35 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
   });
 }
 
+tpg_status tpgemm_stage_ag_noalloc(const tpg_ag_args* args, void* stream) {
+  return guarded([&]() -> tpg_status {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!args) return fail(TPG_ERR_INVALID, "args is NULL");
+    if (args->flags & (TPG_FORCE_GRAPH | TPG_PROFILE))
+      return fail(TPG_ERR_UNSUPPORTED, "tpgemm_stage_ag_noalloc issues eagerly: no TPG_FORCE_GRAPH or TPG_PROFILE");
+    tpg_ag_args a = *args;
+    a.workspace = nullptr;                   // the receive slots are the static scratch
+    a.workspace_bytes = 0;
+    const size_t need = ag_ws(&a);
+    if (need > tpg::kStaticScratchBytes)
+      return fail(TPG_ERR_WORKSPACE, "receive slots need " + std::to_string(need) +
+                                         " bytes, above the static scratch of " +
+                                         std::to_string(tpg::kStaticScratchBytes) + " bytes");
+    tpg_status st = validate_ag(&a, 0);      // everything but the workspace (the scratch overlaps nothing)
+    if (st != TPG_OK) return st;
+    if (a.M == 0 || a.N == 0) return TPG_OK;
+    Ctx* cx = nullptr;
+    st = get_ctx(&cx);
+    if (st != TPG_OK) return st;
+    HIP_TRY(tpg::static_scratch(&a.workspace));
+    a.workspace_bytes = tpg::kStaticScratchBytes;
+    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE)) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+      a.flags |= TPG_SERIAL_STAGES;
+    return run_call(*cx, a.flags | TPG_NO_GRAPH, std::string(), static_cast<hipStream_t>(stream),
+                    [&](const Launch& L) { return enqueue_ag(*cx, a, L); });
+  });
+}
+
 size_t tpgemm_stage_ag_multi_workspace_size(const tpg_agm_args* args) { return agm_ws(args); }
 
 tpg_status tpgemm_stage_ag_multi(const tpg_agm_args* args, void* stream) {

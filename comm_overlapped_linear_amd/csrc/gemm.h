@@ -175,6 +175,14 @@ struct DeliverParams {
 bool deliver_ok(const void* const* src, int n, size_t bytes, const void* dst, size_t dst_stride);
 hipError_t launch_deliver(const void* const* src, int n, size_t bytes, void* dst, size_t dst_stride, hipStream_t s);
 
+// Static receive-slot scratch of the allocation-free all-gather entry point
+// (scratch.hip): its device address on the current device, resolved with
+// hipGetSymbolAddress on the first request per device (callers hold the
+// library's lock).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(void** ptr);
+
 // Bit-exact run permute used by dispatch / combine.
 struct PermuteParams {
   const uint8_t* src[64];

@@ -186,6 +186,28 @@ size_t tpgemm_stage_ag_workspace_size(const tpg_ag_args* args);
 tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * tpgemm_stage_ag without a workspace, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The same computation, kernels and results as
+ * tpgemm_stage_ag (bit for bit); args->workspace and workspace_bytes are
+ * ignored. The receive slots live in a static device array of 64 MiB
+ * (67108864 bytes) that the library holds on every GPU it runs on until the
+ * process ends. The first call on a device also creates the library's
+ * internal streams and events and resolves that array's address; after
+ * that, calls make no device allocation of any kind (no hipMalloc, no
+ * graphs). Always issued eagerly.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: two calls in flight at once on one GPU (different streams, or
+ * different host threads without stream ordering between them) race on it.
+ * Calls on one stream are ordered and safe.
+ * Errors: those of tpgemm_stage_ag; TPG_ERR_WORKSPACE when
+ * tpgemm_stage_ag_workspace_size(args) exceeds 64 MiB (e.g. the e4m3
+ * all-gather of 8192 x 8192 in P = 8 slices needs 56 MiB staged and 64 MiB
+ * unstaged); TPG_ERR_UNSUPPORTED with TPG_FORCE_GRAPH or TPG_PROFILE.
+ * ---------------------------------------------------------------------- */
+tpg_status tpgemm_stage_ag_noalloc(const tpg_ag_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * Several column-parallel projections sharing one all-gathered input
  * ("Add dist GEMM attention and FFN backend", Structure: AllGatherLinearMulti
  * serves several linears that share one input with one all-gather;

@@ -75,6 +75,17 @@ def test_ag_validation_rejects_before_enqueue(kw, status):
     assert tp.last_error()
 
 
+def test_noalloc_rejects_sizes_past_the_static_scratch():
+    """The allocation-free all-gather takes at most 64 MiB of receive slots;
+    the size check needs no GPU (it comes before anything else)."""
+    a = ag(P=8, M=8 * 1280, K=8192, ab_dtype=tp.E4M3, beta=0.0, c=None)
+    assert tp.stage_ag_workspace_size(a) > 64 << 20
+    assert tp.lib().tpgemm_stage_ag_noalloc(ctypes.byref(a), None) == tp.ERR_WORKSPACE
+    assert "static scratch" in tp.last_error()
+    a = ag(flags=tp.FORCE_GRAPH)
+    assert tp.lib().tpgemm_stage_ag_noalloc(ctypes.byref(a), None) == tp.ERR_UNSUPPORTED
+
+
 def test_workspace_sizes_are_pure():
     a = ag(P=8, M=8192, K=8192, ab_dtype=tp.E4M3)
     assert tp.stage_ag_workspace_size(a) == 7 * 1024 * 8192
