@@ -12,10 +12,16 @@ it is reported in "detail"). Inputs are resident in HBM before the timed
 region starts.
 
 Prints ONE JSON line. Diagnostics (compute-only time, delivery-only time,
-hidden fraction, unstaged time, L2-flushed time, other workloads) go into its
-"detail" object and to stderr.
+hidden fraction, unstaged time, L2-flushed time) go into its "detail" object
+and to stderr, together with the rest of the metric, every run: the P = 2
+bf16 all-gather, the bf16 reduce-scatter, the SwiGLU block and the per-slot
+FFN layer (each with its stage GEMM launches against the bf16 MFMA peak; the
+FFN split into its first GEMM, LayerNorm / SiLU pass and second GEMM), and
+the dispatch / combine permutes against the HBM peak. --all adds the
+backward pass, the column-dual schedules and the fused QKV projection;
+--sweep adds the delivered-bytes / compute scale sweep.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--all] [--sweep]
 """
 import argparse
 import ctypes
@@ -161,6 +167,45 @@ def blas_threads():
         return max(i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas")
     except Exception:
         return os.cpu_count()
+
+
+def profile_launches(fn, steps, peak):
+    """Every launch of `steps` calls of fn(flags) with TPG_PROFILE (HIP events
+    on each launch's own stream), grouped by kind: GEMM launches by flop
+    count, against `peak` TFLOP/s; row kernels (negative work = HBM bytes)
+    against the HBM peak. Kinds are listed largest first."""
+    fn(tp.PROFILE)
+    torch.cuda.synchronize()
+    tp.profile_read()
+    for _ in range(steps):
+        fn(tp.PROFILE)
+    torch.cuda.synchronize()
+    recs = tp.profile_read()
+    kinds = {}
+    for ms_, work in recs:
+        kinds.setdefault(work, []).append(ms_)
+    out = []
+    for work, v in sorted(kinds.items(), key=lambda kv: -abs(kv[0])):
+        avg = float(np.mean(v))
+        if work > 0:
+            tf = work / (avg * 1e-3) / 1e12
+            out.append(dict(kind="gemm", gflop=round(work / 1e9, 2), launches=len(v), avg_us=round(avg * 1e3, 2),
+                            tflops=round(tf, 1), frac=round(tf / peak, 4)))
+        else:
+            gbs = -work / (avg * 1e-3) / 1e9
+            out.append(dict(kind="hbm", mbytes=round(-work / 1e6, 1), launches=len(v), avg_us=round(avg * 1e3, 2),
+                            gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4)))
+    return out
+
+
+def gemm_roofline(kinds, peak):
+    """Sum of flops over sum of durations of the GEMM launches of one call."""
+    g = [k for k in kinds if k["kind"] == "gemm"]
+    fl = sum(k["gflop"] * k["launches"] for k in g)
+    us = sum(k["avg_us"] * k["launches"] for k in g)
+    tf = fl * 1e9 / (us * 1e-6) / 1e12 if us > 0 else 0.0
+    return dict(bound="mfma", achieved=round(tf, 1), peak=peak, unit="TFLOP/s", frac=round(tf / peak, 4),
+                by_launch=kinds)
 
 
 # --------------------------------------------------------------------------- workloads
@@ -323,19 +368,34 @@ def bench_ag(case, args, detail):
             "us_staged_l2_flushed": {k: round(v * 1e3, 2) for k, v in flushed.items()},
             "tflops_compute_only": round(flop / (t_compute * 1e-3) / 1e12, 1),
         })
+        value_flushed = flop / (flushed["mean"] * 1e-3) / 1e12
         log(f"[{case.name}] detail: {json.dumps(detail)}")
-    return dict(value=value, ms=ms, dtype=dtype, roofline=roofline, inp=inp)
+    return dict(value=value, ms=ms, dtype=dtype, roofline=roofline, inp=inp,
+                value_l2_flushed=None if args.quick else round(value_flushed, 2))
 
 
 def bench_ffn(case, args):
+    """The per-slot FFN layer forward (two slot streams), and its launches
+    profiled on one stream (TPG_SERIAL_STAGES), so that each of the first
+    GEMM (4096 x 15360 x 1280 per slot), the LayerNorm / SiLU pass (z read,
+    h written: 6 H bytes per row) and the second GEMM (4096 x 1280 x 7680) is
+    timed running alone."""
     inp = W.ffn_inputs(case)
     t = {k: dev(v) for k, v in inp.items()}
     y = torch.empty((case.PB, case.L, case.D), dtype=torch.int16, device="cuda")
+    kw = dict(PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps)
+    serial_ws = torch.empty(tp.ffn_slot_forward_workspace_size(tp.ffn_args(
+        t["x"], t["w1"], t["b1"], t["wout"], t["bout"], t["gx"], t["bx"], t["gg"], t["bg"], y, flags=0, **kw)),
+        dtype=torch.uint8, device="cuda")
     call = tp.prepare_ffn_slot_forward(t["x"], t["w1"], t["b1"], t["wout"], t["bout"], t["gx"], t["bx"],
-                                       t["gg"], t["bg"], y, PB=case.PB, L=case.L, D=case.D, H=case.H,
-                                       eps=case.eps)
-    ms = time_steps(call, max(3, args.steps // 2), 2)
-    return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1))
+                                       t["gg"], t["bg"], y, workspace=serial_ws, **kw)
+    ms = time_steps(lambda: call(flags=0), max(3, args.steps // 2), 2)
+    peak = PEAK_TFLOPS["bf16"]
+    kinds = profile_launches(lambda f: call(flags=f | tp.SERIAL_STAGES), max(2, args.steps // 20), peak)
+    call(flags=0)
+    tf = case.flop / (ms * 1e-3) / 1e12
+    return dict(us=round(ms * 1e3, 1), tflops=round(tf, 1), pct_bf16_peak=round(100 * tf / peak, 2),
+                roofline_one_stream=gemm_roofline(kinds, peak))
 
 
 def bench_ffn_backward(case, args):
@@ -369,12 +429,16 @@ def bench_rs(case, args):
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     call = tp.prepare_stage_rs(a, b, inc, d, workspace=ws, **kw)
     steps = max(5, args.steps // 2)
-    ms = time_steps(call, steps, 3)
+    ms = time_steps(lambda: call(flags=0), steps, 3)
     mc = time_steps(lambda: call(flags=tp.NO_COPY), steps, 3)
     msh = time_steps(lambda: call(flags=tp.COPY_SHADER), steps, 3)
-    return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1),
-                us_shader_copy=round(msh * 1e3, 1),
-                us_compute_only=round(mc * 1e3, 1))
+    peak = PEAK_TFLOPS["bf16"]
+    kinds = profile_launches(lambda f: call(flags=f), max(2, args.steps // 10), peak)
+    call(flags=0)
+    tf = case.flop / (ms * 1e-3) / 1e12
+    return dict(us=round(ms * 1e3, 1), tflops=round(tf, 1), pct_bf16_peak=round(100 * tf / peak, 2),
+                us_shader_copy=round(msh * 1e3, 1), us_compute_only=round(mc * 1e3, 1),
+                roofline=gemm_roofline(kinds, peak))
 
 
 def bench_swiglu(case, args):
@@ -388,11 +452,16 @@ def bench_swiglu(case, args):
     rs = tp.prepare_stage_rs(h, w2, None, out, M=case.M, N=case.D, K=case.F, P=case.P, rank=case.rank,
                              b_layout=tp.B_KN)
 
-    def block():
-        ag()
-        rs()
+    def block(flags=0):
+        ag(flags=flags)
+        rs(flags=flags)
     ms = time_steps(block, max(5, args.steps // 2), 3)
-    return dict(us=round(ms * 1e3, 1), tflops=round(case.flop / (ms * 1e-3) / 1e12, 1))
+    peak = PEAK_TFLOPS["bf16"]
+    kinds = profile_launches(block, max(2, args.steps // 10), peak)
+    block()
+    tf = case.flop / (ms * 1e-3) / 1e12
+    return dict(us=round(ms * 1e3, 1), tflops=round(tf, 1), pct_bf16_peak=round(100 * tf / peak, 2),
+                roofline=gemm_roofline(kinds, peak))
 
 
 def bench_column_duals(args):
@@ -488,11 +557,110 @@ def bench_qkv(args):
 
 
 def bench_small_ag(case, args):
+    """A latency-bound staged call (0.07 GFLOP): microseconds are the figure
+    of merit; the per-launch rates say how far its GEMMs are from peak."""
     inp, call, _, _ = setup_ag(case)
     ms = time_steps(lambda: call(0), args.steps, args.warmup)
     mu = time_steps(lambda: call(tp.UNSTAGED), args.steps, args.warmup)
-    return dict(us=round(ms * 1e3, 2), us_unstaged=round(mu * 1e3, 2),
-                tflops=round(case.flop / (ms * 1e-3) / 1e12, 2))
+    peak = PEAK_TFLOPS["bf16"]
+    kinds = profile_launches(lambda f: call(f), max(5, args.steps // 5), peak)
+    tf = case.flop / (ms * 1e-3) / 1e12
+    return dict(us=round(ms * 1e3, 2), us_unstaged=round(mu * 1e3, 2), tflops=round(tf, 2),
+                pct_bf16_peak=round(100 * tf / peak, 3), roofline=gemm_roofline(kinds, peak))
+
+
+def bench_permutes(args):
+    """dispatch_permute / combine_permute at the per-slot FFN's shapes: 8
+    ranks' [512, 64, 1280] bf16 inputs into the dispatched [4096, 8, 1280],
+    and back. Algorithmic bytes per call: every element read once and written
+    once, 2 x 83.9 MB."""
+    P, B, T, D = 8, 512, 64, 1280
+    L = T // P
+    srcs = [torch.randn((B, T, D), device="cuda").to(torch.bfloat16).view(torch.int16) for _ in range(P)]
+    disp = [torch.empty((P * B, L, D), dtype=torch.int16, device="cuda") for _ in range(P)]
+    back = torch.empty((B, T, D), dtype=torch.int16, device="cuda")
+    nbytes = 2.0 * B * T * D * 2
+    steps = max(10, args.steps)
+    out = {}
+    for name, fn in (("dispatch", lambda: tp.dispatch_permute(srcs, disp[0], rank=3, B=B, T=T, D=D, elem_bytes=2)),
+                     ("combine", lambda: tp.combine_permute(disp, back, rank=3, B=B, T=T, D=D, elem_bytes=2))):
+        ms = time_steps(fn, steps, 3)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = dict(us=round(ms * 1e3, 2), gbs=round(gbs, 1), frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                         mbytes=round(nbytes / 1e6, 1))
+    return out
+
+
+def overlap_point(staged, unstaged, compute_only, deliveries, flop, steps, warmup):
+    """Times of one sweep point (us) and the hidden fraction
+    1 - (T_staged - T_compute) / T_deliveries (negatives kept)."""
+    t = {k: time_steps(f, steps, warmup) for k, f in
+         (("staged", staged), ("unstaged", unstaged), ("compute_only", compute_only), ("deliveries", deliveries))}
+    hidden = 1.0 - (t["staged"] - t["compute_only"]) / t["deliveries"]
+    return dict(us_staged=round(t["staged"] * 1e3, 2), us_unstaged=round(t["unstaged"] * 1e3, 2),
+                us_compute_only=round(t["compute_only"] * 1e3, 2), us_deliveries_alone=round(t["deliveries"] * 1e3, 2),
+                hidden_fraction=round(hidden, 3), tflops_staged=round(flop / (t["staged"] * 1e-3) / 1e12, 1),
+                staged_beats_unstaged=bool(t["staged"] < t["unstaged"]))
+
+
+def bench_scale_sweep(args):
+    """Where one-GPU staging hides its deliveries. The p04 statement's run
+    flags scale the exchanged payload (comm scale) and the hidden width
+    (compute scale). Read here for the all-gather forms: comm scale c
+    multiplies the delivered bytes per flop by c at equal flops (c times the
+    rows of each slice, 1/c of the output columns); compute scale k
+    multiplies the output columns (flops) by k at equal delivered bytes.
+    e4m3 all-gather: M = 8192 c, N = 1024 k / c, K = 8192. SwiGLU block:
+    S = 1024 c tokens per shard, F = 1792 k / c, D = 4096 (its all-gather
+    delivers the token shards; its reduce-scatter emits partials only)."""
+    steps, warm = max(10, args.steps // 2), 3
+    out = {}
+    for c, k in ((1, 1), (2, 1), (1, 2), (2, 2)):
+        case = W.AgCase(f"ag_e4m3_c{c}_k{k}", M=8192 * c, N=1024 * k // c, K=8192, P=8, dtype="e4m3",
+                        dist="n05", c_dist="n01", beta=1.0)
+        inp, call, deliveries, bufs = setup_ag(case)
+        out[f"ag_e4m3_p8 comm x{c} compute x{k}"] = dict(
+            M=case.M, N=case.N, K=case.K, delivered_mib=round(7 * case.m * case.K / 2 ** 20, 1),
+            **overlap_point(lambda: call(0), lambda: call(tp.UNSTAGED), bufs["compute_only"], deliveries(0),
+                            case.flop, steps, warm))
+        log(f"[sweep] {case.name}: {out[f'ag_e4m3_p8 comm x{c} compute x{k}']}")
+        del inp, call, deliveries, bufs
+        torch.cuda.empty_cache()
+    for c, k in ((1, 1), (2, 1), (1, 2), (2, 2)):
+        case = W.SwigluCase(f"swiglu_c{c}_k{k}", S=1024 * c, D=4096, F=1792 * k // c, P=8)
+        inp = W.swiglu_inputs(case)
+        xs = [dev(x) for x in inp["x_shards"]]
+        w13, w2 = dev(inp["w13"]), dev(inp["w2"])
+        whole = torch.cat(xs)
+        views = [whole[i * case.S:(i + 1) * case.S] for i in range(case.P)]
+        h = torch.empty((case.M, case.F), dtype=torch.int16, device="cuda")
+        o = torch.empty((case.M, case.D), dtype=torch.int16, device="cuda")
+        akw = dict(M=case.M, N=2 * case.F, K=case.D, b_layout=tp.B_KN, epilogue=tp.EPI_SWIGLU, alpha=1.0, beta=0.0)
+        need = tp.stage_ag_workspace_size(tp.ag_args(xs, w13, None, h, flags=tp.UNSTAGED, **akw))
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        ag = tp.prepare_stage_ag(xs, w13, None, h, workspace=ws, **akw)
+        ag_in_place = tp.prepare_stage_ag(views, w13, None, h, flags=tp.NO_COPY, **akw)
+        rs = tp.prepare_stage_rs(h, w2, None, o, M=case.M, N=case.D, K=case.F, P=case.P, b_layout=tp.B_KN)
+        slice_bytes = case.S * case.D * 2
+        side = torch.cuda.Stream()
+
+        def deliveries():
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            tp.deliver(xs[1:], ws, nbytes=slice_bytes, stream=side)
+            cur.wait_stream(side)
+
+        def block(flags):
+            ag(flags=flags)
+            rs(flags=flags & tp.UNSTAGED)
+        out[f"swiglu_p8 comm x{c} compute x{k}"] = dict(
+            S=case.S, F=case.F, D=case.D, delivered_mib=round(7 * slice_bytes / 2 ** 20, 1),
+            **overlap_point(lambda: block(0), lambda: block(tp.UNSTAGED),
+                            lambda: (ag_in_place(flags=tp.NO_COPY), rs(flags=0)), deliveries, case.flop, steps, warm))
+        log(f"[sweep] {case.name}: {out[f'swiglu_p8 comm x{c} compute x{k}']}")
+        del xs, w13, w2, whole, views, h, o, ws, ag, ag_in_place, rs
+        torch.cuda.empty_cache()
+    return out
 
 
 WORKLOADS = {"ag_e4m3_p8": W.C2, "ag_e4m3_p8_beta0": W.C2_BETA0, "ag_bf16_p2": W.C1}
@@ -507,7 +675,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline and roofline only")
     ap.add_argument("--no-ffn", action="store_true", help="skip timing the per-slot FFN layer")
-    ap.add_argument("--all", action="store_true", help="also time the other four workloads")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the backward pass, the column-dual schedules and the fused QKV projection")
+    ap.add_argument("--sweep", action="store_true",
+                    help="delivered-bytes / compute scale sweep of the e4m3 all-gather and the SwiGLU block")
     ap.add_argument("--isolate-kernels", action="store_true",
                     help="run every call with no deliveries and one compute stream, so that each GEMM "
                          "dispatch runs alone (for per-dispatch hardware counters)")
@@ -543,19 +714,27 @@ def main():
     measured = probe["e4m3" if r["dtype"] == "fp8_e4m3" else "bf16"]["tflops"]
     r["roofline"]["measured_peak"] = measured
     r["roofline"]["frac_of_measured_peak"] = round(r["roofline"]["achieved"] / measured, 4)
-    if not args.no_ffn and not args.quick:
-        detail["ffn_layer"] = bench_ffn(W.C4, args)
-        if args.all:
-            detail["ffn_layer_backward"] = bench_ffn_backward(W.C4, args)
-        log(f"[ffn] {detail['ffn_layer']}")
-    if args.all:
+    if not args.quick:
+        # the rest of the metric, every run: the other four workloads
         detail["ag_bf16_p2_256x256x512"] = bench_small_ag(W.C1, args)
+        log(f"[c1] {json.dumps(detail['ag_bf16_p2_256x256x512'])}")
         detail["rs_bf16_p8_8192x8192x3584"] = bench_rs(W.C3, args)
+        log(f"[c3] {json.dumps(detail['rs_bf16_p8_8192x8192x3584'])}")
         detail["swiglu_p8_s1024_d4096_f1792"] = bench_swiglu(W.C5, args)
+        log(f"[c5] {json.dumps(detail['swiglu_p8_s1024_d4096_f1792'])}")
+        if not args.no_ffn:
+            detail["ffn_layer"] = bench_ffn(W.C4, args)
+            log(f"[ffn] {json.dumps(detail['ffn_layer'])}")
+        detail["permutes_ffn_shapes"] = bench_permutes(args)
+        log(f"[permutes] {json.dumps(detail['permutes_ffn_shapes'])}")
+    if args.all:
+        if not args.no_ffn:
+            detail["ffn_layer_backward"] = bench_ffn_backward(W.C4, args)
         detail.update(bench_column_duals(args))
         detail.update(bench_wgrad(args))
         detail.update(bench_qkv(args))
-        log(f"[other] {json.dumps({k: detail[k] for k in ('ag_bf16_p2_256x256x512', 'rs_bf16_p8_8192x8192x3584', 'swiglu_p8_s1024_d4096_f1792')})}")
+    if args.sweep:
+        detail["scale_sweep"] = bench_scale_sweep(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -581,6 +760,7 @@ def main():
                    "pct_mfma_peak": round(100.0 * r["value"] / peak, 2),
                    "pct_measured_mfma_peak": round(100.0 * r["value"] / measured, 2),
                    "parallelism": "tp8 rank share"},
+        "value_l2_flushed": r.get("value_l2_flushed"),
         "roofline": r["roofline"],
         "cpu_baseline": cpu,
         "detail": detail,

@@ -182,29 +182,40 @@ struct Launch {
   bool profile;
 };
 
+// TPG_PROFILE: events around one launch on its own stream. `work` is the
+// launch's algorithmic flop count (GEMMs) or the negative of its algorithmic
+// HBM bytes (row kernels), as tpg_profile_read reports it.
+tpg_status prof_begin(Ctx& cx, const Launch& L, hipStream_t s, double work, ProfRec& rec) {
+  rec = ProfRec{nullptr, nullptr, work};
+  if (!L.profile) return TPG_OK;
+  for (hipEvent_t* e : {&rec.a, &rec.b}) {
+    if (!cx.prof_pool.empty()) {
+      *e = cx.prof_pool.back();
+      cx.prof_pool.pop_back();
+    } else {
+      HIP_TRY(hipEventCreate(e));
+    }
+  }
+  HIP_TRY(hipEventRecord(rec.a, s));
+  return TPG_OK;
+}
+
+tpg_status prof_end(Ctx& cx, const Launch& L, hipStream_t s, const ProfRec& rec) {
+  if (!L.profile) return TPG_OK;
+  HIP_TRY(hipEventRecord(rec.b, s));
+  cx.prof.push_back(rec);
+  return TPG_OK;
+}
+
 tpg_status gemm_on(Ctx& cx, const Launch& L, hipStream_t s, const tpg::GemmParams& p, int dtype,
                    int layout, int epi) {
-  ProfRec rec{nullptr, nullptr, 2.0 * p.M * double(p.N) * p.K * p.batch};
-  if (L.profile) {
-    for (hipEvent_t* e : {&rec.a, &rec.b}) {
-      if (!cx.prof_pool.empty()) {
-        *e = cx.prof_pool.back();
-        cx.prof_pool.pop_back();
-      } else {
-        HIP_TRY(hipEventCreate(e));
-      }
-    }
-    HIP_TRY(hipEventRecord(rec.a, s));
-  }
+  ProfRec rec;
+  if (tpg_status st = prof_begin(cx, L, s, 2.0 * p.M * double(p.N) * p.K * p.batch, rec); st != TPG_OK) return st;
   hipError_t e = layout == kLayoutAT      ? tpg::launch_gemm_at(p, s)
                  : p.cp_blocks > 0         ? tpg::launch_gemm_carrying_copy(p, dtype, layout, epi, s)
                                            : tpg::launch_gemm(p, dtype, layout, epi, s);
   if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("gemm launch failed: ") + hipGetErrorString(e));
-  if (L.profile) {
-    HIP_TRY(hipEventRecord(rec.b, s));
-    cx.prof.push_back(rec);
-  }
-  return TPG_OK;
+  return prof_end(cx, L, s, rec);
 }
 
 // Fork n-1 internal compute streams from the root; comp[0] is the root.
@@ -1467,11 +1478,17 @@ tpg_status enqueue_ffn(Ctx& cx, const tpg_ffn_args& a, const Launch& L) {
       g1.alpha = 1.0f;  g1.vec_ok = 1;  g1.keep_out = 1;   // z: read next by the LayerNorm pass
       stat = gemm_on(cx, L, cs, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
       if (stat != TPG_OK) return stat;
+      // algorithmic bytes: z (2H) in and h (H) out per row, bf16
+      ProfRec rec;
+      stat = prof_begin(cx, L, cs, -6.0 * double(PB) * H, rec);
+      if (stat != TPG_OK) return stat;
       hipError_t e = tpg::launch_ln_silu(z, 2 * H, h, H, static_cast<int>(PB), static_cast<int>(H),
                                          static_cast<const uint16_t*>(a.gx), static_cast<const uint16_t*>(a.bx),
                                          static_cast<const uint16_t*>(a.gg), static_cast<const uint16_t*>(a.bg),
                                          a.eps, cs);
       if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("ln_silu launch failed: ") + hipGetErrorString(e));
+      stat = prof_end(cx, L, cs, rec);
+      if (stat != TPG_OK) return stat;
     }
     tpg::GemmParams g2 = base_params();
     g2.a = h;  g2.lda = H;

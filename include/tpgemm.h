@@ -516,9 +516,11 @@ tpg_status tpg_mfma_probe(int32_t dtype, int32_t iters, int32_t blocks, uint64_t
  * tpg_release_caches: synchronises the device, then destroys cached graphs,
  *   internal streams and events. Later calls recreate them.
  * tpg_profile_read: after calls made with TPG_PROFILE (and a host sync),
- *   writes up to `cap` per-GEMM-launch durations in milliseconds and their
- *   algorithmic flop counts, oldest first, clears the record and returns how
- *   many were written.
+ *   writes up to `cap` per-launch durations in milliseconds and their
+ *   algorithmic work, oldest first, clears the record and returns how many
+ *   were written. The work is the flop count of a GEMM launch, or the
+ *   negative of the algorithmic HBM bytes of a row-kernel launch (the per-slot
+ *   FFN's LayerNorm / SiLU pass: z read, h written).
  * ---------------------------------------------------------------------- */
 const char* tpg_last_error(void);
 void tpg_release_caches(void);
