@@ -1402,17 +1402,24 @@ std::string wg_key(const tpg_wg_args& a) {
 }
 
 // ---------------------------------------------------------------- FFN
-// Slots are pipelined over two compute streams, each with its own z / h
-// buffers: the LayerNorm pass of one slot (HBM-bound) overlaps the GEMMs of
-// the next (MFMA-bound), and the two slots' z (126 MB each at the workload
-// size) stay in the 256 MB Infinity Cache between GEMM1 and the LayerNorm
-// pass. (One batched launch over all slots was measured slower: its 1 GB z
-// round-trips through HBM.) TPG_SERIAL_STAGES uses one stream and one buffer.
+// Two phases. (1) Per slot, pipelined over two compute streams, each with
+// its own z buffer: GEMM1 writes z, the LayerNorm / SiLU pass turns it into
+// the slot's h. The row pass of one slot (HBM-bound) overlaps GEMM1 of the
+// next (MFMA-bound), and the two slots' z (126 MB each at the workload size)
+// stay in the 256 MB Infinity Cache between GEMM1 and the row pass. (One
+// batched GEMM1 over all slots was measured slower: its 1 GB z round-trips
+// through HBM.) (2) GEMM2 of every slot as one batched launch over the h of
+// all slots: per slot it is only PB x D output (80 tiles of 256 x 256 at the
+// workload size), so slot by slot it filled a third of the chip.
+// TPG_SERIAL_STAGES uses one stream and one z buffer.
 int ffn_bufs(uint32_t flags) { return (flags & TPG_SERIAL_STAGES) ? 1 : 2; }
 
+// Workspace: ffn_bufs z buffers [PB][2H], then h of every slot [L][PB][H], bf16.
+size_t ffn_zbuf(const tpg_ffn_args* a) { return round_up(size_t(a->PB) * 2 * a->H * 2, 256); }
+
 size_t ffn_ws(const tpg_ffn_args* a) {
-  if (!a || a->PB < 0 || a->H < 0) return 0;
-  return size_t(ffn_bufs(a->flags)) * round_up(size_t(a->PB) * 3 * a->H * 2, 256);
+  if (!a || a->PB < 0 || a->H < 0 || a->L < 0) return 0;
+  return size_t(ffn_bufs(a->flags)) * ffn_zbuf(a) + round_up(size_t(a->L) * a->PB * a->H * 2, 256);
 }
 
 tpg_status validate_ffn(const tpg_ffn_args* a, size_t need) {
@@ -1457,50 +1464,53 @@ tpg_status enqueue_ffn(Ctx& cx, const tpg_ffn_args& a, const Launch& L) {
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, nb, st);
   if (stat != TPG_OK) return stat;
-  const size_t buf_b = round_up(size_t(PB) * 3 * H * 2, 256);
+  const size_t zbuf_b = ffn_zbuf(&a);
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* w1 = static_cast<const uint16_t*>(a.w1);
   const uint16_t* b1 = static_cast<const uint16_t*>(a.b1);
   const uint16_t* wo = static_cast<const uint16_t*>(a.wout);
   const uint16_t* bo = static_cast<const uint16_t*>(a.bout);
   uint16_t* y = static_cast<uint16_t*>(a.y);
-  for (int64_t l = 0; l < Ls; ++l) {
+  uint16_t* h_all = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + nb * zbuf_b);
+  // phase 1: z and h of every slot
+  for (int64_t l = 0; l < Ls && H > 0; ++l) {
     hipStream_t cs = st[l % nb];
-    uint16_t* z = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + (l % nb) * buf_b);
-    uint16_t* h = z + PB * 2 * H;
-    if (H > 0) {
-      tpg::GemmParams g1 = base_params();
-      g1.a = x + l * D;  g1.lda = Ls * D;
-      g1.b = w1 + l * D * 2 * H;  g1.ldb = 2 * H;
-      g1.bias = b1 + l * 2 * H;
-      g1.d = z;  g1.ldd = 2 * H;
-      g1.M = static_cast<int>(PB);  g1.N = static_cast<int>(2 * H);  g1.K = static_cast<int>(D);
-      g1.alpha = 1.0f;  g1.vec_ok = 1;  g1.keep_out = 1;   // z: read next by the LayerNorm pass
-      stat = gemm_on(cx, L, cs, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
-      if (stat != TPG_OK) return stat;
-      // algorithmic bytes: z (2H) in and h (H) out per row, bf16
-      ProfRec rec;
-      stat = prof_begin(cx, L, cs, -6.0 * double(PB) * H, rec);
-      if (stat != TPG_OK) return stat;
-      hipError_t e = tpg::launch_ln_silu(z, 2 * H, h, H, static_cast<int>(PB), static_cast<int>(H),
-                                         static_cast<const uint16_t*>(a.gx), static_cast<const uint16_t*>(a.bx),
-                                         static_cast<const uint16_t*>(a.gg), static_cast<const uint16_t*>(a.bg),
-                                         a.eps, cs);
-      if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("ln_silu launch failed: ") + hipGetErrorString(e));
-      stat = prof_end(cx, L, cs, rec);
-      if (stat != TPG_OK) return stat;
-    }
-    tpg::GemmParams g2 = base_params();
-    g2.a = h;  g2.lda = H;
-    g2.b = wo + l * H * D;  g2.ldb = D;
-    g2.bias = bo + l * D;
-    g2.d = y + l * D;  g2.ldd = Ls * D;
-    g2.M = static_cast<int>(PB);  g2.N = static_cast<int>(D);  g2.K = static_cast<int>(H);
-    g2.alpha = 1.0f;  g2.vec_ok = 1;
-    stat = gemm_on(cx, L, cs, g2, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
+    uint16_t* z = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + (l % nb) * zbuf_b);
+    uint16_t* h = h_all + l * PB * H;
+    tpg::GemmParams g1 = base_params();
+    g1.a = x + l * D;  g1.lda = Ls * D;
+    g1.b = w1 + l * D * 2 * H;  g1.ldb = 2 * H;
+    g1.bias = b1 + l * 2 * H;
+    g1.d = z;  g1.ldd = 2 * H;
+    g1.M = static_cast<int>(PB);  g1.N = static_cast<int>(2 * H);  g1.K = static_cast<int>(D);
+    g1.alpha = 1.0f;  g1.vec_ok = 1;  g1.keep_out = 1;   // z: read next by the LayerNorm pass
+    stat = gemm_on(cx, L, cs, g1, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
+    if (stat != TPG_OK) return stat;
+    // algorithmic bytes: z (2H) in and h (H) out per row, bf16
+    ProfRec rec;
+    stat = prof_begin(cx, L, cs, -6.0 * double(PB) * H, rec);
+    if (stat != TPG_OK) return stat;
+    hipError_t e = tpg::launch_ln_silu(z, 2 * H, h, H, static_cast<int>(PB), static_cast<int>(H),
+                                       static_cast<const uint16_t*>(a.gx), static_cast<const uint16_t*>(a.bx),
+                                       static_cast<const uint16_t*>(a.gg), static_cast<const uint16_t*>(a.bg),
+                                       a.eps, cs);
+    if (e != hipSuccess) return fail(TPG_ERR_HIP, std::string("ln_silu launch failed: ") + hipGetErrorString(e));
+    stat = prof_end(cx, L, cs, rec);
     if (stat != TPG_OK) return stat;
   }
-  return join_streams(cx, L.root, nb, st);
+  stat = join_streams(cx, L.root, nb, st);
+  if (stat != TPG_OK) return stat;
+  // phase 2: y[:, l, :] = h_l wout[l] + bout[l] for every slot, one batched
+  // launch (blockIdx.y = slot)
+  tpg::GemmParams g2 = base_params();
+  g2.a = h_all;  g2.lda = H;  g2.a_bstride = PB * H;
+  g2.b = wo;  g2.ldb = D;  g2.b_bstride = H * D;
+  g2.bias = bo;  g2.bias_bstride = D;
+  g2.d = y;  g2.ldd = Ls * D;  g2.d_bstride = D;
+  g2.M = static_cast<int>(PB);  g2.N = static_cast<int>(D);  g2.K = static_cast<int>(H);
+  g2.alpha = 1.0f;  g2.vec_ok = 1;
+  g2.batch = static_cast<int>(Ls);      // H == 0: an empty contraction, y is the bias
+  return gemm_on(cx, L, L.root, g2, tpg::kBf16, tpg::kKN, tpg::kEpiAlphaBeta);
 }
 
 std::string ffn_key(const tpg_ffn_args& a) {

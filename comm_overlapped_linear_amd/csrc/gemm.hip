@@ -718,7 +718,10 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // uniform per wave: each DMA destination below is then scalar arithmetic
+  // (s_add, s_mov m0) instead of a VALU add read back with v_readfirstlane
+  // (measured 1-3% on the stage-GEMM shapes)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5;
   const int l32 = lane & 31;

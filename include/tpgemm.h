@@ -381,7 +381,9 @@ tpg_status tpgemm_stage_wgrad(const tpg_wg_args* args, void* stream);
  * All tensors bf16, row-major: x, y [PB, L, D]; w1 [L, D, 2H]; b1 [L, 2H];
  * wout [L, H, D]; bout [L, D]; gx, bx, gg, bg [H]. D % 8 == 0, H % 8 == 0.
  * Intermediates z (bf16) and h (bf16) live in the workspace
- * (>= ffn_slot_forward_workspace_size() bytes); accumulation and the
+ * (>= ffn_slot_forward_workspace_size() bytes: two z buffers of PB x 2H,
+ * one with TPG_SERIAL_STAGES, and the h of every slot, L x PB x H, so that
+ * the second GEMM of all slots is one launch); accumulation and the
  * LayerNorm statistics are fp32.
  * ---------------------------------------------------------------------- */
 typedef struct {

@@ -99,9 +99,10 @@ def test_workspace_sizes_are_pure():
                   workspace=None, workspace_bytes=0, flags=0)
     assert tp.stage_rs_workspace_size(r) == 7 * 1024 * 8192 * 2
     f = tp.FfnArgs(PB=4096, L=8, D=1280, H=7680, flags=0)
-    assert tp.ffn_slot_forward_workspace_size(f) == 2 * 4096 * 3 * 7680 * 2      # two slots in flight
+    h_all = 8 * 4096 * 7680 * 2                                                    # h of every slot
+    assert tp.ffn_slot_forward_workspace_size(f) == 2 * 4096 * 2 * 7680 * 2 + h_all  # two z in flight
     f.flags = tp.SERIAL_STAGES
-    assert tp.ffn_slot_forward_workspace_size(f) == 4096 * 3 * 7680 * 2
+    assert tp.ffn_slot_forward_workspace_size(f) == 4096 * 2 * 7680 * 2 + h_all
 
 
 def test_rs_and_ffn_and_permute_validation():
