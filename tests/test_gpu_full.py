@@ -2,10 +2,12 @@
 configuration the benchmark times (the library's default issue and copy kind
 for each call).
 
-The oracle computes sampled output rows one by one (every stage's first and
-last row plus seeded random rows); properties that hold at any size (staged
-equals unstaged bit for bit, the own reduce-scatter block minus the incoming
-partials equals the plain partial) cover the rest of each output.
+The float64 oracle computes every output element (BLAS products on the
+host's cores: about 1 s for the e4m3 all-gather, 4 s for the reduce-scatter,
+20 s for the FFN layer), and every element is held to the tolerance. On top,
+properties that hold at any size: staged equals unstaged bit for bit, and
+the own reduce-scatter block minus the incoming partials equals the plain
+partial at a tolerance scaled to that partial.
 """
 import numpy as np
 import pytest
@@ -20,14 +22,6 @@ from tests.parity import assert_parity
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def sample_rows(M, m, n_random=24, seed=0):
-    rows = set()
-    for s in range(M // m):
-        rows.update({s * m, s * m + m - 1})
-    rows.update(np.random.default_rng(seed).integers(0, M, n_random).tolist())
-    return sorted(rows)
-
-
 @pytest.mark.parametrize("case", [W.C2, W.C2_BETA0], ids=lambda c: c.name)
 def test_full_ag_fp8(case):
     say(f"full: {case.name} generate")
@@ -39,9 +33,9 @@ def test_full_ag_fp8(case):
     say(f"full: {case.name} staged")
     tp.stage_ag(slices, b, c, d, **kw)
     torch.cuda.synchronize()
-    rows = sample_rows(case.M, case.m)
-    ref = oracle.gemm_ag_rows(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, "e4m3", "nk", rows)
-    assert_parity(host_f64(d)[rows], ref, case.name)
+    say(f"full: {case.name} oracle")
+    ref = oracle.gemm_ag(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, case.rank, "e4m3", "nk")
+    assert_parity(host_f64(d), ref, case.name)
     d2 = bf16_empty(case.M, case.N)
     say(f"full: {case.name} unstaged")
     tp.stage_ag(slices, b, c, d2, flags=tp.UNSTAGED, **kw)
@@ -61,18 +55,18 @@ def test_full_rs_bf16():
     tp.stage_rs(a, b, inc, d, **kw)
     torch.cuda.synchronize()
     got = host_f64(d)
-    rows = sample_rows(case.M, case.m)
-    ref = oracle.gemm_rs_rows(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P, "nk", rows)
-    r_rows = [i for i, r in enumerate(rows) if r // case.m == case.rank]
-    e_rows = [i for i, r in enumerate(rows) if r // case.m != case.rank]
-    assert_parity(got[rows][e_rows], ref[e_rows], "emitted blocks")
-    assert_parity(got[rows][r_rows], ref[r_rows], "own block")
+    say(f"full: {case.name} oracle")
+    ref = oracle.gemm_rs(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P)
+    for blk in range(case.P):           # tolerance per block
+        rows = slice(blk * case.m, (blk + 1) * case.m)
+        assert_parity(got[rows], ref[rows], f"block {blk}")
     # own partial inside the reduced block, at a tolerance scaled to the partial itself
-    own_rows = [r for r in rows if r // case.m == case.rank]
-    inc_sum = sum(oracle.decode_bf16(x[[r % case.m for r in own_rows]]) for x in inp["incoming"] if x is not None)
-    e_r = oracle.gemm_rs_rows(inp["a"], inp["b"], None, 1.0, case.rank, case.P, "nk", own_rows)
-    ulp_out = np.exp2(np.floor(np.log2(np.maximum(np.abs(got[own_rows]), 1e-30))) - 7)
-    assert np.all(np.abs(got[own_rows] - inc_sum - e_r) <= 0.02 * np.sqrt(np.mean(e_r ** 2)) + ulp_out)
+    own = slice(case.rank * case.m, (case.rank + 1) * case.m)
+    inc_sum = sum(oracle.decode_bf16(x) for x in inp["incoming"] if x is not None)
+    e_r = oracle.gemm_rs_rows(inp["a"], inp["b"], None, 1.0, case.rank, case.P, "nk",
+                              list(range(own.start, own.stop)))
+    ulp_out = np.exp2(np.floor(np.log2(np.maximum(np.abs(got[own]), 1e-30))) - 7)
+    assert np.all(np.abs(got[own] - inc_sum - e_r) <= 0.02 * np.sqrt(np.mean(e_r ** 2)) + ulp_out)
     d2 = bf16_empty(case.M, case.N)
     say(f"full: {case.name} unstaged")
     tp.stage_rs(a, b, inc, d2, flags=tp.UNSTAGED, **kw)
@@ -91,11 +85,9 @@ def test_full_ffn():
                         PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps)
     torch.cuda.synchronize()
     got = host_f64(y)
-    rng = np.random.default_rng(1)
-    pairs = [(0, 0), (case.PB - 1, case.L - 1)] + [(int(n), int(l)) for n, l in
-                                                   zip(rng.integers(0, case.PB, 30), rng.integers(0, case.L, 30))]
-    ref = oracle.ffn_slot_rows(inp, pairs, case.eps)
-    assert_parity(np.stack([got[n, l] for n, l in pairs]), ref, case.name)
+    say(f"full: {case.name} oracle")
+    ref = oracle.ffn_slot_forward(inp, case.eps)
+    assert_parity(got, ref, case.name)
     y2 = bf16_empty(case.PB, case.L, case.D)
     tp.ffn_slot_forward(t["x"], t["w1"], t["b1"], t["wout"], t["bout"], t["gx"], t["bx"], t["gg"], t["bg"], y2,
                         PB=case.PB, L=case.L, D=case.D, H=case.H, eps=case.eps, flags=tp.SERIAL_STAGES)
@@ -116,11 +108,13 @@ def test_full_swiglu_block():
                 epilogue=tp.EPI_SWIGLU, alpha=1.0, beta=0.0)
     tp.stage_rs(h, w2, None, out, M=case.M, N=case.D, K=case.F, P=case.P, rank=case.rank, b_layout=tp.B_KN)
     torch.cuda.synchronize()
-    rows = sample_rows(case.M, case.S)
-    h_ref = oracle.swiglu_hidden_rows(inp["x_shards"], inp["w13"], rows)
-    assert_parity(host_f64(h)[rows], h_ref, "h")
+    say(f"full: {case.name} oracle")
+    h_ref = oracle.swiglu_hidden(inp["x_shards"], inp["w13"])
+    assert_parity(host_f64(h), h_ref, "h")
     out_ref = h_ref @ oracle.decode_bf16(inp["w2"])
-    assert_parity(host_f64(out)[rows], out_ref, "partial blocks")
+    for blk in range(case.P):           # the reduce-scatter blocks
+        rows = slice(blk * case.S, (blk + 1) * case.S)
+        assert_parity(host_f64(out)[rows], out_ref[rows], f"partial block {blk}")
 
 
 def test_full_ag_rotb_e4m3():
@@ -138,9 +132,9 @@ def test_full_ag_rotb_e4m3():
     say(f"full: {case.name} staged")
     tp.stage_ag(a, bs, c, d, **kw)
     torch.cuda.synchronize()
-    rows = sample_rows(case.M, 1024)
-    ref = oracle.gemm_ag_rotb_rows(inp["a"], inp["b_slices"], inp["c"], case.alpha, case.beta, "e4m3", "nk", rows)
-    assert_parity(host_f64(d)[rows], ref, case.name)
+    say(f"full: {case.name} oracle")
+    ref = oracle.gemm_ag_rotb(inp["a"], inp["b_slices"], inp["c"], case.alpha, case.beta, case.rank, "e4m3", "nk")
+    assert_parity(host_f64(d), ref, case.name)
     d2 = bf16_empty(case.M, case.N)
     say(f"full: {case.name} unstaged")
     tp.stage_ag(a, bs, c, d2, flags=tp.UNSTAGED, **kw)
@@ -162,9 +156,9 @@ def test_full_rs_tileb_bf16():
     say(f"full: {case.name} staged")
     tp.stage_rs(a, b, inc, d, **kw)
     torch.cuda.synchronize()
-    rows = sample_rows(case.M, 1024)
-    ref = oracle.gemm_rs_tileb_rows(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P, "nk", rows)
-    got = host_f64(d)[rows]
+    say(f"full: {case.name} oracle")
+    ref = oracle.gemm_rs_tileb(inp["a"], inp["b"], inp["incoming"], 1.0, case.rank, case.P, "nk")
+    got = host_f64(d)
     n = case.N // case.P
     own = slice(case.rank * n, (case.rank + 1) * n)
     emitted = np.r_[0:case.rank * n, (case.rank + 1) * n:case.N]
@@ -185,33 +179,32 @@ WGRAD_FULL = [W.WgCase("wg_x_1024x8192_c8192", M=8192, N=1024, K=8192, P=8, rank
 def test_full_wgrad(case):
     """Weight gradients at full size: of the e4m3 all-gather shape (in bf16, X
     gathered) and of the SwiGLU block's w13 (G = the gathered input), both
-    the library's single gathered launch and the staged chain, on sampled
-    output rows."""
+    the library's single gathered launch and the staged chain, every output
+    element against the oracle."""
     say(f"full: {case.name} generate")
     inp = W.wgrad_inputs(case)
     local, sl = dev(inp["local"]), [dev(x) for x in inp["slices"]]
     g = tp.GATHER_X if case.gathered == "x" else tp.GATHER_G
-    rows = sorted(set([0, case.N - 1] + np.random.default_rng(2).integers(0, case.N, 30).tolist()))
-    ref = oracle.wgrad_rows(inp["local"], inp["slices"], case.gathered, rows)
+    say(f"full: {case.name} oracle")
+    ref = oracle.wgrad_rows(inp["local"], inp["slices"], case.gathered, list(range(case.N)))
     for groups in (0, 1):
         d = bf16_empty(case.N, case.K)
         say(f"full: {case.name} groups={groups}")
         tp.stage_wgrad(local, sl, d, M=case.M, N=case.N, K=case.K, rank=case.rank, gathered=g, groups=groups)
         torch.cuda.synchronize()
-        assert_parity(host_f64(d)[rows], ref, f"{case.name}/groups={groups}")
+        assert_parity(host_f64(d), ref, f"{case.name}/groups={groups}")
 
 
 def test_full_qkv():
     """The fused QKV projection at full size (8192 tokens, K = 4096, 512 + 128
-    + 128 columns per rank), weights apart, staged and unstaged, on sampled
-    rows."""
+    + 128 columns per rank), weights apart, staged and unstaged, every output
+    element against the oracle."""
     case = W.QKV
     say(f"full: {case.name} generate")
     inp = W.ag_multi_inputs(case)
     slices = [dev(s) for s in inp["a_slices"]]
     bs = [dev(b) for b in inp["bs"]]
-    rows = sample_rows(case.M, case.m)
-    A = np.stack([oracle.decode_bf16(inp["a_slices"][r // case.m][r % case.m]) for r in rows])
+    A = np.concatenate([oracle.decode_bf16(s) for s in inp["a_slices"]], axis=0)
     outs = {}
     for flags in (0, tp.UNSTAGED):
         ds = [bf16_empty(case.M, n) for n in case.ns]
@@ -219,7 +212,7 @@ def test_full_qkv():
         tp.stage_ag_multi(slices, bs, ds, M=case.M, K=case.K, rank=case.rank, flags=flags)
         torch.cuda.synchronize()
         for i, (d, b) in enumerate(zip(ds, inp["bs"])):
-            assert_parity(host_f64(d)[rows], A @ oracle.decode_bf16(b).T, f"{case.name}/{flags}/out{i}")
+            assert_parity(host_f64(d), A @ oracle.decode_bf16(b).T, f"{case.name}/{flags}/out{i}")
         outs[flags] = [d.cpu() for d in ds]
     for x, y in zip(outs[0], outs[tp.UNSTAGED]):
         assert torch.equal(x, y)
