@@ -242,6 +242,9 @@ def setup_ag(case, extra_flags=0):
     def call_compute_only():
         prepared_whole(flags=tp.NO_COPY | extra_flags)
 
+    def call_compute_only_ikg():
+        prepared_whole(flags=tp.NO_COPY | tp.IN_KERNEL_GATES | extra_flags)
+
     side = torch.cuda.Stream()
 
     def deliveries(flags):
@@ -261,7 +264,7 @@ def setup_ag(case, extra_flags=0):
         with torch.cuda.graph(g):
             issue()
         return g.replay
-    return inp, call, deliveries, dict(d=d, compute_only=call_compute_only)
+    return inp, call, deliveries, dict(d=d, compute_only=call_compute_only, compute_only_ikg=call_compute_only_ikg)
 
 
 CPU_SECONDS = 10.0      # bounded CPU sample: repeat the oracle call until this much time has passed
@@ -345,7 +348,11 @@ def bench_ag(case, args, detail):
         t_per_stage = time_steps(lambda: call(0, case.P - 1), args.steps, args.warmup)
         t_sdma = time_steps(lambda: call(tp.COPY_SDMA), args.steps, args.warmup)
         t_graph = time_steps(lambda: call(tp.FORCE_GRAPH), args.steps, args.warmup)
+        # the staged call as one launch whose tiles wait in-kernel on chunk counters
+        t_ikg = time_steps(lambda: call(tp.IN_KERNEL_GATES), args.steps, args.warmup)
+        t_ikg_compute = time_steps(bufs["compute_only_ikg"], args.steps, args.warmup)
         hidden = 1.0 - (ms - t_compute) / t_copy if t_copy > 0 else None
+        hidden_ikg = 1.0 - (t_ikg - t_ikg_compute) / t_copy if t_copy > 0 else None
         hidden_sdma = 1.0 - (t_sdma - t_compute) / t_copy_sdma if t_copy_sdma > 0 else None
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         flushed = time_flushed(lambda: call(0), max(args.steps, 100), 2, scratch)
@@ -360,6 +367,9 @@ def bench_ag(case, args, detail):
             "us_unstaged": round(t_unstaged * 1e3, 2),
             "us_one_gate_per_stage": round(t_per_stage * 1e3, 2),
             "us_staged_graph": round(t_graph * 1e3, 2),
+            "us_in_kernel_gates": round(t_ikg * 1e3, 2),
+            "us_in_kernel_gates_compute_only": round(t_ikg_compute * 1e3, 2),
+            "hidden_fraction_in_kernel_gates": None if hidden_ikg is None else round(hidden_ikg, 3),
             "us_staged_copy_engines": round(t_sdma * 1e3, 2),
             "us_deliveries_alone_copy_engines": round(t_copy_sdma * 1e3, 2),
             "hidden_fraction_copy_engines": None if hidden_sdma is None else round(hidden_sdma, 3),

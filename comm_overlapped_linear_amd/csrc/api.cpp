@@ -54,8 +54,12 @@ constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
                                  TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH |
                                  TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER | TPG_COPY_KERNEL |
-                                 TPG_DEBUG_NO_GATE;
+                                 TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES;
 constexpr uint32_t kCopyFlags = TPG_COPY_SDMA | TPG_COPY_SHADER | TPG_COPY_KERNEL;
+// In-kernel gate counters after the all-gather's receive slots: one 32-bit
+// counter per (delivered slice, K-chunk)
+constexpr int kMaxGateChunks = 8;
+constexpr size_t kGateCounterBytes = size_t(tpg::kMaxGateSlices) * kMaxGateChunks * 4;
 // Staged calls below this many flops run on one stream: their GEMMs take
 // well under the few microseconds each cross-stream event costs (the P = 2
 // bf16 workload: 20 us on one stream, 40-45 us on two).
@@ -353,6 +357,17 @@ tpg_status validate_no_gate(uint32_t flags, bool supported) {
   return TPG_OK;
 }
 
+// TPG_IN_KERNEL_GATES applies to the staged rotating-A all-gather only.
+tpg_status validate_in_kernel_gates(uint32_t flags, bool supported) {
+  if (!(flags & TPG_IN_KERNEL_GATES)) return TPG_OK;
+  if (!supported) return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES: not implemented by this call");
+  if (flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES))
+    return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES needs a staged call on several streams");
+  if (flags & (TPG_COPY_SDMA | TPG_COPY_SHADER))
+    return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES delivers with the library's copy kernel");
+  return TPG_OK;
+}
+
 // ---------------------------------------------------------------- all-gather
 // Default stage runs of the all-gather: one gate for all P-1 remote stages.
 // On one GPU the deliveries (the copy kernel: ~23-26 us for 7 x 8 MiB) are
@@ -380,6 +395,7 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
   if (!copy_flags_ok(a->flags))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (tpg_status ng = validate_no_gate(a->flags, !rotb); ng != TPG_OK) return ng;
+  if (tpg_status ig = validate_in_kernel_gates(a->flags, !rotb); ig != TPG_OK) return ig;
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
   if (a->b_layout != TPG_B_NK && a->b_layout != TPG_B_KN) return fail(TPG_ERR_INVALID, "bad b_layout");
   if (a->epilogue != TPG_EPI_ALPHA_BETA && a->epilogue != TPG_EPI_SWIGLU)
@@ -449,6 +465,17 @@ tpg_status validate_ag(const tpg_ag_args* a, size_t need) {
       if (static_cast<const char*>(sl[s]) != static_cast<const char*>(sl[0]) + s * slice_b)
         return fail(TPG_ERR_UNSUPPORTED, "UNSTAGED|NO_COPY needs the slices to be contiguous");
   }
+  if (a->flags & TPG_IN_KERNEL_GATES) {
+    if (a->P > tpg::kMaxGateSlices) return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES needs P <= 8");
+    if ((a->M / a->P) % 128) return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES needs M/P a multiple of 128");
+    if ((a->K * eb) % 128) return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES needs K * element bytes a multiple of 128");
+    if ((a->flags & TPG_NO_COPY) && a->M > 0) {
+      const size_t slice_b = size_t(a->M / a->P) * a->K * eb;
+      for (int s = 1; s < a->P; ++s)
+        if (static_cast<const char*>(a->a_slices[s]) != static_cast<const char*>(a->a_slices[0]) + s * slice_b)
+          return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES|NO_COPY needs the slices to be contiguous");
+    }
+  }
   return TPG_OK;
 }
 
@@ -462,6 +489,7 @@ size_t ag_ws(const tpg_ag_args* a) {
   if (!a || a->P < 1 || a->M < 0 || a->N < 0 || a->K < 0 || (a->flags & TPG_NO_COPY)) return 0;
   const size_t slice = ag_slice_bytes(a);
   if (a->flags & TPG_UNSTAGED) return slice * a->P;
+  if (a->flags & TPG_IN_KERNEL_GATES) return round_up(slice * (a->P - 1), 256) + kGateCounterBytes;
   return slice * (a->P - 1);
 }
 
@@ -632,6 +660,72 @@ void set_out_rows(tpg::GemmParams& q, const tpg_ag_args& a, const OutSegs* segs,
   q.d = q.seg_d[0];
 }
 
+// TPG_IN_KERNEL_GATES: the staged all-gather as one launch. The stages are
+// those of the rotating-A form (the local slice needs no delivery; slice
+// (rank + t) mod P arrives in slot t-1), but instead of one GEMM launch per
+// run behind a stream event, one launch covers all M rows and each tile of a
+// delivered slice waits inside the kernel, before the DMA of each K-chunk,
+// for that chunk's counter. The copy kernel runs beside it on a side stream,
+// K-chunk-major, storing write-through and bumping the counter of each
+// chunk it completes; the counters are zeroed on the root first.
+// (TPG_NO_COPY: one launch over the slices in place, no gates.)
+tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutSegs* segs,
+                            tpg::GemmParams p, int dtype, int layout, int epi, int64_t nout) {
+  const int P = a.P, r = a.rank;
+  const int eb = elem_bytes(a.ab_dtype);
+  const int64_t m = a.M / P;
+  const int64_t row_b = a.K * eb;
+  const size_t slice_b = size_t(m) * row_b;
+  const bool copies = !(a.flags & TPG_NO_COPY) && slice_b > 0 && P > 1;
+  char* ws = static_cast<char*>(a.workspace);
+  const int nk = static_cast<int>(row_b / 128);                   // 128-byte K-steps
+  const int ksteps = (nk + kMaxGateChunks - 1) / kMaxGateChunks;  // K-steps per chunk
+  const int nch = (nk + ksteps - 1) / ksteps;
+  const int wgs = tpg::chunk_deliver_wgs_per_slice(static_cast<int>(m));
+  unsigned* gate = copies ? reinterpret_cast<unsigned*>(ws + round_up(slice_b * (P - 1), 256)) : nullptr;
+
+  p.a = a.a_slices[r];
+  p.M = static_cast<int>(a.M);
+  p.c = static_cast<const uint16_t*>(a.c);
+  set_out_rows(p, a, segs, 0, nout);
+  p.a_slice_rows = static_cast<int>(m);
+  // delivered slices in their slots after the local one; in place (no
+  // copies) the slices are back to back from a_slices[0]
+  p.a_local = copies ? static_cast<const uint8_t*>(a.a_slices[r]) : nullptr;
+  p.a_slots = copies ? reinterpret_cast<const uint8_t*>(ws) : static_cast<const uint8_t*>(a.a_slices[0]);
+  p.gate_local = copies ? r : -1;
+  p.gate = gate;
+  p.gate_nch = nch;
+  p.gate_ksteps = ksteps;
+  p.gate_off = (a.flags & TPG_DEBUG_NO_GATE) ? 1 : 0;
+  p.gate_need = static_cast<unsigned>(wgs);
+  if (!copies) return gemm_on(cx, L, L.root, p, dtype, layout, epi);
+
+  HIP_TRY(tpg::launch_fill_zero16(gate, kGateCounterBytes, L.root));
+  hipStream_t st[kStreams];
+  tpg_status stat = fork_streams(cx, L.root, 2, st);   // the side stream starts after the zeroing
+  if (stat != TPG_OK) return stat;
+  // the copy is issued first: were the two launches ever run one after the
+  // other, it must be the copy that goes first
+  stat = hold_deliveries(a.flags, st[1]);
+  if (stat != TPG_OK) return stat;
+  tpg::ChunkDeliverParams d;
+  std::memset(&d, 0, sizeof(d));
+  for (int t = 1; t < P; ++t) d.src[t - 1] = static_cast<const uint8_t*>(a.a_slices[(r + t) % P]);
+  d.dst = reinterpret_cast<uint8_t*>(ws);
+  d.gate = gate;
+  d.rows = static_cast<int>(m);
+  d.row_bytes = row_b;
+  d.chunk_bytes = int64_t(ksteps) * 128;
+  d.n = P - 1;
+  d.nch = nch;
+  d.wg_per_slice = wgs;
+  HIP_TRY(tpg::launch_chunk_deliver(d, st[1]));
+  stat = gemm_on(cx, L, L.root, p, dtype, layout, epi);
+  if (stat != TPG_OK) return stat;
+  return join_streams(cx, L.root, 2, st);
+}
+
 tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutSegs* segs = nullptr) {
   if (a.schedule == TPG_ROTATE_B) return enqueue_ag_rotb(cx, a, L);
   const int P = a.P, r = a.rank;
@@ -658,6 +752,8 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
   const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
   const int layout = a.b_layout == TPG_B_KN ? tpg::kKN : tpg::kNK;
   const int epi = sw ? tpg::kEpiSwiglu : tpg::kEpiAlphaBeta;
+
+  if (a.flags & TPG_IN_KERNEL_GATES) return enqueue_ag_gated(cx, a, L, segs, p, dtype, layout, epi, nout);
 
   if (a.flags & TPG_UNSTAGED) {
     // single stage: gather every slice (rank order), then one GEMM over all M rows
@@ -982,6 +1078,7 @@ tpg_status validate_rs(const tpg_rs_args* a, size_t need) {
   if (tileb && (a->N / a->P) % 8) return fail(TPG_ERR_UNSUPPORTED, "TPG_TILE_B: N/P must be a multiple of 8");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
   if (tpg_status ng = validate_no_gate(a->flags, true); ng != TPG_OK) return ng;
+  if (tpg_status ig = validate_in_kernel_gates(a->flags, false); ig != TPG_OK) return ig;
   if (!copy_flags_ok(a->flags))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (a->ab_dtype != TPG_BF16 && a->ab_dtype != TPG_E4M3) return fail(TPG_ERR_INVALID, "bad ab_dtype");
@@ -1222,6 +1319,7 @@ tpg_status validate_wg(const tpg_wg_args* a, size_t need) {
   if (a->gathered != TPG_GATHER_X && a->gathered != TPG_GATHER_G) return fail(TPG_ERR_INVALID, "bad gathered");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
   if (tpg_status ng = validate_no_gate(a->flags, false); ng != TPG_OK) return ng;
+  if (tpg_status ig = validate_in_kernel_gates(a->flags, false); ig != TPG_OK) return ig;
   if (!copy_flags_ok(a->flags))
     return fail(TPG_ERR_INVALID, "TPG_COPY_SDMA, TPG_COPY_SHADER and TPG_COPY_KERNEL are exclusive");
   if (!fits_int(a->M) || !fits_int(a->N) || !fits_int(a->K))
@@ -1427,6 +1525,7 @@ tpg_status validate_ffn(const tpg_ffn_args* a, size_t need) {
   if (a->PB < 0 || a->L < 0 || a->D < 0 || a->H < 0) return fail(TPG_ERR_INVALID, "negative dimension");
   if (a->flags & ~kKnownFlags) return fail(TPG_ERR_INVALID, "unknown flag bits");
   if (tpg_status ng = validate_no_gate(a->flags, false); ng != TPG_OK) return ng;
+  if (tpg_status ig = validate_in_kernel_gates(a->flags, false); ig != TPG_OK) return ig;
   if (!fits_int(a->PB) || !fits_int(a->L * a->D) || !fits_int(2 * a->H))
     return fail(TPG_ERR_UNSUPPORTED, "dimensions too large");
   if (a->D % 8 || a->H % 8) return fail(TPG_ERR_UNSUPPORTED, "D and H must be multiples of 8");
@@ -1789,8 +1888,10 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
     tpg_ag_args a = *args;
-    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE)) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES)) && a.groups == 0 &&
+        2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
+    if (a.flags & TPG_IN_KERNEL_GATES) a.flags |= TPG_NO_GRAPH;   // the two launches must run concurrently
     return run_call(*cx, a.flags, ag_key(a), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ag(*cx, a, L); });
   });
@@ -1818,7 +1919,8 @@ tpg_status tpgemm_stage_ag_noalloc(const tpg_ag_args* args, void* stream) {
     if (st != TPG_OK) return st;
     HIP_TRY(tpg::static_scratch(&a.workspace));
     a.workspace_bytes = tpg::kStaticScratchBytes;
-    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE)) && a.groups == 0 && 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES)) && a.groups == 0 &&
+        2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
     return run_call(*cx, a.flags | TPG_NO_GRAPH, std::string(), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ag(*cx, a, L); });

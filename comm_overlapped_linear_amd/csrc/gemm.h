@@ -12,6 +12,12 @@ constexpr int kMaxAddList = 16;
 // row stride ldb. C / D / bias / addends are bf16 bit patterns.
 constexpr int kMaxSeg = 4;
 constexpr int kMaxCopySlices = 8;
+constexpr int kMaxGateSlices = 8;
+// Deadline of one in-kernel gate wait, in ticks of the 100 MHz wall clock
+// (2 s; the low 32 bits of the clock are compared): a wave that has waited
+// this long stops waiting, and its workgroup writes NaN for the whole tile
+// instead of hanging.
+constexpr unsigned kGateDeadline = 200000000u;
 
 struct GemmParams {
   const void* a;
@@ -88,6 +94,25 @@ struct GemmParams {
   // Tile-rows per group of the direct-to-LDS kernel's tile order, set by its
   // launcher (callers leave 0: the kernel's own power-of-two rule).
   int tile_gm;
+  // In-kernel stage gates: the staged all-gather as one launch over all M
+  // rows. With a_slice_rows > 0 (a multiple of 128 dividing M), A is read
+  // in slices of a_slice_rows rows (row stride lda) and a is not: slice
+  // gate_local at a_local, and slice i != gate_local at a_slots + j * (its
+  // bytes), j = (i - gate_local - 1) mod (M / a_slice_rows) its delivery
+  // slot (slices arrive in ring order after the local one; gate_local = -1:
+  // slice i at a_slots + i * (its bytes)). With gate != nullptr, a tile of
+  // slice i != gate_local waits, before it issues the DMA of a K-step that
+  // starts one of its chunks of gate_ksteps K-steps, until
+  // gate[j * gate_nch + chunk] >= gate_need, and loads that slice
+  // device-coherently (the copy kernel writes it from another stream while
+  // this launch runs). gate_off = 1 skips the waits (negative control). Only
+  // the direct-to-LDS kernel takes gates.
+  int a_slice_rows;
+  const uint8_t* a_local;
+  const uint8_t* a_slots;
+  const unsigned* gate;
+  int gate_nch, gate_ksteps, gate_local, gate_off;
+  unsigned gate_need;
 };
 
 // Raises a kernel's dynamic-LDS limit on the current device the first time
@@ -160,6 +185,24 @@ hipError_t launch_colsum_bf16(const uint16_t* src, int rows, int cols, int64_t l
 // Zeroes `bytes` (a multiple of 16) at p (16-byte aligned) with a kernel, so
 // the fill may sit in a captured graph.
 hipError_t launch_fill_zero16(void* p, size_t bytes, hipStream_t s);
+
+// Stage deliveries K-chunk by K-chunk for in-kernel gates: n slices of rows
+// x row_bytes (row-major, src row stride = dst row stride = row_bytes), slice
+// i from src[i] to dst + i * rows * row_bytes, in nch chunks of chunk_bytes
+// of every row (the last may be shorter); after a workgroup has stored its
+// rows of chunk c of slice i it adds 1 to gate[i * nch + c], so that a
+// chunk is complete when the count reaches wg_per_slice (the host takes
+// chunk_deliver_wgs_per_slice(rows)). Stores
+// are write-through (device-coherent). 16-byte alignment of everything.
+struct ChunkDeliverParams {
+  const uint8_t* src[kMaxGateSlices];
+  uint8_t* dst;
+  unsigned* gate;
+  int64_t rows, row_bytes, chunk_bytes;
+  int n, nch, wg_per_slice;
+};
+int chunk_deliver_wgs_per_slice(int64_t rows);
+hipError_t launch_chunk_deliver(const ChunkDeliverParams& p, hipStream_t s);
 
 // Stage deliveries (the library's own copy kernel): n slices of `bytes`,
 // slice i from src[i] to dst + i * dst_stride. deliver_ok says whether the

@@ -617,6 +617,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 }
 #pragma clang diagnostic pop
 
+// The same load, device-coherent (sc0 sc1): it reads data another kernel has
+// just written through to memory, not a stale line of this XCD's L2.
+__device__ __forceinline__ void dma16_coherent(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc0 sc1" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
 // all LDS reads of this wave done, then workgroup barrier (no fence: the
 // DMA loads still in flight must not be waited for here)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -678,7 +685,12 @@ __device__ __forceinline__ void copy_job(const GemmParams& p, int b) {
   }
 }
 
-template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT>
+// GATE: A rows come from slices (GemmParams a_slice), and the tiles of
+// delivered slices wait on their chunk counters before each chunk's DMA
+// (GemmParams gate; the staged all-gather as one launch). The loop is
+// otherwise the same, so the results are the same bits.
+template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT,
+          bool GATE = false>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(const GemmParams p) {
   // workgroups past the tile workgroups carry the launch's copy job, if any
   const int tile_grid = static_cast<int>(gridDim.x) - p.cp_blocks;
@@ -746,15 +758,36 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   // With a grid that is a multiple of 8, all tiles of a workgroup come from
   // its own XCD's run of the tile order.
   const int rsub = lane / CPR, pc = lane % CPR;
+  static_assert(!GATE || !AT, "gated launches have row-major A");
   auto run_tile = [&](int vt) {
   int tm, tn;
   tile_of_block(vt, ntiles, ntm, p.tile_gm, tm, tn);
   const int m0 = tm * BM;
+  // gated launches: the slice holding this tile's rows, and the counters of
+  // its delivery slot (nullptr: no waits)
+  const unsigned* gate_row = nullptr;
+  bool timed_out = false;
+  const uint8_t* a_base = A;
+  int64_t a_row0 = m0;
+  if constexpr (GATE) {
+    // slice sl: the local one in place, the others in their delivery slots
+    // (all scalar arithmetic: no table in the arguments to index)
+    const int sl = m0 / p.a_slice_rows;
+    const int nsl = p.M / p.a_slice_rows;
+    int slot = sl - p.gate_local - 1;
+    if (slot < 0) slot += nsl;
+    const bool local = sl == p.gate_local;
+    a_base = local ? p.a_local : p.a_slots + int64_t(slot) * p.a_slice_rows * lda_b;
+    a_row0 = m0 - int64_t(sl) * p.a_slice_rows;
+    if (p.gate != nullptr && !p.gate_off && !local) gate_row = p.gate + slot * p.gate_nch;
+    // the wait's state lives in VGPRs: the mainloop needs every SGPR
+    asm volatile("" : "+v"(gate_row));
+  }
   // This lane's source chunk in each DMA instruction, as a 32-bit offset
   // from a uniform base (the tile's first A row; B itself), which the host
   // keeps below 2^31. Rows past the edge read a valid row instead (their
   // products only reach outputs never stored).
-  const uint8_t* a_tile = A + int64_t(m0) * lda_b;
+  const uint8_t* a_tile = a_base + a_row0 * lda_b;
   uint32_t aoff[A_INSTR];
   uint32_t boff[B_INSTR];
 #pragma unroll
@@ -805,9 +838,34 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
     } else {
       bb = Bp + int64_t(kt) * b_step;
     }
+    if constexpr (GATE) {
+      if (gate_row != nullptr) {
+        // a K-step that starts a chunk waits for that chunk to have landed
+        // (bounded: past the deadline the wait gives up and the tile's
+        // output becomes NaN)
+        if (kt % p.gate_ksteps == 0) {
+          const unsigned* g = gate_row + kt / p.gate_ksteps;
+          unsigned need = p.gate_need;
+          asm volatile("" : "+v"(g), "+v"(need));
+          const unsigned t0 = static_cast<unsigned>(__builtin_amdgcn_s_memrealtime());
+          while (!timed_out && __hip_atomic_load(g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+            if (static_cast<unsigned>(__builtin_amdgcn_s_memrealtime()) - t0 > kGateDeadline) timed_out = true;
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < A_INSTR; ++j)
+          dma16_coherent(ab, aoff[j], __builtin_amdgcn_readfirstlane(sb + (j * NW + wave) * 1024));
+      } else {
+#pragma unroll
+        for (int j = 0; j < A_INSTR; ++j)
+          dma16(ab, aoff[j], __builtin_amdgcn_readfirstlane(sb + (j * NW + wave) * 1024));
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
       dma16(ab, aoff[j], __builtin_amdgcn_readfirstlane(sb + (j * NW + wave) * 1024));
+    }
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j)
       dma16(bb, boff[j], __builtin_amdgcn_readfirstlane(sb + A_BYTES + (j * NW + wave) * 1024));
@@ -907,7 +965,24 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
     }
   }
   wait_vmcnt<0>();
-  __syncthreads();
+  bool nan_out = false;
+  if constexpr (GATE) {
+    // a workgroup any of whose waves gave up waiting leaves NaN, never a
+    // silent wrong value
+    nan_out = __syncthreads_or(timed_out);
+  } else {
+    __syncthreads();
+  }
+  if constexpr (GATE) {
+    if (nan_out) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_nanf("");
+    }
+  }
   store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm, tn);   // ends with a barrier: LDS free
   };
   if constexpr (persistent_tiles<Op, BM, BN, AT>()) {
@@ -956,11 +1031,12 @@ int group_rows(int ntm, int ntn, int bm, int bn, int grid) {
   return best;
 }
 
-template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT = false>
+template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT = false,
+          bool GATE = false>
 hipError_t launch_dma_tile(const GemmParams& p_in, hipStream_t s) {
   constexpr int smem = STAGES * (BM + BN) * ROWB;
   constexpr int nt = 64 * WM * WN;
-  auto kern = gemm_dma_kernel<Op, BM, BN, WM, WN, ROWB, STAGES, KN, SWIGLU, AT>;
+  auto kern = gemm_dma_kernel<Op, BM, BN, WM, WN, ROWB, STAGES, KN, SWIGLU, AT, GATE>;
   static uint64_t lds_set = 0;
   if (hipError_t e = lds_limit_once(reinterpret_cast<const void*>(kern), smem, lds_set); e != hipSuccess) return e;
   GemmParams p = p_in;
@@ -1045,6 +1121,15 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   // 64-byte K-steps with twice the ring depth: half the barriers per byte)
   const bool dma = dma_path(p, Op::kElemBytes, KN);
   const int epi = SW ? kEpiSwiglu : kEpiAlphaBeta;
+  if (p.a_slice_rows > 0) {
+    // the staged all-gather as one launch (gated): 128 x 256 tiles, whose
+    // registers leave each SIMD room for a wave of the copy kernel
+    if (!dma || p.batch != 1 || p.a_slice_rows % 128 != 0 || p.M % p.a_slice_rows != 0 ||
+        p.M / p.a_slice_rows > kMaxGateSlices || p.cp_blocks > 0 || p.gate_local < -1 ||
+        p.gate_local >= p.M / p.a_slice_rows || !p.a_slots || (p.gate_local >= 0 && !p.a_local))
+      return hipErrorInvalidValue;
+    return launch_dma_tile<Op, 128, 256, 2, 4, 128, 3, KN, SW, false, true>(p, s);
+  }
   if (dma) {
     switch (pick_tile(p.M, p.N, epi, p.batch, p.cu_budget)) {
       case 0: return launch_dma_tile<Op, 256, 256, 2, 4, 128, 2, KN, SW>(p, s);

@@ -104,7 +104,7 @@ enum {
                                        host callback; every gated stage must still see its data */
   TPG_COPY_SHADER = 256u,   /* deliver with the runtime's shader copy (hipMemcpyAsync, uses CUs) */
   TPG_COPY_KERNEL = 512u,   /* deliver with the library's copy kernel (uses CUs); the AG and wgrad default */
-  TPG_DEBUG_NO_GATE = 1024u /* testing, the negative control of the gate tests: staged rotating-A
+  TPG_DEBUG_NO_GATE = 1024u, /* testing, the negative control of the gate tests: staged rotating-A
                                all-gathers and reduce-scatters issue every stage run that reads
                                delivered data on an internal stream WITHOUT waiting for its
                                deliveries. With TPG_DEBUG_HOLD_DELIVERIES those runs read the
@@ -112,7 +112,23 @@ enum {
                                (never a fault: the slots are valid workspace memory). Issues
                                eagerly; rejected with TPG_UNSTAGED or TPG_SERIAL_STAGES
                                (TPG_ERR_INVALID) and by the other entry points
-                               (TPG_ERR_UNSUPPORTED). */
+                               (TPG_ERR_UNSUPPORTED). With TPG_IN_KERNEL_GATES the launch's
+                               tiles skip their counter waits instead. */
+  TPG_IN_KERNEL_GATES = 2048u /* staged rotating-A all-gather as ONE GEMM launch over all M rows:
+                                 the tiles of each delivered slice wait inside the kernel, K-chunk
+                                 by K-chunk, on counters that the library's copy kernel (running
+                                 beside it on an internal stream) bumps as each chunk lands. No
+                                 stage boundaries between launches. Needs P <= 8, M/P a multiple
+                                 of 128, K * element bytes a multiple of 128 and the copy kernel
+                                 (no other TPG_COPY_* flag); rejected with TPG_UNSTAGED,
+                                 TPG_SERIAL_STAGES, TPG_ROTATE_B and by the other entry points
+                                 (TPG_ERR_UNSUPPORTED); with TPG_NO_COPY the slices must be back to
+                                 back in memory. The workspace grows by 256 bytes of
+                                 counters. Always issued eagerly (TPG_FORCE_GRAPH is ignored):
+                                 the GEMM depends on the copy kernel running concurrently, which
+                                 the call arranges on its own streams; do not capture such a call
+                                 into a graph. A tile that waits 2 s without its data gives up
+                                 and writes NaN (never a hang). groups is ignored. */
 };
 
 /* ------------------------------------------------------------------------

@@ -68,6 +68,14 @@ def ag(**kw):
     (dict(flags=tp.DEBUG_NO_GATE | tp.UNSTAGED), tp.ERR_INVALID),         # the negative control is staged
     (dict(flags=tp.DEBUG_NO_GATE | tp.SERIAL_STAGES), tp.ERR_INVALID),
     (dict(flags=tp.DEBUG_NO_GATE, schedule=tp.ROTATE_B, N=2 * 64), tp.ERR_UNSUPPORTED),
+    (dict(flags=tp.IN_KERNEL_GATES | tp.UNSTAGED), tp.ERR_UNSUPPORTED),   # in-kernel gates are staged
+    (dict(flags=tp.IN_KERNEL_GATES | tp.SERIAL_STAGES), tp.ERR_UNSUPPORTED),
+    (dict(flags=tp.IN_KERNEL_GATES | tp.COPY_SDMA), tp.ERR_UNSUPPORTED),  # the copy kernel bumps the counters
+    (dict(flags=tp.IN_KERNEL_GATES | tp.COPY_SHADER), tp.ERR_UNSUPPORTED),
+    (dict(flags=tp.IN_KERNEL_GATES, schedule=tp.ROTATE_B, N=2 * 64), tp.ERR_UNSUPPORTED),
+    (dict(flags=tp.IN_KERNEL_GATES, P=16, M=16 * 128), tp.ERR_UNSUPPORTED),   # at most 8 slices
+    (dict(flags=tp.IN_KERNEL_GATES, M=2 * 96), tp.ERR_UNSUPPORTED),           # M/P % 128
+    (dict(flags=tp.IN_KERNEL_GATES, K=200), tp.ERR_UNSUPPORTED),              # K * 2 bytes % 128
 ])
 def test_ag_validation_rejects_before_enqueue(kw, status):
     a = ag(**kw)
@@ -93,6 +101,13 @@ def test_workspace_sizes_are_pure():
     assert tp.stage_ag_workspace_size(a) == 8 * 1024 * 8192
     a.flags = tp.NO_COPY
     assert tp.stage_ag_workspace_size(a) == 0
+    a.flags = tp.IN_KERNEL_GATES                      # slots, then 8 slices x 8 chunks of u32 counters
+    assert tp.stage_ag_workspace_size(a) == 7 * 1024 * 8192 + 256
+    a.flags = tp.IN_KERNEL_GATES | tp.NO_COPY
+    assert tp.stage_ag_workspace_size(a) == 0
+    a = ag(P=4, M=4 * 128, K=200)                     # slots of 51200 bytes: counters 256-aligned after them
+    a.flags = tp.IN_KERNEL_GATES
+    assert tp.stage_ag_workspace_size(a) == -(-(3 * 128 * 200 * 2) // 256) * 256 + 256
     inc = (ctypes.c_void_p * 8)(*[FAKE] * 8)
     r = tp.RsArgs(M=8192, N=8192, K=3584, P=8, rank=0, ab_dtype=0, b_layout=0, a=FAKE, b=FAKE,
                   incoming=ctypes.cast(inc, ctypes.POINTER(ctypes.c_void_p)), d=FAKE, alpha=1.0,
@@ -116,6 +131,10 @@ def test_rs_and_ffn_and_permute_validation():
     assert tp.lib().ffn_slot_forward(ctypes.byref(f), None) == tp.ERR_UNSUPPORTED   # no gate to drop
     r.M, r.flags = 8 * 64, tp.DEBUG_NO_GATE | tp.UNSTAGED
     assert tp.lib().tpgemm_stage_rs(ctypes.byref(r), None) == tp.ERR_INVALID
+    r.flags = tp.IN_KERNEL_GATES
+    assert tp.lib().tpgemm_stage_rs(ctypes.byref(r), None) == tp.ERR_UNSUPPORTED   # all-gather only
+    f.flags = tp.IN_KERNEL_GATES
+    assert tp.lib().ffn_slot_forward(ctypes.byref(f), None) == tp.ERR_UNSUPPORTED
     srcs = (ctypes.c_void_p * 2)(FAKE, FAKE + 0x100000)
     sp = ctypes.cast(srcs, ctypes.POINTER(ctypes.c_void_p))
     assert tp.lib().dispatch_permute(sp, FAKE + 0x200000, 2, 0, 1, 3, 4, 2, None) == tp.ERR_INVALID  # T % P
