@@ -572,11 +572,13 @@ def bench_small_ag(case, args):
     inp, call, _, _ = setup_ag(case)
     ms = time_steps(lambda: call(0), args.steps, args.warmup)
     mu = time_steps(lambda: call(tp.UNSTAGED), args.steps, args.warmup)
+    # the staged call as one launch carrying its deliveries, gated in-kernel
+    mi = time_steps(lambda: call(tp.IN_KERNEL_GATES), args.steps, args.warmup)
     peak = PEAK_TFLOPS["bf16"]
     kinds = profile_launches(lambda f: call(f), max(5, args.steps // 5), peak)
     tf = case.flop / (ms * 1e-3) / 1e12
-    return dict(us=round(ms * 1e3, 2), us_unstaged=round(mu * 1e3, 2), tflops=round(tf, 2),
-                pct_bf16_peak=round(100 * tf / peak, 3), roofline=gemm_roofline(kinds, peak))
+    return dict(us=round(ms * 1e3, 2), us_unstaged=round(mu * 1e3, 2), us_in_kernel_gates=round(mi * 1e3, 2),
+                tflops=round(tf, 2), pct_bf16_peak=round(100 * tf / peak, 3), roofline=gemm_roofline(kinds, peak))
 
 
 def bench_permutes(args):

@@ -668,6 +668,13 @@ void set_out_rows(tpg::GemmParams& q, const tpg_ag_args& a, const OutSegs* segs,
 // for that chunk's counter. The copy kernel runs beside it on a side stream,
 // K-chunk-major, storing write-through and bumping the counter of each
 // chunk it completes; the counters are zeroed on the root first.
+// A latency-bound call (under kLatencyBoundFlop) whose tiles and copy
+// workgroups fit on the chip at once instead carries the deliveries in the
+// GEMM launch itself, as extra workgroups that each bump one counter when
+// done, and its delivered slices' tiles wait for all of them before their
+// first DMA: one stream, a zeroing kernel and one launch. (Not with
+// TPG_DEBUG_HOLD_DELIVERIES or TPG_DEBUG_NO_GATE, whose tests need the
+// deliveries on a stream of their own.)
 // (TPG_NO_COPY: one launch over the slices in place, no gates.)
 tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutSegs* segs,
                             tpg::GemmParams p, int dtype, int layout, int epi, int64_t nout) {
@@ -702,6 +709,24 @@ tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, cons
   if (!copies) return gemm_on(cx, L, L.root, p, dtype, layout, epi);
 
   HIP_TRY(tpg::launch_fill_zero16(gate, kGateCounterBytes, L.root));
+  const int64_t vecs = int64_t(slice_b / 16) * (P - 1);
+  const int cp_blocks = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (vecs + 2047) / 2048)));
+  const bool carried = 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop && P - 1 <= tpg::kMaxCopySlices &&
+                       !(a.flags & (TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE)) &&
+                       tpg::gated_tiles(static_cast<int>(a.M), static_cast<int>(a.N), dtype, epi) + cp_blocks <=
+                           tpg::device_cus();
+  if (carried) {
+    p.cp_blocks = cp_blocks;
+    p.cp_n = P - 1;
+    for (int t = 1; t < P; ++t) p.cp_src[t - 1] = static_cast<const uint8_t*>(a.a_slices[(r + t) % P]);
+    p.cp_dst = reinterpret_cast<uint8_t*>(ws);
+    p.cp_dst_stride = static_cast<int64_t>(slice_b);
+    p.cp_nvec = static_cast<int64_t>(slice_b / 16);
+    p.gate_nch = 0;          // one counter (gate[0]) for every delivered slice
+    p.gate_ksteps = nk;      // waited for once, before a tile's first DMA
+    p.gate_need = static_cast<unsigned>(cp_blocks);
+    return gemm_on(cx, L, L.root, p, dtype, layout, epi);
+  }
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, 2, st);   // the side stream starts after the zeroing
   if (stat != TPG_OK) return stat;

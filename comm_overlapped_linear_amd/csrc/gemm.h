@@ -106,11 +106,15 @@ struct GemmParams {
   // gate[j * gate_nch + chunk] >= gate_need, and loads that slice
   // device-coherently (the copy kernel writes it from another stream while
   // this launch runs). gate_off = 1 skips the waits (negative control). Only
-  // the direct-to-LDS kernel takes gates.
+  // the direct-to-LDS kernel takes gates. When the launch also carries a copy
+  // job (cp_blocks > 0) and gate != nullptr, each copy workgroup stores
+  // system-scope and then adds 1 to gate[0]; with gate_nch = 0 and
+  // gate_ksteps >= the K-steps, every tile of a delivered slice waits once,
+  // before its first DMA, for gate[0] >= gate_need = cp_blocks.
   int a_slice_rows;
   const uint8_t* a_local;
   const uint8_t* a_slots;
-  const unsigned* gate;
+  unsigned* gate;
   int gate_nch, gate_ksteps, gate_local, gate_off;
   unsigned gate_need;
 };
@@ -138,6 +142,8 @@ int device_cus();
 
 // Output tiles the DMA launcher would make for this shape and CU budget.
 int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget);
+// Output tiles of a gated launch (GemmParams a_slice_rows > 0).
+int gated_tiles(int M, int N, int dtype, int epi);
 
 // Picks a tile shape for (M, N) and launches on `s`. Host-side checks of the
 // shapes and alignment are the caller's job (api.cpp validates every call).

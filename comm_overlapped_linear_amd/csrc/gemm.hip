@@ -677,18 +677,30 @@ __device__ __forceinline__ void copy_job(const GemmParams& p, int b) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const int64_t total = int64_t(p.cp_n) * p.cp_nvec;
   const int64_t step = int64_t(p.cp_blocks) * blockDim.x;
+  const bool gated = p.gate != nullptr;
   for (int64_t i = int64_t(b) * blockDim.x + threadIdx.x; i < total; i += step) {
     const int sl = static_cast<int>(i / p.cp_nvec);
     const int64_t v = i - sl * p.cp_nvec;
     const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cp_src[sl]) + v);
-    reinterpret_cast<u32x4*>(p.cp_dst + sl * p.cp_dst_stride)[v] = x;
+    u32x4* dst = reinterpret_cast<u32x4*>(p.cp_dst + sl * p.cp_dst_stride) + v;
+    if (gated)   // read by this launch's gated tiles: system-scope store
+      asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(dst), "v"(x) : "memory");
+    else
+      *dst = x;
+  }
+  if (gated) {
+    // every store of this workgroup has completed (and is visible at the
+    // device coherence point) before it counts itself done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p.gate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// GATE: A rows come from slices (GemmParams a_slice), and the tiles of
-// delivered slices wait on their chunk counters before each chunk's DMA
-// (GemmParams gate; the staged all-gather as one launch). The loop is
-// otherwise the same, so the results are the same bits.
+// GATE: A rows come from slices (GemmParams a_slice_rows, a_local,
+// a_slots), and the tiles of delivered slices wait on their chunk counters
+// before each chunk's DMA (GemmParams gate; the staged all-gather as one
+// launch). The loop is otherwise the same, so the results are the same bits.
 template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, bool KN, bool SWIGLU, bool AT,
           bool GATE = false>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(const GemmParams p) {
@@ -1123,12 +1135,17 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
   const int epi = SW ? kEpiSwiglu : kEpiAlphaBeta;
   if (p.a_slice_rows > 0) {
     // the staged all-gather as one launch (gated): 128 x 256 tiles, whose
-    // registers leave each SIMD room for a wave of the copy kernel
+    // registers leave each SIMD room for a wave of the copy kernel, or
+    // 128 x 128 for a small call
     if (!dma || p.batch != 1 || p.a_slice_rows % 128 != 0 || p.M % p.a_slice_rows != 0 ||
-        p.M / p.a_slice_rows > kMaxGateSlices || p.cp_blocks > 0 || p.gate_local < -1 ||
+        p.M / p.a_slice_rows > kMaxGateSlices || p.gate_local < -1 ||
         p.gate_local >= p.M / p.a_slice_rows || !p.a_slots || (p.gate_local >= 0 && !p.a_local))
       return hipErrorInvalidValue;
-    return launch_dma_tile<Op, 128, 256, 2, 4, 128, 3, KN, SW, false, true>(p, s);
+    if (!gated_small_tile(p.M, p.N, Op::kElemBytes == 1 ? kE4m3 : kBf16, epi))
+      return launch_dma_tile<Op, 128, 256, 2, 4, 128, 3, KN, SW, false, true>(p, s);
+    if constexpr (SW) return launch_dma_tile<Op, 128, 128, 4, 2, 128, 4, KN, SW, false, true>(p, s);
+    else if constexpr (Op::kElemBytes == 2) return launch_dma_tile<Op, 128, 128, 2, 4, 128, 4, KN, SW, false, true>(p, s);
+    else return hipErrorInvalidValue;   // not reached: gated_small_tile is false for it
   }
   if (dma) {
     switch (pick_tile(p.M, p.N, epi, p.batch, p.cu_budget)) {
@@ -1224,6 +1241,23 @@ hipError_t launch_mfma_probe(int dtype, int iters, int blocks, unsigned long lon
   else
     hipLaunchKernelGGL(mfma_probe_kernel<OpBf16>, dim3(blocks), dim3(kProbeThreads), 0, s, sink, iters);
   return hipGetLastError();
+}
+
+// Tile of a gated launch: 128 x 256, or 128 x 128 when 128 x 256 tiles
+// would fill at most half the chip (a latency-bound call: twice the CUs,
+// half the time per tile). The e4m3 alpha/beta 128 x 128 form is left out:
+// with the gate's registers it needs a stack frame.
+bool gated_small_tile(int M, int N, int dtype, int epi) {
+  if (dtype == kE4m3 && epi != kEpiSwiglu) return false;
+  const int ncols = epi == kEpiSwiglu ? (N / 2 + 127) / 128 : (N + 255) / 256;
+  return int64_t((M + 127) / 128) * ncols * 2 <= cu_count();
+}
+
+int gated_tiles(int M, int N, int dtype, int epi) {
+  const bool small = gated_small_tile(M, N, dtype, epi);
+  const int bn = small ? 128 : 256;
+  const int ncols = epi == kEpiSwiglu ? (N / 2 + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
+  return ((M + 127) / 128) * ncols;
 }
 
 int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget) {
