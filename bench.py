@@ -271,10 +271,10 @@ CPU_SECONDS = 10.0      # bounded CPU sample: repeat the oracle call until this 
 CPU_MAX_CALLS = 20
 
 
-def cpu_baseline_ag(case, inp):
-    """The oracle, as it stands, on the same workload: whole calls repeated
-    until about CPU_SECONDS of host time (at most CPU_MAX_CALLS), throughput
-    from the total."""
+def cpu_baseline_ag_numpy(case, inp):
+    """The numpy oracle, as it stands, on the same workload: whole calls
+    repeated until about CPU_SECONDS of host time (at most CPU_MAX_CALLS),
+    throughput from the total."""
     import oracle
     t0 = time.perf_counter()
     calls = 0
@@ -286,6 +286,36 @@ def cpu_baseline_ag(case, inp):
     return dict(value=case.flop * calls / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
                 sample=f"the whole workload {calls} times ({case.flop / 1e9:.1f} GFLOP each, float64 numpy), "
                        f"{dt:.2f} s in total",
+                cpu=cpu_model(), host_cpus=os.cpu_count())
+
+
+CPP_SAMPLE_ROWS = 16     # rows per slice of the C++ oracle's bounded sample
+
+
+def cpu_baseline_ag(case, inp):
+    """The C++17 oracle (float64, OpenMP over output rows), as it stands, on a
+    bounded sample of the workload: the first CPP_SAMPLE_ROWS rows of every
+    slice against the whole B and K, repeated until about CPU_SECONDS of host
+    time; throughput is the sample's flops over the time."""
+    from oracle import cref
+    rows = min(CPP_SAMPLE_ROWS, case.m)
+    slices = [np.ascontiguousarray(s[:rows]) for s in inp["a_slices"]]
+    c = inp["c"]
+    if c is not None:
+        c = np.ascontiguousarray(np.concatenate([c[s * case.m:s * case.m + rows] for s in range(case.P)]))
+    flop = 2.0 * case.P * rows * case.N * case.K
+    t0 = time.perf_counter()
+    calls = 0
+    while calls < CPU_MAX_CALLS and (calls == 0 or time.perf_counter() - t0 < CPU_SECONDS):
+        cref.gemm_ag(slices, inp["b"], c, case.alpha, case.beta, case.rank, case.dtype, case.b_layout,
+                     swiglu=case.swiglu)
+        calls += 1
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return dict(value=flop * calls / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"C++17 oracle (float64, OpenMP): {rows} rows of each of the {case.P} slices "
+                       f"({case.P * rows} of {case.M} rows, whole N and K; {flop / 1e9:.2f} GFLOP) "
+                       f"{calls} times, {dt:.2f} s in total",
                 cpu=cpu_model(), host_cpus=os.cpu_count())
 
 
@@ -752,6 +782,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_ag(case, r["inp"])
         log(f"[cpu] {cpu}")
+        detail["cpu_baseline_numpy_oracle"] = cpu_baseline_ag_numpy(case, r["inp"])
+        log(f"[cpu numpy] {detail['cpu_baseline_numpy_oracle']}")
 
     peak = PEAK_TFLOPS[r["dtype"]]
     out = {

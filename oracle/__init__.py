@@ -26,6 +26,11 @@ Sources (pages of the reference set, cited by title and section):
 Every function is pinned by a CPU test against something other than itself
 (closed forms, brute-force loops, library routines, the pages' worked
 example); see tests/test_oracle_*.py.
+
+oracle.cref binds a second, independent writing of the same definitions in
+plain C++17 (oracle/cpp/oracle.cpp: float64 sums, OpenMP over output rows),
+checked against this one in tests/test_oracle_cpp.py and timed as the
+benchmark's CPU baseline.
 """
 from .formats import decode_bf16, decode_e4m3, decode
 from .gemm import (ag_stage_order, rs_block_order, gemm_ag, gemm_ag_rows, gemm_rs, gemm_rs_rows,
