@@ -290,6 +290,7 @@ def cpu_baseline_ag_numpy(case, inp):
 
 
 CPP_SAMPLE_ROWS = 16     # rows per slice of the C++ oracle's bounded sample
+CPP_MAX_CALLS = 200
 
 
 def cpu_baseline_ag(case, inp):
@@ -306,7 +307,7 @@ def cpu_baseline_ag(case, inp):
     flop = 2.0 * case.P * rows * case.N * case.K
     t0 = time.perf_counter()
     calls = 0
-    while calls < CPU_MAX_CALLS and (calls == 0 or time.perf_counter() - t0 < CPU_SECONDS):
+    while calls < CPP_MAX_CALLS and (calls == 0 or time.perf_counter() - t0 < CPU_SECONDS):
         cref.gemm_ag(slices, inp["b"], c, case.alpha, case.beta, case.rank, case.dtype, case.b_layout,
                      swiglu=case.swiglu)
         calls += 1
