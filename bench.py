@@ -379,10 +379,13 @@ def bench_ag(case, args, detail):
         t_per_stage = time_steps(lambda: call(0, case.P - 1), args.steps, args.warmup)
         t_sdma = time_steps(lambda: call(tp.COPY_SDMA), args.steps, args.warmup)
         t_graph = time_steps(lambda: call(tp.FORCE_GRAPH), args.steps, args.warmup)
+        # the same stages one after another on one stream: deliveries, then each stage launch
+        t_serial = time_steps(lambda: call(tp.SERIAL_STAGES), args.steps, args.warmup)
         # the staged call as one launch whose tiles wait in-kernel on chunk counters
         t_ikg = time_steps(lambda: call(tp.IN_KERNEL_GATES), args.steps, args.warmup)
         t_ikg_compute = time_steps(bufs["compute_only_ikg"], args.steps, args.warmup)
         hidden = 1.0 - (ms - t_compute) / t_copy if t_copy > 0 else None
+        hidden_serial = (t_serial - ms) / t_copy if t_copy > 0 else None
         hidden_ikg = 1.0 - (t_ikg - t_ikg_compute) / t_copy if t_copy > 0 else None
         hidden_sdma = 1.0 - (t_sdma - t_compute) / t_copy_sdma if t_copy_sdma > 0 else None
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -395,6 +398,8 @@ def bench_ag(case, args, detail):
             "us_compute_only": round(t_compute * 1e3, 2),
             "us_deliveries_alone": round(t_copy * 1e3, 2),
             "hidden_fraction": None if hidden is None else round(hidden, 3),
+            "us_serial_stages": round(t_serial * 1e3, 2),
+            "hidden_fraction_serial": None if hidden_serial is None else round(hidden_serial, 3),
             "us_unstaged": round(t_unstaged * 1e3, 2),
             "us_one_gate_per_stage": round(t_per_stage * 1e3, 2),
             "us_staged_graph": round(t_graph * 1e3, 2),
@@ -634,15 +639,22 @@ def bench_permutes(args):
     return out
 
 
-def overlap_point(staged, unstaged, compute_only, deliveries, flop, steps, warmup):
-    """Times of one sweep point (us) and the hidden fraction
-    1 - (T_staged - T_compute) / T_deliveries (negatives kept)."""
+def overlap_point(staged, unstaged, serial, compute_only, deliveries, flop, steps, warmup):
+    """Times of one sweep point (us) and the hidden fractions, negatives kept:
+    (T_serial - T_staged) / T_deliveries with T_serial the same stages run one
+    after another on one stream (the p04 statement's estimate), and
+    1 - (T_staged - T_compute) / T_deliveries (T_serial taken as the sum of
+    the isolated compute and deliveries)."""
     t = {k: time_steps(f, steps, warmup) for k, f in
-         (("staged", staged), ("unstaged", unstaged), ("compute_only", compute_only), ("deliveries", deliveries))}
+         (("staged", staged), ("unstaged", unstaged), ("serial", serial), ("compute_only", compute_only),
+          ("deliveries", deliveries))}
     hidden = 1.0 - (t["staged"] - t["compute_only"]) / t["deliveries"]
+    hidden_serial = (t["serial"] - t["staged"]) / t["deliveries"]
     return dict(us_staged=round(t["staged"] * 1e3, 2), us_unstaged=round(t["unstaged"] * 1e3, 2),
+                us_serial_stages=round(t["serial"] * 1e3, 2),
                 us_compute_only=round(t["compute_only"] * 1e3, 2), us_deliveries_alone=round(t["deliveries"] * 1e3, 2),
-                hidden_fraction=round(hidden, 3), tflops_staged=round(flop / (t["staged"] * 1e-3) / 1e12, 1),
+                hidden_fraction_serial=round(hidden_serial, 3), hidden_fraction=round(hidden, 3),
+                tflops_staged=round(flop / (t["staged"] * 1e-3) / 1e12, 1),
                 staged_beats_unstaged=bool(t["staged"] < t["unstaged"]))
 
 
@@ -664,8 +676,8 @@ def bench_scale_sweep(args):
         inp, call, deliveries, bufs = setup_ag(case)
         out[f"ag_e4m3_p8 comm x{c} compute x{k}"] = dict(
             M=case.M, N=case.N, K=case.K, delivered_mib=round(7 * case.m * case.K / 2 ** 20, 1),
-            **overlap_point(lambda: call(0), lambda: call(tp.UNSTAGED), bufs["compute_only"], deliveries(0),
-                            case.flop, steps, warm))
+            **overlap_point(lambda: call(0), lambda: call(tp.UNSTAGED), lambda: call(tp.SERIAL_STAGES),
+                            bufs["compute_only"], deliveries(0), case.flop, steps, warm))
         log(f"[sweep] {case.name}: {out[f'ag_e4m3_p8 comm x{c} compute x{k}']}")
         del inp, call, deliveries, bufs
         torch.cuda.empty_cache()
@@ -695,10 +707,10 @@ def bench_scale_sweep(args):
 
         def block(flags):
             ag(flags=flags)
-            rs(flags=flags & tp.UNSTAGED)
+            rs(flags=flags & (tp.UNSTAGED | tp.SERIAL_STAGES))
         out[f"swiglu_p8 comm x{c} compute x{k}"] = dict(
             S=case.S, F=case.F, D=case.D, delivered_mib=round(7 * slice_bytes / 2 ** 20, 1),
-            **overlap_point(lambda: block(0), lambda: block(tp.UNSTAGED),
+            **overlap_point(lambda: block(0), lambda: block(tp.UNSTAGED), lambda: block(tp.SERIAL_STAGES),
                             lambda: (ag_in_place(flags=tp.NO_COPY), rs(flags=0)), deliveries, case.flop, steps, warm))
         log(f"[sweep] {case.name}: {out[f'swiglu_p8 comm x{c} compute x{k}']}")
         del xs, w13, w2, whole, views, h, o, ws, ag, ag_in_place, rs

@@ -844,11 +844,14 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
   // On one stream (a latency-bound call) the local stage's launch carries
   // the deliveries as extra workgroups: the local stage then runs beside
   // them, as the staged schedule intends, with one launch fewer. The remote
-  // run follows in stream order. (Only with the library's copy kernel and
-  // a single remote run of at most kMaxCopySlices slices.)
+  // run follows in stream order. (Only with the library's copy kernel, a
+  // single remote run of at most kMaxCopySlices slices, and a latency-bound
+  // call: a larger call on one stream, TPG_SERIAL_STAGES asked for, runs its
+  // deliveries and stages strictly one after another.)
   tpg::GemmParams job = base_params();
   bool carry = false;
-  if (copies && ns == 1 && G == 1 && ck == Copy::Kernel && remote <= tpg::kMaxCopySlices) {
+  if (copies && ns == 1 && G == 1 && ck == Copy::Kernel && remote <= tpg::kMaxCopySlices &&
+      2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop) {
     const void* src[kMaxP];
     for (int t = 1; t < P; ++t) src[t - 1] = a.a_slices[(r + t) % P];
     const int64_t vecs = int64_t(slice_b / 16) * remote;
