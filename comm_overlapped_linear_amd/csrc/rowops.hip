@@ -53,6 +53,8 @@ __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
   }
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // CH = 8-element chunks per thread per half (H <= 8 * 256 * CH).
 template <int CH>
 __global__ __launch_bounds__(kRowThreads) void ln_silu_kernel(
@@ -70,8 +72,12 @@ __global__ __launch_bounds__(kRowThreads) void ln_silu_kernel(
   for (int c = 0; c < CH; ++c) {
     const int ch = c * kRowThreads + threadIdx.x;
     if (ch < nchunk) {
-      unpack8(*reinterpret_cast<const uint4*>(zu + ch * 8), u[c]);
-      unpack8(*reinterpret_cast<const uint4*>(zg + ch * 8), g[c]);
+      // z is read once: non-temporal, so it does not evict what the GEMM
+      // running beside this pass keeps in L2 (layer 2171 -> 2127 us)
+      const u32x4 vu = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zu + ch * 8));
+      const u32x4 vg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zg + ch * 8));
+      unpack8(make_uint4(vu.x, vu.y, vu.z, vu.w), u[c]);
+      unpack8(make_uint4(vg.x, vg.y, vg.z, vg.w), g[c]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) { su += u[c][e]; sg += g[c][e]; }
     }
@@ -113,7 +119,9 @@ __global__ __launch_bounds__(kRowThreads) void ln_silu_kernel(
         const float y1 = (g[c][e + 1] - mg) * rg * cc[e + 1] + d[e + 1];
         o[e / 2] = pack_bf16x2(x0 * silu_f32(y0), x1 * silu_f32(y1));
       }
-      *reinterpret_cast<uint4*>(hr + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+      // h is read back only after every slot's pass: non-temporal too
+      const u32x4 ov = {o[0], o[1], o[2], o[3]};
+      __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(hr + ch * 8));
     }
   }
 }
