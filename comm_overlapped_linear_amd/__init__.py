@@ -29,7 +29,7 @@ TILE_A, TILE_B = 0, 1           # reduce-scatter schedules
 GATHER_X, GATHER_G = 0, 1       # weight gradient: which operand arrives as slices
 UNSTAGED, NO_COPY, NO_GRAPH, COPY_SDMA, SERIAL_STAGES, PROFILE, FORCE_GRAPH = 1, 2, 4, 8, 16, 32, 64
 DEBUG_HOLD_DELIVERIES, COPY_SHADER, COPY_KERNEL, DEBUG_NO_GATE = 128, 256, 512, 1024
-IN_KERNEL_GATES = 2048
+IN_KERNEL_GATES, DEBUG_GATE_TIMEOUT = 2048, 4096
 
 _STATUS = {OK: "OK", ERR_INVALID: "INVALID", ERR_UNSUPPORTED: "UNSUPPORTED",
            ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP"}

@@ -54,7 +54,7 @@ constexpr size_t kMaxGraphs = 512;
 constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG_COPY_SDMA |
                                  TPG_SERIAL_STAGES | TPG_PROFILE | TPG_FORCE_GRAPH |
                                  TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER | TPG_COPY_KERNEL |
-                                 TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES;
+                                 TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES | TPG_DEBUG_GATE_TIMEOUT;
 constexpr uint32_t kCopyFlags = TPG_COPY_SDMA | TPG_COPY_SHADER | TPG_COPY_KERNEL;
 // In-kernel gate counters after the all-gather's receive slots: one 32-bit
 // counter per (delivered slice, K-chunk)
@@ -359,6 +359,8 @@ tpg_status validate_no_gate(uint32_t flags, bool supported) {
 
 // TPG_IN_KERNEL_GATES applies to the staged rotating-A all-gather only.
 tpg_status validate_in_kernel_gates(uint32_t flags, bool supported) {
+  if ((flags & TPG_DEBUG_GATE_TIMEOUT) && !(flags & TPG_IN_KERNEL_GATES))
+    return fail(TPG_ERR_INVALID, "TPG_DEBUG_GATE_TIMEOUT needs TPG_IN_KERNEL_GATES");
   if (!(flags & TPG_IN_KERNEL_GATES)) return TPG_OK;
   if (!supported) return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES: not implemented by this call");
   if (flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES))
@@ -706,6 +708,10 @@ tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, cons
   p.gate_ksteps = ksteps;
   p.gate_off = (a.flags & TPG_DEBUG_NO_GATE) ? 1 : 0;
   p.gate_need = static_cast<unsigned>(wgs);
+  // TPG_DEBUG_GATE_TIMEOUT: one arrival more than will come, 20 us deadline
+  const unsigned extra = (a.flags & TPG_DEBUG_GATE_TIMEOUT) ? 1u : 0u;
+  if (extra) p.gate_deadline = 2000u;
+  p.gate_need += extra;
   if (!copies) return gemm_on(cx, L, L.root, p, dtype, layout, epi);
 
   HIP_TRY(tpg::launch_fill_zero16(gate, kGateCounterBytes, L.root));
@@ -724,7 +730,7 @@ tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, cons
     p.cp_nvec = static_cast<int64_t>(slice_b / 16);
     p.gate_nch = 0;          // one counter (gate[0]) for every delivered slice
     p.gate_ksteps = nk;      // waited for once, before a tile's first DMA
-    p.gate_need = static_cast<unsigned>(cp_blocks);
+    p.gate_need = static_cast<unsigned>(cp_blocks) + extra;
     return gemm_on(cx, L, L.root, p, dtype, layout, epi);
   }
   hipStream_t st[kStreams];

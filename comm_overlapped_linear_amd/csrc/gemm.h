@@ -117,6 +117,7 @@ struct GemmParams {
   unsigned* gate;
   int gate_nch, gate_ksteps, gate_local, gate_off;
   unsigned gate_need;
+  unsigned gate_deadline;   // ticks of the 100 MHz clock per wait; 0: kGateDeadline
 };
 
 // Raises a kernel's dynamic-LDS limit on the current device the first time

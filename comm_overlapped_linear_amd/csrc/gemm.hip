@@ -865,10 +865,11 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
         if (kt % p.gate_ksteps == 0) {
           const unsigned* g = gate_row + kt / p.gate_ksteps;
           unsigned need = p.gate_need;
-          asm volatile("" : "+v"(g), "+v"(need));
+          unsigned deadline = p.gate_deadline != 0u ? p.gate_deadline : kGateDeadline;
+          asm volatile("" : "+v"(g), "+v"(need), "+v"(deadline));
           const unsigned t0 = static_cast<unsigned>(__builtin_amdgcn_s_memrealtime());
           while (!timed_out && __hip_atomic_load(g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-            if (static_cast<unsigned>(__builtin_amdgcn_s_memrealtime()) - t0 > kGateDeadline) timed_out = true;
+            if (static_cast<unsigned>(__builtin_amdgcn_s_memrealtime()) - t0 > deadline) timed_out = true;
             __builtin_amdgcn_s_sleep(2);
           }
         }

@@ -114,7 +114,7 @@ enum {
                                (TPG_ERR_INVALID) and by the other entry points
                                (TPG_ERR_UNSUPPORTED). With TPG_IN_KERNEL_GATES the launch's
                                tiles skip their counter waits instead. */
-  TPG_IN_KERNEL_GATES = 2048u /* staged rotating-A all-gather as ONE GEMM launch over all M rows:
+  TPG_IN_KERNEL_GATES = 2048u, /* staged rotating-A all-gather as ONE GEMM launch over all M rows:
                                  the tiles of each delivered slice wait inside the kernel, K-chunk
                                  by K-chunk, on counters that the library's copy kernel (running
                                  beside it on an internal stream) bumps as each chunk lands. No
@@ -129,6 +129,11 @@ enum {
                                  the call arranges on its own streams; do not capture such a call
                                  into a graph. A tile that waits 2 s without its data gives up
                                  and writes NaN (never a hang). groups is ignored. */
+  TPG_DEBUG_GATE_TIMEOUT = 4096u /* testing, the bounded wait of TPG_IN_KERNEL_GATES (required with
+                                    it, else TPG_ERR_INVALID): every in-kernel wait asks for one
+                                    arrival more than will ever come and gives up after 20 us, so
+                                    every tile of a delivered slice writes NaN while the local
+                                    slice's rows stay right, and every kernel still exits. */
 };
 
 /* ------------------------------------------------------------------------

@@ -76,6 +76,7 @@ def ag(**kw):
     (dict(flags=tp.IN_KERNEL_GATES, P=16, M=16 * 128), tp.ERR_UNSUPPORTED),   # at most 8 slices
     (dict(flags=tp.IN_KERNEL_GATES, M=2 * 96), tp.ERR_UNSUPPORTED),           # M/P % 128
     (dict(flags=tp.IN_KERNEL_GATES, K=200), tp.ERR_UNSUPPORTED),              # K * 2 bytes % 128
+    (dict(flags=tp.DEBUG_GATE_TIMEOUT), tp.ERR_INVALID),                      # only with in-kernel gates
 ])
 def test_ag_validation_rejects_before_enqueue(kw, status):
     a = ag(**kw)

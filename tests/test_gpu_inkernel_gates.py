@@ -131,3 +131,28 @@ def test_in_kernel_gates_negative_control():
             assert_parity(got[rows], ref[rows], "local slice")
         else:
             assert np.isnan(got[rows]).all(), f"slice {s} read its slot after the delivery"
+
+
+def test_in_kernel_gates_bounded_wait():
+    """The bounded wait, forced from the host: every in-kernel wait asks for
+    one arrival more than will come and gives up after 20 us. Every tile of
+    a delivered slice must then write NaN (never a silent wrong value), the
+    local slice's rows stay right, and the call ends at once: the kernels
+    exit. Both forms: deliveries carried in the GEMM launch, and on their own
+    stream behind the host hold."""
+    import time
+    case = CASES[0]
+    ref, slices, b, c = setup(case)
+    m = case.m
+    for flags in (IKG | tp.DEBUG_GATE_TIMEOUT, IKG | tp.DEBUG_GATE_TIMEOUT | HOLD):
+        say(f"in-kernel gates: bounded wait flags={flags}")
+        t0 = time.perf_counter()
+        d = call(case, slices, b, c, flags)
+        assert time.perf_counter() - t0 < 5.0
+        got = host_f64(d)
+        for s in range(case.P):
+            rows = slice(s * m, (s + 1) * m)
+            if s == case.rank:
+                assert_parity(got[rows], ref[rows], "local slice")
+            else:
+                assert np.isnan(got[rows]).all(), f"slice {s}: a tile that gave up did not write NaN"
