@@ -118,8 +118,13 @@ enum {
                                  the tiles of each delivered slice wait inside the kernel, K-chunk
                                  by K-chunk, on counters that the library's copy kernel (running
                                  beside it on an internal stream) bumps as each chunk lands. No
-                                 stage boundaries between launches. Needs P <= 8, M/P a multiple
-                                 of 128, K * element bytes a multiple of 128 and the copy kernel
+                                 stage boundaries between launches. A latency-bound call (under
+                                 1 GFLOP) whose tiles and copy workgroups fit on the chip at once
+                                 (and without the two TPG_DEBUG_* delivery flags) carries the copy
+                                 in the GEMM launch itself as extra workgroups, one counter for
+                                 all of them: one stream, a zeroing kernel and one launch.
+                                 Needs P <= 8, M/P a multiple of 128, K * element bytes a
+                                 multiple of 128 and the copy kernel
                                  (no other TPG_COPY_* flag); rejected with TPG_UNSTAGED,
                                  TPG_SERIAL_STAGES, TPG_ROTATE_B and by the other entry points
                                  (TPG_ERR_UNSUPPORTED); with TPG_NO_COPY the slices must be back to
