@@ -16,11 +16,18 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 # first a larger call (7 MiB of receive slots, two full-chip launches), then
-# smaller ones: a bf16 call on the register-staged kernel (K * 2 bytes not a
-# multiple of 128), a latency-bound one on one stream, and an unstaged one
+# smaller ones: two with in-kernel gates (a copy kernel beside the GEMM, then
+# a latency-bound call carrying its copy), a bf16 call on the register-staged
+# kernel (K * 2 bytes not a multiple of 128), a latency-bound one on one
+# stream, and an unstaged one
 SEQUENCE = [
     (W.AgCase("noalloc_e4m3_p8", M=8 * 512, N=1024, K=2048, P=8, rank=3, dtype="e4m3", dist="n05",
               c_dist="n01"), 0),
+    # in-kernel gates: counters in the static scratch after the slots, both forms
+    (W.AgCase("noalloc_e4m3_p4_in_kernel_gates", M=4 * 256, N=512, K=2048, P=4, rank=2, dtype="e4m3",
+              dist="n05", c_dist="n01"), tp.IN_KERNEL_GATES),
+    (W.AgCase("noalloc_bf16_p4_in_kernel_gates_carried", M=4 * 128, N=256, K=256, P=4, rank=1, dist="u11"),
+     tp.IN_KERNEL_GATES),
     (W.AgCase("noalloc_bf16_p4_small", M=4 * 136, N=264, K=200, P=4, rank=1, dist="u11", alpha=0.5,
               beta=-1.0), 0),
     (W.AgCase("noalloc_bf16_p2_latency", M=2 * 128, N=256, K=512, P=2, rank=1, dist="u11"), 0),
