@@ -199,8 +199,9 @@ hipError_t launch_fill_zero16(void* p, size_t bytes, hipStream_t s);
 // of every row (the last may be shorter); after a workgroup has stored its
 // rows of chunk c of slice i it adds 1 to gate[i * nch + c], so that a
 // chunk is complete when the count reaches wg_per_slice (the host takes
-// chunk_deliver_wgs_per_slice(rows)). Stores
-// are write-through (device-coherent). 16-byte alignment of everything.
+// chunk_deliver_wgs_per_slice(rows)). Stores are system-scope (visible at
+// the device coherence point once complete). 16-byte alignment of
+// everything.
 struct ChunkDeliverParams {
   const uint8_t* src[kMaxGateSlices];
   uint8_t* dst;
