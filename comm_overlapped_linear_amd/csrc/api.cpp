@@ -56,6 +56,9 @@ constexpr uint32_t kKnownFlags = TPG_UNSTAGED | TPG_NO_COPY | TPG_NO_GRAPH | TPG
                                  TPG_DEBUG_HOLD_DELIVERIES | TPG_COPY_SHADER | TPG_COPY_KERNEL |
                                  TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES | TPG_DEBUG_GATE_TIMEOUT;
 constexpr uint32_t kCopyFlags = TPG_COPY_SDMA | TPG_COPY_SHADER | TPG_COPY_KERNEL;
+// Internal (never accepted from a caller): a latency-bound staged all-gather
+// the library runs as one launch carrying its deliveries (enqueue_ag_gated).
+constexpr uint32_t kAutoCarried = 1u << 31;
 // In-kernel gate counters after the all-gather's receive slots: one 32-bit
 // counter per (delivered slice, K-chunk)
 constexpr int kMaxGateChunks = 8;
@@ -88,6 +91,7 @@ struct Ctx {
   std::vector<GraphEntry> retired;
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> prof_pool;
+  uint64_t gate_seq = 0;             // calls that took a token-stamped gate word
 };
 
 std::mutex g_mu;
@@ -367,6 +371,26 @@ tpg_status validate_in_kernel_gates(uint32_t flags, bool supported) {
     return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES needs a staged call on several streams");
   if (flags & (TPG_COPY_SDMA | TPG_COPY_SHADER))
     return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES delivers with the library's copy kernel");
+  return TPG_OK;
+}
+
+// In-kernel gates depend on the copy running while the GEMM waits (and the
+// carried form on a per-call token): a call being captured into a graph
+// cannot take them.
+// Whether `stream` is being captured (a failed query counts as captured, and
+// its error is cleared so that no later launch check reports it).
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
+tpg_status gates_not_captured(uint32_t flags, hipStream_t stream) {
+  if ((flags & TPG_IN_KERNEL_GATES) && stream_capturing(stream))
+    return fail(TPG_ERR_UNSUPPORTED, "TPG_IN_KERNEL_GATES: the call cannot be captured into a graph");
   return TPG_OK;
 }
 
@@ -662,6 +686,45 @@ void set_out_rows(tpg::GemmParams& q, const tpg_ag_args& a, const OutSegs* segs,
   q.d = q.seg_d[0];
 }
 
+// Copy workgroups carried by a gated launch: about 2048 vectors each, at most
+// 64, a multiple of 8 (copy first, the tiles keep their XCD placement).
+int carried_copy_blocks(size_t slice_b, int P) {
+  const int64_t vecs = int64_t(slice_b / 16) * (P - 1);
+  const int64_t n = std::min<int64_t>(64, std::max<int64_t>(1, (vecs + 2047) / 2048));
+  return static_cast<int>((n + 7) / 8 * 8);
+}
+
+// A gated call that carries its deliveries in the GEMM launch: latency-bound,
+// every tile and copy workgroup on the chip at once, and no test flag that
+// needs the deliveries on a stream of their own.
+bool carried_gates_fit(const tpg_ag_args& a, int dtype, int epi) {
+  const int P = a.P;
+  if (P < 2 || P - 1 > tpg::kMaxCopySlices || 2.0 * a.M * double(a.N) * a.K >= kLatencyBoundFlop) return false;
+  if (a.flags & (TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE | TPG_NO_COPY)) return false;
+  const size_t slice_b = size_t(a.M / P) * a.K * elem_bytes(a.ab_dtype);
+  return tpg::gated_tiles(static_cast<int>(a.M), static_cast<int>(a.N), dtype, epi) + carried_copy_blocks(slice_b, P) <=
+         tpg::device_cus();
+}
+
+// Whether a latency-bound staged call with library-chosen grouping can run as
+// one gated launch carrying its deliveries (the staged all-gather's
+// prepended per-stage wait inside one persistent launch): the shape rules of
+// TPG_IN_KERNEL_GATES, the library's copy kernel, eager issue, and a caller
+// stream that is not being captured (a replayed token would pass the gate
+// without waiting).
+bool auto_carried(const tpg_ag_args& a, hipStream_t stream) {
+  if (a.schedule != TPG_ROTATE_A || a.groups != 0 || a.P < 2 || a.P > tpg::kMaxGateSlices) return false;
+  if (a.flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES | TPG_FORCE_GRAPH | TPG_COPY_SDMA | TPG_COPY_SHADER |
+                 TPG_IN_KERNEL_GATES | TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE | TPG_NO_COPY))
+    return false;
+  const int eb = elem_bytes(a.ab_dtype);
+  if ((a.M / a.P) % 128 || (a.K * eb) % 128) return false;
+  if (stream_capturing(stream)) return false;
+  const int dtype = a.ab_dtype == TPG_E4M3 ? tpg::kE4m3 : tpg::kBf16;
+  const int epi = a.epilogue == TPG_EPI_SWIGLU ? tpg::kEpiSwiglu : tpg::kEpiAlphaBeta;
+  return carried_gates_fit(a, dtype, epi);
+}
+
 // TPG_IN_KERNEL_GATES: the staged all-gather as one launch. The stages are
 // those of the rotating-A form (the local slice needs no delivery; slice
 // (rank + t) mod P arrives in slot t-1), but instead of one GEMM launch per
@@ -714,25 +777,28 @@ tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, cons
   p.gate_need += extra;
   if (!copies) return gemm_on(cx, L, L.root, p, dtype, layout, epi);
 
-  HIP_TRY(tpg::launch_fill_zero16(gate, kGateCounterBytes, L.root));
-  const int64_t vecs = int64_t(slice_b / 16) * (P - 1);
-  const int cp_blocks = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (vecs + 2047) / 2048)));
-  const bool carried = 2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop && P - 1 <= tpg::kMaxCopySlices &&
-                       !(a.flags & (TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE)) &&
-                       tpg::gated_tiles(static_cast<int>(a.M), static_cast<int>(a.N), dtype, epi) + cp_blocks <=
-                           tpg::device_cus();
-  if (carried) {
-    p.cp_blocks = cp_blocks;
+  if (carried_gates_fit(a, dtype, epi)) {
+    // the copy rides in the GEMM launch, its workgroups first; one
+    // token-stamped word (a slot of the static array, no zeroing launch)
+    unsigned long long* words = nullptr;
+    HIP_TRY(tpg::gate_words(&words));
+    const uint64_t seq = cx.gate_seq++;
+    p.gate = nullptr;
+    p.gate64 = words + seq % tpg::kGateWords;
+    p.gate_token = static_cast<unsigned>(seq / tpg::kGateWords + 1);   // never 0: the words start at 0
+    p.cp_blocks = carried_copy_blocks(slice_b, P);
     p.cp_n = P - 1;
     for (int t = 1; t < P; ++t) p.cp_src[t - 1] = static_cast<const uint8_t*>(a.a_slices[(r + t) % P]);
     p.cp_dst = reinterpret_cast<uint8_t*>(ws);
     p.cp_dst_stride = static_cast<int64_t>(slice_b);
     p.cp_nvec = static_cast<int64_t>(slice_b / 16);
-    p.gate_nch = 0;          // one counter (gate[0]) for every delivered slice
+    p.gate_nch = 0;          // one word for every delivered slice
     p.gate_ksteps = nk;      // waited for once, before a tile's first DMA
-    p.gate_need = static_cast<unsigned>(cp_blocks) + extra;
+    p.gate_need = static_cast<unsigned>(p.cp_blocks) + extra;
     return gemm_on(cx, L, L.root, p, dtype, layout, epi);
   }
+  if (a.flags & kAutoCarried) return fail(TPG_ERR_INVALID, "internal: carried gates chosen but not possible");
+  HIP_TRY(tpg::launch_fill_zero16(gate, kGateCounterBytes, L.root));
   hipStream_t st[kStreams];
   tpg_status stat = fork_streams(cx, L.root, 2, st);   // the side stream starts after the zeroing
   if (stat != TPG_OK) return stat;
@@ -784,7 +850,8 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
   const int layout = a.b_layout == TPG_B_KN ? tpg::kKN : tpg::kNK;
   const int epi = sw ? tpg::kEpiSwiglu : tpg::kEpiAlphaBeta;
 
-  if (a.flags & TPG_IN_KERNEL_GATES) return enqueue_ag_gated(cx, a, L, segs, p, dtype, layout, epi, nout);
+  if (a.flags & (TPG_IN_KERNEL_GATES | kAutoCarried))
+    return enqueue_ag_gated(cx, a, L, segs, p, dtype, layout, epi, nout);
 
   if (a.flags & TPG_UNSTAGED) {
     // single stage: gather every slice (rank order), then one GEMM over all M rows
@@ -1922,8 +1989,12 @@ tpg_status tpgemm_stage_ag(const tpg_ag_args* args, void* stream) {
     st = get_ctx(&cx);
     if (st != TPG_OK) return st;
     tpg_ag_args a = *args;
-    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES)) && a.groups == 0 &&
-        2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+    hipStream_t us = static_cast<hipStream_t>(stream);
+    if (tpg_status gs = gates_not_captured(a.flags, us); gs != TPG_OK) return gs;
+    if (auto_carried(a, us))
+      a.flags |= kAutoCarried | TPG_NO_GRAPH;
+    else if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES)) && a.groups == 0 &&
+             2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
     if (a.flags & TPG_IN_KERNEL_GATES) a.flags |= TPG_NO_GRAPH;   // the two launches must run concurrently
     return run_call(*cx, a.flags, ag_key(a), static_cast<hipStream_t>(stream),
@@ -1953,8 +2024,12 @@ tpg_status tpgemm_stage_ag_noalloc(const tpg_ag_args* args, void* stream) {
     if (st != TPG_OK) return st;
     HIP_TRY(tpg::static_scratch(&a.workspace));
     a.workspace_bytes = tpg::kStaticScratchBytes;
-    if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES)) && a.groups == 0 &&
-        2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
+    hipStream_t us = static_cast<hipStream_t>(stream);
+    if (tpg_status gs = gates_not_captured(a.flags, us); gs != TPG_OK) return gs;
+    if (auto_carried(a, us))
+      a.flags |= kAutoCarried;
+    else if (!(a.flags & (TPG_UNSTAGED | TPG_DEBUG_NO_GATE | TPG_IN_KERNEL_GATES)) && a.groups == 0 &&
+             2.0 * a.M * double(a.N) * a.K < kLatencyBoundFlop)
       a.flags |= TPG_SERIAL_STAGES;
     return run_call(*cx, a.flags | TPG_NO_GRAPH, std::string(), static_cast<hipStream_t>(stream),
                     [&](const Launch& L) { return enqueue_ag(*cx, a, L); });

@@ -118,6 +118,15 @@ struct GemmParams {
   int gate_nch, gate_ksteps, gate_local, gate_off;
   unsigned gate_need;
   unsigned gate_deadline;   // ticks of the 100 MHz clock per wait; 0: kGateDeadline
+  // Carried gates without a zeroing launch: with gate64 != nullptr the copy
+  // workgroups come first (blockIdx.x < cp_blocks, ahead of the tiles), each
+  // stamps *gate64 with (gate_token << 32 | count + 1) once its stores have
+  // completed (restarting the count when the word holds another token), and
+  // every tile of a delivered slice waits, before its first DMA, for
+  // *gate64 == (gate_token << 32 | gate_need). gate_nch and gate_ksteps are
+  // then 0 and the K-steps.
+  unsigned long long* gate64;
+  unsigned gate_token;
 };
 
 // Raises a kernel's dynamic-LDS limit on the current device the first time
@@ -233,6 +242,13 @@ hipError_t launch_deliver(const void* const* src, int n, size_t bytes, void* dst
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
 hipError_t static_scratch(void** ptr);
+// Token-stamped gate words of the carried in-kernel gates (scratch.hip): a
+// static device array, zero when the library loads, one 64-bit word per
+// call slot, resolved like the scratch. Calls take slots round-robin and
+// stamp them with a token that grows on every reuse of the slot, so a word
+// never has to be cleared before a call.
+constexpr int kGateWords = 4096;
+hipError_t gate_words(unsigned long long** ptr);
 
 // Bit-exact run permute used by dispatch / combine.
 struct PermuteParams {

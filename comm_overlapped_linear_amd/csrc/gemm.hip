@@ -684,7 +684,7 @@ __device__ __forceinline__ void copy_job(const GemmParams& p, int b) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const int64_t total = int64_t(p.cp_n) * p.cp_nvec;
   const int64_t step = int64_t(p.cp_blocks) * blockDim.x;
-  const bool gated = p.gate != nullptr;
+  const bool gated = p.gate != nullptr || p.gate64 != nullptr;
   for (int64_t i = int64_t(b) * blockDim.x + threadIdx.x; i < total; i += step) {
     const int sl = static_cast<int>(i / p.cp_nvec);
     const int64_t v = i - sl * p.cp_nvec;
@@ -700,7 +700,22 @@ __device__ __forceinline__ void copy_job(const GemmParams& p, int b) {
     // device coherence point) before it counts itself done
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(p.gate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      if (p.gate64 != nullptr) {
+        // (token << 32 | count): count one more under this call's token,
+        // starting from 1 if the word still holds an earlier call's token
+        const unsigned long long tok = static_cast<unsigned long long>(p.gate_token) << 32;
+        unsigned long long old = __hip_atomic_load(p.gate64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (;;) {
+          const unsigned long long nw = (old >> 32) == p.gate_token ? old + 1ull : (tok | 1ull);
+          if (__hip_atomic_compare_exchange_strong(p.gate64, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;
+        }
+      } else {
+        __hip_atomic_fetch_add(p.gate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -712,9 +727,13 @@ template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, boo
           bool GATE = false>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(const GemmParams p) {
   // workgroups past the tile workgroups carry the launch's copy job, if any
+  // (ahead of them with token-stamped gates: dispatched first, the copy can
+  // never wait behind tiles that wait for it)
   const int tile_grid = static_cast<int>(gridDim.x) - p.cp_blocks;
-  if (static_cast<int>(blockIdx.x) >= tile_grid) {
-    copy_job(p, static_cast<int>(blockIdx.x) - tile_grid);
+  const bool copy_first = GATE && p.gate64 != nullptr;
+  const int wg = copy_first ? static_cast<int>(blockIdx.x) - p.cp_blocks : static_cast<int>(blockIdx.x);
+  if (wg < 0 || wg >= tile_grid) {
+    copy_job(p, copy_first ? static_cast<int>(blockIdx.x) : wg - tile_grid);
     return;
   }
   const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
@@ -785,6 +804,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   // gated launches: the slice holding this tile's rows, and the counters of
   // its delivery slot (nullptr: no waits)
   const unsigned* gate_row = nullptr;
+  const unsigned long long* gate_word = nullptr;   // token-stamped word (carried copy)
   bool timed_out = false;
   const uint8_t* a_base = A;
   int64_t a_row0 = m0;
@@ -799,8 +819,9 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
     a_base = local ? p.a_local : p.a_slots + int64_t(slot) * p.a_slice_rows * lda_b;
     a_row0 = m0 - int64_t(sl) * p.a_slice_rows;
     if (p.gate != nullptr && !p.gate_off && !local) gate_row = p.gate + slot * p.gate_nch;
+    if (p.gate64 != nullptr && !p.gate_off && !local) gate_word = p.gate64;
     // the wait's state lives in VGPRs: the mainloop needs every SGPR
-    asm volatile("" : "+v"(gate_row));
+    asm volatile("" : "+v"(gate_row), "+v"(gate_word));
   }
   // This lane's source chunk in each DMA instruction, as a 32-bit offset
   // from a uniform base (the tile's first A row; B itself), which the host
@@ -858,19 +879,30 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
       bb = Bp + int64_t(kt) * b_step;
     }
     if constexpr (GATE) {
-      if (gate_row != nullptr) {
+      if (gate_row != nullptr || gate_word != nullptr) {
         // a K-step that starts a chunk waits for that chunk to have landed
         // (bounded: past the deadline the wait gives up and the tile's
         // output becomes NaN)
         if (kt % p.gate_ksteps == 0) {
-          const unsigned* g = gate_row + kt / p.gate_ksteps;
-          unsigned need = p.gate_need;
           unsigned deadline = p.gate_deadline != 0u ? p.gate_deadline : kGateDeadline;
-          asm volatile("" : "+v"(g), "+v"(need), "+v"(deadline));
           const unsigned t0 = static_cast<unsigned>(__builtin_amdgcn_s_memrealtime());
-          while (!timed_out && __hip_atomic_load(g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-            if (static_cast<unsigned>(__builtin_amdgcn_s_memrealtime()) - t0 > deadline) timed_out = true;
-            __builtin_amdgcn_s_sleep(2);
+          if (gate_word != nullptr) {
+            // the whole copy, stamped with this call's token
+            unsigned long long want =
+                (static_cast<unsigned long long>(p.gate_token) << 32) | static_cast<unsigned long long>(p.gate_need);
+            asm volatile("" : "+v"(want), "+v"(deadline));
+            while (!timed_out && __hip_atomic_load(gate_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+              if (static_cast<unsigned>(__builtin_amdgcn_s_memrealtime()) - t0 > deadline) timed_out = true;
+              __builtin_amdgcn_s_sleep(2);
+            }
+          } else {
+            const unsigned* g = gate_row + kt / p.gate_ksteps;
+            unsigned need = p.gate_need;
+            asm volatile("" : "+v"(g), "+v"(need), "+v"(deadline));
+            while (!timed_out && __hip_atomic_load(g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+              if (static_cast<unsigned>(__builtin_amdgcn_s_memrealtime()) - t0 > deadline) timed_out = true;
+              __builtin_amdgcn_s_sleep(2);
+            }
           }
         }
 #pragma unroll
@@ -1006,9 +1038,9 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm, tn);   // ends with a barrier: LDS free
   };
   if constexpr (persistent_tiles<Op, BM, BN, AT>()) {
-    for (int vt = blockIdx.x; vt < ntiles; vt += tile_grid) run_tile(vt);
+    for (int vt = wg; vt < ntiles; vt += tile_grid) run_tile(vt);
   } else {
-    run_tile(blockIdx.x);
+    run_tile(wg);
   }
 }
 

@@ -1,4 +1,5 @@
-// Static device scratch of the allocation-free all-gather entry point.
+// Static device scratch of the allocation-free all-gather entry point, and
+// the gate words of the carried in-kernel gates.
 //
 // The receive slots of tpgemm_stage_ag_noalloc live in a file-scope device
 // array, so that call needs no caller workspace and allocates nothing. Each
@@ -13,11 +14,14 @@
 #include "gemm.h"
 
 static __device__ __align__(256) uint8_t scratch[tpg::kStaticScratchBytes];
+// Gate words of the carried in-kernel gates (zero at load; see gemm.h).
+static __device__ __align__(256) unsigned long long gate_word[tpg::kGateWords];
 
 namespace tpg {
 
 namespace {
 void* g_scratch[kMaxDevices] = {};   // device address of `scratch` per device (nullptr: not resolved)
+void* g_words[kMaxDevices] = {};     // device address of `gate_word` per device
 }
 
 hipError_t static_scratch(void** ptr) {
@@ -33,6 +37,22 @@ hipError_t static_scratch(void** ptr) {
     g_scratch[dev] = p;
   }
   *ptr = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t gate_words(unsigned long long** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (g_words[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(gate_word));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+    g_words[dev] = p;
+  }
+  *ptr = static_cast<unsigned long long*>(g_words[dev]);
   return hipSuccess;
 }
 

@@ -169,9 +169,13 @@ enum {
  *                (contiguous) receive slots, and deliveries of slices that are
  *                adjacent in memory are merged into one copy. groups = P-1 is
  *                one gate per stage; 1 runs the local stage while everything
- *                else is delivered; 0 lets the library choose (one gate).
- *                Values above P-1 are clamped. The result does not depend on
- *                it.
+ *                else is delivered; 0 lets the library choose (one gate; a
+ *                latency-bound call, under 1 GFLOP, that meets the shape
+ *                rules of TPG_IN_KERNEL_GATES and is not being captured runs
+ *                as one GEMM launch carrying its deliveries, the delivered
+ *                slices' tiles waiting in-kernel for them; other latency-bound
+ *                calls run on one stream). Values above P-1 are clamped. The
+ *                result does not depend on it.
  *   schedule     TPG_ROTATE_A (the above) or TPG_ROTATE_B, the column dual
  *                (Approach: schedule AllGather1D_TilingCD_RotatingB; its
  *                layout is the plain reading stated here): A (M, K) is local,

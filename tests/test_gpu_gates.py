@@ -148,3 +148,31 @@ def test_no_gate_negative_control_rs():
     emitted = np.ones(case.M, dtype=bool)
     emitted[own] = False
     assert_parity(got[emitted], ref[emitted], "emitted blocks")
+
+
+def test_latency_bound_call_is_one_gated_launch():
+    """A latency-bound staged call with library-chosen grouping runs as one
+    GEMM launch that carries its deliveries and gates the delivered slices'
+    tiles in-kernel (one launch record over all M rows); with a test flag
+    that needs the deliveries on their own stream it keeps the two-launch
+    schedule. Both match the oracle on a poisoned workspace."""
+    case = W.AgCase("one_launch_bf16", M=8 * 128, N=264, K=256, P=8, rank=3, dist="u11")   # M/P % 128 == 0
+    inp = W.ag_inputs(case)
+    ref = oracle.gemm_ag(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, case.rank, case.dtype)
+    slices = [dev(s) for s in inp["a_slices"]]
+    b, c = dev(inp["b"]), dev(inp["c"])
+    kw = dict(M=case.M, N=case.N, K=case.K, rank=case.rank, alpha=case.alpha, beta=case.beta)
+    need = tp.stage_ag_workspace_size(tp.ag_args(slices, b, c, bf16_empty(case.M, case.N), **kw))
+    # one gated launch; else the local stage, then the remote stages (one
+    # launch per stretch of rows that does not wrap past slice P-1)
+    for flags, launches in ((tp.PROFILE, 1), (tp.PROFILE | HOLD, 3)):
+        say(f"latency-bound launch count: flags={flags}")
+        ws = poisoned(need, 2)
+        d = bf16_empty(case.M, case.N)
+        tp.profile_read()
+        tp.stage_ag(slices, b, c, d, flags=flags, groups=0, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        recs = tp.profile_read()
+        assert len(recs) == launches, recs
+        assert sum(r[1] for r in recs) == pytest.approx(case.flop)
+        assert_parity(host_f64(d), ref, f"flags={flags}")
