@@ -299,6 +299,7 @@ def cpu_baseline_ag(case, inp):
     slice against the whole B and K, repeated until about CPU_SECONDS of host
     time; throughput is the sample's flops over the time."""
     from oracle import cref
+    cref.ensure_built()
     rows = min(CPP_SAMPLE_ROWS, case.m)
     slices = [np.ascontiguousarray(s[:rows]) for s in inp["a_slices"]]
     c = inp["c"]

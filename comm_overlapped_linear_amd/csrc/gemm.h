@@ -249,6 +249,11 @@ hipError_t static_scratch(void** ptr);
 // never has to be cleared before a call.
 constexpr int kGateWords = 4096;
 hipError_t gate_words(unsigned long long** ptr);
+// Words of the cross-stream dependencies of eager calls (scratch.hip): a
+// static device array, zero at load; each dependency takes a word
+// round-robin and a value that grows on every reuse of the word.
+constexpr int kSyncWords = 65536;
+hipError_t sync_words(unsigned long long** ptr);
 
 // Bit-exact run permute used by dispatch / combine.
 struct PermuteParams {

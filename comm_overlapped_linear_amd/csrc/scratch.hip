@@ -16,44 +16,42 @@
 static __device__ __align__(256) uint8_t scratch[tpg::kStaticScratchBytes];
 // Gate words of the carried in-kernel gates (zero at load; see gemm.h).
 static __device__ __align__(256) unsigned long long gate_word[tpg::kGateWords];
+// Words of the cross-stream dependencies of eager calls (see gemm.h).
+static __device__ __align__(256) unsigned long long sync_word[tpg::kSyncWords];
 
 namespace tpg {
 
 namespace {
 void* g_scratch[kMaxDevices] = {};   // device address of `scratch` per device (nullptr: not resolved)
 void* g_words[kMaxDevices] = {};     // device address of `gate_word` per device
-}
+void* g_sync[kMaxDevices] = {};      // device address of `sync_word` per device
 
-hipError_t static_scratch(void** ptr) {
+// Device address of a static array on the current device, resolved once.
+hipError_t resolve(const void* symbol, void** cache, void** ptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  if (g_scratch[dev] == nullptr) {
+  if (cache[dev] == nullptr) {
     void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    e = hipGetSymbolAddress(&p, symbol);
     if (e != hipSuccess) return e;
     if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
-    g_scratch[dev] = p;
+    cache[dev] = p;
   }
-  *ptr = g_scratch[dev];
+  *ptr = cache[dev];
   return hipSuccess;
 }
+}
+
+hipError_t static_scratch(void** ptr) { return resolve(HIP_SYMBOL(scratch), g_scratch, ptr); }
 
 hipError_t gate_words(unsigned long long** ptr) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  if (g_words[dev] == nullptr) {
-    void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(gate_word));
-    if (e != hipSuccess) return e;
-    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
-    g_words[dev] = p;
-  }
-  *ptr = static_cast<unsigned long long*>(g_words[dev]);
-  return hipSuccess;
+  return resolve(HIP_SYMBOL(gate_word), g_words, reinterpret_cast<void**>(ptr));
+}
+
+hipError_t sync_words(unsigned long long** ptr) {
+  return resolve(HIP_SYMBOL(sync_word), g_sync, reinterpret_cast<void**>(ptr));
 }
 
 }  // namespace tpg

@@ -23,12 +23,19 @@ _LAYOUT = {"nk": 0, "kn": 1}
 
 def build():
     """Compiles liboracle.so beside its source (g++ -O2 -fopenmp)."""
-    tmp = LIB + ".tmp"
+    tmp = f"{LIB}.{os.getpid()}.tmp"        # concurrent builders each write their own
     cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, SRC]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("g++ failed on the C++ oracle:\n" + r.stderr)
     os.replace(tmp, LIB)
+    return LIB
+
+
+def ensure_built():
+    """Builds liboracle.so if it is missing or older than its source."""
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        build()
     return LIB
 
 

@@ -156,3 +156,31 @@ def test_in_kernel_gates_bounded_wait():
                 assert_parity(got[rows], ref[rows], "local slice")
             else:
                 assert np.isnan(got[rows]).all(), f"slice {s}: a tile that gave up did not write NaN"
+
+
+def test_static_words_survive_release_caches():
+    """The library's static gate and dependency words keep their last values
+    when tpg_release_caches drops the per-device contexts, so the numbers that
+    stamp them must not start again: a wait would then pass at once. With
+    the deliveries held 20 ms behind the host and the receive slots poisoned,
+    a run that passed its wait early reads NaN. Both forms: the staged
+    schedule on several streams (stream memory operations between them) and
+    the latency-bound call carrying its deliveries (a token-stamped word)."""
+    staged = CASES[4]
+    for case, flags in ((staged, HOLD), (CASES[0], 0)):
+        ref, slices, b, c = setup(case)
+        probe = bf16_empty(case.M, case.N)
+        need = tp.stage_ag_workspace_size(tp.ag_args(slices, b, c, probe, M=case.M, N=case.N, K=case.K,
+                                                     rank=case.rank, flags=flags))
+        ws = poisoned(need, 2)
+        outs = []
+        for life in range(2):
+            say(f"static words: {case.name} flags={flags} life {life}")
+            ws[:slot_bytes(case)] = poisoned(slot_bytes(case), 2)
+            d = call(case, slices, b, c, flags | tp.NO_GRAPH, ws)
+            got = host_f64(d)
+            assert not np.isnan(got).any(), f"{case.name}/life {life}: a wait passed before its delivery"
+            assert_parity(got, ref, f"{case.name}/life {life}")
+            outs.append(d.cpu())
+            tp.release_caches()
+        assert torch.equal(outs[0], outs[1])

@@ -14,7 +14,7 @@ from synth import workloads as W
 
 @pytest.fixture(scope="module", autouse=True)
 def built():
-    cref.build()
+    cref.ensure_built()
 
 
 def close(got, ref):
