@@ -152,3 +152,29 @@ def test_ag_stage_groups_are_bitwise_identical(contiguous):
             outs.append(d.cpu())
     assert_parity(host_f64(d), ref, "groups")
     assert all(torch.equal(o, outs[0]) for o in outs)
+
+
+# One launch over all rows (the unstaged call) whose 256 x 256 tiles would
+# end in a partial round: 4096 x 4352 is 272 tiles on 256 CUs, so the
+# launcher runs the first 4096 columns as one whole round and the last 256
+# columns as a second launch of 128 x 256 tiles. Column offsets of B (both
+# layouts), C and D must then land right.
+ROUND_SPLIT = [
+    W.AgCase("ag_bf16_round_split", M=4096, N=4352, K=256, P=2, rank=1, dist="u11", alpha=0.5, beta=1.0),
+    W.AgCase("ag_bf16_kn_round_split", M=4096, N=4352, K=192, P=2, rank=0, b_layout="kn", beta=-1.0),
+    W.AgCase("ag_e4m3_round_split", M=4096, N=4352, K=384, P=2, rank=1, dtype="e4m3", dist="n05",
+             c_dist="n01"),
+]
+
+
+@pytest.mark.parametrize("case", ROUND_SPLIT, ids=lambda c: c.name)
+def test_ag_round_split_launch(case):
+    inp = W.ag_inputs(case)
+    ref = oracle_ag(case, inp)
+    outs = {}
+    for name in ("unstaged", "default"):
+        say(f"ag: {case.name} mode={name}")
+        d = run_ag(case, inp, MODES[name])
+        assert_parity(host_f64(d), ref, f"{case.name}/{name}")
+        outs[name] = d.cpu()
+    assert torch.equal(outs["unstaged"], outs["default"])
