@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <deque>
 #include <limits>
 #include <chrono>
 #include <thread>
@@ -80,13 +81,46 @@ struct GraphEntry {
   hipEvent_t done = nullptr;
 };
 
-// Numbers handed out for the static gate words (calls that took a
-// token-stamped gate word) and the static dependency words (cross-stream
-// dependencies issued as stream memory operations) of one device.
-struct WordSeq {
-  uint64_t gate = 0;
-  uint64_t sync = 0;
+// Numbers handed out for one static word array of a device: number n is
+// word n mod size, stamped with n / size + 1.
+//
+// The dependency words: every word a call stamps is written on one of the
+// library's internal streams, or awaited there (the fork, a run's wait for
+// its deliveries), so once each internal stream has passed a point, every
+// dependency of the calls issued before it has been both written and read.
+// The numbers are therefore handed out in blocks: when a call ends with at
+// least kSyncBlock numbers taken since the last block closed, the block is
+// closed with an event on each internal stream; before number n is handed
+// out, the block holding n - size must have completed (its events fired), so
+// calls in flight never share a word, whatever streams they run on. That
+// wait blocks the host only when the device lags so far behind that calls
+// in flight hold all but a block of the array. No call stamps more than a
+// block's worth.
+//
+// The gate words (one per latency-bound call carrying its deliveries, on the
+// caller's stream only) are simply many: two calls share a word only 65536
+// such calls apart, and a call whose word another call in flight stamped
+// over does not pass its gate: its tiles give up after the bounded wait and
+// write NaN.
+struct WordRing {
+  struct Block {
+    uint64_t first;                 // the block's first number
+    hipEvent_t done[kStreams];      // fired once all of its calls' dependencies have been written and read
+  };
+  uint64_t next = 0;
+  uint64_t open = 0;                // first number of the block not yet closed
+  std::deque<Block> closed;
 };
+
+// The gate words (calls that took a token-stamped gate word) and the
+// dependency words (cross-stream dependencies issued as stream memory
+// operations) of one device, with completed events kept for reuse.
+struct WordSeq {
+  WordRing gate, sync;
+  std::vector<hipEvent_t> spare;
+};
+
+constexpr uint64_t kSyncBlock = tpg::kSyncWords / 8;
 
 struct Ctx {
   int device = -1;
@@ -100,6 +134,7 @@ struct Ctx {
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> prof_pool;
   WordSeq* seq = nullptr;            // this device's gate and dependency word numbers
+  uint64_t sync_first = 0;           // the dependency word number next when the current call began
   bool capturing = false;            // the call being enqueued is being recorded into a graph
 };
 
@@ -240,6 +275,62 @@ tpg_status gemm_on(Ctx& cx, const Launch& L, hipStream_t s, const tpg::GemmParam
   return prof_end(cx, L, s, rec);
 }
 
+// Next gate word number (a token-stamped word of the static array).
+uint64_t take_gate_number(WordSeq& ws) { return ws.gate.next++; }
+
+// Next dependency word number, for a call that took its first at call_first
+// (or takes this one first).
+tpg_status take_sync_number(WordSeq& ws, uint64_t call_first, uint64_t* out) {
+  WordRing& r = ws.sync;
+  const uint64_t n = r.next;
+  if (n - call_first >= kSyncBlock)
+    return fail(TPG_ERR_UNSUPPORTED, "a call with more cross-stream dependencies than the library tracks at once");
+  if (n >= tpg::kSyncWords) {
+    while (!r.closed.empty() && r.closed.front().first <= n - tpg::kSyncWords) {
+      for (int i = 1; i < kStreams; ++i) {
+        HIP_TRY(hipEventSynchronize(r.closed.front().done[i]));
+        ws.spare.push_back(r.closed.front().done[i]);
+      }
+      r.closed.pop_front();
+    }
+  }
+  *out = r.next++;
+  return TPG_OK;
+}
+
+// After an eager call: close the dependency words' open block once it holds
+// kSyncBlock numbers. A call that failed part way may have marked
+// dependencies its streams never awaited: the host waits for the streams
+// instead, after which every number handed out so far is free.
+tpg_status close_sync_block(Ctx& cx, hipStream_t stream, bool failed) {
+  WordSeq& ws = *cx.seq;
+  WordRing& r = ws.sync;
+  if (failed) {
+    if (r.next == cx.sync_first) return TPG_OK;          // this call stamped nothing
+    for (int i = 1; i < kStreams; ++i) (void)hipStreamSynchronize(cx.comp[i]);
+    (void)hipStreamSynchronize(stream);
+    for (auto& b : r.closed)
+      for (int i = 1; i < kStreams; ++i) ws.spare.push_back(b.done[i]);
+    r.closed.clear();
+    r.open = r.next;
+    return TPG_OK;
+  }
+  if (r.next - r.open < kSyncBlock) return TPG_OK;
+  WordRing::Block b{r.open, {}};
+  for (int i = 1; i < kStreams; ++i) {
+    if (!ws.spare.empty()) {
+      b.done[i] = ws.spare.back();
+      ws.spare.pop_back();
+    } else {
+      HIP_TRY(hipEventCreateWithFlags(&b.done[i], hipEventDisableTiming));
+    }
+    HIP_TRY(hipEventRecord(b.done[i], cx.comp[i]));
+  }
+  r.closed.push_back(b);
+  r.open = r.next;
+  return TPG_OK;
+}
+
 // A cross-stream dependency: marked on the producing stream after its work
 // so far, awaited on the consuming one. An eager call marks it with a
 // stream memory operation: a 64-bit word of a static device array, taken
@@ -266,7 +357,8 @@ tpg_status dep_mark(Ctx& cx, hipEvent_t ev, hipStream_t from, Dep* d, bool as_ev
   }
   unsigned long long* words = nullptr;
   HIP_TRY(tpg::sync_words(&words));
-  const uint64_t seq = cx.seq->sync++;
+  uint64_t seq = 0;
+  if (tpg_status st = take_sync_number(*cx.seq, cx.sync_first, &seq); st != TPG_OK) return st;
   *d = Dep{nullptr, words + seq % tpg::kSyncWords, seq / tpg::kSyncWords + 1};
   HIP_TRY(hipStreamWriteValue64(from, d->word, d->value, 0));
   return TPG_OK;
@@ -367,7 +459,12 @@ tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t
                     const std::function<tpg_status(const Launch&)>& enqueue) {
   const bool eager = !(flags & TPG_FORCE_GRAPH) ||
                      (flags & (TPG_NO_GRAPH | TPG_PROFILE | TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE)) != 0;
-  if (eager) return enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
+  if (eager) {
+    cx.sync_first = cx.seq->sync.next;
+    const tpg_status st = enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
+    const tpg_status cs = close_sync_block(cx, user, st != TPG_OK);
+    return st != TPG_OK ? st : cs;
+  }
   auto it = cx.graphs.find(key);
   if (it == cx.graphs.end()) {
     // retired graphs whose last replay has completed are destroyed; the
@@ -387,8 +484,11 @@ tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t
     }
     HIP_TRY(hipStreamBeginCapture(cx.capture, hipStreamCaptureModeThreadLocal));
     cx.capturing = true;                      // dependencies as events (recordable)
+    const uint64_t g0 = cx.seq->gate.next, s0 = cx.seq->sync.next;
     tpg_status st = enqueue(Launch{cx.capture, false});
     cx.capturing = false;
+    if (st == TPG_OK && (cx.seq->gate.next != g0 || cx.seq->sync.next != s0))   // a replay would repeat them
+      st = fail(TPG_ERR_UNSUPPORTED, "internal: a static word was stamped in a recorded call");
     hipGraph_t g = nullptr;
     hipError_t e = hipStreamEndCapture(cx.capture, &g);
     if (st != TPG_OK) {
@@ -848,7 +948,7 @@ tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, cons
     // token-stamped word (a slot of the static array, no zeroing launch)
     unsigned long long* words = nullptr;
     HIP_TRY(tpg::gate_words(&words));
-    const uint64_t seq = cx.seq->gate++;
+    const uint64_t seq = take_gate_number(*cx.seq);
     p.gate = nullptr;
     p.gate64 = words + seq % tpg::kGateWords;
     p.gate_token = static_cast<unsigned>(seq / tpg::kGateWords + 1);   // never 0: the words start at 0
@@ -1029,7 +1129,7 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
       for (int t = t0(g); t < t0(g + 1); ++t) src[t - t0(g)] = a.a_slices[(r + t) % P];
       stat = deliver_slices(ck, src, t0(g + 1) - t0(g), slice_b, ws + (t0(g) - 1) * slice_b, slice_b, L.root);
       if (stat != TPG_OK) return stat;
-      if (g < G - 1 && ns > 1) {
+      if (g < G - 1 && ns > 1 && !no_gate) {
         stat = dep_mark(cx, cx.ev_copy[g], L.root, &copied[g]);
         if (stat != TPG_OK) return stat;
       }

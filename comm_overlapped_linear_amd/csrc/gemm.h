@@ -247,11 +247,12 @@ hipError_t static_scratch(void** ptr);
 // call slot, resolved like the scratch. Calls take slots round-robin and
 // stamp them with a token that grows on every reuse of the slot, so a word
 // never has to be cleared before a call.
-constexpr int kGateWords = 4096;
+constexpr int kGateWords = 65536;
 hipError_t gate_words(unsigned long long** ptr);
 // Words of the cross-stream dependencies of eager calls (scratch.hip): a
 // static device array, zero at load; each dependency takes a word
-// round-robin and a value that grows on every reuse of the word.
+// round-robin and a value that grows on every reuse of the word (the host
+// hands a word out again only once its previous users have completed).
 constexpr int kSyncWords = 65536;
 hipError_t sync_words(unsigned long long** ptr);
 
