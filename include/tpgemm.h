@@ -29,7 +29,13 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t, NULL = the
  *     legacy default stream): the call forks its internal streams from
  *     `stream` and joins them back before returning, so work enqueued later
- *     on `stream` sees the results. No call blocks the host on the GPU.
+ *     on `stream` sees the results. No call blocks the host on the GPU,
+ *     with two exceptions: a call that fails after enqueuing work waits for
+ *     the streams it used; and a call waits for older calls to finish when
+ *     the device lags so far behind the host that calls in flight hold 7/8
+ *     of the library's 65536 cross-stream dependency words (a dependency
+ *     between the library's streams is a stream memory write and wait on
+ *     one of them; a word is reused only once its last user has finished).
  *   - Inputs are never written (p04 statement, "Interface, layout, and
  *     parameters": inputs must not be mutated).
  *   - Arguments are validated before anything is enqueued; a failing call
@@ -43,11 +49,12 @@
  *     35, SwiGLU AG 250 vs 273; bf16 RS 477 vs 472). A staged AG or RS call
  *     of under 1 GFLOP that leaves the grouping to the library
  *     (groups = 0) is latency-bound and runs as if TPG_SERIAL_STAGES were
- *     set: the same stages in the same order on one stream, without the
- *     cross-stream events; an all-gather's deliveries (library copy kernel,
- *     one remote run) are then carried by the local stage's own launch, as
- *     extra workgroups that copy the slices beside its tiles (20.1 -> 17.6 us
- *     for the P = 2 bf16 share). TPG_NO_GRAPH, TPG_PROFILE and
+ *     set: the same stages in the same order on one stream, without
+ *     cross-stream dependencies. An all-gather that also meets the shape
+ *     rules of TPG_IN_KERNEL_GATES (and whose stream is not being captured)
+ *     instead runs as one launch carrying its deliveries as extra workgroups,
+ *     the delivered slices' tiles waiting inside the kernel for them (20.1 ->
+ *     14.3 us for the P = 2 bf16 share). TPG_NO_GRAPH, TPG_PROFILE and
  *     TPG_DEBUG_HOLD_DELIVERIES never replay a graph.
  *   - Graph cache: a recorded graph is keyed by (entry point, shapes,
  *     pointers, scalars, flags). A changed pointer makes a new graph, never
