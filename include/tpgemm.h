@@ -5,7 +5,9 @@
  * stages. The peers' shards are ordinary device buffers in the same HBM;
  * each stage's input is delivered by an asynchronous device-to-device copy
  * (the library's copy kernel, the runtime's shader copy or the SDMA copy
- * engines, below) and gated by a HIP event, so the matrix cores start on
+ * engines, below) and gated by a cross-stream dependency (a stream memory
+ * write and wait on a word of the library's; a HIP event in a recorded
+ * graph), so the matrix cores start on
  * the local shard while the rest is delivered ("Distributed GEMM", Hassani
  * et al., SHI Labs, Dec 2024: Introduction and Background, Figures 3 and 4).
  * Which copy: the all-gather's deliveries are on its critical path, so it
@@ -172,7 +174,7 @@ enum {
  *                is 0. Contents are scratch.
  *   groups       how the P-1 remote stages are gated: they are cut, in ring
  *                order, into `groups` runs of consecutive stages; each run
- *                gets one completion event and one GEMM launch over its
+ *                gets one completion dependency and one GEMM launch over its
  *                (contiguous) receive slots, and deliveries of slices that are
  *                adjacent in memory are merged into one copy. groups = P-1 is
  *                one gate per stage; 1 runs the local stage while everything
@@ -252,7 +254,7 @@ tpg_status tpgemm_stage_ag_noalloc(const tpg_ag_args* args, void* stream);
  * stock layouts). For i < n_out:
  *   d[i] = alpha * A * b[i]^T,   A = the P row slices gathered in rank order,
  * staged exactly as tpgemm_stage_ag (stage t multiplies slice (rank + t) mod
- * P, local first, deliveries gated by events). The projections run as one
+ * P, local first, deliveries gated as there). The projections run as one
  * GEMM over the weights side by side, each output column block stored to
  * its own d[i]; weights that do not already sit back to back in memory are
  * copied side by side into the workspace first.
