@@ -164,6 +164,9 @@ ROUND_SPLIT = [
     W.AgCase("ag_bf16_kn_round_split", M=4096, N=4352, K=192, P=2, rank=0, b_layout="kn", beta=-1.0),
     W.AgCase("ag_e4m3_round_split", M=4096, N=4352, K=384, P=2, rank=1, dtype="e4m3", dist="n05",
              c_dist="n01"),
+    # a ragged last tile-row (4000 rows: 16 tile-rows of 256, the last 160
+    # rows deep) and a ragged remainder (4344 columns: 248 after the split)
+    W.AgCase("ag_bf16_round_split_ragged", M=4000, N=4344, K=256, P=2, rank=0, dist="u11", beta=1.0),
 ]
 
 
