@@ -135,7 +135,7 @@ struct Ctx {
   std::vector<hipEvent_t> prof_pool;
   WordSeq* seq = nullptr;            // this device's gate and dependency word numbers
   uint64_t sync_first = 0;           // the dependency word number next when the current call began
-  bool capturing = false;            // the call being enqueued is being recorded into a graph
+  bool capturing = false;            // the call being enqueued is being recorded into a graph (ours or the caller's)
 };
 
 std::mutex g_mu;
@@ -455,13 +455,26 @@ tpg_status deliver_slices(Copy k, const void* const* src, int n, size_t bytes, c
 // runs it eagerly.
 // Issue policy (stated and measured in tpgemm.h): eager unless
 // TPG_FORCE_GRAPH asks for a recorded graph.
+bool stream_capturing(hipStream_t stream);
+
 tpg_status run_call(Ctx& cx, uint32_t flags, const std::string& key, hipStream_t user,
                     const std::function<tpg_status(const Launch&)>& enqueue) {
   const bool eager = !(flags & TPG_FORCE_GRAPH) ||
                      (flags & (TPG_NO_GRAPH | TPG_PROFILE | TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE)) != 0;
   if (eager) {
+    // a caller recording its stream into a graph records this call too: its
+    // dependencies must then be events, which join the internal streams to
+    // the capture and replay correctly
+    cx.capturing = stream_capturing(user);
     cx.sync_first = cx.seq->sync.next;
     const tpg_status st = enqueue(Launch{user, (flags & TPG_PROFILE) != 0});
+    const bool recorded = cx.capturing;
+    cx.capturing = false;
+    if (recorded) {
+      if (st == TPG_OK && cx.seq->sync.next != cx.sync_first)
+        return fail(TPG_ERR_UNSUPPORTED, "internal: a static word was stamped in a recorded call");
+      return st;
+    }
     const tpg_status cs = close_sync_block(cx, user, st != TPG_OK);
     return st != TPG_OK ? st : cs;
   }
