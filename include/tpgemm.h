@@ -58,6 +58,11 @@
  *     the delivered slices' tiles waiting inside the kernel for them (20.1 ->
  *     14.3 us for the P = 2 bf16 share). TPG_NO_GRAPH, TPG_PROFILE and
  *     TPG_DEBUG_HOLD_DELIVERIES never replay a graph.
+ *   - A caller may record a call into its own graph by capturing `stream`
+ *     around it: the call then orders its internal streams with events,
+ *     which join them to the capture, and never takes the latency-bound
+ *     single-launch form (its token would replay). TPG_IN_KERNEL_GATES
+ *     calls are refused under capture.
  *   - Graph cache: a recorded graph is keyed by (entry point, shapes,
  *     pointers, scalars, flags). A changed pointer makes a new graph, never
  *     a stale replay. Freeing a buffer a cached graph refers to is safe as
