@@ -118,9 +118,14 @@ struct WordRing {
 struct WordSeq {
   WordRing gate, sync;
   std::vector<hipEvent_t> spare;
+  bool events_made = false;
 };
 
 constexpr uint64_t kSyncBlock = tpg::kSyncWords / 8;
+// Closed blocks held at once: at most the array's blocks, plus the one that
+// a wrapping number is about to free. Their events are created with the
+// device's first context, so later calls create none.
+constexpr int kSyncBlockEvents = int(tpg::kSyncWords / kSyncBlock + 1) * (kStreams - 1);
 
 struct Ctx {
   int device = -1;
@@ -161,7 +166,19 @@ tpg_status make_ctx(int dev, Ctx** out) {
   Ctx* c = new Ctx();
   c->device = dev;
   c->seq = &g_seq[dev];            // element references survive rehashing
-  const tpg_status st = make_ctx_into(c);
+  tpg_status st = TPG_OK;
+  if (!c->seq->events_made) {
+    while (c->seq->spare.size() < size_t(kSyncBlockEvents) && st == TPG_OK) {
+      hipEvent_t e = nullptr;
+      const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (err != hipSuccess)
+        st = fail(TPG_ERR_HIP, std::string("hipEventCreateWithFlags failed: ") + hipGetErrorString(err));
+      else
+        c->seq->spare.push_back(e);
+    }
+    if (st == TPG_OK) c->seq->events_made = true;
+  }
+  if (st == TPG_OK) st = make_ctx_into(c);
   if (st != TPG_OK) {
     destroy_ctx(c);
     return st;
