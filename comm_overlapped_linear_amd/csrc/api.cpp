@@ -98,10 +98,11 @@ struct GraphEntry {
 // block's worth.
 //
 // The gate words (one per latency-bound call carrying its deliveries, on the
-// caller's stream only) are simply many: two calls share a word only 65536
-// such calls apart, and a call whose word another call in flight stamped
-// over does not pass its gate: its tiles give up after the bounded wait and
-// write NaN.
+// caller's stream only) are counters that only grow: each copy workgroup of
+// a call adds 1, and the host, which enqueued every add, knows the total a
+// call's tiles wait for. They are simply many: two calls share a word only
+// 2^20 such calls apart, so that two calls sharing one are never in flight
+// at once (their adds would mix).
 struct WordRing {
   struct Block {
     uint64_t first;                 // the block's first number
@@ -112,13 +113,14 @@ struct WordRing {
   std::deque<Block> closed;
 };
 
-// The gate words (calls that took a token-stamped gate word) and the
+// The gate words (calls that took a gate counter) and the
 // dependency words (cross-stream dependencies issued as stream memory
 // operations) of one device, with completed events kept for reuse.
 struct WordSeq {
   WordRing gate, sync;
   std::vector<hipEvent_t> spare;
   bool events_made = false;
+  std::vector<uint64_t> gate_total;   // each gate word's count: all the adds enqueued to it so far
 };
 
 constexpr uint64_t kSyncBlock = tpg::kSyncWords / 8;
@@ -178,6 +180,7 @@ tpg_status make_ctx(int dev, Ctx** out) {
     }
     if (st == TPG_OK) c->seq->events_made = true;
   }
+  if (c->seq->gate_total.empty()) c->seq->gate_total.assign(tpg::kGateWords, 0);
   if (st == TPG_OK) st = make_ctx_into(c);
   if (st != TPG_OK) {
     destroy_ctx(c);
@@ -292,7 +295,7 @@ tpg_status gemm_on(Ctx& cx, const Launch& L, hipStream_t s, const tpg::GemmParam
   return prof_end(cx, L, s, rec);
 }
 
-// Next gate word number (a token-stamped word of the static array).
+// Next gate word number (a counter of the static array).
 uint64_t take_gate_number(WordSeq& ws) { return ws.gate.next++; }
 
 // Next dependency word number, for a call that took its first at call_first
@@ -571,7 +574,7 @@ tpg_status validate_in_kernel_gates(uint32_t flags, bool supported) {
 }
 
 // In-kernel gates depend on the copy running while the GEMM waits (and the
-// carried form on a per-call token): a call being captured into a graph
+// carried form on a count known when it is issued): a call being captured into a graph
 // cannot take them.
 // Whether `stream` is being captured (a failed query counts as captured, and
 // its error is cleared so that no later launch check reports it).
@@ -905,8 +908,8 @@ bool carried_gates_fit(const tpg_ag_args& a, int dtype, int epi) {
 // one gated launch carrying its deliveries (the staged all-gather's
 // prepended per-stage wait inside one persistent launch): the shape rules of
 // TPG_IN_KERNEL_GATES, the library's copy kernel, eager issue, and a caller
-// stream that is not being captured (a replayed token would pass the gate
-// without waiting).
+// stream that is not being captured (a replay would wait for a count its
+// counter has already passed).
 bool auto_carried(const tpg_ag_args& a, hipStream_t stream) {
   if (a.schedule != TPG_ROTATE_A || a.groups != 0 || a.P < 2 || a.P > tpg::kMaxGateSlices) return false;
   if (a.flags & (TPG_UNSTAGED | TPG_SERIAL_STAGES | TPG_FORCE_GRAPH | TPG_COPY_SDMA | TPG_COPY_SHADER |
@@ -932,7 +935,7 @@ bool auto_carried(const tpg_ag_args& a, hipStream_t stream) {
 // workgroups fit on the chip at once instead carries the deliveries in the
 // GEMM launch itself, as extra workgroups that each bump one counter when
 // done, and its delivered slices' tiles wait for all of them before their
-// first DMA: one stream and one launch, the counter a token-stamped word
+// first DMA: one stream and one launch, the counter a word
 // of a static array (no zeroing launch). (Not with
 // TPG_DEBUG_HOLD_DELIVERIES or TPG_DEBUG_NO_GATE, whose tests need the
 // deliveries on a stream of their own.)
@@ -975,13 +978,13 @@ tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, cons
 
   if (carried_gates_fit(a, dtype, epi)) {
     // the copy rides in the GEMM launch, its workgroups first; one
-    // token-stamped word (a slot of the static array, no zeroing launch)
+    // counter (a slot of the static array that only grows: no zeroing launch)
     unsigned long long* words = nullptr;
     HIP_TRY(tpg::gate_words(&words));
-    const uint64_t seq = take_gate_number(*cx.seq);
+    const size_t w = static_cast<size_t>(take_gate_number(*cx.seq) % tpg::kGateWords);
+    std::vector<uint64_t>& total = cx.seq->gate_total;
     p.gate = nullptr;
-    p.gate64 = words + seq % tpg::kGateWords;
-    p.gate_token = static_cast<unsigned>(seq / tpg::kGateWords + 1);   // never 0: the words start at 0
+    p.gate64 = words + w;
     p.cp_blocks = carried_copy_blocks(slice_b, P);
     p.cp_n = P - 1;
     for (int t = 1; t < P; ++t) p.cp_src[t - 1] = static_cast<const uint8_t*>(a.a_slices[(r + t) % P]);
@@ -990,8 +993,10 @@ tpg_status enqueue_ag_gated(Ctx& cx, const tpg_ag_args& a, const Launch& L, cons
     p.cp_nvec = static_cast<int64_t>(slice_b / 16);
     p.gate_nch = 0;          // one word for every delivered slice
     p.gate_ksteps = nk;      // waited for once, before a tile's first DMA
-    p.gate_need = static_cast<unsigned>(p.cp_blocks) + extra;
-    return gemm_on(cx, L, L.root, p, dtype, layout, epi);
+    p.gate_want64 = total[w] + static_cast<uint64_t>(p.cp_blocks) + extra;
+    const tpg_status gs = gemm_on(cx, L, L.root, p, dtype, layout, epi);
+    if (gs == TPG_OK) total[w] += static_cast<uint64_t>(p.cp_blocks);   // the copy workgroups' adds
+    return gs;
   }
   if (a.flags & kAutoCarried) return fail(TPG_ERR_INVALID, "internal: carried gates chosen but not possible");
   HIP_TRY(tpg::launch_fill_zero16(gate, kGateCounterBytes, L.root));

@@ -120,13 +120,13 @@ struct GemmParams {
   unsigned gate_deadline;   // ticks of the 100 MHz clock per wait; 0: kGateDeadline
   // Carried gates without a zeroing launch: with gate64 != nullptr the copy
   // workgroups come first (blockIdx.x < cp_blocks, ahead of the tiles), each
-  // stamps *gate64 with (gate_token << 32 | count + 1) once its stores have
-  // completed (restarting the count when the word holds another token), and
-  // every tile of a delivered slice waits, before its first DMA, for
-  // *gate64 == (gate_token << 32 | gate_need). gate_nch and gate_ksteps are
-  // then 0 and the K-steps.
+  // adds 1 to *gate64 once its stores have completed (one atomic add, no
+  // compare-and-swap), and every tile of a delivered slice waits, before its
+  // first DMA, for *gate64 == gate_want64: the word's count before this
+  // launch (kept by the host, which knows every add to it) plus cp_blocks.
+  // gate_nch and gate_ksteps are then 0 and the K-steps.
   unsigned long long* gate64;
-  unsigned gate_token;
+  unsigned long long gate_want64;
 };
 
 // Raises a kernel's dynamic-LDS limit on the current device the first time
@@ -242,12 +242,12 @@ hipError_t launch_deliver(const void* const* src, int n, size_t bytes, void* dst
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
 hipError_t static_scratch(void** ptr);
-// Token-stamped gate words of the carried in-kernel gates (scratch.hip): a
-// static device array, zero when the library loads, one 64-bit word per
-// call slot, resolved like the scratch. Calls take slots round-robin and
-// stamp them with a token that grows on every reuse of the slot, so a word
-// never has to be cleared before a call.
-constexpr int kGateWords = 65536;
+// Gate words of the carried in-kernel gates (scratch.hip): a static device
+// array, zero when the library loads, one 64-bit counter per call slot,
+// resolved like the scratch. Calls take slots round-robin; a counter only
+// ever grows, and the host keeps each one's total, so a word never has to
+// be cleared before a call.
+constexpr int kGateWords = 1 << 20;
 hipError_t gate_words(unsigned long long** ptr);
 // Words of the cross-stream dependencies of eager calls (scratch.hip): a
 // static device array, zero at load; each dependency takes a word

@@ -702,16 +702,10 @@ __device__ __forceinline__ void copy_job(const GemmParams& p, int b) {
     __syncthreads();
     if (threadIdx.x == 0) {
       if (p.gate64 != nullptr) {
-        // (token << 32 | count): count one more under this call's token,
-        // starting from 1 if the word still holds an earlier call's token
-        const unsigned long long tok = static_cast<unsigned long long>(p.gate_token) << 32;
-        unsigned long long old = __hip_atomic_load(p.gate64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (;;) {
-          const unsigned long long nw = (old >> 32) == p.gate_token ? old + 1ull : (tok | 1ull);
-          if (__hip_atomic_compare_exchange_strong(p.gate64, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT))
-            break;
-        }
+        // one add per workgroup: the host knows the count every earlier
+        // call left and waits for it plus this launch's copy workgroups (a
+        // compare-and-swap loop here cost a round trip per retry)
+        __hip_atomic_fetch_add(p.gate64, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         __hip_atomic_fetch_add(p.gate, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -727,7 +721,7 @@ template <typename Op, int BM, int BN, int WM, int WN, int ROWB, int STAGES, boo
           bool GATE = false>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(const GemmParams p) {
   // workgroups past the tile workgroups carry the launch's copy job, if any
-  // (ahead of them with token-stamped gates: dispatched first, the copy can
+  // (ahead of them with a carried gate counter: dispatched first, the copy can
   // never wait behind tiles that wait for it)
   const int tile_grid = static_cast<int>(gridDim.x) - p.cp_blocks;
   const bool copy_first = GATE && p.gate64 != nullptr;
@@ -804,7 +798,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   // gated launches: the slice holding this tile's rows, and the counters of
   // its delivery slot (nullptr: no waits)
   const unsigned* gate_row = nullptr;
-  const unsigned long long* gate_word = nullptr;   // token-stamped word (carried copy)
+  const unsigned long long* gate_word = nullptr;   // the carried copy's counter
   bool timed_out = false;
   const uint8_t* a_base = A;
   int64_t a_row0 = m0;
@@ -887,9 +881,8 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
           unsigned deadline = p.gate_deadline != 0u ? p.gate_deadline : kGateDeadline;
           const unsigned t0 = static_cast<unsigned>(__builtin_amdgcn_s_memrealtime());
           if (gate_word != nullptr) {
-            // the whole copy, stamped with this call's token
-            unsigned long long want =
-                (static_cast<unsigned long long>(p.gate_token) << 32) | static_cast<unsigned long long>(p.gate_need);
+            // the whole copy: the counter's total once every copy workgroup has added to it
+            unsigned long long want = p.gate_want64;
             asm volatile("" : "+v"(want), "+v"(deadline));
             while (!timed_out && __hip_atomic_load(gate_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
               if (static_cast<unsigned>(__builtin_amdgcn_s_memrealtime()) - t0 > deadline) timed_out = true;

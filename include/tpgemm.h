@@ -61,7 +61,7 @@
  *   - A caller may record a call into its own graph by capturing `stream`
  *     around it: the call then orders its internal streams with events,
  *     which join them to the capture, and never takes the latency-bound
- *     single-launch form (its token would replay). TPG_IN_KERNEL_GATES
+ *     single-launch form (a replay would wait on a stale count). TPG_IN_KERNEL_GATES
  *     calls are refused under capture.
  *   - Graph cache: a recorded graph is keyed by (entry point, shapes,
  *     pointers, scalars, flags). A changed pointer makes a new graph, never
