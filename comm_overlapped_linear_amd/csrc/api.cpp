@@ -68,6 +68,14 @@ constexpr size_t kGateCounterBytes = size_t(tpg::kMaxGateSlices) * kMaxGateChunk
 // well under the few microseconds each cross-stream event costs (the P = 2
 // bf16 workload: 20 us on one stream, 40-45 us on two).
 constexpr double kLatencyBoundFlop = 1e9;
+// The staged all-gather runs as one launch carrying its deliveries (its
+// tiles and copy workgroups all on the chip at once) up to this many flops.
+// Measured on MI355X against the default multi-stream schedule, bf16, µs:
+// 1024^3 in 2 slices 17.0 vs 33-35, 4096 x 512 x 1024 in 8: 28.5 vs 38-39,
+// 1024 x 2048 x 4096 in 4: 53.5 vs 72, 1024 x 1024 x 8192 in 8: 95.5 vs 116;
+// but 2048 x 1024 x 8192 in 2 (34 GFLOP): 99 vs 65, whose remote tiles read
+// their one 16 MiB delivered slice device-coherently, past L2, eight times.
+constexpr double kCarriedMaxFlop = 2e10;
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -892,20 +900,20 @@ int carried_copy_blocks(size_t slice_b, int P) {
   return static_cast<int>((n + 7) / 8 * 8);
 }
 
-// A gated call that carries its deliveries in the GEMM launch: latency-bound,
-// every tile and copy workgroup on the chip at once, and no test flag that
-// needs the deliveries on a stream of their own.
+// A gated call that carries its deliveries in the GEMM launch: under
+// kCarriedMaxFlop, every tile and copy workgroup on the chip at once, and no
+// test flag that needs the deliveries on a stream of their own.
 bool carried_gates_fit(const tpg_ag_args& a, int dtype, int epi) {
   const int P = a.P;
-  if (P < 2 || P - 1 > tpg::kMaxCopySlices || 2.0 * a.M * double(a.N) * a.K >= kLatencyBoundFlop) return false;
+  if (P < 2 || P - 1 > tpg::kMaxCopySlices || 2.0 * a.M * double(a.N) * a.K >= kCarriedMaxFlop) return false;
   if (a.flags & (TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE | TPG_NO_COPY)) return false;
   const size_t slice_b = size_t(a.M / P) * a.K * elem_bytes(a.ab_dtype);
   return tpg::gated_tiles(static_cast<int>(a.M), static_cast<int>(a.N), dtype, epi) + carried_copy_blocks(slice_b, P) <=
          tpg::device_cus();
 }
 
-// Whether a latency-bound staged call with library-chosen grouping can run as
-// one gated launch carrying its deliveries (the staged all-gather's
+// Whether a staged call with library-chosen grouping can run as one gated
+// launch carrying its deliveries (the staged all-gather's
 // prepended per-stage wait inside one persistent launch): the shape rules of
 // TPG_IN_KERNEL_GATES, the library's copy kernel, eager issue, and a caller
 // stream that is not being captured (a replay would wait for a count its
@@ -931,8 +939,8 @@ bool auto_carried(const tpg_ag_args& a, hipStream_t stream) {
 // for that chunk's counter. The copy kernel runs beside it on a side stream,
 // K-chunk-major, storing write-through and bumping the counter of each
 // chunk it completes; the counters are zeroed on the root first.
-// A latency-bound call (under kLatencyBoundFlop) whose tiles and copy
-// workgroups fit on the chip at once instead carries the deliveries in the
+// A call under kCarriedMaxFlop whose tiles and copy workgroups fit on the
+// chip at once instead carries the deliveries in the
 // GEMM launch itself, as extra workgroups that each bump one counter when
 // done, and its delivered slices' tiles wait for all of them before their
 // first DMA: one stream and one launch, the counter a word

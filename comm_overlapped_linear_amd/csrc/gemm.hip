@@ -680,20 +680,37 @@ struct Interleave {
 // The copy job of a launch that carries stage deliveries (GemmParams cp_*):
 // workgroup b of the p.cp_blocks copy workgroups strides over the vectors of
 // every slice.
+constexpr int kCopyUnroll = 4;
+
 __device__ __forceinline__ void copy_job(const GemmParams& p, int b) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const int64_t total = int64_t(p.cp_n) * p.cp_nvec;
   const int64_t step = int64_t(p.cp_blocks) * blockDim.x;
   const bool gated = p.gate != nullptr || p.gate64 != nullptr;
-  for (int64_t i = int64_t(b) * blockDim.x + threadIdx.x; i < total; i += step) {
-    const int sl = static_cast<int>(i / p.cp_nvec);
-    const int64_t v = i - sl * p.cp_nvec;
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cp_src[sl]) + v);
-    u32x4* dst = reinterpret_cast<u32x4*>(p.cp_dst + sl * p.cp_dst_stride) + v;
-    if (gated)   // read by this launch's gated tiles: system-scope store
-      asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(dst), "v"(x) : "memory");
-    else
-      *dst = x;
+  // kCopyUnroll vectors in flight per thread: their loads are all issued
+  // before the first store
+  for (int64_t i0 = int64_t(b) * blockDim.x + threadIdx.x; i0 < total; i0 += kCopyUnroll * step) {
+    u32x4 x[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * step;
+      if (i < total) {
+        const int sl = static_cast<int>(i / p.cp_nvec);
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cp_src[sl]) + (i - sl * p.cp_nvec));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * step;
+      if (i < total) {
+        const int sl = static_cast<int>(i / p.cp_nvec);
+        u32x4* dst = reinterpret_cast<u32x4*>(p.cp_dst + sl * p.cp_dst_stride) + (i - sl * p.cp_nvec);
+        if (gated)   // read by this launch's gated tiles: system-scope store
+          asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(dst), "v"(x[u]) : "memory");
+        else
+          *dst = x[u];
+      }
+    }
   }
   if (gated) {
     // every store of this workgroup has completed (and is visible at the

@@ -52,11 +52,13 @@
  *     of under 1 GFLOP that leaves the grouping to the library
  *     (groups = 0) is latency-bound and runs as if TPG_SERIAL_STAGES were
  *     set: the same stages in the same order on one stream, without
- *     cross-stream dependencies. An all-gather that also meets the shape
- *     rules of TPG_IN_KERNEL_GATES (and whose stream is not being captured)
- *     instead runs as one launch carrying its deliveries as extra workgroups,
- *     the delivered slices' tiles waiting inside the kernel for them (20.1 ->
- *     14.3 us for the P = 2 bf16 share). TPG_NO_GRAPH, TPG_PROFILE and
+ *     cross-stream dependencies. An all-gather under 20 GFLOP with library
+ *     grouping that meets the shape rules of TPG_IN_KERNEL_GATES, whose
+ *     tiles and copy workgroups fit on the chip at once and whose stream is
+ *     not being captured instead runs as one launch carrying its deliveries
+ *     as extra workgroups, the delivered slices' tiles waiting inside the
+ *     kernel for them (P = 2 bf16 share 256 x 256 x 512: 20.1 -> 11.4 us;
+ *     1024^3 in 2 slices: 34 -> 17 us). TPG_NO_GRAPH, TPG_PROFILE and
  *     TPG_DEBUG_HOLD_DELIVERIES never replay a graph.
  *   - A caller may record a call into its own graph by capturing `stream`
  *     around it: the call then orders its internal streams with events,
@@ -132,11 +134,11 @@ enum {
                                  the tiles of each delivered slice wait inside the kernel, K-chunk
                                  by K-chunk, on counters that the library's copy kernel (running
                                  beside it on an internal stream) bumps as each chunk lands. No
-                                 stage boundaries between launches. A latency-bound call (under
-                                 1 GFLOP) whose tiles and copy workgroups fit on the chip at once
-                                 (and without the two TPG_DEBUG_* delivery flags) carries the copy
-                                 in the GEMM launch itself as extra workgroups, one counter for
-                                 all of them: one stream, a zeroing kernel and one launch.
+                                 stage boundaries between launches. A call under 20 GFLOP whose
+                                 tiles and copy workgroups fit on the chip at once (and without
+                                 the two TPG_DEBUG_* delivery flags) carries the copy in the GEMM
+                                 launch itself as extra workgroups, one counter for all of them:
+                                 one stream and one launch.
                                  Needs P <= 8, M/P a multiple of 128, K * element bytes a
                                  multiple of 128 and the copy kernel
                                  (no other TPG_COPY_* flag); rejected with TPG_UNSTAGED,
@@ -184,11 +186,12 @@ enum {
  *                adjacent in memory are merged into one copy. groups = P-1 is
  *                one gate per stage; 1 runs the local stage while everything
  *                else is delivered; 0 lets the library choose (one gate; a
- *                latency-bound call, under 1 GFLOP, that meets the shape
- *                rules of TPG_IN_KERNEL_GATES and is not being captured runs
- *                as one GEMM launch carrying its deliveries, the delivered
- *                slices' tiles waiting in-kernel for them; other latency-bound
- *                calls run on one stream). Values above P-1 are clamped. The
+ *                call under 20 GFLOP that meets the shape rules of
+ *                TPG_IN_KERNEL_GATES, fits on the chip with its copy
+ *                workgroups and is not being captured runs as one GEMM launch
+ *                carrying its deliveries, the delivered slices' tiles waiting
+ *                in-kernel for them; other calls under 1 GFLOP run on one
+ *                stream). Values above P-1 are clamped. The
  *                result does not depend on it.
  *   schedule     TPG_ROTATE_A (the above) or TPG_ROTATE_B, the column dual
  *                (Approach: schedule AllGather1D_TilingCD_RotatingB; its

@@ -160,12 +160,14 @@ def test_in_kernel_gates_bounded_wait():
 
 def test_static_words_survive_release_caches():
     """The library's static gate and dependency words keep their last values
-    when tpg_release_caches drops the per-device contexts, so the numbers that
-    stamp them must not start again: a wait would then pass at once. With
-    the deliveries held 20 ms behind the host and the receive slots poisoned,
-    a run that passed its wait early reads NaN. Both forms: the staged
-    schedule on several streams (stream memory operations between them) and
-    the latency-bound call carrying its deliveries (a token-stamped word)."""
+    when tpg_release_caches drops the per-device contexts, so the host's
+    record of them (the numbers that stamp the dependency words, the totals
+    the gate counters have reached) must survive too: a wait would otherwise
+    pass at once or never. With the deliveries held 20 ms behind the host and
+    the receive slots poisoned, a run that passed its wait early reads NaN.
+    Both forms: the staged schedule on several streams (stream memory
+    operations between them) and the latency-bound call carrying its
+    deliveries (one gate counter)."""
     staged = CASES[4]
     for case, flags in ((staged, HOLD), (CASES[0], 0)):
         ref, slices, b, c = setup(case)

@@ -21,14 +21,14 @@ SYNC_WORDS = 65536
 HOLD_CYCLES = 400_000_000          # about 200 ms of the shader clock
 
 
-def prepared_pair(case, inp):
+def prepared_pair(case, inp, groups=0):
     slices = [dev(s) for s in inp["a_slices"]]
     b, c = dev(inp["b"]), dev(inp["c"])
     outs, calls = [], []
     for _ in range(2):             # one output and workspace per stream
         d = bf16_empty(case.M, case.N)
         calls.append(tp.prepare_stage_ag(slices, b, c, d, M=case.M, N=case.N, K=case.K, rank=case.rank,
-                                         alpha=case.alpha, beta=case.beta))
+                                         alpha=case.alpha, beta=case.beta, groups=groups))
         outs.append(d)
     return calls, outs, (slices, b, c)
 
@@ -69,7 +69,7 @@ def test_dependency_words_reused_across_streams():
     assert 2.0 * case.M * case.N * case.K >= 1e9       # not latency-bound: a staged call on two streams
     inp = W.ag_inputs(case)
     ref = oracle.gemm_ag(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, case.rank)
-    calls, outs, keep = prepared_pair(case, inp)
+    calls, outs, keep = prepared_pair(case, inp, groups=1)   # one explicit run: never the one-launch form
     calls[0]()
     torch.cuda.synchronize()
     assert_parity(host_f64(outs[0]), ref, case.name)
