@@ -908,7 +908,8 @@ bool carried_gates_fit(const tpg_ag_args& a, int dtype, int epi) {
   if (P < 2 || P - 1 > tpg::kMaxCopySlices || 2.0 * a.M * double(a.N) * a.K >= kCarriedMaxFlop) return false;
   if (a.flags & (TPG_DEBUG_HOLD_DELIVERIES | TPG_DEBUG_NO_GATE | TPG_NO_COPY)) return false;
   const size_t slice_b = size_t(a.M / P) * a.K * elem_bytes(a.ab_dtype);
-  return tpg::gated_tiles(static_cast<int>(a.M), static_cast<int>(a.N), dtype, epi) + carried_copy_blocks(slice_b, P) <=
+  const int cp = carried_copy_blocks(slice_b, P);
+  return tpg::gated_tiles(static_cast<int>(a.M), static_cast<int>(a.N), dtype, epi, cp) + cp <=
          tpg::device_cus();
 }
 

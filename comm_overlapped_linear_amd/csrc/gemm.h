@@ -153,7 +153,7 @@ int device_cus();
 // Output tiles the DMA launcher would make for this shape and CU budget.
 int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget);
 // Output tiles of a gated launch (GemmParams a_slice_rows > 0).
-int gated_tiles(int M, int N, int dtype, int epi);
+int gated_tiles(int M, int N, int dtype, int epi, int copy_wgs);
 
 // Picks a tile shape for (M, N) and launches on `s`. Host-side checks of the
 // shapes and alignment are the caller's job (api.cpp validates every call).

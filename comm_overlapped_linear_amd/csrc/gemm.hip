@@ -1228,7 +1228,7 @@ hipError_t dispatch_tile(const GemmParams& p, hipStream_t s) {
         p.M / p.a_slice_rows > kMaxGateSlices || p.gate_local < -1 ||
         p.gate_local >= p.M / p.a_slice_rows || !p.a_slots || (p.gate_local >= 0 && !p.a_local))
       return hipErrorInvalidValue;
-    if (!gated_small_tile(p.M, p.N, Op::kElemBytes == 1 ? kE4m3 : kBf16, epi))
+    if (!gated_small_tile(p.M, p.N, Op::kElemBytes == 1 ? kE4m3 : kBf16, epi, p.cp_blocks))
       return launch_dma_tile<Op, 128, 256, 2, 4, 128, 3, KN, SW, false, true>(p, s);
     if constexpr (SW) return launch_dma_tile<Op, 128, 128, 4, 2, 128, 4, KN, SW, false, true>(p, s);
     else if constexpr (Op::kElemBytes == 2) return launch_dma_tile<Op, 128, 128, 2, 4, 128, 4, KN, SW, false, true>(p, s);
@@ -1330,18 +1330,19 @@ hipError_t launch_mfma_probe(int dtype, int iters, int blocks, unsigned long lon
   return hipGetLastError();
 }
 
-// Tile of a gated launch: 128 x 256, or 128 x 128 when 128 x 256 tiles
-// would fill at most half the chip (a latency-bound call: twice the CUs,
-// half the time per tile). The e4m3 alpha/beta 128 x 128 form is left out:
-// with the gate's registers it needs a stack frame.
-bool gated_small_tile(int M, int N, int dtype, int epi) {
+// Tile of a gated launch: 128 x 256, or 128 x 128 when twice as many tiles
+// still fit on the chip beside the copy workgroups the launch carries
+// (copy_wgs; 0 with the copy on a stream of its own): twice the CUs, half
+// the time per tile. The e4m3 alpha/beta 128 x 128 form is left out: with
+// the gate's registers it needs a stack frame.
+bool gated_small_tile(int M, int N, int dtype, int epi, int copy_wgs) {
   if (dtype == kE4m3 && epi != kEpiSwiglu) return false;
   const int ncols = epi == kEpiSwiglu ? (N / 2 + 127) / 128 : (N + 255) / 256;
-  return int64_t((M + 127) / 128) * ncols * 2 <= cu_count();
+  return int64_t((M + 127) / 128) * ncols * 2 + copy_wgs <= cu_count();
 }
 
-int gated_tiles(int M, int N, int dtype, int epi) {
-  const bool small = gated_small_tile(M, N, dtype, epi);
+int gated_tiles(int M, int N, int dtype, int epi, int copy_wgs) {
+  const bool small = gated_small_tile(M, N, dtype, epi, copy_wgs);
   const int bn = small ? 128 : 256;
   const int ncols = epi == kEpiSwiglu ? (N / 2 + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
   return ((M + 127) / 128) * ncols;
