@@ -1093,13 +1093,20 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
     return true;
   };
   const bool no_gate = (a.flags & TPG_DEBUG_NO_GATE) != 0;
-  // A run whose slices pass slice P-1 writes two stretches of output rows,
-  // one launch each; the second goes on a stream of its own, beside the
-  // first (on one stream, one after the other, the two took twice as long:
-  // 1024 x 2048 x 16384 bf16 in 4 slices at rank 1, 207 against 109 us
-  // unstaged).
+  // A run whose slices pass slice P-1 writes two stretches of output rows.
+  // With slices of a multiple of 256 rows (no tile straddles the wrap) it is
+  // one launch whose tiles past the wrap write P * m rows earlier, reading A
+  // from the slots in arrival order or, in place, from the slices back to
+  // back from a_slices[0]. Otherwise it is one launch per stretch, the
+  // second on a stream of its own beside the first (on one stream, one
+  // after the other, the two took twice as long: 1024 x 2048 x 16384 bf16
+  // in 4 slices at rank 1, 207 against 109 us unstaged).
+  auto passes_last = [&](int g) { return (r + t0(g)) % P + (t0(g + 1) - t0(g)) > P; };
+  tpg::GemmParams probe = p;
+  probe.M = static_cast<int>(m);
+  const bool wrap_one = m % 256 == 0 && tpg::wrap_in_one_launch(probe, dtype, layout) && (copies || adjacent(0, P));
   bool wraps = false;
-  for (int g = 0; g < G && !no_gate; ++g) wraps = wraps || (r + t0(g)) % P + (t0(g + 1) - t0(g)) > P;
+  for (int g = 0; g < G && !no_gate; ++g) wraps = wraps || (!wrap_one && passes_last(g));
   const int ns = (a.flags & TPG_SERIAL_STAGES) ? 1 : std::min(G + 1 + (wraps ? 1 : 0), kStreams);
   const bool split_side = wraps && ns > 2;
   hipStream_t st[kStreams];
@@ -1115,13 +1122,19 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
     return static_cast<int>(std::min<int64_t>(tpg::device_cus(),
                                               std::max<int64_t>(8, int64_t(tpg::device_cus()) * stages * stack / P)));
   };
-  auto launch_rows = [&](hipStream_t cs, const void* A, int s, int run, int cus, const tpg::GemmParams* job) {
+  auto launch_rows = [&](hipStream_t cs, const void* A, int s, int run, int cus, const tpg::GemmParams* job,
+                         int wrap_row = 0) {
     tpg::GemmParams q = p;
     q.a = A;
     q.M = static_cast<int>(run * m);
     q.c = a.c ? static_cast<const uint16_t*>(a.c) + s * m * nout : nullptr;
     set_out_rows(q, a, segs, s * m, nout);
     q.cu_budget = cus;
+    if (wrap_row > 0) {
+      q.wrap_row = wrap_row;
+      q.wrap_back = static_cast<int>(P * m);
+      q.wrap_a = copies ? 0 : 1;
+    }
     if (job) {
       q.cp_blocks = job->cp_blocks;
       q.cp_n = job->cp_n;
@@ -1202,7 +1215,14 @@ tpg_status enqueue_ag(Ctx& cx, const tpg_ag_args& a, const Launch& L, const OutS
       stat = dep_await(cs, copied[g]);
       if (stat != TPG_OK) return stat;
     }
-    const bool run_wraps = split_side && (r + t0(g)) % P + (t0(g + 1) - t0(g)) > P;
+    if (wrap_one && passes_last(g)) {
+      const int s = (r + t0(g)) % P, run = t0(g + 1) - t0(g);
+      const void* A = copies ? static_cast<const void*>(ws + (t0(g) - 1) * slice_b) : a.a_slices[s];
+      stat = launch_rows(cs, A, s, run, budget(run), nullptr, static_cast<int>((P - s) * m));
+      if (stat != TPG_OK) return stat;
+      continue;
+    }
+    const bool run_wraps = split_side && passes_last(g);
     for (int t = t0(g); t < t0(g + 1);) {
       const int s = (r + t) % P;
       int run = std::min(t0(g + 1) - t, P - s);
@@ -1560,12 +1580,17 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   // it sizes its tiles for the CUs the emitted launches leave idle in their
   // last round of tiles, so that it fills that round instead of adding one.
   int64_t emitted_tiles = 0;
-  auto launch_blocks = [&](hipStream_t cs, int blk, int run, bool own) {
+  auto launch_blocks = [&](hipStream_t cs, int blk, int run, bool own, int wrap_row = 0) {
     tpg::GemmParams q = p;
     if (!tileb) {     // row blocks: rows of A and D
       q.M = static_cast<int>(run * m);
       q.a = static_cast<const char*>(a.a) + size_t(blk) * m * a.K * eb;
       q.d = static_cast<uint16_t*>(a.d) + blk * m * a.N;
+      if (wrap_row > 0) {    // blocks past P-1: A's and D's rows P * m earlier
+        q.wrap_row = wrap_row;
+        q.wrap_back = static_cast<int>(P * m);
+        q.wrap_a = 1;
+      }
     } else {          // column blocks: rows of B (NK) or its columns (KN), columns of D
       q.M = static_cast<int>(a.M);
       q.a = a.a;
@@ -1585,11 +1610,23 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
     }
     return gemm_on(cx, L, cs, q, dtype, layout, tpg::kEpiAlphaBeta);
   };
+  // A run of row blocks that passes block P-1 is one launch whose tiles
+  // past the wrap go P * m rows back (blocks of a multiple of 256 rows: no
+  // tile straddles the wrap), else one launch per stretch.
+  tpg::GemmParams probe = p;
+  probe.M = static_cast<int>(m);
+  const bool wrap_one = !tileb && m % 256 == 0 && tpg::wrap_in_one_launch(probe, dtype, layout);
   // Stream roles as in the all-gather: the emitted runs on the other streams
   // start at once; the root takes the deliveries and then the own block,
   // which reads them, in stream order.
   for (int g = 0; g < G; ++g) {
     hipStream_t cs = side(g);
+    const int first = (r + 1 + t0(g)) % P, span = t0(g + 1) - t0(g);
+    if (wrap_one && first + span > P) {
+      stat = launch_blocks(cs, first, span, false, static_cast<int>((P - first) * m));
+      if (stat != TPG_OK) return stat;
+      continue;
+    }
     for (int t = t0(g); t < t0(g + 1);) {
       const int blk = (r + 1 + t) % P;
       const int run = std::min(t0(g + 1) - t, P - blk);

@@ -43,6 +43,13 @@ struct GemmParams {
   int add_row0, add_row1;
   int add_col0, add_col1;
   int vec_ok;                  // 1 if ldc, ldd and ld_add are multiples of 8 (16-byte row vectors)
+  // A run of stages that wraps past the last slice as one launch: with
+  // wrap_row > 0 (a multiple of the tile height), the tiles at or past row
+  // wrap_row write C's and D's rows wrap_back earlier, and with wrap_a also
+  // read A's rows wrap_back earlier. (Direct-to-LDS kernel, row-major A.)
+  int wrap_row;
+  int wrap_back;
+  int wrap_a;
   // batched launch (blockIdx.y = batch index): element strides between the
   // operands of consecutive batches (0 = shared); C and addends unbatched
   int batch;                   // >= 1
@@ -158,6 +165,9 @@ int gated_tiles(int M, int N, int dtype, int epi, int copy_wgs);
 // Picks a tile shape for (M, N) and launches on `s`. Host-side checks of the
 // shapes and alignment are the caller's job (api.cpp validates every call).
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s);
+// Whether launch_gemm runs a wrapping launch (GemmParams wrap_row > 0) of
+// these operands as one kernel (else as two launches, one per stretch).
+bool wrap_in_one_launch(const GemmParams& p, int dtype, int layout);
 
 // launch_gemm with the copy job of p (cp_n slices, see GemmParams) done by
 // extra workgroups of the same launch when the direct-to-LDS kernel runs the

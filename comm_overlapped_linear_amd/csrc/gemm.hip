@@ -834,6 +834,15 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
     // the wait's state lives in VGPRs: the mainloop needs every SGPR
     asm volatile("" : "+v"(gate_row), "+v"(gate_word));
   }
+  // a tile past the wrap of a run that goes on past the last slice writes
+  // (and reads C of) rows wrap_back earlier, and with wrap_a reads A there too
+  int tm_out = tm;
+  if constexpr (!GATE && !AT) {
+    if (p.wrap_row > 0 && m0 >= p.wrap_row) {
+      tm_out = tm - p.wrap_back / BM;
+      if (p.wrap_a) a_row0 = m0 - p.wrap_back;
+    }
+  }
   // This lane's source chunk in each DMA instruction, as a 32-bit offset
   // from a uniform base (the tile's first A row; B itself), which the host
   // keeps below 2^31. Rows past the edge read a valid row instead (their
@@ -1045,7 +1054,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
           for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_nanf("");
     }
   }
-  store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm, tn);   // ends with a barrier: LDS free
+  store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm_out, tn);   // ends with a barrier: LDS free
   };
   if constexpr (persistent_tiles<Op, BM, BN, AT>()) {
     for (int vt = wg; vt < ntiles; vt += tile_grid) run_tile(vt);
@@ -1359,6 +1368,24 @@ int gemm_tiles(int M, int N, int dtype, int epi, int batch, int cu_budget) {
 hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s) {
   const bool kn = layout == kKN, sw = epi == kEpiSwiglu;
   const int64_t eb = dtype == kE4m3 ? 1 : 2;
+  if (p.wrap_row > 0) {
+    if (p.wrap_row >= p.M || p.wrap_row % 256 != 0 || p.wrap_back % 256 != 0 || p.wrap_back < p.wrap_row ||
+        p.M % 256 != 0 || p.batch != 1 || p.a_slice_rows != 0 || p.add_row1 > p.add_row0)
+      return hipErrorInvalidValue;
+    if (!dma_path(p, eb, kn)) {
+      // the register-staged kernel takes no wrap: the two stretches as two launches
+      GemmParams head = p, tail = p;
+      head.wrap_row = tail.wrap_row = 0;
+      head.M = p.wrap_row;
+      tail.M = p.M - p.wrap_row;
+      const int64_t back = int64_t(p.wrap_row) - p.wrap_back;       // the tail's first output row, from d
+      tail.a = static_cast<const char*>(p.a) + (p.wrap_a ? back : int64_t(p.wrap_row)) * p.lda * eb;
+      tail.d = p.d + back * p.ldd;
+      if (p.c) tail.c = p.c + back * p.ldc;
+      if (hipError_t e = launch_gemm(head, dtype, layout, epi, s); e != hipSuccess) return e;
+      return launch_gemm(tail, dtype, layout, epi, s);
+    }
+  }
   if (const int n1 = round_split_cols(p, epi); n1 > 0 && dma_path(p, eb, kn)) {
     GemmParams left = p, right = p;
     left.N = n1;
@@ -1376,6 +1403,10 @@ hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipS
   }
   if (kn) return hipErrorInvalidValue;     // fp8 is NK only (validated on the host)
   return sw ? dispatch_tile<OpE4m3, false, true>(p, s) : dispatch_tile<OpE4m3, false, false>(p, s);
+}
+
+bool wrap_in_one_launch(const GemmParams& p, int dtype, int layout) {
+  return dma_path(p, dtype == kE4m3 ? 1 : 2, layout == kKN);
 }
 
 hipError_t launch_gemm_carrying_copy(const GemmParams& p, int dtype, int layout, int epi, hipStream_t s) {
