@@ -479,12 +479,14 @@ def bench_rs(case, args):
     ms = time_steps(lambda: call(flags=0), steps, 3)
     mc = time_steps(lambda: call(flags=tp.NO_COPY), steps, 3)
     msh = time_steps(lambda: call(flags=tp.COPY_SHADER), steps, 3)
+    msd = time_steps(lambda: call(flags=tp.COPY_SDMA), steps, 3)
     peak = PEAK_TFLOPS["bf16"]
     kinds = profile_launches(lambda f: call(flags=f), max(2, args.steps // 10), peak)
     call(flags=0)
     tf = case.flop / (ms * 1e-3) / 1e12
     return dict(us=round(ms * 1e3, 1), tflops=round(tf, 1), pct_bf16_peak=round(100 * tf / peak, 2),
-                us_shader_copy=round(msh * 1e3, 1), us_compute_only=round(mc * 1e3, 1),
+                us_shader_copy=round(msh * 1e3, 1), us_copy_engines=round(msd * 1e3, 1),
+                us_compute_only=round(mc * 1e3, 1),
                 roofline=gemm_roofline(kinds, peak))
 
 

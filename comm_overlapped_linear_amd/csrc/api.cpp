@@ -1495,7 +1495,7 @@ tpg_status enqueue_rs(Ctx& cx, const tpg_rs_args& a, const Launch& L) {
   const size_t part_b = rs_part_bytes(&a);
   const size_t slot = rs_slot(&a);
   char* ws = static_cast<char*>(a.workspace);
-  const Copy ck = copy_of(a.flags, Copy::Sdma);
+  const Copy ck = copy_of(a.flags, Copy::Kernel);
 
   // peers whose partial for block `rank` arrives, in ring order rank+1, rank+2, ...
   std::vector<int> peers;

@@ -10,15 +10,17 @@
  * graph), so the matrix cores start on
  * the local shard while the rest is delivered ("Distributed GEMM", Hassani
  * et al., SHI Labs, Dec 2024: Introduction and Background, Figures 3 and 4).
- * Which copy: the all-gather's deliveries are on its critical path, so it
- * uses the library's own copy kernel (non-temporal loads, eight 16-byte
- * vectors in flight per thread: seven 8 MiB slices in 22.8 us with cold
- * caches, against 40 us for the runtime's copies and ~64 us on the SDMA
- * copy engines). The reduce-scatter's deliveries hide behind the emitted
- * blocks, so it uses the copy engines, which take no CUs from those GEMMs,
- * as the pages' copy-engine design intends (the bf16 RS share: equal within
- * noise, 460 vs 459 us against the shader copy). TPG_COPY_SDMA /
- * TPG_COPY_SHADER / TPG_COPY_KERNEL override either default (one at most).
+ * Which copy: by default the library's own copy kernel (non-temporal
+ * loads, eight 16-byte vectors in flight per thread: seven 8 MiB slices in
+ * 22.8 us with cold caches, against 40 us for the runtime's copies and
+ * ~64 us on the SDMA copy engines). The all-gather's deliveries are on its
+ * critical path; the reduce-scatter's hide behind the emitted blocks, and
+ * there too the copy kernel measured fastest, although its workgroups take
+ * CUs from those GEMMs where the pages' design uses copy engines (the bf16
+ * RS share, 8192 x 8192 x 3584 in 8 blocks: 403-404 us, against 413 with the
+ * shader copy and 423-430 on the copy engines; tiling B 403-405 / 415 /
+ * 455-459). TPG_COPY_SDMA / TPG_COPY_SHADER / TPG_COPY_KERNEL override the
+ * default (one at most).
  *
  * Conventions shared by every entry point
  *   - All pointers to tensor data are DEVICE pointers owned by the caller;
@@ -112,14 +114,14 @@ enum {
   TPG_UNSTAGED = 1u,        /* single stage: deliver everything, then one GEMM (the non-overlapped baseline) */
   TPG_NO_COPY = 2u,         /* read peer buffers in place; no deliveries (compute-only timing) */
   TPG_NO_GRAPH = 4u,        /* enqueue eagerly even with TPG_FORCE_GRAPH */
-  TPG_COPY_SDMA = 8u,       /* deliver with the SDMA copy engines (no CUs); the RS default */
+  TPG_COPY_SDMA = 8u,       /* deliver with the SDMA copy engines (no CUs) */
   TPG_SERIAL_STAGES = 16u,  /* run all stage GEMMs on one compute stream (no inter-stage concurrency) */
   TPG_PROFILE = 32u,        /* eager only: time every GEMM launch with HIP events (tpg_profile_read) */
   TPG_FORCE_GRAPH = 64u,    /* record the call into a hipGraph once, replay it after */
   TPG_DEBUG_HOLD_DELIVERIES = 128u, /* testing: issue eagerly, with the deliveries queued behind a 20 ms
                                        host callback; every gated stage must still see its data */
   TPG_COPY_SHADER = 256u,   /* deliver with the runtime's shader copy (hipMemcpyAsync, uses CUs) */
-  TPG_COPY_KERNEL = 512u,   /* deliver with the library's copy kernel (uses CUs); the AG and wgrad default */
+  TPG_COPY_KERNEL = 512u,   /* deliver with the library's copy kernel (uses CUs); the default */
   TPG_DEBUG_NO_GATE = 1024u, /* testing, the negative control of the gate tests: staged rotating-A
                                all-gathers and reduce-scatters issue every stage run that reads
                                delivered data on an internal stream WITHOUT waiting for its
