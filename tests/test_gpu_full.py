@@ -9,6 +9,8 @@ properties that hold at any size: staged equals unstaged bit for bit, and
 the own reduce-scatter block minus the incoming partials equals the plain
 partial at a tolerance scaled to that partial.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -22,7 +24,10 @@ from tests.parity import assert_parity
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-@pytest.mark.parametrize("case", [W.C2, W.C2_BETA0], ids=lambda c: c.name)
+# rank 3 of 8: the remote run passes slice 7 and goes on from slice 0, one
+# launch whose tiles past the wrap write 8192 rows earlier
+@pytest.mark.parametrize("case", [W.C2, W.C2_BETA0, dataclasses.replace(W.C2, name=W.C2.name + "_rank3", rank=3)],
+                         ids=lambda c: c.name)
 def test_full_ag_fp8(case):
     say(f"full: {case.name} generate")
     inp = W.ag_inputs(case)
@@ -43,8 +48,11 @@ def test_full_ag_fp8(case):
     assert torch.equal(d, d2)
 
 
-def test_full_rs_bf16():
-    case = W.C3
+# rank 4 of 8: the emitted blocks 5, 6, 7, 0, 1, 2, 3 as one launch whose
+# tiles past block 7 read A and write D 8192 rows earlier
+@pytest.mark.parametrize("case", [W.C3, dataclasses.replace(W.C3, name=W.C3.name + "_rank4", rank=4)],
+                         ids=lambda c: c.name)
+def test_full_rs_bf16(case):
     say(f"full: {case.name} generate")
     inp = W.rs_inputs(case)
     a, b = dev(inp["a"]), dev(inp["b"])
