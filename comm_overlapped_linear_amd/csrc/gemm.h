@@ -50,6 +50,12 @@ struct GemmParams {
   int wrap_row;
   int wrap_back;
   int wrap_a;
+  // The same along columns (a run of B column slices): with wrap_col > 0 (a
+  // multiple of 256) the tiles at or past column wrap_col write C's and D's
+  // columns wrap_back_col earlier; B is read unshifted. (Direct-to-LDS
+  // kernel, alpha/beta epilogue, no addends.)
+  int wrap_col;
+  int wrap_back_col;
   // batched launch (blockIdx.y = batch index): element strides between the
   // operands of consecutive batches (0 = shared); C and addends unbatched
   int batch;                   // >= 1

@@ -1054,7 +1054,11 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
           for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_nanf("");
     }
   }
-  store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm_out, tn);   // ends with a barrier: LDS free
+  int tn_out = tn;
+  if constexpr (!GATE && !AT && !SWIGLU) {
+    if (p.wrap_col > 0 && tn * BN >= p.wrap_col) tn_out = tn - p.wrap_back_col / BN;
+  }
+  store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm_out, tn_out);   // ends with a barrier: LDS free
   };
   if constexpr (persistent_tiles<Op, BM, BN, AT>()) {
     for (int vt = wg; vt < ntiles; vt += tile_grid) run_tile(vt);
@@ -1192,7 +1196,8 @@ int pick_tile(int M, int N, int epi, int batch, int budget, double* cost_out = n
 // gates, addends, column segments or SwiGLU pairing.
 int round_split_cols(const GemmParams& p, int epi) {
   if (epi != kEpiAlphaBeta || p.cu_budget != 0 || p.grid_cap != 0 || p.cp_blocks != 0 || p.a_slice_rows != 0 ||
-      p.n_seg != 0 || p.n_add_list != 0 || p.n_add_strided != 0 || p.acc_in || p.acc_out || p.M <= 0 ||
+      p.n_seg != 0 || p.n_add_list != 0 || p.n_add_strided != 0 || p.acc_in || p.acc_out || p.wrap_col != 0 ||
+      p.M <= 0 ||
       p.N <= 256 || p.batch < 1)
     return 0;
   double whole = 0.0;
@@ -1382,6 +1387,26 @@ hipError_t launch_gemm(const GemmParams& p, int dtype, int layout, int epi, hipS
       tail.a = static_cast<const char*>(p.a) + (p.wrap_a ? back : int64_t(p.wrap_row)) * p.lda * eb;
       tail.d = p.d + back * p.ldd;
       if (p.c) tail.c = p.c + back * p.ldc;
+      if (hipError_t e = launch_gemm(head, dtype, layout, epi, s); e != hipSuccess) return e;
+      return launch_gemm(tail, dtype, layout, epi, s);
+    }
+  }
+  if (p.wrap_col > 0) {
+    if (p.wrap_col >= p.N || p.wrap_col % 256 != 0 || p.wrap_back_col % 256 != 0 ||
+        p.wrap_back_col < p.wrap_col || p.N % 256 != 0 || p.batch != 1 || p.a_slice_rows != 0 ||
+        p.wrap_row != 0 || sw || p.n_add_list + p.n_add_strided != 0 || p.n_seg != 0)
+      return hipErrorInvalidValue;
+    if (!dma_path(p, eb, kn)) {
+      // the register-staged kernel takes no wrap: the two stretches as two launches
+      GemmParams head = p, tail = p;
+      head.wrap_col = tail.wrap_col = 0;
+      head.N = p.wrap_col;
+      tail.N = p.N - p.wrap_col;
+      const int64_t back = int64_t(p.wrap_col) - p.wrap_back_col;   // the tail's first output column, from d
+      tail.b = static_cast<const char*>(p.b) + (kn ? int64_t(p.wrap_col) * eb : int64_t(p.wrap_col) * p.ldb * eb);
+      tail.d = p.d + back;
+      if (p.c) tail.c = p.c + back;
+      if (p.bias) tail.bias = p.bias + back;
       if (hipError_t e = launch_gemm(head, dtype, layout, epi, s); e != hipSuccess) return e;
       return launch_gemm(tail, dtype, layout, epi, s);
     }

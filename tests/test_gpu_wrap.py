@@ -97,3 +97,45 @@ def test_rs_wrapping_runs(case):
                 assert_parity(got[rows], ref[rows], f"{case.name}/rank {r}/flags {flags}/block {blk}")
             outs.append(d.cpu())
         assert all(torch.equal(o, outs[0]) for o in outs), f"{case.name}/rank {r}"
+
+
+# Rotating B: a run of delivered B column slices that passes slice P-1 is one
+# launch whose tiles past the wrap write D's and C's columns P * n earlier
+# (slices of a multiple of 256 columns).
+ROTB_CASES = [
+    W.AgCase("wrap_rotb_bf16_p4", M=4 * 64, N=4 * 256, K=256, P=4, dist="u11", alpha=0.5, beta=1.0),
+    W.AgCase("wrap_rotb_e4m3_p4", M=4 * 128, N=4 * 256, K=512, P=4, dtype="e4m3", dist="n05", c_dist="n01"),
+    W.AgCase("wrap_rotb_bf16_p4_kn", M=4 * 64, N=4 * 256, K=192, P=4, b_layout="kn", dist="u11", beta=-1.0),
+]
+
+
+@pytest.mark.parametrize("case", ROTB_CASES, ids=lambda c: c.name)
+def test_ag_rotb_wrapping_runs(case):
+    inp = W.ag_rotb_inputs(case)
+    a = dev(inp["a"])
+    bs = [dev(x) for x in inp["b_slices"]]
+    c = dev(inp["c"]) if inp["c"] is not None else None
+
+    def call(rank, flags, groups):
+        d = bf16_empty(case.M, case.N)
+        tp.stage_ag(a, bs, c, d, M=case.M, N=case.N, K=case.K, rank=rank,
+                    dtype=tp.E4M3 if case.dtype == "e4m3" else tp.BF16,
+                    b_layout=tp.B_KN if case.b_layout == "kn" else tp.B_NK,
+                    alpha=case.alpha, beta=case.beta, flags=flags, groups=groups, schedule=tp.ROTATE_B)
+        torch.cuda.synchronize()
+        return d
+
+    for r in range(case.P):
+        ref = oracle.gemm_ag_rotb(inp["a"], inp["b_slices"], inp["c"], case.alpha, case.beta, r, case.dtype,
+                                  case.b_layout)
+        say(f"wrap rotb: {case.name} rank {r} unstaged")
+        base = call(r, tp.UNSTAGED, 0)
+        assert_parity(host_f64(base), ref, f"{case.name}/rank {r}/unstaged")
+        base = base.cpu()
+        for groups in (0, 1, 2, 3):
+            for label, flags in (("default", 0), ("eager", tp.NO_GRAPH), ("graph", tp.FORCE_GRAPH),
+                                 ("serial", tp.SERIAL_STAGES), ("in place", tp.NO_COPY)):
+                say(f"wrap rotb: {case.name} rank {r} groups {groups} {label}")
+                d = call(r, flags, groups)
+                assert_parity(host_f64(d), ref, f"{case.name}/rank {r}/groups {groups}/{label}")
+                assert torch.equal(d.cpu(), base), f"{case.name}/rank {r}/groups {groups}/{label}"
