@@ -788,6 +788,10 @@ tpg_status enqueue_ag_rotb(Ctx& cx, const tpg_ag_args& a, const Launch& L) {
     q.d = D + s * n;
     q.c = C ? C + s * n : nullptr;
     q.cu_budget = cus;
+    // the persistent grid too (e4m3 8192 x 1024 x 8192 in 8 slices of 128
+    // columns, ranks 1 and 4: 96-97 / 94-95 us against 100 / 97-98 uncapped;
+    // ranks 0 and 7 alike within noise)
+    q.grid_cap = cus;
     if (wrap_col > 0) {    // slices past P-1: D's and C's columns P * n earlier
       q.wrap_col = wrap_col;
       q.wrap_back_col = static_cast<int>(P * n);
