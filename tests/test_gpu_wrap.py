@@ -139,3 +139,69 @@ def test_ag_rotb_wrapping_runs(case):
                 d = call(r, flags, groups)
                 assert_parity(host_f64(d), ref, f"{case.name}/rank {r}/groups {groups}/{label}")
                 assert torch.equal(d.cpu(), base), f"{case.name}/rank {r}/groups {groups}/{label}"
+
+
+def random_plans(seed, count):
+    """Seeded stage plans: slice heights that take the one-launch wrap (256,
+    512) and the per-stretch launches (128, 320), any rank and grouping."""
+    rng = np.random.default_rng(seed)
+    plans = []
+    for i in range(count):
+        P = int(rng.choice([2, 3, 4, 5, 8]))
+        m = int(rng.choice([128, 256, 320, 512]))
+        dtype = str(rng.choice(["bf16", "e4m3"]))
+        layout = "nk" if dtype == "e4m3" else str(rng.choice(["nk", "kn"]))
+        K = int(rng.choice([256, 384])) * (2 if dtype == "e4m3" else 1)
+        N = int(rng.choice([264, 512]))
+        rank = int(rng.integers(0, P))
+        groups = int(rng.integers(1, P)) if P > 1 else 1
+        plans.append((f"plan{seed}_{i}", P, m, dtype, layout, K, N, rank, groups))
+    return plans
+
+
+@pytest.mark.parametrize("plan", random_plans(7, 16), ids=lambda p: p[0])
+def test_ag_random_stage_plans(plan):
+    name, P, m, dtype, layout, K, N, rank, groups = plan
+    case = W.AgCase(name, M=P * m, N=N, K=K, P=P, rank=rank, dtype=dtype, b_layout=layout,
+                    dist="n05" if dtype == "e4m3" else "u11", c_dist="n01" if dtype == "e4m3" else "u11",
+                    alpha=0.75, beta=1.0)
+    inp = W.ag_inputs(case)
+    ref = oracle.gemm_ag(inp["a_slices"], inp["b"], inp["c"], case.alpha, case.beta, rank, dtype, layout)
+    apart = [dev(s) for s in inp["a_slices"]]
+    whole = dev(np.concatenate(inp["a_slices"], axis=0))
+    joined = [whole[s * m:(s + 1) * m] for s in range(P)]
+    b, c = dev(inp["b"]), dev(inp["c"])
+    say(f"random plan: {name} P={P} m={m} {dtype}/{layout} K={K} N={N} rank={rank} groups={groups} unstaged")
+    base = ag_call(case, apart, b, c, rank, tp.UNSTAGED, 0)
+    assert_parity(host_f64(base), ref, f"{name}/unstaged")
+    base = base.cpu()
+    for label, slices, flags in (("copied", apart, 0), ("graph", apart, tp.FORCE_GRAPH),
+                                 ("in place joined", joined, tp.NO_COPY), ("serial", apart, tp.SERIAL_STAGES)):
+        say(f"random plan: {name} {label}")
+        d = ag_call(case, slices, b, c, rank, flags, groups)
+        assert_parity(host_f64(d), ref, f"{name}/{label}")
+        assert torch.equal(d.cpu(), base), f"{name}/{label}"
+
+
+@pytest.mark.parametrize("plan", random_plans(11, 10), ids=lambda p: p[0])
+def test_rs_random_stage_plans(plan):
+    name, P, m, _, layout, K, N, rank, groups = plan
+    case = W.RsCase(name, M=P * m, N=N, K=K, P=P, rank=rank, b_layout=layout, std=0.5, alpha=1.25)
+    inp = W.rs_inputs(case)
+    a, b = dev(inp["a"]), dev(inp["b"])
+    inc = [dev(x) if x is not None else None for x in inp["incoming"]]
+    ref = oracle.gemm_rs(inp["a"], inp["b"], inp["incoming"], case.alpha, rank, P, layout)
+    outs = []
+    for flags, g in ((tp.UNSTAGED, 0), (0, 0), (tp.FORCE_GRAPH, groups), (tp.NO_COPY, groups),
+                     (tp.SERIAL_STAGES, groups)):
+        say(f"random plan: {name} P={P} m={m} {layout} K={K} N={N} rank={rank} flags={flags} groups={g}")
+        d = bf16_empty(case.M, case.N)
+        tp.stage_rs(a, b, inc, d, M=case.M, N=case.N, K=case.K, P=P, rank=rank,
+                    b_layout=tp.B_KN if layout == "kn" else tp.B_NK, alpha=case.alpha, flags=flags, groups=g)
+        torch.cuda.synchronize()
+        got = host_f64(d)
+        for blk in range(P):
+            rows = slice(blk * m, (blk + 1) * m)
+            assert_parity(got[rows], ref[rows], f"{name}/flags {flags}/block {blk}")
+        outs.append(d.cpu())
+    assert all(torch.equal(o, outs[0]) for o in outs), name
