@@ -641,8 +641,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // (K, N)-layout B tiles: chunk swizzle of a k-row and the transposing
-// fragment read (ds_read_b64_tr_b16, two per 8-k fragment).
-__device__ __forceinline__ int kn_swz(int kr) { return (kr & 7) << 1; }
+// fragment read (ds_read_b64_tr_b16, two per 8-k fragment). Each half-wave
+// of a transposing read takes 4 consecutive k-rows (k mod 4 = 0..3) by 4
+// consecutive 16-byte chunks (chunk mod 4 = 0..3), and every row starts on
+// the same bank (rows of 256 or 512 bytes): XOR-ing the chunk with
+// (k mod 4) * 4 puts those 16 chunks on 16 distinct chunk positions mod 16,
+// i.e. all 64 banks once. (With (k mod 8) * 2 two of them shared each
+// position: the (K, N) GEMM at the FFN's first-GEMM shape counted 6x the
+// bank-conflict cycles of the (N, K) one.)
+__device__ __forceinline__ int kn_swz(int kr) { return (kr & 3) << 2; }
 
 template <int BN>
 __device__ __forceinline__ bf16x8_t load_kn_frag(const uint8_t* lb, int kr, int n) {
