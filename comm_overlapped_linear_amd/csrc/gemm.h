@@ -56,6 +56,11 @@ struct GemmParams {
   // kernel, alpha/beta epilogue, no addends.)
   int wrap_col;
   int wrap_back_col;
+  // set by the launcher: a batched launch of 8k batches gives each XCD
+  // whole batches (workgroup i, in dispatch order, takes batch i mod 8 of
+  // its group of 8 and that batch's tiles in row-major order), so the tiles
+  // an XCD runs at once share their A rows and B columns
+  int batch_xcd;
   // batched launch (blockIdx.y = batch index): element strides between the
   // operands of consecutive batches (0 = shared); C and addends unbatched
   int batch;                   // >= 1

@@ -99,7 +99,7 @@ __device__ __forceinline__ int b_col(int tn, int i, int N) {
   return u < nh ? u + half * nh : -1;
 }
 
-// Operand pointers of batch blockIdx.y of a batched launch. (The parameter
+// Operand pointers of batch z of a batched launch. (The parameter
 // block itself stays in the kernel-argument segment: a private copy would be
 // spilled to scratch because the epilogue indexes add_list dynamically.)
 struct BatchPtrs {
@@ -110,8 +110,7 @@ struct BatchPtrs {
 };
 
 template <int EB>
-__device__ __forceinline__ BatchPtrs batch_ptrs(const GemmParams& p) {
-  const int64_t z = blockIdx.y;
+__device__ __forceinline__ BatchPtrs batch_ptrs(const GemmParams& p, int64_t z) {
   BatchPtrs q;
   q.a = static_cast<const uint8_t*>(p.a) + z * p.a_bstride * EB;
   q.b = static_cast<const uint8_t*>(p.b) + z * p.b_bstride * EB;
@@ -405,7 +404,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const BatchPtrs&
 
 template <typename Op, int BM, int BN, bool KN, bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmParams p) {
-  const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
+  const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p, blockIdx.y);
   constexpr int WM = 2, WN = 2;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -754,7 +753,6 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
     copy_job(p, copy_first ? static_cast<int>(blockIdx.x) : wg - tile_grid);
     return;
   }
-  const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p);
   constexpr int NW = WM * WN;                  // waves: 4 (one per SIMD) or 8 (two per SIMD)
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -769,8 +767,9 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   static_assert(KSUB >= 1 && STAGES >= 2 && (STAGES - 1) * INSTR <= 63, "pipeline shape");
   static_assert(!KN || (Op::kElemBytes == 2 && ROWB == 128), "(K, N) B tiles: bf16, 64 k-rows per K-step");
   // (K, N) layout: the B tile sits in LDS as [64 k-rows][BN n] exactly as in
-  // memory; 16-byte chunks of a k-row are XOR-swizzled by (k-row mod 8) so the
-  // transposing fragment reads of four consecutive k-rows hit distinct banks
+  // memory; 16-byte chunks of a k-row are XOR-swizzled by (k-row mod 4) * 4 so
+  // the transposing fragment reads of four consecutive k-rows hit distinct
+  // banks (kn_swz)
   constexpr int CPRB = BN * 2 / 16;            // chunks per k-row
   constexpr int RPIB = 64 / CPRB;              // k-rows per DMA instruction
   // Contraction-major A (AT): the A tile sits in LDS as [64 k-rows][BM m],
@@ -797,6 +796,17 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   const int ntm = (p.M + BM - 1) / BM;
   const int ntn = SWIGLU ? ((p.N >> 1) + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int ntiles = ntm * ntn;
+  // the batch and first tile of this workgroup: blockIdx (y, x), or whole
+  // batches per XCD (consecutive workgroups in dispatch order go to
+  // consecutive XCDs)
+  int64_t bz = blockIdx.y;
+  int wgt = wg;
+  if (p.batch_xcd) {
+    const int64_t linear = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+    bz = (linear / (8 * int64_t(ntiles))) * 8 + linear % 8;
+    wgt = static_cast<int>((linear / 8) % ntiles);
+  }
+  const BatchPtrs bp = batch_ptrs<Op::kElemBytes>(p, bz);
 
   const uint8_t* A = bp.a;
   const uint8_t* Bp = bp.b;
@@ -817,7 +827,12 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   static_assert(!GATE || !AT, "gated launches have row-major A");
   auto run_tile = [&](int vt) {
   int tm, tn;
-  tile_of_block(vt, ntiles, ntm, p.tile_gm, tm, tn);
+  if (p.batch_xcd) {            // row-major within the batch: an XCD's round is whole tile-rows
+    tm = vt / ntn;
+    tn = vt % ntn;
+  } else {
+    tile_of_block(vt, ntiles, ntm, p.tile_gm, tm, tn);
+  }
   const int m0 = tm * BM;
   // gated launches: the slice holding this tile's rows, and the counters of
   // its delivery slot (nullptr: no waits)
@@ -1068,9 +1083,10 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_dma_kernel(con
   store_tile<BM, BN, WM, WN, SWIGLU, AT>(p, bp, acc, smem, tm_out, tn_out);   // ends with a barrier: LDS free
   };
   if constexpr (persistent_tiles<Op, BM, BN, AT>()) {
-    for (int vt = wg; vt < ntiles; vt += tile_grid) run_tile(vt);
+    // (batched launches have one workgroup per tile: one trip, at wgt)
+    for (int vt = wgt; vt < ntiles; vt += tile_grid) run_tile(vt);
   } else {
-    run_tile(wg);
+    run_tile(wgt);
   }
 }
 
@@ -1132,6 +1148,7 @@ hipError_t launch_dma_tile(const GemmParams& p_in, hipStream_t s) {
   if (p.grid_cap >= 8 && p.batch == 1 && persistent_tiles<Op, BM, BN, AT>()) grid = std::min(grid, p.grid_cap & ~7);
   if (p.cp_blocks > 0 && p.batch != 1) return hipErrorInvalidValue;   // a copy job needs a single batch
   p.tile_gm = p.batch == 1 ? group_rows((p.M + BM - 1) / BM, nout_tiles, BM, BN, grid) : 0;
+  p.batch_xcd = (p.batch > 1 && p.batch % 8 == 0 && p.cp_blocks == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3(grid + p.cp_blocks, p.batch), dim3(nt), smem, s, p);
   return hipGetLastError();
 }

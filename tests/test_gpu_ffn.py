@@ -22,7 +22,10 @@ def run_ffn(case, inp, flags):
 
 
 FFN_CASES = W.SMALL_FFN + [W.FfnCase("ffn_mid_ragged", B=9, T=32, D=264, k=3, P=4, rank=2, big_bias=True),
-                           W.FfnCase("ffn_dma_ragged", B=5, T=16, D=192, k=2, P=4, rank=1, affine=True)]
+                           W.FfnCase("ffn_dma_ragged", B=5, T=16, D=192, k=2, P=4, rank=1, affine=True),
+                           # 8 slots of a second GEMM with 2 x 2 tiles of 256 x 256 each: the batched launch
+                           # gives each XCD whole slots, so every tile must pair with its own slot
+                           W.FfnCase("ffn_eight_slots_many_tiles", B=64, T=64, D=512, k=2, P=8, affine=True)]
 
 
 @pytest.mark.parametrize("case", FFN_CASES, ids=lambda c: c.name)
